@@ -1,0 +1,230 @@
+"""Benchmark of the Mamba-2 mixer hot path on one MI355X.
+
+One step = one pass of the whole hot path on synthetic Ultra-shaped layers:
+  prefill  batch 1 x 8192 tokens (256 heads, head_dim 64, d_state 128, 8 groups,
+           chunk 128): ssd_conv1d_fwd over the 18432 x|B|C channels, then
+           ssd_chunk_scan on views into the conv output -> y (bf16) + fp32 final state;
+  decode   batch 64, one token: ssd_conv1d_update, then ssd_state_update in place
+           on the (64, 256, 64, 128) fp32 state.
+All inputs are resident in HBM before timing.  Every kernel launch is bracketed
+by HIP events on the launch stream; averages per kernel feed the roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints ONE JSON line.  value = prefill tokens/s per layer (conv + scan time);
+the decode state-update GB/s and its roofline fraction sit under "decode".
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16, published
+METRIC = "SSD prefill tokens/s per layer + decode state-update GB/s (frac. of roofline)"
+
+
+def scan_bytes(d):
+    """Algorithmic HBM bytes of one chunk-scan launch: read x, B, C, dt once, write y and
+    the final fp32 state once (no initial state in this workload)."""
+    per_token = 2 * (d.nheads * d.head_dim) * 2 + 2 * d.ngroups * d.d_state * 2 + d.nheads * 2
+    state = d.batch * d.nheads * d.head_dim * d.d_state * 4
+    return d.batch * d.seqlen * per_token + state
+
+
+def scan_flops(d):
+    """Algorithmic flops of the chunked scan (dense forms): C.B^T per group and chunk,
+    the masked scores times x, C.H and the chunk state, per head."""
+    Q, P, N, H, G = d.chunk, d.head_dim, d.d_state, d.nheads, d.ngroups
+    per_token = 2 * H * P * (Q + 2 * N) + 2 * G * Q * N
+    return d.batch * d.seqlen * per_token
+
+
+def conv_bytes(d, L):
+    """conv in + out (bf16) + taps/bias + conv state out."""
+    return d.batch * L * d.conv_dim * 2 * 2 + d.conv_dim * 5 * 2 + d.batch * d.conv_dim * 4 * 2
+
+
+def update_bytes(d):
+    """State read + write (fp32) + x, B, C, dt in and y out (bf16) for one token."""
+    st = d.batch * d.nheads * d.head_dim * d.d_state * 4 * 2
+    io = d.batch * (d.nheads * d.head_dim * 2 + 2 * d.ngroups * d.d_state + d.nheads + d.nheads * d.head_dim) * 2
+    return st + io
+
+
+def conv_update_bytes(d):
+    return d.batch * d.conv_dim * (2 + 2 + 4 * 2 * 2) + d.conv_dim * 5 * 2
+
+
+def cpu_baseline(orc, inp, d, n_heads=256):
+    """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
+    over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
+    to all heads."""
+    import numpy as np
+    import torch
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+    u, w, bias = f64(inp["xbc"]), f64(inp["w"]), f64(inp["bias"])
+    t0 = time.perf_counter()
+    v, _ = orc.conv1d_fwd(u, w, bias, None)
+    t_conv = time.perf_counter() - t0
+    v = torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+    I, GN, P, N = d.nheads * d.head_dim, d.ngroups * d.d_state, d.head_dim, d.d_state
+    hpg = d.nheads // d.ngroups
+    heads = [(i * d.nheads) // n_heads for i in range(n_heads)]
+    L = d.seqlen
+    dt, A, D = f64(inp["dt"]), f64(inp["A"]), f64(inp["D"])
+    xs = np.ascontiguousarray(np.stack([v[0, :, h * P:(h + 1) * P] for h in heads], 1))[None]
+    # one scan call over the sampled heads, each given its own group's B/C (G = sampled heads)
+    Bs = np.ascontiguousarray(np.stack([v[0, :, I + (h // hpg) * N:I + (h // hpg + 1) * N] for h in heads], 1))[None]
+    Cs = np.ascontiguousarray(np.stack([v[0, :, I + GN + (h // hpg) * N:I + GN + (h // hpg + 1) * N]
+                                        for h in heads], 1))[None]
+    t0 = time.perf_counter()
+    orc.scan(xs, Bs, Cs, dt[:, :, heads], A[heads], D[heads], None)
+    t_scan = time.perf_counter() - t0
+    t_layer = t_conv + t_scan * d.nheads / n_heads
+    return {"value": L * d.batch / t_layer, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle: conv over all {d.conv_dim} channels x {L} tokens ({t_conv:.2f} s) + "
+                      f"scan of {n_heads}/{d.nheads} heads x {L} tokens ({t_scan:.2f} s), scan time scaled "
+                      f"to {d.nheads} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU leg); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_conv1d_amd import ssd
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, decode_state, decode_tokens, mixer_inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dp = WORKLOADS["prefill_ultra_8k"]
+    dd = WORKLOADS["decode_ultra_b64"]
+    print(f"[bench] generating inputs: prefill {dp}, decode {dd}", file=sys.stderr, flush=True)
+    pin = mixer_inputs(dp, 1002, device=dev)
+    v = torch.empty(dp.batch, dp.seqlen, dp.conv_dim, dtype=dp.dtype, device=dev)
+    cso = torch.empty(dp.batch, dp.conv_dim, 4, dtype=dp.dtype, device=dev)
+    fin = torch.empty(dp.batch, dp.nheads, dp.head_dim, dp.d_state, device=dev)
+    y = torch.empty(dp.batch, dp.seqlen, dp.nheads, dp.head_dim, dtype=dp.dtype, device=dev)
+    x, Bm, Cm = ssd.split_xbc(v, dp.nheads, dp.head_dim, dp.ngroups, dp.d_state)
+
+    dst = decode_state(dd, 1001, device=dev)
+    dpar = mixer_inputs(dd.with_(seqlen=1), 1001, device=dev)
+    ntok = 16
+    dtok = decode_tokens(dd, 1011, ntok, device=dev)
+    state = dst["state"]
+    cstate = dst["conv_state"]
+    u = torch.empty(dd.batch, dd.conv_dim, dtype=dd.dtype, device=dev)
+    xu, Bu, Cu = ssd.split_xbc(u, dd.nheads, dd.head_dim, dd.ngroups, dd.d_state)
+    yd = torch.empty(dd.batch, dd.nheads, dd.head_dim, dtype=dd.dtype, device=dev)
+    torch.cuda.synchronize()
+
+    names = ["conv1d_fwd", "chunk_scan", "conv1d_update", "state_update"]
+
+    def step(i, ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record()
+        mark(0)
+        ssd.ssd_conv1d_fwd(pin["xbc"], pin["w"], pin["bias"], None, cso, out=v)
+        mark(1)
+        ssd.ssd_chunk_scan(x, Bm, Cm, pin["dt"], pin["A"], pin["D"], None, fin, y=y, chunk=dp.chunk)
+        mark(2)
+        k = i % ntok
+        ssd.ssd_conv1d_update(dtok["xbc"][k], dpar["w"], dpar["bias"], cstate, out=u)
+        mark(3)
+        ssd.ssd_state_update(state, xu, Bu, Cu, dtok["dt"][k], dpar["A"], dpar["D"], y=yd)
+        mark(4)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e-3)  # seconds
+    avg = {n: sum(t) / len(t) for n, t in per.items()}
+    gpu_step = sum(avg.values())
+
+    prefill_s = avg["conv1d_fwd"] + avg["chunk_scan"]
+    tok_s = dp.batch * dp.seqlen / prefill_s
+    sb = scan_bytes(dp)
+    scan_gbs = sb / avg["chunk_scan"] / 1e9
+    sf = scan_flops(dp)
+    ub = update_bytes(dd)
+    upd_gbs = ub / avg["state_update"] / 1e9
+    cb = conv_bytes(dp, dp.seqlen)
+    cub = conv_update_bytes(dd)
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_ultra_8k + decode_ultra_b64",
+                   "prefill": {"batch": dp.batch, "seqlen": dp.seqlen, "nheads": dp.nheads, "head_dim": dp.head_dim,
+                               "d_state": dp.d_state, "ngroups": dp.ngroups, "chunk": dp.chunk,
+                               "conv_dim": dp.conv_dim, "conv_width": 4},
+                   "decode": {"batch": dd.batch, "tokens_per_step": 1, "nheads": dd.nheads,
+                              "head_dim": dd.head_dim, "d_state": dd.d_state, "ngroups": dd.ngroups,
+                              "state": "fp32 (64, 256, 64, 128)"}},
+        "kernels_us": {n: avg[n] * 1e6 for n in names},
+        "gpu_ms_per_step": gpu_step * 1e3,
+        "prefill": {"tokens_per_s": tok_s, "ms": prefill_s * 1e3,
+                    "scan_tokens_per_s": dp.batch * dp.seqlen / avg["chunk_scan"],
+                    "scan_GBps": scan_gbs, "scan_TFLOPs": sf / avg["chunk_scan"] / 1e12,
+                    "scan_mfma_frac": sf / avg["chunk_scan"] / 1e12 / MFMA_BF16_PEAK_TFS,
+                    "conv_GBps": cb / avg["conv1d_fwd"] / 1e9,
+                    "conv_frac": cb / avg["conv1d_fwd"] / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "chunk_scan", "achieved": scan_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": sb},
+        "decode": {"value": upd_gbs, "unit": "GB/s", "kernel": "state_update",
+                   "frac": upd_gbs / HBM_PEAK_GBS, "tokens_per_s": dd.batch / avg["state_update"],
+                   "step_tokens_per_s": dd.batch / (avg["state_update"] + avg["conv1d_update"]),
+                   "algorithmic_bytes_per_launch": ub,
+                   "roofline": {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": upd_gbs / HBM_PEAK_GBS, "traffic": None},
+                   "conv_update_GBps": cub / avg["conv1d_update"] / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu_in = {k: pin[k].cpu() for k in ("xbc", "w", "bias", "dt", "A", "D")}
+        out["cpu_baseline"] = cpu_baseline(oracle.load(), cpu_in, dp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

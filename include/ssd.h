@@ -1,0 +1,163 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 selective-SSM mixer hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, all asynchronous on the caller's HIP stream:
+ *   ssd_conv1d_fwd     causal depthwise conv1d (width 4) + SiLU over the packed
+ *                      x|B|C channels of a prefill, with a conv-state halo
+ *   ssd_conv1d_update  the same conv for one new token per sequence (decode)
+ *   ssd_chunk_scan     the SSD chunked scan of a prefill: y and the fp32 final
+ *                      state from x, dt, A, B, C, D and an optional initial state
+ *   ssd_state_update   the single-token selective state update (decode)
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
+ *       (state recurrence and output), "状态契约" (state shapes, decode has
+ *       seqlen 1 and never scans the cumulative context).
+ *  [P2] walk-through of NVIDIA-Nemotron-Labs-Teacher-Chat modeling_nemotron_h.py:
+ *       "Prefill 阶段" (causal conv keeps the last 4 conv inputs; 128-token
+ *       chunked scan returns the final state, copied into the cache), "Decode
+ *       阶段" (conv-state roll; in-place state update), fp32 state cache.
+ *  [P3] "MAX 平台 Nemotron-H 混合架构解析": 4.5 (conv_dim = H*P + 2*G*N, channel
+ *       order x | B | C), 5.4 (channels-last conv and in-place SSD scan that reads
+ *       the initial state and writes the final state to the same slot).
+ *
+ * Semantics (fp32 arithmetic on the device; g(h) = h / (H/G)):
+ *   conv:   v[b,t,c] = silu(bias[c] + sum_{k<4} w[c,k] * u~[b, t-3+k, c]), where
+ *           u~ is the input for t >= 0 and conv_state_in[b, c, 4+t] for t in -3..-1;
+ *           conv_state_out[b,c,k] = u~[b, L-4+k, c]  (the last 4 inputs).
+ *   scan:   per (b,h,p), S = init[b,h,p,:] (or 0); for each token t:
+ *             S = exp(dt*A[h]) * S + dt * B[b,t,g(h),:] * x[b,t,h,p]
+ *             y[b,t,h,p] = <S, C[b,t,g(h),:]> + D[h] * x[b,t,h,p]
+ *           final[b,h,p,:] = S.  The scan reaches this result by 128-token (or
+ *           `chunk`) blocks; it equals the recurrence up to rounding.
+ *   update: the scan with one token, state updated in place.
+ *
+ * Ownership: the caller allocates and frees every buffer (device memory);
+ * the library allocates nothing and holds no state between calls, so calls
+ * on different streams are independent.  Nothing synchronises.
+ * Errors: every argument is checked on the host before anything is launched;
+ * a call that returns an error has launched nothing and written nothing.
+ * A launch failure returns SSD_ERR_HIP.  No call throws.
+ * Buffers must not overlap unless marked "may alias".
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* negative size, H % G != 0, stride too small, ... */
+    SSD_ERR_DTYPE = 3,       /* unknown dtype code */
+    SSD_ERR_ALIGN = 4,       /* pointer not 16-byte aligned / stride not a multiple of 16 bytes */
+    SSD_ERR_UNSUPPORTED = 5, /* size outside the compiled instantiations */
+    SSD_ERR_WORKSPACE = 6,   /* workspace too small */
+    SSD_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} ssd_status_t;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Sizes of one mixer layer.  act_dtype is the element type of the conv input,
+ * taps, bias, conv state and output, and of x, B, C and dt.  y_dtype is the
+ * element type of y.  A, D and the SSM state are always fp32. */
+typedef struct {
+    int64_t batch;      /* B >= 0 */
+    int64_t seqlen;     /* L >= 0 (prefill calls; the one-token calls ignore it) */
+    int32_t nheads;     /* H */
+    int32_t head_dim;   /* P: 16, 32, 64 or 128 */
+    int32_t ngroups;    /* G, H % G == 0 */
+    int32_t d_state;    /* N: 16, 32, 64 or 128 */
+    int32_t conv_width; /* K: must be 4 */
+    int32_t act_dtype;  /* ssd_dtype_t */
+    int32_t y_dtype;    /* ssd_dtype_t */
+} ssd_dims_t;
+
+/* Conv channels CD = H*P + 2*G*N. */
+int64_t ssd_conv_dim(const ssd_dims_t* d);
+
+/*
+ * Prefill conv ([P2] "Prefill 阶段"; [P3] 5.4, channels last, no transposes).
+ *  xbc            [B, L, CD] act dtype; token rows xbc_row_stride elements apart
+ *                 (>= CD, multiple of 8 elements), batch rows L*xbc_row_stride apart.
+ *                 May be a view into a wider in_proj output.
+ *  w              [CD, 4]  act dtype; w[c,3] multiplies the newest token.
+ *  bias           [CD]     act dtype, or NULL (no bias).
+ *  conv_state_in  [B, CD, 4] act dtype, or NULL (zeros: a fresh sequence).
+ *  conv_state_out [B, CD, 4] act dtype, or NULL (not written).  May alias
+ *                 conv_state_in (in-place cache update).
+ *  out            [B, L, CD] contiguous, act dtype.  Must not alias xbc.
+ * CD must be a multiple of 8.  L = 0 copies the state through.
+ */
+ssd_status_t ssd_conv1d_fwd(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                            const void* w, const void* bias, const void* conv_state_in,
+                            void* conv_state_out, void* out, hipStream_t stream);
+
+/*
+ * One-token conv update ([P2] "Decode 阶段": roll the window by one, the new
+ * input enters the last slot, then convolve).
+ *  xbc        [B, CD] act dtype, rows xbc_row_stride elements apart (>= CD).
+ *  w, bias    as ssd_conv1d_fwd.
+ *  conv_state [B, CD, 4] act dtype, updated in place.
+ *  out        [B, CD] contiguous act dtype.
+ */
+ssd_status_t ssd_conv1d_update(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                               const void* w, const void* bias, void* conv_state, void* out,
+                               hipStream_t stream);
+
+/* Workspace bytes ssd_chunk_scan needs for these sizes (currently always 0). */
+size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
+
+/*
+ * SSD chunked scan of a prefill ([P1] section 1 for the recurrence; [P2]
+ * "Prefill 阶段" for the 128-token chunks and the final state; [P3] 5.4 for
+ * the in-place initial/final state).
+ *  chunk        64, 128 or 256 (tokens per block; the result does not depend on it
+ *               beyond rounding).  L need not be a multiple of chunk.
+ *  x            x[b,t,h,p] at x[(b*L + t)*x_row_stride + h*P + p], act dtype.
+ *  B, C         B[b,t,g,n] at B[(b*L + t)*bc_row_stride + g*N + n] (same for C).
+ *               x, B and C may be views into the conv output (row stride CD).
+ *  dt           [B, L, H] act dtype, already positive (no bias, no softplus).
+ *  A            [H] fp32 (negative decay rates).  D: [H] fp32 or NULL (no skip).
+ *  init_state   [B, H, P, N] fp32, or NULL (zeros).
+ *  final_state  [B, H, P, N] fp32, or NULL (not written).  May alias init_state.
+ *  y            [B, L, H, P] contiguous, y dtype.
+ *  workspace    may be NULL when ssd_chunk_scan_workspace_size() is 0.
+ * Row strides are in elements: >= the row's extent, multiples of 8 (bf16) or 4 (fp32).
+ */
+ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
+                            const void* x, int64_t x_row_stride,
+                            const void* B, const void* C, int64_t bc_row_stride,
+                            const void* dt, const float* A, const float* D,
+                            const float* init_state, float* final_state, void* y,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Single-token selective state update, in place ([P2] "Decode 阶段"; [P1]
+ * "状态契约": one token per call, no scan length).
+ *  state  [B, H, P, N] fp32, updated in place.
+ *  x      x[b,h,p] at x[b*x_row_stride + h*P + p]; B, C: B[b,g,n] at
+ *         B[b*bc_row_stride + g*N + n]; act dtype.
+ *  dt     [B, H] act dtype.  A [H] fp32; D [H] fp32 or NULL.
+ *  y      [B, H, P] contiguous, y dtype.
+ */
+ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state,
+                              const void* x, int64_t x_row_stride,
+                              const void* B, const void* C, int64_t bc_row_stride,
+                              const void* dt, const float* A, const float* D, void* y,
+                              hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* ssd_status_string(ssd_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

@@ -1,0 +1,140 @@
+// libssd C ABI: argument validation on the host, then one launch per call.
+// All checks run before anything is launched, so a failed call has no effect.
+#include "../../include/ssd.h"
+#include "ssd_kernels.h"
+
+#include <stdint.h>
+
+namespace {
+
+using ssd::Dt;
+
+bool valid_dtype(int32_t d) { return d == SSD_F32 || d == SSD_BF16; }
+int elem_size(int32_t d) { return d == SSD_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2_16_128(int32_t v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+// row stride (elements) keeps every row start 16-byte aligned
+bool stride_ok(int64_t stride, int32_t dt) { return (stride * elem_size(dt)) % 16 == 0; }
+
+ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
+    if (!d) return SSD_ERR_NULL;
+    if (!valid_dtype(d->act_dtype) || !valid_dtype(d->y_dtype)) return SSD_ERR_DTYPE;
+    if (d->batch < 0 || (need_seqlen && d->seqlen < 0)) return SSD_ERR_SHAPE;
+    if (d->nheads <= 0 || d->head_dim <= 0 || d->ngroups <= 0 || d->d_state <= 0) return SSD_ERR_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
+    if (d->conv_width != 4) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status_t hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t ssd_conv_dim(const ssd_dims_t* d) {
+    if (!d) return -1;
+    return static_cast<int64_t>(d->nheads) * d->head_dim + 2LL * d->ngroups * d->d_state;
+}
+
+const char* ssd_status_string(ssd_status_t s) {
+    switch (s) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid shape or stride";
+        case SSD_ERR_DTYPE: return "invalid dtype";
+        case SSD_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case SSD_ERR_UNSUPPORTED: return "size not supported by the compiled kernels";
+        case SSD_ERR_WORKSPACE: return "workspace too small";
+        case SSD_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+ssd_status_t ssd_conv1d_fwd(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                            const void* w, const void* bias, const void* conv_state_in,
+                            void* conv_state_out, void* out, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    const int64_t CD = ssd_conv_dim(d);
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!xbc || !w || !out)) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (tokens && xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, w, bias, conv_state_in, static_cast<const void*>(conv_state_out),
+                          static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::ConvFwdArgs a{xbc, xbc_row_stride, w, bias, conv_state_in, conv_state_out, out,
+                       d->batch, d->seqlen, CD};
+    return hip_status(ssd::launch_conv1d_fwd(a, static_cast<Dt>(d->act_dtype), stream));
+}
+
+ssd_status_t ssd_conv1d_update(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                               const void* w, const void* bias, void* conv_state, void* out,
+                               hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    const int64_t CD = ssd_conv_dim(d);
+    if (!xbc || !w || !conv_state || !out) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, w, bias, static_cast<const void*>(conv_state), static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::ConvUpdateArgs a{xbc, xbc_row_stride, w, bias, conv_state, out, d->batch, CD};
+    return hip_status(ssd::launch_conv1d_update(a, static_cast<Dt>(d->act_dtype), stream));
+}
+
+size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
+    (void)d;
+    (void)chunk;
+    return 0;
+}
+
+ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                            const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                            const float* A, const float* D, const float* init_state,
+                            float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return SSD_ERR_UNSUPPORTED;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (tokens && (x_row_stride < I || bc_row_stride < GN)) return SSD_ERR_SHAPE;
+    if (!stride_ok(x_row_stride, d->act_dtype) || !stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {x, B, C, static_cast<const void*>(y), static_cast<const void*>(init_state), static_cast<const void*>(final_state)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
+    if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
+    (void)workspace;
+    ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, init_state, final_state, y,
+                    d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk};
+    const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
+    if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
+        return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
+    return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
+}
+
+ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state, const void* x, int64_t x_row_stride,
+                              const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                              const float* A, const float* D, void* y, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    if (d->batch > 0 && (!state || !x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
+    if (!aligned16(state)) return SSD_ERR_ALIGN;
+    ssd::UpdateArgs a{state, x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state};
+    return hip_status(ssd::launch_state_update(a, static_cast<Dt>(d->act_dtype),
+                                               static_cast<Dt>(d->y_dtype), stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Single-token selective state update for decode, in place on the fp32 state
+// (modeling_nemotron_h.py walk-through, "Decode 阶段": the state decays by
+// exp(dt*A), gains dt*B*x, and y contracts the updated state with C and adds
+// D*x; "Mamba 与 Nemotron 系列模型深度调研", 状态契约: state [B, H, P, N]).
+//
+// The state is read once and written once per token, so the kernel is a pure
+// HBM stream.  The whole [B, H, P, N] state is walked as one flat array of
+// float4: each thread keeps 8 float4 in flight (one per 256-thread stride, so
+// every wave-wide access is 1 KB contiguous), with non-temporal loads and
+// stores because the state is far larger than the caches and is not re-read
+// this step.  One state row p (N floats) spans N/4 consecutive lanes; the
+// output y[p] is a butterfly reduction over those lanes.  No MFMA: the
+// arithmetic is 2 FMAs per 4-byte element.
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+constexpr int kUpdThreads = 256;
+constexpr int kUpdPerThread = 8;
+
+template <typename T, typename TY, int N>
+__global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
+    float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, TY* __restrict__ y, int64_t total4, int H, int P, int hpg) {
+    constexpr int QPR = N / 4;  // float4 per state row
+    f32x4* st4 = reinterpret_cast<f32x4*>(state);
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread) + threadIdx.x;
+
+    f32x4 s[kUpdPerThread];
+#pragma unroll
+    for (int i = 0; i < kUpdPerThread; ++i) {
+        const int64_t f = base + i * kUpdThreads;
+        if (f < total4) s[i] = __builtin_nontemporal_load(st4 + f);
+    }
+#pragma unroll
+    for (int i = 0; i < kUpdPerThread; ++i) {
+        const int64_t f = base + i * kUpdThreads;
+        const bool ok = f < total4;
+        const int64_t ff = ok ? f : 0;
+        const int64_t row = ff / QPR;          // (b, h, p)
+        const int q = static_cast<int>(ff - row * QPR);
+        const int64_t bh = row / P;
+        const int p = static_cast<int>(row - bh * P);
+        const int64_t b = bh / H;
+        const int h = static_cast<int>(bh - b * H);
+        const int g = h / hpg;
+        const float dtv = static_cast<float>(dt[bh]);
+        const float a = __expf(dtv * A[h]);
+        const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
+        const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 4 * q;
+        float bv[4], cv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bv[k] = static_cast<float>(Bm[bo + k]);
+            cv[k] = static_cast<float>(Cm[bo + k]);
+        }
+        const float dx = dtv * xv;
+        f32x4 v = s[i];
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = fmaf(a, v[k], dx * bv[k]);
+            part = fmaf(v[k], cv[k], part);
+        }
+        if (!ok) part = 0.f;
+#pragma unroll
+        for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        if (ok) {
+            if (q == 0) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+            __builtin_nontemporal_store(v, st4 + f);
+        }
+    }
+}
+
+template <typename T, typename TY, int N>
+static hipError_t upd_n(const UpdateArgs& a, hipStream_t s) {
+    const int64_t total4 = a.batch * a.nheads * static_cast<int64_t>(a.head_dim) * (N / 4);
+    if (total4 == 0) return hipSuccess;
+    const int64_t per_block = kUpdThreads * kUpdPerThread;
+    const int64_t blocks = (total4 + per_block - 1) / per_block;
+    hipLaunchKernelGGL((state_update_kernel<T, TY, N>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kUpdThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
+                       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
+                       static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), total4, a.nheads,
+                       a.head_dim, a.nheads / a.ngroups);
+    return hipGetLastError();
+}
+
+template <typename T, typename TY>
+static hipError_t upd_t(const UpdateArgs& a, hipStream_t s) {
+    switch (a.d_state) {
+        case 16: return upd_n<T, TY, 16>(a, s);
+        case 32: return upd_n<T, TY, 32>(a, s);
+        case 64: return upd_n<T, TY, 64>(a, s);
+        case 128: return upd_n<T, TY, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_state_update(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s) {
+    if (act == Dt::BF16)
+        return ydt == Dt::BF16 ? upd_t<bf16, bf16>(a, s) : upd_t<bf16, float>(a, s);
+    return ydt == Dt::BF16 ? upd_t<float, bf16>(a, s) : upd_t<float, float>(a, s);
+}
+
+}  // namespace ssd

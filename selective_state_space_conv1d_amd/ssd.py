@@ -1,0 +1,224 @@
+"""Python binding of libssd (ctypes): argument marshalling only.
+
+Every function here checks tensor shapes/strides, derives the ABI's sizes and
+row strides, and calls the C entry point of the same name on the current HIP
+stream.  All arithmetic runs in the library's HIP kernels; there is no other
+code path.  If libssd.so is missing this module raises on first use.
+
+torch is used for device memory and streams only.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+_DT = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_DTYPE", "SSD_ERR_ALIGN",
+          "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
+EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan_workspace_size",
+           "ssd_chunk_scan", "ssd_state_update", "ssd_status_string"]
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ngroups", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("conv_width", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        name = STATUS[code] if 0 <= code < len(STATUS) else str(code)
+        super().__init__(f"{where}: {name} ({_lib().ssd_status_string(code).decode()})")
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_PD = ctypes.POINTER(SsdDims)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libssd.so is not built ({LIB_PATH}); run "
+                               "python -m selective_state_space_conv1d_amd.build_lib")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ssd_conv_dim.argtypes = [_PD]
+        lib.ssd_conv_dim.restype = _I64
+        lib.ssd_conv1d_fwd.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_conv1d_update.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_chunk_scan_workspace_size.argtypes = [_PD, _I32]
+        lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, _VP, ctypes.c_size_t, _VP]
+        lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def lib_handle():
+    """The loaded ctypes library (loads it on first call)."""
+    return _lib()
+
+
+def _ptr(t):
+    return None if t is None else _VP(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _VP(stream.cuda_stream)
+
+
+def _uniform_rows(t, L):
+    """[B, L, ...] view whose batch stride is L token strides (trivially true when empty)."""
+    return t.shape[0] <= 1 or L == 0 or t.stride(0) == L * t.stride(1)
+
+
+def _check(code, where):
+    if code != 0:
+        raise SsdError(code, where)
+
+
+def _dims(batch, seqlen, H, P, G, N, act, ydt):
+    return SsdDims(batch, seqlen, H, P, G, N, 4, _DT[act], _DT[ydt])
+
+
+def ssd_status_string(code):
+    return _lib().ssd_status_string(code).decode()
+
+
+def ssd_conv1d_fwd(xbc, w, bias=None, conv_state_in=None, conv_state_out=None, out=None,
+                   nheads=None, head_dim=None, ngroups=None, d_state=None, stream=None):
+    """Prefill conv.  xbc [B, L, CD] (token rows may be strided, channels packed),
+    w [CD, 4], bias [CD]|None, conv states [B, CD, 4]|None (out may alias in).
+    Returns out [B, L, CD].  The conv only needs CD; (H, P, G, N) may be given
+    to describe the layer (CD = H*P + 2*G*N), otherwise any consistent split is used."""
+    Bt, L, CD = xbc.shape
+    if (xbc.stride(2) != 1 and CD > 1) or not _uniform_rows(xbc, L):
+        raise ValueError("xbc must be [B, L, CD] with packed channels and uniform token stride")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    if out is None:
+        out = torch.empty((Bt, L, CD), dtype=xbc.dtype, device=xbc.device)
+    d = _dims(Bt, L, H, P, G, N, xbc.dtype, xbc.dtype)
+    xs = CD if L == 0 else xbc.stride(1)
+    if L == 0:
+        xbc = None
+    _check(_lib().ssd_conv1d_fwd(ctypes.byref(d), _ptr(xbc), xs, _ptr(w), _ptr(bias),
+                                 _ptr(conv_state_in), _ptr(conv_state_out), _ptr(out), _stream(stream)),
+           "ssd_conv1d_fwd")
+    return out
+
+
+def _split_cd(CD, H, P, G, N):
+    if H is None:
+        # any split with the right total channel count; the conv only uses CD
+        G, N, P = 1, 8, 8
+        H = (CD - 2 * G * N) // P
+    if H * P + 2 * G * N != CD:
+        raise ValueError(f"conv channels {CD} != H*P + 2*G*N")
+    return H, P, G, N
+
+
+def ssd_conv1d_update(xbc, w, bias, conv_state, out=None, nheads=None, head_dim=None, ngroups=None,
+                      d_state=None, stream=None):
+    """One-token conv.  xbc [B, CD] (rows may be strided), conv_state [B, CD, 4] updated in place.
+    Returns out [B, CD]."""
+    Bt, CD = xbc.shape
+    if xbc.stride(1) != 1:
+        raise ValueError("xbc channels must be packed")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    if out is None:
+        out = torch.empty((Bt, CD), dtype=xbc.dtype, device=xbc.device)
+    d = _dims(Bt, 1, H, P, G, N, xbc.dtype, xbc.dtype)
+    _check(_lib().ssd_conv1d_update(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias),
+                                    _ptr(conv_state), _ptr(out), _stream(stream)), "ssd_conv1d_update")
+    return out
+
+
+def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, head_dim, ngroups, d_state, chunk=128,
+                                  act_dtype=torch.bfloat16, y_dtype=torch.bfloat16):
+    d = _dims(batch, seqlen, nheads, head_dim, ngroups, d_state, act_dtype, y_dtype)
+    return int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
+
+
+def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=None, chunk=128,
+                   y_dtype=None, workspace=None, stream=None):
+    """SSD chunked scan.  x [B, L, H, P], B/C [B, L, G, N] (token rows may be strided, e.g.
+    views into the conv output), dt [B, L, H], A [H] fp32, D [H] fp32|None,
+    init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).
+    Returns y [B, L, H, P] in y_dtype (default: x's dtype)."""
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if L > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, L)):
+        raise ValueError("x must be [B, L, H, P] with packed (H, P) and uniform token stride")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, L, G, N) or (L > 0 and (t.stride(3) != 1 or t.stride(2) != N
+                                                    or not _uniform_rows(t, L))):
+            raise ValueError(f"{nm} must be [B, L, G, N] with packed (G, N) and uniform token stride")
+    if B.stride(1) != C.stride(1):
+        raise ValueError("B and C must share a token stride")
+    if dt.shape != (Bt, L, H) or not dt.is_contiguous():
+        raise ValueError("dt must be contiguous [B, L, H]")
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((Bt, L, H, P), dtype=ydt, device=x.device)
+    if L == 0:
+        x = B = C = dt = None
+    d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    xs = P * H if x is None else x.stride(1)
+    bcs = G * N if B is None else B.stride(1)
+    _check(_lib().ssd_chunk_scan(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
+                                 _ptr(dt), _ptr(A), _ptr(D), _ptr(init_state), _ptr(final_state), _ptr(y),
+                                 _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
+    return y
+
+
+def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None):
+    """One decode token, in place on state [B, H, P, N] fp32.  x [B, H, P], B/C [B, G, N]
+    (batch rows may be strided, e.g. views into the conv-update output), dt [B, H].
+    Returns y [B, H, P]."""
+    Bt, H, P, N = state.shape
+    G = B.shape[1]
+    if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
+        raise ValueError("x must be [B, H, P] with packed (H, P)")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, G, N) or t.stride(2) != 1 or t.stride(1) != N:
+            raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
+    if B.stride(0) != C.stride(0):
+        raise ValueError("B and C must share a batch stride")
+    if dt.shape != (Bt, H) or not dt.is_contiguous() or not state.is_contiguous():
+        raise ValueError("dt [B, H] and state must be contiguous")
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
+    _check(_lib().ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), x.stride(0), _ptr(B), _ptr(C),
+                                   B.stride(0), _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(stream)),
+           "ssd_state_update")
+    return y
+
+
+def split_xbc(v, nheads, head_dim, ngroups, d_state):
+    """Views x [.., H, P], B [.., G, N], C [.., G, N] into a conv output v [.., CD] (no copy)."""
+    I = nheads * head_dim
+    GN = ngroups * d_state
+    lead = v.shape[:-1]
+    x = v[..., :I].unflatten(-1, (nheads, head_dim))
+    Bm = v[..., I:I + GN].unflatten(-1, (ngroups, d_state))
+    Cm = v[..., I + GN:I + 2 * GN].unflatten(-1, (ngroups, d_state))
+    assert x.shape[:-2] == lead
+    return x, Bm, Cm

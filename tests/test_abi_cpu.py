@@ -1,0 +1,147 @@
+"""The C ABI on the host: exports and argument validation (no GPU needed).
+
+Every call below fails validation before anything is launched, so it never
+reaches the device; pointers are fake 16-byte-aligned addresses that are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def ssd():
+    from selective_state_space_conv1d_amd import ssd as mod
+    if not os.path.exists(mod.LIB_PATH):
+        from selective_state_space_conv1d_amd import build_lib
+        build_lib.build()
+    return mod
+
+
+@pytest.fixture(scope="module")
+def lib(ssd):
+    return ssd.lib_handle()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(ssd):
+    assert declared_functions() == sorted(ssd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def dims(ssd, **kw):
+    d = dict(batch=2, seqlen=300, nheads=4, head_dim=64, ngroups=2, d_state=128, conv_width=4,
+             act_dtype=1, y_dtype=0)
+    d.update(kw)
+    return ssd.SsdDims(**d)
+
+
+P0 = 0x10000  # fake aligned device addresses (never dereferenced: every case fails validation)
+
+
+def fp(i=0):
+    return ctypes.c_void_p(P0 + 0x1000 * i)
+
+
+def scan(lib, d, chunk=128, x=fp(1), xs=256, B=fp(2), C=fp(3), bcs=256, dt=fp(4), A=fp(5), D=None,
+         init=None, fin=None, y=fp(6), ws=None, wsb=0):
+    return lib.ssd_chunk_scan(ctypes.byref(d), chunk, x, xs, B, C, bcs, dt, A, D, init, fin, y, ws, wsb, None)
+
+
+def test_status_strings(ssd, lib):
+    for code in range(8):
+        assert ssd.ssd_status_string(code)
+    assert ssd.ssd_status_string(99) == "unknown status"
+
+
+def test_conv_dim(ssd, lib):
+    d = dims(ssd, nheads=256, head_dim=64, ngroups=8, d_state=128)
+    assert lib.ssd_conv_dim(ctypes.byref(d)) == 18432
+    assert lib.ssd_conv_dim(None) == -1
+
+
+def test_scan_validation(ssd, lib):
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    assert lib.ssd_chunk_scan(None, 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None, None, None,
+                              fp(6), None, 0, None) == E["SSD_ERR_NULL"]
+    assert scan(lib, dims(ssd, act_dtype=7)) == E["SSD_ERR_DTYPE"]
+    assert scan(lib, dims(ssd, y_dtype=-1)) == E["SSD_ERR_DTYPE"]
+    assert scan(lib, dims(ssd, batch=-1)) == E["SSD_ERR_SHAPE"]
+    assert scan(lib, dims(ssd, seqlen=-5)) == E["SSD_ERR_SHAPE"]
+    assert scan(lib, dims(ssd, nheads=6, ngroups=4)) == E["SSD_ERR_SHAPE"]
+    assert scan(lib, dims(ssd, nheads=0)) == E["SSD_ERR_SHAPE"]
+    assert scan(lib, dims(ssd, conv_width=3)) == E["SSD_ERR_UNSUPPORTED"]
+    assert scan(lib, dims(ssd), x=None) == E["SSD_ERR_NULL"]
+    assert scan(lib, dims(ssd), dt=None) == E["SSD_ERR_NULL"]
+    assert scan(lib, dims(ssd), A=None) == E["SSD_ERR_NULL"]
+    assert scan(lib, dims(ssd), y=None) == E["SSD_ERR_NULL"]
+    assert scan(lib, dims(ssd), chunk=96) == E["SSD_ERR_UNSUPPORTED"]
+    assert scan(lib, dims(ssd, head_dim=48)) == E["SSD_ERR_UNSUPPORTED"]
+    assert scan(lib, dims(ssd, d_state=256)) == E["SSD_ERR_UNSUPPORTED"]
+    assert scan(lib, dims(ssd), xs=255) == E["SSD_ERR_SHAPE"]          # shorter than H*P
+    assert scan(lib, dims(ssd), bcs=200) == E["SSD_ERR_SHAPE"]         # shorter than G*N
+    assert scan(lib, dims(ssd), xs=260) == E["SSD_ERR_ALIGN"]          # 520 B rows
+    assert scan(lib, dims(ssd), x=ctypes.c_void_p(P0 + 2)) == E["SSD_ERR_ALIGN"]
+    assert scan(lib, dims(ssd), y=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert scan(lib, dims(ssd), init=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+
+
+def test_workspace_size_is_zero(ssd, lib):
+    assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(dims(ssd)), 128) == 0
+
+
+def test_conv_validation(ssd, lib):
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd)  # CD = 4*64 + 2*2*128 = 768
+    ok = dict(xbc=fp(1), xs=768, w=fp(2), bias=None, sin=None, sout=None, out=fp(3))
+
+    def call(dd=d, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.ssd_conv1d_fwd(ctypes.byref(dd), a["xbc"], a["xs"], a["w"], a["bias"], a["sin"],
+                                  a["sout"], a["out"], None)
+    assert call(xbc=None) == E["SSD_ERR_NULL"]
+    assert call(w=None) == E["SSD_ERR_NULL"]
+    assert call(out=None) == E["SSD_ERR_NULL"]
+    assert call(xs=700) == E["SSD_ERR_SHAPE"]
+    assert call(xs=772) == E["SSD_ERR_ALIGN"]
+    assert call(bias=ctypes.c_void_p(P0 + 6)) == E["SSD_ERR_ALIGN"]
+    assert call(dims(ssd, conv_width=2)) == E["SSD_ERR_UNSUPPORTED"]
+    assert call(dims(ssd, nheads=3, head_dim=1, ngroups=1, d_state=2)) == E["SSD_ERR_UNSUPPORTED"]  # CD=7
+    assert lib.ssd_conv1d_update(ctypes.byref(d), fp(1), 768, fp(2), None, None, fp(3), None) == E["SSD_ERR_NULL"]
+    assert lib.ssd_conv1d_update(ctypes.byref(d), fp(1), 767, fp(2), None, fp(4), fp(3), None) == E["SSD_ERR_SHAPE"]
+
+
+def test_state_update_validation(ssd, lib):
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd)
+
+    def call(dd=d, state=fp(1), x=fp(2), xs=256, B=fp(3), C=fp(4), bcs=256, dt=fp(5), A=fp(6), y=fp(7)):
+        return lib.ssd_state_update(ctypes.byref(dd), state, x, xs, B, C, bcs, dt, A, None, y, None)
+    assert call(state=None) == E["SSD_ERR_NULL"]
+    assert call(y=None) == E["SSD_ERR_NULL"]
+    assert call(dims(ssd, head_dim=24)) == E["SSD_ERR_UNSUPPORTED"]
+    assert call(xs=100) == E["SSD_ERR_SHAPE"]
+    assert call(state=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert call(dims(ssd, nheads=5, ngroups=2)) == E["SSD_ERR_SHAPE"]
+
+
+def test_binding_raises_without_library(ssd, monkeypatch):
+    monkeypatch.setattr(ssd, "_LIB", None)
+    monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        ssd.lib_handle()
