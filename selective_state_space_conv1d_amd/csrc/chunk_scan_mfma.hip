@@ -1,349 +1,488 @@
-// SSD chunked scan for prefill on bf16 MFMA (gfx950), head_dim 64, d_state 128,
+// SSD chunked scan for prefill on bf16 MFMA (gfx950): head_dim 64, d_state 128,
 // chunk 128 -- the Ultra-family Mamba layer.
 //
 // Method (the structured-semiseparable / chunked form of the Mamba-2 scan:
-// "Mamba 与 Nemotron 系列模型深度调研", Mamba 架构, and the 128-token chunked
-// scan that returns the final state in the modeling_nemotron_h.py walk-through,
+// "Mamba 与 Nemotron 系列模型深度调研", Mamba 架构; the 128-token chunked scan
+// that returns the final state in the modeling_nemotron_h.py walk-through,
 // "Prefill 阶段").  Per chunk of Q tokens, with cs the inclusive prefix sum of
-// dt*A (base-2 units so that decays are exp2 of differences):
-//   M[i][j] = (C_i . B_j) * exp(cs_i - cs_j) * dt_j   (j <= i), + D on the diagonal
-//   y_i     = sum_j M[i][j] x_j  +  exp(cs_i) * (C_i . H)
-//   H       = exp(cs_last) * H + sum_j exp(cs_last - cs_j) dt_j  x_j (x) B_j
+// dt*A in base-2 units (decays are exp2 of differences):
+//   M[i][j] = (C_i . B_j) * exp2(cs_i - cs_j) * dt_j   (j <= i), + D on the diagonal
+//   y_i     = sum_j M[i][j] x_j  +  exp2(cs_i) * (C_i . H)
+//   H       = exp2(cs_last) * H + sum_j exp2(cs_last - cs_j) dt_j  x_j (x) B_j
 // which is the token recurrence re-associated exactly.
 //
-// Mapping: one persistent workgroup (4 waves) per (batch, head) walks the
-// chunks in order; the fp32 state H never leaves registers between chunks
-// (no per-chunk states in HBM).  Wave w owns head_dim rows p in [16w, 16w+16):
-// it keeps H^T[n][p] for those p as eight 16x16 MFMA accumulator tiles, and
-// produces y^T[p][i] for its p and every token i of the chunk.
+// Mapping.  One persistent workgroup of 4 waves per (batch, head) walks the
+// chunks in order; the fp32 state H lives in registers of the waves that own
+// its tiles and never goes to HBM between chunks.  All products are
+// v_mfma_f32_32x32x16_bf16 (a single wave issues these at full rate when it
+// keeps >= 4 independent accumulators in flight).  Wave w owns token tile w
+// (32 tokens): it computes C.B^T for the tiles j <= i of its rows, turns them
+// into M in registers, and uses the accumulators directly as the B operand of
+// y^T = X^T M^T (accumulator rows are the MFMA's k, so k is permuted the same
+// way on both operands).  It then adds exp2(cs_i) C.H (H read from LDS) and
+// writes y for its 32 tokens.  The chunk-state tiles H[p-tile][n-tile] are
+// spread over the waves with the least causal work (wave 0: p-tile 0 x all four
+// n-tiles, waves 1 and 2: p-tile 1 x two n-tiles, wave 3: none), which balances
+// the MFMA count at <= 112 per wave and chunk; the decay weight of the chunk
+// state is applied to the x operand, once per wave and p-tile.
 //
-// All products are v_mfma_f32_16x16x32_bf16.  x, B and C arrive in bf16 and
-// are exact operands; operands derived in fp32 (the score matrix M, the state
-// H and the decay-weighted x) are split into bf16 hi + lo and issued as two
-// MFMAs, which keeps the products at about 16 mantissa bits.  Accumulator
-// tiles are reused directly as MFMA operands (accumulator column = lane, rows
-// = k), permuting k consistently on both operands; that is how H feeds the
-// C.H product and how nothing else round-trips through LDS except M.
+// Precision.  x, B and C arrive in bf16 and are exact operands.  Operands
+// computed in fp32 (M, H and the decay-weighted B) are split into bf16 hi + lo
+// and issued as two MFMAs, keeping ~16 significant bits.  Decays inside a
+// chunk are exp2 of differences of the prefix sums (exact exp2(0) = 1 on the
+// diagonal); off-diagonal 32x32 blocks use the factorisation
+// exp2(cs_i - cs_e) * exp2(cs_e - cs_j) about the block's last token e, both
+// factors <= 1, so nothing overflows.
 //
-// LDS per chunk (bf16, rows padded by 16 B): B[j][n], B^T[n][j], C[i][n],
-// X^T[p][j] and one half (64 rows) of M hi/lo at a time: ~154 KB.
+// Data movement.  x, B and C tiles are staged row-major in LDS; the operands
+// that contract over tokens are read with ds_read_b64_tr_b16 (LDS transpose
+// read), so no transposed copies are kept.  The next chunk's x, B, C and dt
+// are loaded into registers while the current chunk computes.  Per-token
+// decay vectors are built once per chunk by the wave with the fewest MFMAs.
+// Workgroups are numbered so that the heads sharing a B/C group sit on one XCD.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
+namespace scan32 {
 
-namespace mfma64 {
-
-constexpr int Q = 128;   // tokens per chunk
-constexpr int P = 64;    // head_dim
-constexpr int NS = 128;  // d_state
-constexpr int LD = 136;  // padded row length (bf16 elements) of the [.][128] tiles
+constexpr int Q = 128;    // tokens per chunk
+constexpr int P = 64;     // head_dim
+constexpr int NS = 128;   // d_state
+constexpr int BS = 144;   // LDS row stride (bf16) of the [.][128] tiles: 72 dwords, 8-bank shift per row
+constexpr int XS = 80;    // LDS row stride (bf16) of the x tile: 40 dwords
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct Smem {
-    bf16 B[Q][LD];
-    bf16 BT[NS][LD];
-    bf16 C[Q][LD];
-    bf16 XT[P][LD];
-    bf16 Mhi[Q / 2][LD];
-    bf16 Mlo[Q / 2][LD];
-    float cs[Q];
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+struct Vec {            // per-token quantities of one chunk
+    float cs[Q];        // inclusive prefix sum of dt*A*log2(e)
     float dt[Q];
+    float fM[Q];        // exp2(cs_e - cs_j) * dt_j, e = last token of j's 32-token tile
+    float wS[Q];        // exp2(cs_last - cs_j) * dt_j for real tokens, 0 for padding
+    float eY[Q];        // exp2(cs_i)
+    float csE[4];       // cs at the end of each 32-token tile
+    float pad[4];
 };
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+struct Smem {
+    bf16 B[Q][BS];      // B[j][n]
+    bf16 C[Q][BS];      // C[i][n]
+    bf16 X[Q][XS];      // x[j][p]
+    bf16 Hhi[P][BS];    // H[p][n], high and low bf16 parts
+    bf16 Hlo[P][BS];
+    Vec vec[2];         // double-buffered: the current chunk's and the next one's
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+__device__ __forceinline__ bf16 bhi(float v) { return static_cast<bf16>(v); }
+__device__ __forceinline__ bf16 blo(float v, bf16 hi) { return static_cast<bf16>(v - static_cast<float>(hi)); }
+
+// MFMA operand whose k runs over tokens, read from a row-major [token][col] LDS
+// tile with two transpose reads.  Lane (c32 = lane%32, hf = lane/32) receives
+// column col_base + c32 at tokens j0 + 4hf + {0..3} (slots 0..3) and
+// j0 + 8 + 4hf + {0..3} (slots 4..7) -- the row order of a 32x32 accumulator
+// used as an operand.  Within each 16-lane group, lane m supplies the address
+// of row (first + m/4), columns col0 + 4(m%4) .. +3.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* mat, int rs, int j0, int col_base, int lane) {
+    const int m = lane & 15;
+    const int col = col_base + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
+    const int row = j0 + 4 * (lane >> 5) + (m >> 2);
+    const bf16* p0 = mat + row * rs + col;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)p0);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(p0 + 8 * rs));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(v); }
+// Global tiles of one chunk held in registers between load and LDS store.
+// Thread tid moves rows tid/16 + 16k of B and C (16-byte column tid%16) and
+// rows tid/8 + 32k of x (column tid%8).
+struct StageX { u32x4 x[4]; };
+struct StageBC { u32x4 b[8], c[8]; };
 
-// 8x8 transpose of bf16 held as 8 rows of 4 dwords (dword d = columns 2d, 2d+1).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&c)[8]) {
+struct Ctx {
+    const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
+    int64_t xs, bcs, b, L;
+    int H, h, grp;
+};
+
+__device__ __forceinline__ void load_x(StageX& st, const bf16* xrow, int64_t xs, int valid, int tid) {
 #pragma unroll
-    for (int col = 0; col < 8; ++col) {
-        const int d = col >> 1;
+    for (int k = 0; k < 4; ++k) {
+        const int row = (tid >> 3) + 32 * k;
+        if (row < valid) st.x[k] = *reinterpret_cast<const u32x4*>(xrow + (32 * k) * xs);
+        else st.x[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+__device__ __forceinline__ void load_bc(StageBC& st, const bf16* brow, const bf16* crow, int64_t bcs, int valid, int tid) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = r[2 * e][d], hi = r[2 * e + 1][d];
-            c[col][e] = (col & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    for (int k = 0; k < 8; ++k) {
+        const int row = (tid >> 4) + 16 * k;
+        if (row < valid) {
+            st.b[k] = *reinterpret_cast<const u32x4*>(brow + (16 * k) * bcs);
+            st.c[k] = *reinterpret_cast<const u32x4*>(crow + (16 * k) * bcs);
+        } else {
+            st.b[k] = u32x4{0u, 0u, 0u, 0u};
+            st.c[k] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
+__device__ __forceinline__ void store_x(Smem& sm, const StageX& st, int tid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<u32x4*>(&sm.X[(tid >> 3) + 32 * k][(tid & 7) * 8]) = st.x[k];
+}
+__device__ __forceinline__ void store_bc(Smem& sm, const StageBC& st, int tid) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        *reinterpret_cast<u32x4*>(&sm.B[(tid >> 4) + 16 * k][(tid & 15) * 8]) = st.b[k];
+        *reinterpret_cast<u32x4*>(&sm.C[(tid >> 4) + 16 * k][(tid & 15) * 8]) = st.c[k];
+    }
+}
 
-// v ~= hi + lo with both in bf16 (about 16 significant bits in total).
-__device__ __forceinline__ bf16 bf_hi(float v) { return static_cast<bf16>(v); }
-__device__ __forceinline__ bf16 bf_lo(float v, bf16 hi) { return static_cast<bf16>(v - static_cast<float>(hi)); }
+// Per-token vectors of a chunk from its dt (two tokens per lane of one wave).
+__device__ __forceinline__ void build_vec(Vec& v, float d0, float d1, float A2, int valid, int lane) {
+    const float a0 = d0 * A2, a1 = d1 * A2;
+    float s = a0 + a1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float u = __shfl_up(s, off, 64);
+        if (lane >= off) s += u;
+    }
+    const float c1 = s, c0 = s - a1;  // inclusive sums at tokens 2*lane+1 and 2*lane
+    const int last = valid - 1;
+    const float cl0 = __shfl(c0, last >> 1, 64), cl1 = __shfl(c1, last >> 1, 64);
+    const float csl = (last & 1) ? cl1 : cl0;
+    const float ce = __shfl(c1, (lane & ~15) | 15, 64);   // end of this lane's 32-token tile
+    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    v.cs[j0] = c0;
+    v.cs[j1] = c1;
+    v.dt[j0] = d0;
+    v.dt[j1] = d1;
+    v.fM[j0] = fexp2(ce - c0) * d0;
+    v.fM[j1] = fexp2(ce - c1) * d1;
+    v.wS[j0] = j0 < valid ? fexp2(csl - c0) * d0 : 0.f;
+    v.wS[j1] = j1 < valid ? fexp2(csl - c1) * d1 : 0.f;
+    v.eY[j0] = fexp2(c0);
+    v.eY[j1] = fexp2(c1);
+    if ((lane & 15) == 15) v.csE[lane >> 4] = c1;
+}
+
+// Owned chunk-state tiles of wave W: tile k is H[p-tile pt][n-tile nt(k)].
+template <int W> struct Own {
+    static constexpr int n = W == 0 ? 4 : (W == 3 ? 0 : 2);
+    static constexpr int pt = W == 0 ? 0 : 1;
+    static constexpr int nt(int k) { return W == 2 ? 2 + k : k; }
+};
+
+template <int W, typename TY>
+__device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
+    constexpr int IT = W;                       // this wave's token tile
+    constexpr int NO = Own<W>::n;
+    constexpr int NOA = NO > 0 ? NO : 1;
+    constexpr int PT = Own<W>::pt;
+    const int tid = 64 * W + lane;
+    const int c32 = lane & 31, hf = lane >> 5;
+    const int64_t L = cx.L;
+    const float A2 = a.A[cx.h] * kLog2e;
+    const float Dh = a.D ? a.D[cx.h] : 0.f;
+    TY* yg = static_cast<TY*>(a.y);
+    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    const int64_t nchunks = (L + Q - 1) / Q;
+    // this thread's first staging row of the sequence (advanced by Q rows per chunk)
+    const bf16* xrow = cx.xg + (cx.b * L + (tid >> 3)) * cx.xs + static_cast<int64_t>(cx.h) * P + (tid & 7) * 8;
+    const int64_t boff = (cx.b * L + (tid >> 4)) * cx.bcs + static_cast<int64_t>(cx.grp) * NS + (tid & 15) * 8;
+    const bf16* brow = cx.Bg + boff;
+    const bf16* crow = cx.Cg + boff;
+    const bf16* dtrow = cx.dtg + (cx.b * L + 2 * lane) * cx.H + cx.h;
+    const int64_t xstep = Q * cx.xs, bstep = Q * cx.bcs, dstep = static_cast<int64_t>(Q) * cx.H;
+
+    // ---- owned state tiles: Hs[k][4j + r] = H[p = 32PT + c32][n = 32nt + 8j + 4hf + r]
+    f32x16 Hs[NOA];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) {
+        const int p = 32 * PT + c32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p * NS + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Hs[k][4 * j + r] = v[r];
+        }
+    }
+    auto write_h = [&]() {
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int p = 32 * PT + c32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
+                bf16x4 hh, hl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hh[r] = bhi(Hs[k][4 * j + r]);
+                    hl[r] = blo(Hs[k][4 * j + r], hh[r]);
+                }
+                *reinterpret_cast<bf16x4*>(&sm.Hhi[p][n]) = hh;
+                *reinterpret_cast<bf16x4*>(&sm.Hlo[p][n]) = hl;
+            }
+        }
+    };
+
+    if (nchunks > 0) {
+        const int valid0 = static_cast<int>(L < Q ? L : Q);
+        float d0 = 0.f, d1 = 0.f;
+        if (W == 3) {
+            if (2 * lane < valid0) d0 = static_cast<float>(dtrow[0]);
+            if (2 * lane + 1 < valid0) d1 = static_cast<float>(dtrow[cx.H]);
+        }
+        StageX sx;
+        StageBC sbc;
+        load_x(sx, xrow, cx.xs, valid0, tid);
+        load_bc(sbc, brow, crow, cx.bcs, valid0, tid);
+        store_x(sm, sx, tid);
+        store_bc(sm, sbc, tid);
+        if (W == 3) build_vec(sm.vec[0], d0, d1, A2, valid0, lane);
+        write_h();
+    }
+    __syncthreads();
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t t0 = c * Q;
+        const int valid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
+        const bool has_next = c + 1 < nchunks;
+        const int valid1 = has_next ? static_cast<int>((L - t0 - Q) < Q ? (L - t0 - Q) : Q) : 0;
+        const Vec& v = sm.vec[c & 1];
+
+        // ---- prefetch the next chunk's dt and x (long-latency HBM reads) now
+        float nd0 = 0.f, nd1 = 0.f;
+        if (W == 3 && has_next) {
+            const bf16* dn = dtrow + (c + 1) * dstep;
+            if (2 * lane < valid1) nd0 = static_cast<float>(dn[0]);
+            if (2 * lane + 1 < valid1) nd1 = static_cast<float>(dn[cx.H]);
+        }
+        StageX sx;
+        if (has_next) load_x(sx, xrow + (c + 1) * xstep, cx.xs, valid1, tid);
+
+        // ---- C fragments of this wave's tokens (B operand of C.B^T and of C.H)
+        bf16x8 cf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(&sm.C[32 * IT + c32][16 * ks + 8 * hf]);
+
+        // ---- carried state: yo^T[p][i] = sum_n H[p][n] C[i][n]  (hi and lo of H, one chain per p tile)
+        f32x16 yo[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const bf16x8 hh = *reinterpret_cast<const bf16x8*>(&sm.Hhi[32 * pt + c32][16 * ks + 8 * hf]);
+                const bf16x8 hl = *reinterpret_cast<const bf16x8*>(&sm.Hlo[32 * pt + c32][16 * ks + 8 * hf]);
+                yo[pt] = mfma32(hh, cf[ks], yo[pt]);
+                yo[pt] = mfma32(hl, cf[ks], yo[pt]);
+            }
+
+        // ---- C.B^T tiles (jt, IT), jt <= IT: acc rows = tokens j, cols = tokens i
+        constexpr int KP = IT == 0 ? 2 : 1;  // independent partial sums per tile
+        f32x16 cb[IT + 1][KP];
+#pragma unroll
+        for (int jt = 0; jt <= IT; ++jt)
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) cb[jt][kp] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+            for (int jt = 0; jt <= IT; ++jt) {
+                const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&sm.B[32 * jt + c32][16 * ks + 8 * hf]);
+                cb[jt][ks % KP] = mfma32(bf, cf[ks], cb[jt][ks % KP]);
+            }
+        }
+
+        // ---- per j tile: M = C.B^T * decay * dt (+ D on the diagonal) as bf16 hi/lo,
+        //      then y^T[p][i] += sum_j X^T[p][j] M^T[j][i]
+        const int i = 32 * IT + c32;
+        const float csi = v.cs[i];
+        f32x16 yd[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int jt = 0; jt <= IT; ++jt) {
+            f32x16 m = cb[jt][0];
+#pragma unroll
+            for (int kp = 1; kp < KP; ++kp) m += cb[jt][kp];
+            if (jt < IT) {
+                const float ai = fexp2(csi - v.csE[jt]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 f = *reinterpret_cast<const f32x4*>(&v.fM[32 * jt + 8 * j + 4 * hf]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[4 * j + r] *= f[r] * ai;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 cj = *reinterpret_cast<const f32x4*>(&v.cs[32 * jt + 8 * j + 4 * hf]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(&v.dt[32 * jt + 8 * j + 4 * hf]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int jj = 32 * jt + 8 * j + 4 * hf + r;
+                        float e = m[4 * j + r] * fexp2(csi - cj[r]) * dj[r];
+                        if (jj == i) e += Dh;
+                        m[4 * j + r] = jj <= i ? e : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                bf16x8 mh, ml;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    mh[s] = bhi(m[8 * q + s]);
+                    ml[s] = blo(m[8 * q + s], mh[s]);
+                }
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const bf16x8 xf = tr_frag(&sm.X[0][0], XS, 32 * jt + 16 * q, 32 * pt, lane);
+                    yd[pt] = mfma32(xf, mh, yd[pt]);
+                    yd[pt] = mfma32(xf, ml, yd[pt]);
+                }
+            }
+        }
+
+        // ---- prefetch the next chunk's B and C (L2-resident across the group's heads)
+        StageBC sbc;
+        if (has_next) load_bc(sbc, brow + (c + 1) * bstep, crow + (c + 1) * bstep, cx.bcs, valid1, tid);
+
+        // ---- y = y_diag + exp2(cs_i) * y_off for this wave's 32 tokens
+        const float ey = v.eY[i];
+        if (i < valid) {
+            TY* dst = yg + ((cx.b * L + t0 + i) * cx.H + cx.h) * static_cast<int64_t>(P);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const f32x16 yv = yd[pt] + ey * yo[pt];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = 32 * pt + 8 * j + 4 * hf;
+                    if constexpr (sizeof(TY) == 4) {
+                        *reinterpret_cast<f32x4*>(dst + p) = f32x4{yv[4 * j], yv[4 * j + 1], yv[4 * j + 2], yv[4 * j + 3]};
+                    } else {
+                        *reinterpret_cast<bf16x4*>(dst + p) =
+                            bf16x4{bf16(yv[4 * j]), bf16(yv[4 * j + 1]), bf16(yv[4 * j + 2]), bf16(yv[4 * j + 3])};
+                    }
+                }
+            }
+        }
+
+        // ---- owned state tiles: H^T[n][p] = exp2(cs_last) H^T + sum_j B^T[n][j] (w_j x_j)[p]
+        if constexpr (NO > 0) {
+            const float alpha = fexp2(v.cs[valid - 1]);
+#pragma unroll
+            for (int k = 0; k < NO; ++k) Hs[k] *= alpha;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int j0 = 32 * jt + 16 * q;
+                    const f32x4 w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
+                    const f32x4 w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
+                    const bf16x8 xf = tr_frag(&sm.X[0][0], XS, j0, 32 * PT, lane);
+                    bf16x8 xh, xl;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const float e = static_cast<float>(xf[s]) * (s < 4 ? w0[s] : w1[s - 4]);
+                        xh[s] = bhi(e);
+                        xl[s] = blo(e, xh[s]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < NO; ++k) {
+                        const bf16x8 bt = tr_frag(&sm.B[0][0], BS, j0, 32 * Own<W>::nt(k), lane);
+                        Hs[k] = mfma32(bt, xh, Hs[k]);
+                        Hs[k] = mfma32(bt, xl, Hs[k]);
+                    }
+                }
+        }
+
+        if (W == 3 && has_next) build_vec(sm.vec[(c + 1) & 1], nd0, nd1, A2, valid1, lane);
+        __syncthreads();   // every wave is done with this chunk's B, C, X and H in LDS
+        if (has_next) {
+            store_x(sm, sx, tid);
+            store_bc(sm, sbc, tid);
+        }
+        write_h();
+        __syncthreads();
+    }
+
+    if (a.final_state) {
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int p = 32 * PT + c32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
+                *reinterpret_cast<f32x4*>(a.final_state + sbase + p * NS + n) =
+                    f32x4{Hs[k][4 * j], Hs[k][4 * j + 1], Hs[k][4 * j + 2], Hs[k][4 * j + 3]};
+            }
+        }
+    }
+}
 
 template <typename TY>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;          // wave: head_dim rows [16w, 16w+16)
-    const int lane = tid & 63;
-    const int li = lane & 15;        // MFMA row/col index
-    const int lg = lane >> 4;        // MFMA k-group
-    const int H = a.nheads;
-    const int64_t L = a.seqlen;
-    const int64_t b = blockIdx.x / H;
-    const int h = static_cast<int>(blockIdx.x % H);
-    const int grp = h / (H / a.ngroups);
-    const float A2 = a.A[h] * kLog2e;
-    const float Dh = a.D ? a.D[h] : 0.f;
-    const bf16* xg = static_cast<const bf16*>(a.x);
-    const bf16* Bg = static_cast<const bf16*>(a.B);
-    const bf16* Cg = static_cast<const bf16*>(a.C);
-    const bf16* dtg = static_cast<const bf16*>(a.dt);
-    TY* yg = static_cast<TY*>(a.y);
-
-    // H^T accumulators: accH[nt][r] = H[p = 16w + li][n = 16nt + 4lg + r]
-    const int64_t srow = ((b * H + h) * P + 16 * w + li) * static_cast<int64_t>(NS);
-    f32x4 accH[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        if (a.init_state) accH[nt] = *reinterpret_cast<const f32x4*>(a.init_state + srow + 16 * nt + 4 * lg);
-        else accH[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int64_t nchunks = (L + Q - 1) / Q;
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * Q;
-        const int valid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
-        __syncthreads();  // previous chunk is done with LDS
-
-        // ---- stage B (natural + transposed), C, X^T, dt
-        {
-            const int ta = tid >> 4;        // token block: tokens 8ta .. 8ta+7
-            const int nb = tid & 15;        // state block: n 8nb .. 8nb+7
-            u32x4 rb[8], rc[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int j = 8 * ta + r;
-                if (j < valid) {
-                    const int64_t o = (b * L + t0 + j) * a.bc_row_stride + static_cast<int64_t>(grp) * NS + 8 * nb;
-                    rb[r] = *reinterpret_cast<const u32x4*>(Bg + o);
-                    rc[r] = *reinterpret_cast<const u32x4*>(Cg + o);
-                } else {
-                    rb[r] = u32x4{0u, 0u, 0u, 0u};
-                    rc[r] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-            u32x4 xr[8];
-            const bool xthread = tid < 128;
-            const int xa = tid >> 3;        // token block for X (tid < 128)
-            const int pb = tid & 7;         // p block: p 8pb .. 8pb+7
-            if (xthread) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int j = 8 * xa + r;
-                    if (j < valid)
-                        xr[r] = *reinterpret_cast<const u32x4*>(
-                            xg + (b * L + t0 + j) * a.x_row_stride + static_cast<int64_t>(h) * P + 8 * pb);
-                    else
-                        xr[r] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-            float dv = 0.f;
-            if (tid >= 128) {
-                const int j = tid - 128;
-                if (j < valid) dv = static_cast<float>(dtg[(b * L + t0 + j) * H + h]);
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                *reinterpret_cast<u32x4*>(&sm.B[8 * ta + r][8 * nb]) = rb[r];
-                *reinterpret_cast<u32x4*>(&sm.C[8 * ta + r][8 * nb]) = rc[r];
-            }
-            u32x4 tb[8];
-            transpose8x8(rb, tb);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(&sm.BT[8 * nb + k][8 * ta]) = tb[k];
-            if (xthread) {
-                u32x4 tx[8];
-                transpose8x8(xr, tx);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(&sm.XT[8 * pb + k][8 * xa]) = tx[k];
-            } else {
-                const int j = tid - 128;
-                sm.dt[j] = dv;
-                sm.cs[j] = dv * A2;
-            }
-        }
-        __syncthreads();
-        if (w == 0) {  // inclusive prefix sum of dt*A*log2(e), two tokens per lane
-            const float v0 = sm.cs[2 * lane], v1 = sm.cs[2 * lane + 1];
-            float s = v0 + v1;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float u = __shfl_up(s, off, 64);
-                if (lane >= off) s += u;
-            }
-            const float ex = s - (v0 + v1);
-            sm.cs[2 * lane] = ex + v0;
-            sm.cs[2 * lane + 1] = ex + v0 + v1;
-        }
-        __syncthreads();
-
-        // X^T fragments of this wave (A operand of y^T, and, decay-weighted, B operand of S)
-        bf16x8 xf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) xf[ks] = *reinterpret_cast<const bf16x8*>(&sm.XT[16 * w + li][32 * ks + 8 * lg]);
-
-        f32x4 accY[8];
-#pragma unroll
-        for (int it = 0; it < 8; ++it) accY[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // ---- M for token rows of this half: wave w builds i-tile it = 4*half + w
-            {
-                const int it = 4 * half + w;
-                const int i = 16 * it + li;
-                const float csi = sm.cs[i];
-                bf16x8 cf[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(&sm.C[i][32 * ks + 8 * lg]);
-                for (int jt = 0; jt <= it; ++jt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        acc = mfma(*reinterpret_cast<const bf16x8*>(&sm.B[16 * jt + li][32 * ks + 8 * lg]), cf[ks], acc);
-                    // acc[r] = (C_i . B_j), j = 16jt + 4lg + r
-                    bf16x4 mh, ml;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * jt + 4 * lg + r;
-                        float m = 0.f;
-                        if (j <= i) m = acc[r] * fexp2(csi - sm.cs[j]) * sm.dt[j] + (j == i ? Dh : 0.f);
-                        mh[r] = bf_hi(m);
-                        ml[r] = bf_lo(m, mh[r]);
-                    }
-                    *reinterpret_cast<bf16x4*>(&sm.Mhi[i - 64 * half][16 * jt + 4 * lg]) = mh;
-                    *reinterpret_cast<bf16x4*>(&sm.Mlo[i - 64 * half][16 * jt + 4 * lg]) = ml;
-                }
-                if ((it & 1) == 0) {  // the upper half of the last 32-wide k step is read: zero it
-                    const bf16x4 z = {bf16(0.f), bf16(0.f), bf16(0.f), bf16(0.f)};
-                    *reinterpret_cast<bf16x4*>(&sm.Mhi[i - 64 * half][16 * (it + 1) + 4 * lg]) = z;
-                    *reinterpret_cast<bf16x4*>(&sm.Mlo[i - 64 * half][16 * (it + 1) + 4 * lg]) = z;
-                }
-            }
-            __syncthreads();
-            // ---- y^T[p][i] += sum_j X^T[p][j] M^T[j][i]  (causal: k steps up to the diagonal)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int it = 4 * half + q;
-                const int row = 16 * q + li;
-#pragma unroll
-                for (int ks = 0; ks <= it / 2; ++ks) {
-                    const bf16x8 mh = *reinterpret_cast<const bf16x8*>(&sm.Mhi[row][32 * ks + 8 * lg]);
-                    const bf16x8 ml = *reinterpret_cast<const bf16x8*>(&sm.Mlo[row][32 * ks + 8 * lg]);
-                    accY[it] = mfma(xf[ks], mh, accY[it]);
-                    accY[it] = mfma(xf[ks], ml, accY[it]);
-                }
-            }
-            __syncthreads();
-        }
-
-        // ---- carried state: y^T[p][i] += exp(cs_i) * sum_n H[p][n] C[i][n]
-        {
-            bf16x8 hh[4], hl[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    hh[ks][r] = bf_hi(accH[2 * ks][r]);
-                    hl[ks][r] = bf_lo(accH[2 * ks][r], hh[ks][r]);
-                    hh[ks][4 + r] = bf_hi(accH[2 * ks + 1][r]);
-                    hl[ks][4 + r] = bf_lo(accH[2 * ks + 1][r], hh[ks][4 + r]);
-                }
-            }
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int i = 16 * it + li;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(&sm.C[i][32 * ks + 4 * lg]);
-                    const bf16x4 c1 = *reinterpret_cast<const bf16x4*>(&sm.C[i][32 * ks + 16 + 4 * lg]);
-                    const bf16x8 cfr = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                    acc = mfma(hh[ks], cfr, acc);
-                    acc = mfma(hl[ks], cfr, acc);
-                }
-                const float e = fexp2(sm.cs[i]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) accY[it][r] = fmaf(e, acc[r], accY[it][r]);
-            }
-        }
-
-        // ---- write y: lane holds y[token 16it+li][p = 16w + 4lg .. +3]
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int i = 16 * it + li;
-            if (i < valid) {
-                TY* dst = yg + ((b * L + t0 + i) * H + h) * static_cast<int64_t>(P) + 16 * w + 4 * lg;
-                if constexpr (sizeof(TY) == 4) {
-                    *reinterpret_cast<f32x4*>(dst) = accY[it];
-                } else {
-                    const bf16x4 v = {bf16(accY[it][0]), bf16(accY[it][1]), bf16(accY[it][2]), bf16(accY[it][3])};
-                    *reinterpret_cast<bf16x4*>(dst) = v;
-                }
-            }
-        }
-
-        // ---- state: H = exp(cs_last) H + sum_j B^T[n][j] (w_j x_j)[p]
-        {
-            // decay to the chunk's last real token; the cumulative sum is read at that
-            // token itself so that its own weight is exp2(0) = 1 exactly
-            const float cl = sm.cs[valid - 1];
-            const float alpha = fexp2(cl);
-            bf16x8 xh[4], xl[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int j = 32 * ks + 8 * lg + s;
-                    const float v = j < valid ? static_cast<float>(xf[ks][s]) * (fexp2(cl - sm.cs[j]) * sm.dt[j]) : 0.f;
-                    xh[ks][s] = bf_hi(v);
-                    xl[ks][s] = bf_lo(v, xh[ks][s]);
-                }
-            }
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                f32x4 acc = accH[nt] * alpha;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.BT[16 * nt + li][32 * ks + 8 * lg]);
-                    acc = mfma(bt, xh[ks], acc);
-                    acc = mfma(bt, xl[ks], acc);
-                }
-                accH[nt] = acc;
-            }
-        }
-    }
-
-    if (a.final_state) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * nt + 4 * lg) = accH[nt];
+    // XCD-aware numbering: workgroup id % 8 picks the XCD, so give each XCD a
+    // contiguous run of (batch, head) -- heads of one group share B and C in its L2.
+    const int64_t nb = a.batch * a.nheads;
+    int64_t id = blockIdx.x;
+    if (nb % 8 == 0) id = (id % 8) * (nb / 8) + id / 8;
+    Ctx cx;
+    cx.xg = static_cast<const bf16*>(a.x);
+    cx.Bg = static_cast<const bf16*>(a.B);
+    cx.Cg = static_cast<const bf16*>(a.C);
+    cx.dtg = static_cast<const bf16*>(a.dt);
+    cx.xs = a.x_row_stride;
+    cx.bcs = a.bc_row_stride;
+    cx.b = id / a.nheads;
+    cx.h = static_cast<int>(id % a.nheads);
+    cx.L = a.seqlen;
+    cx.H = a.nheads;
+    cx.grp = cx.h / (a.nheads / a.ngroups);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    switch (wave) {
+        case 0: run_wave<0, TY>(sm, a, cx, lane); break;
+        case 1: run_wave<1, TY>(sm, a, cx, lane); break;
+        case 2: run_wave<2, TY>(sm, a, cx, lane); break;
+        default: run_wave<3, TY>(sm, a, cx, lane); break;
     }
 }
 
-}  // namespace mfma64
+}  // namespace scan32
 
 bool mfma_scan_supports(int head_dim, int d_state, int chunk) {
-    return head_dim == mfma64::P && d_state == mfma64::NS && chunk == mfma64::Q;
+    return head_dim == scan32::P && d_state == scan32::NS && chunk == scan32::Q;
 }
 
 template <typename TY>
 static hipError_t mfma_t(const ScanArgs& a, hipStream_t s) {
     const int64_t blocks = a.batch * a.nheads;
     if (blocks == 0) return hipSuccess;
-    auto kern = mfma64::chunk_scan_kernel<TY>;
-    const size_t smem = sizeof(mfma64::Smem);
+    auto kern = scan32::chunk_scan_kernel<TY>;
+    const size_t smem = sizeof(scan32::Smem);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(mfma64::kThreads), smem, s, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(scan32::kThreads), smem, s, a);
     return hipGetLastError();
 }
 

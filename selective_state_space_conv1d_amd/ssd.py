@@ -175,12 +175,11 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, L, H, P), dtype=ydt, device=x.device)
-    if L == 0:
-        x = B = C = dt = None
     d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    xs = P * H if x is None else x.stride(1)
-    bcs = G * N if B is None else B.stride(1)
+    xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))
+    if L == 0:
+        x = B = C = dt = None
     _check(_lib().ssd_chunk_scan(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
                                  _ptr(dt), _ptr(A), _ptr(D), _ptr(init_state), _ptr(final_state), _ptr(y),
                                  _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
