@@ -34,12 +34,16 @@
 // exp2(cs_i - cs_e) * exp2(cs_e - cs_j) about the block's last token e, both
 // factors <= 1, so nothing overflows.
 //
-// Data movement.  x, B and C tiles are staged row-major in LDS; the operands
-// that contract over tokens are read with ds_read_b64_tr_b16 (LDS transpose
-// read), so no transposed copies are kept.  The next chunk's x, B, C and dt
-// are loaded into registers while the current chunk computes.  Per-token
-// decay vectors are built once per chunk by the wave with the fewest MFMAs.
-// Workgroups are numbered so that the heads sharing a B/C group sit on one XCD.
+// Data movement.  B and x tiles are staged row-major in LDS, double-buffered:
+// the next chunk's tiles stream in with direct global->LDS loads
+// (global_load_lds_dwordx4, no registers) while the current chunk computes.
+// Only the wave that owns a token tile reads its rows of C, so C goes straight
+// from global memory into that wave's MFMA operand registers (prefetched one
+// chunk ahead).  Operands that contract over tokens are read with
+// ds_read_b64_tr_b16 (LDS transpose read), so no transposed copies are kept.
+// Per-token decay vectors are built once per chunk by the wave with the fewest
+// MFMAs.  Workgroups are numbered so that the heads sharing a B/C group sit on
+// one XCD (its L2 then serves their common B and C).
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -53,6 +57,8 @@ constexpr int BS = 144;   // LDS row stride (bf16) of the [.][128] tiles: 72 dwo
 constexpr int XS = 80;    // LDS row stride (bf16) of the x tile: 40 dwords
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBInstr = Q * BS * 2 / 1024;   // 1-KB direct-load instructions per B tile (36)
+constexpr int kXInstr = Q * XS * 2 / 1024;   // per x tile (20)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
@@ -69,13 +75,14 @@ struct Vec {            // per-token quantities of one chunk
 };
 
 struct Smem {
-    bf16 B[Q][BS];      // B[j][n]
-    bf16 C[Q][BS];      // C[i][n]
-    bf16 X[Q][XS];      // x[j][p]
+    bf16 B[2][Q][BS];   // B[j][n], double-buffered over chunks
+    bf16 X[2][Q][XS];   // x[j][p], double-buffered over chunks
     bf16 Hhi[P][BS];    // H[p][n], high and low bf16 parts
     bf16 Hlo[P][BS];
-    Vec vec[2];         // double-buffered: the current chunk's and the next one's
+    Vec vec[2];         // the current chunk's and the next one's
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(Q * BS * 2 % 1024 == 0 && Q * XS * 2 % 1024 == 0, "tiles are whole 1-KB load blocks");
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -106,54 +113,42 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* mat, int rs, int j0, int c
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Global tiles of one chunk held in registers between load and LDS store.
-// Thread tid moves rows tid/16 + 16k of B and C (16-byte column tid%16) and
-// rows tid/8 + 32k of x (column tid%8).
-struct StageX { u32x4 x[4]; };
-struct StageBC { u32x4 b[8], c[8]; };
-
 struct Ctx {
     const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
     int64_t xs, bcs, b, L;
     int H, h, grp;
 };
 
-__device__ __forceinline__ void load_x(StageX& st, const bf16* xrow, int64_t xs, int valid, int tid) {
+// Direct global->LDS copy of one chunk's row-major tile into a padded LDS tile.
+// The tile is a sequence of 1-KB blocks; block k is written by wave k % 4 with
+// lane l storing LDS bytes [1024k + 16l, +16).  A lane whose bytes fall in a row's
+// padding, or in a row past the sequence end, re-reads a real row instead (the
+// padding is never read and rows past the end only meet zero weights).
+template <int RS, int DC, int NBLK>
+__device__ __forceinline__ void copy_tile(bf16* lds_tile, const bf16* g, int64_t row_stride, int64_t first_row,
+                                          int valid, int col_off, int W, int lane) {
+    constexpr int RB = RS * 2;            // LDS row bytes
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int row = (tid >> 3) + 32 * k;
-        if (row < valid) st.x[k] = *reinterpret_cast<const u32x4*>(xrow + (32 * k) * xs);
-        else st.x[k] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-__device__ __forceinline__ void load_bc(StageBC& st, const bf16* brow, const bf16* crow, int64_t bcs, int valid, int tid) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int row = (tid >> 4) + 16 * k;
-        if (row < valid) {
-            st.b[k] = *reinterpret_cast<const u32x4*>(brow + (16 * k) * bcs);
-            st.c[k] = *reinterpret_cast<const u32x4*>(crow + (16 * k) * bcs);
-        } else {
-            st.b[k] = u32x4{0u, 0u, 0u, 0u};
-            st.c[k] = u32x4{0u, 0u, 0u, 0u};
+    for (int m = 0; m < (NBLK + 3) / 4; ++m) {
+        const int k = W + 4 * m;
+        if (k < NBLK) {
+            const int o = 1024 * k + 16 * lane;
+            const int row = o / RB;
+            const int cb = o - row * RB;
+            const int r = row < valid ? row : valid - 1;
+            const int col = cb < 2 * DC ? cb / 2 : 0;    // DC real columns, the rest is padding
+            const bf16* src = g + (first_row + r) * row_stride + col_off + col;
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)((unsigned char*)lds_tile + 1024 * k),
+                                             16, 0, 0);
         }
-    }
-}
-__device__ __forceinline__ void store_x(Smem& sm, const StageX& st, int tid) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<u32x4*>(&sm.X[(tid >> 3) + 32 * k][(tid & 7) * 8]) = st.x[k];
-}
-__device__ __forceinline__ void store_bc(Smem& sm, const StageBC& st, int tid) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        *reinterpret_cast<u32x4*>(&sm.B[(tid >> 4) + 16 * k][(tid & 15) * 8]) = st.b[k];
-        *reinterpret_cast<u32x4*>(&sm.C[(tid >> 4) + 16 * k][(tid & 15) * 8]) = st.c[k];
     }
 }
 
 // Per-token vectors of a chunk from its dt (two tokens per lane of one wave).
-__device__ __forceinline__ void build_vec(Vec& v, float d0, float d1, float A2, int valid, int lane) {
+__device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, int valid, int lane) {
+    const float d0 = 2 * lane < valid ? static_cast<float>(r0) : 0.f;
+    const float d1 = 2 * lane + 1 < valid ? static_cast<float>(r1) : 0.f;
     const float a0 = d0 * A2, a1 = d1 * A2;
     float s = a0 + a1;
 #pragma unroll
@@ -193,7 +188,6 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
     constexpr int NO = Own<W>::n;
     constexpr int NOA = NO > 0 ? NO : 1;
     constexpr int PT = Own<W>::pt;
-    const int tid = 64 * W + lane;
     const int c32 = lane & 31, hf = lane >> 5;
     const int64_t L = cx.L;
     const float A2 = a.A[cx.h] * kLog2e;
@@ -201,13 +195,25 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
     TY* yg = static_cast<TY*>(a.y);
     const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
     const int64_t nchunks = (L + Q - 1) / Q;
-    // this thread's first staging row of the sequence (advanced by Q rows per chunk)
-    const bf16* xrow = cx.xg + (cx.b * L + (tid >> 3)) * cx.xs + static_cast<int64_t>(cx.h) * P + (tid & 7) * 8;
-    const int64_t boff = (cx.b * L + (tid >> 4)) * cx.bcs + static_cast<int64_t>(cx.grp) * NS + (tid & 15) * 8;
-    const bf16* brow = cx.Bg + boff;
-    const bf16* crow = cx.Cg + boff;
-    const bf16* dtrow = cx.dtg + (cx.b * L + 2 * lane) * cx.H + cx.h;
-    const int64_t xstep = Q * cx.xs, bstep = Q * cx.bcs, dstep = static_cast<int64_t>(Q) * cx.H;
+    const int64_t row0 = cx.b * L;                                  // first token row of the sequence
+    const int bc_col = cx.grp * NS, x_col = cx.h * P;
+    const bf16* crow = cx.Cg + bc_col + 8 * hf;                     // + row * bcs + 16 ks
+    const int i = 32 * IT + c32;                                    // this lane's token in the chunk
+
+    auto load_c = [&](bf16x8 (&cf)[8], int64_t t0, int valid) {
+        const int r = i < valid ? i : valid - 1;
+        const bf16* src = crow + (row0 + t0 + r) * cx.bcs;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+    };
+    // dt of tokens 2*lane and 2*lane+1, read unconditionally from in-range rows; tokens past
+    // the sequence end are zeroed later, in build_vec, so nothing waits on these loads early
+    auto load_dt = [&](bf16& d0, bf16& d1, int64_t t0, int valid) {
+        const int r0 = 2 * lane < valid ? 2 * lane : valid - 1;
+        const int r1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
+        d0 = cx.dtg[(row0 + t0 + r0) * cx.H + cx.h];
+        d1 = cx.dtg[(row0 + t0 + r1) * cx.H + cx.h];
+    };
 
     // ---- owned state tiles: Hs[k][4j + r] = H[p = 32PT + c32][n = 32nt + 8j + 4hf + r]
     f32x16 Hs[NOA];
@@ -242,21 +248,19 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
         }
     };
 
+    bf16x8 cf[8];
     if (nchunks > 0) {
         const int valid0 = static_cast<int>(L < Q ? L : Q);
-        float d0 = 0.f, d1 = 0.f;
+        copy_tile<BS, NS, kBInstr>(&sm.B[0][0][0], cx.Bg, cx.bcs, row0, valid0, bc_col, W, lane);
+        copy_tile<XS, P, kXInstr>(&sm.X[0][0][0], cx.xg, cx.xs, row0, valid0, x_col, W, lane);
+        load_c(cf, 0, valid0);
         if (W == 3) {
-            if (2 * lane < valid0) d0 = static_cast<float>(dtrow[0]);
-            if (2 * lane + 1 < valid0) d1 = static_cast<float>(dtrow[cx.H]);
+            bf16 d0, d1;
+            load_dt(d0, d1, 0, valid0);
+            build_vec(sm.vec[0], d0, d1, A2, valid0, lane);
         }
-        StageX sx;
-        StageBC sbc;
-        load_x(sx, xrow, cx.xs, valid0, tid);
-        load_bc(sbc, brow, crow, cx.bcs, valid0, tid);
-        store_x(sm, sx, tid);
-        store_bc(sm, sbc, tid);
-        if (W == 3) build_vec(sm.vec[0], d0, d1, A2, valid0, lane);
         write_h();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
 
@@ -265,22 +269,20 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
         const int valid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
         const bool has_next = c + 1 < nchunks;
         const int valid1 = has_next ? static_cast<int>((L - t0 - Q) < Q ? (L - t0 - Q) : Q) : 0;
-        const Vec& v = sm.vec[c & 1];
+        const int cur = static_cast<int>(c & 1), nxt = cur ^ 1;
+        const Vec& v = sm.vec[cur];
+        const bf16* sB = &sm.B[cur][0][0];
+        const bf16* sX = &sm.X[cur][0][0];
 
-        // ---- prefetch the next chunk's dt and x (long-latency HBM reads) now
-        float nd0 = 0.f, nd1 = 0.f;
-        if (W == 3 && has_next) {
-            const bf16* dn = dtrow + (c + 1) * dstep;
-            if (2 * lane < valid1) nd0 = static_cast<float>(dn[0]);
-            if (2 * lane + 1 < valid1) nd1 = static_cast<float>(dn[cx.H]);
+        // ---- stream the next chunk in: B and x straight to LDS, C rows and dt to registers
+        bf16x8 cfn[8];
+        bf16 nd0 = bf16(0.f), nd1 = bf16(0.f);
+        if (has_next) {
+            if (W == 3) load_dt(nd0, nd1, t0 + Q, valid1);
+            copy_tile<BS, NS, kBInstr>(&sm.B[nxt][0][0], cx.Bg, cx.bcs, row0 + t0 + Q, valid1, bc_col, W, lane);
+            copy_tile<XS, P, kXInstr>(&sm.X[nxt][0][0], cx.xg, cx.xs, row0 + t0 + Q, valid1, x_col, W, lane);
+            load_c(cfn, t0 + Q, valid1);
         }
-        StageX sx;
-        if (has_next) load_x(sx, xrow + (c + 1) * xstep, cx.xs, valid1, tid);
-
-        // ---- C fragments of this wave's tokens (B operand of C.B^T and of C.H)
-        bf16x8 cf[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(&sm.C[32 * IT + c32][16 * ks + 8 * hf]);
 
         // ---- carried state: yo^T[p][i] = sum_n H[p][n] C[i][n]  (hi and lo of H, one chain per p tile)
         f32x16 yo[2] = {zero16(), zero16()};
@@ -305,14 +307,13 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int jt = 0; jt <= IT; ++jt) {
-                const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&sm.B[32 * jt + c32][16 * ks + 8 * hf]);
+                const bf16x8 bf = *reinterpret_cast<const bf16x8*>(sB + (32 * jt + c32) * BS + 16 * ks + 8 * hf);
                 cb[jt][ks % KP] = mfma32(bf, cf[ks], cb[jt][ks % KP]);
             }
         }
 
         // ---- per j tile: M = C.B^T * decay * dt (+ D on the diagonal) as bf16 hi/lo,
         //      then y^T[p][i] += sum_j X^T[p][j] M^T[j][i]
-        const int i = 32 * IT + c32;
         const float csi = v.cs[i];
         f32x16 yd[2] = {zero16(), zero16()};
 #pragma unroll
@@ -352,33 +353,9 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
                 }
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    const bf16x8 xf = tr_frag(&sm.X[0][0], XS, 32 * jt + 16 * q, 32 * pt, lane);
+                    const bf16x8 xf = tr_frag(sX, XS, 32 * jt + 16 * q, 32 * pt, lane);
                     yd[pt] = mfma32(xf, mh, yd[pt]);
                     yd[pt] = mfma32(xf, ml, yd[pt]);
-                }
-            }
-        }
-
-        // ---- prefetch the next chunk's B and C (L2-resident across the group's heads)
-        StageBC sbc;
-        if (has_next) load_bc(sbc, brow + (c + 1) * bstep, crow + (c + 1) * bstep, cx.bcs, valid1, tid);
-
-        // ---- y = y_diag + exp2(cs_i) * y_off for this wave's 32 tokens
-        const float ey = v.eY[i];
-        if (i < valid) {
-            TY* dst = yg + ((cx.b * L + t0 + i) * cx.H + cx.h) * static_cast<int64_t>(P);
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                const f32x16 yv = yd[pt] + ey * yo[pt];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = 32 * pt + 8 * j + 4 * hf;
-                    if constexpr (sizeof(TY) == 4) {
-                        *reinterpret_cast<f32x4*>(dst + p) = f32x4{yv[4 * j], yv[4 * j + 1], yv[4 * j + 2], yv[4 * j + 3]};
-                    } else {
-                        *reinterpret_cast<bf16x4*>(dst + p) =
-                            bf16x4{bf16(yv[4 * j]), bf16(yv[4 * j + 1]), bf16(yv[4 * j + 2]), bf16(yv[4 * j + 3])};
-                    }
                 }
             }
         }
@@ -395,7 +372,7 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
                     const int j0 = 32 * jt + 16 * q;
                     const f32x4 w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
                     const f32x4 w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
-                    const bf16x8 xf = tr_frag(&sm.X[0][0], XS, j0, 32 * PT, lane);
+                    const bf16x8 xf = tr_frag(sX, XS, j0, 32 * PT, lane);
                     bf16x8 xh, xl;
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
@@ -405,21 +382,42 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
                     }
 #pragma unroll
                     for (int k = 0; k < NO; ++k) {
-                        const bf16x8 bt = tr_frag(&sm.B[0][0], BS, j0, 32 * Own<W>::nt(k), lane);
+                        const bf16x8 bt = tr_frag(sB, BS, j0, 32 * Own<W>::nt(k), lane);
                         Hs[k] = mfma32(bt, xh, Hs[k]);
                         Hs[k] = mfma32(bt, xl, Hs[k]);
                     }
                 }
         }
 
-        if (W == 3 && has_next) build_vec(sm.vec[(c + 1) & 1], nd0, nd1, A2, valid1, lane);
-        __syncthreads();   // every wave is done with this chunk's B, C, X and H in LDS
-        if (has_next) {
-            store_x(sm, sx, tid);
-            store_bc(sm, sbc, tid);
+        // ---- y = y_diag + exp2(cs_i) * y_off for this wave's 32 tokens (lane = token i)
+        const float ey = v.eY[i];
+        if (i < valid) {
+            TY* dst = yg + ((row0 + t0 + i) * cx.H + cx.h) * static_cast<int64_t>(P);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const f32x16 yv = yd[pt] + ey * yo[pt];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = 32 * pt + 8 * j + 4 * hf;
+                    if constexpr (sizeof(TY) == 4) {
+                        *reinterpret_cast<f32x4*>(dst + p) = f32x4{yv[4 * j], yv[4 * j + 1], yv[4 * j + 2], yv[4 * j + 3]};
+                    } else {
+                        *reinterpret_cast<bf16x4*>(dst + p) =
+                            bf16x4{bf16(yv[4 * j]), bf16(yv[4 * j + 1]), bf16(yv[4 * j + 2]), bf16(yv[4 * j + 3])};
+                    }
+                }
+            }
         }
+
+        if (W == 3 && has_next) build_vec(sm.vec[nxt], nd0, nd1, A2, valid1, lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next chunk's tiles have landed
+        __syncthreads();   // ... and every wave is done with this chunk's LDS and H
         write_h();
         __syncthreads();
+        if (has_next) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) cf[ks] = cfn[ks];
+        }
     }
 
     if (a.final_state) {
