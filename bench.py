@@ -15,6 +15,7 @@ Prints ONE JSON line.  value = prefill tokens/s per layer (conv + scan time);
 the decode state-update GB/s and its roofline fraction sit under "decode".
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16, published
 METRIC = "SSD prefill tokens/s per layer + decode state-update GB/s (frac. of roofline)"
+
+
+COPY_BYTES = 1 << 30         # plain device copy used as the practical HBM ceiling and counter calibration
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_scan_traffic.json")
+SCAN_SRC = os.path.join(ROOT, "selective_state_space_conv1d_amd", "csrc", "chunk_scan_mfma.hip")
+
+
+def scan_source_sha():
+    with open(SCAN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per chunk-scan launch from FETCH_SIZE/WRITE_SIZE counters (scaled by the same
+    counters on the plain copy), if they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t.get("bytes_per_launch") if t.get("kernel_source_sha") == scan_source_sha() else None
 
 
 def scan_bytes(d):
@@ -133,6 +155,21 @@ def main():
     yd = torch.empty(dd.batch, dd.nheads, dd.head_dim, dtype=dd.dtype, device=dev)
     torch.cuda.synchronize()
 
+    # plain device copy: the practical HBM ceiling (and the calibration kernel for byte counters)
+    csrc = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    csrc.fill_(1)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del csrc, cdst
+
     names = ["conv1d_fwd", "chunk_scan", "conv1d_update", "state_update"]
 
     def step(i, ev=None):
@@ -206,8 +243,9 @@ def main():
                     "conv_GBps": cb / avg["conv1d_fwd"] / 1e9,
                     "conv_frac": cb / avg["conv1d_fwd"] / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": "chunk_scan", "achieved": scan_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": sb},
+                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": sb, "kernel_source_sha": scan_source_sha()},
+        "copy_GBps": copy_gbs,
         "decode": {"value": upd_gbs, "unit": "GB/s", "kernel": "state_update",
                    "frac": upd_gbs / HBM_PEAK_GBS, "tokens_per_s": dd.batch / avg["state_update"],
                    "step_tokens_per_s": dd.batch / (avg["state_update"] + avg["conv1d_update"]),
