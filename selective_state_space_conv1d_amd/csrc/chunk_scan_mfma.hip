@@ -8,42 +8,48 @@
 // dt*A in base-2 units (decays are exp2 of differences):
 //   M[i][j] = (C_i . B_j) * exp2(cs_i - cs_j) * dt_j   (j <= i), + D on the diagonal
 //   y_i     = sum_j M[i][j] x_j  +  exp2(cs_i) * (C_i . H)
-//   H       = exp2(cs_last) * H + sum_j exp2(cs_last - cs_j) dt_j  x_j (x) B_j
+//   H       = exp2(cs_last) * H + sum_j (exp2(cs_last - cs_j) dt_j x_j) (x) B_j
 // which is the token recurrence re-associated exactly.
 //
-// Mapping.  One persistent workgroup of 4 waves per (batch, head) walks the
-// chunks in order; the fp32 state H lives in registers of the waves that own
-// its tiles and never goes to HBM between chunks.  All products are
-// v_mfma_f32_32x32x16_bf16 (a single wave issues these at full rate when it
-// keeps >= 4 independent accumulators in flight).  Wave w owns token tile w
-// (32 tokens): it computes C.B^T for the tiles j <= i of its rows, turns them
-// into M in registers, and uses the accumulators directly as the B operand of
-// y^T = X^T M^T (accumulator rows are the MFMA's k, so k is permuted the same
-// way on both operands).  It then adds exp2(cs_i) C.H (H read from LDS) and
-// writes y for its 32 tokens.  The chunk-state tiles H[p-tile][n-tile] are
-// spread over the waves with the least causal work (wave 0: p-tile 0 x all four
-// n-tiles, waves 1 and 2: p-tile 1 x two n-tiles, wave 3: none), which balances
-// the MFMA count at <= 112 per wave and chunk; the decay weight of the chunk
-// state is applied to the x operand, once per wave and p-tile.
+// Mapping.  One persistent workgroup of 8 waves (two per SIMD) per (batch,
+// head) walks the chunks in order; the fp32 state stays in registers and never
+// goes to HBM between chunks.  The waves have fixed roles:
+//   * y waves 0..3: wave t owns the 32 tokens of token tile t and both 32-wide
+//     p tiles.  It keeps its tokens' C rows in registers (the B operand of both
+//     C.H and C.B^T) and fetches the next chunk's rows itself, through a private
+//     LDS staging area, in two direct-copy rounds.  Per chunk it computes
+//     y^T = H C^T, scales by exp2(cs_i), then for each causal key tile the C.B^T
+//     tile, turns it into score-matrix operands M (bf16 hi + lo) in registers and
+//     accumulates y^T += X^T M^T; y goes out through the same staging area as
+//     whole 128-byte rows.
+//   * state waves 4..6 own the 8 [n-tile][p-tile] tiles of H^T (4, 3 and 1 of
+//     them) and add B^T (w x) per chunk; the decay-weighted x is formed in
+//     registers from x^T fragments.
+//   * wave 7 (with state wave 6) streams the next chunk's B and x tiles into the
+//     other half of double-buffered LDS and builds its per-token decay vectors.
+// MFMAs per SIMD and chunk (wave w and wave w + 4 share SIMD w): 48 + 64,
+// 64 + 48, 80 + 16, 96 + 0.  The C.B^T accumulator is used directly as the
+// B operand of X^T M^T: accumulator rows are that MFMA's k, and k is permuted
+// the same way on both operands.  All products are v_mfma_f32_32x32x16_bf16.
+// One workgroup barrier per chunk (the chunk's tiles, vectors and the previous
+// state are in LDS).  The state is single-buffered in LDS: each y wave bumps an
+// LDS counter once it has read it, and the state waves wait for all four before
+// writing the new one (a bounded wait; the y waves never wait on the state waves
+// inside a chunk, so the counter always fills).
 //
 // Precision.  x, B and C arrive in bf16 and are exact operands.  Operands
-// computed in fp32 (M, H and the decay-weighted B) are split into bf16 hi + lo
-// and issued as two MFMAs, keeping ~16 significant bits.  Decays inside a
-// chunk are exp2 of differences of the prefix sums (exact exp2(0) = 1 on the
-// diagonal); off-diagonal 32x32 blocks use the factorisation
-// exp2(cs_i - cs_e) * exp2(cs_e - cs_j) about the block's last token e, both
-// factors <= 1, so nothing overflows.
+// computed in fp32 (M, H and the decay-weighted x) are split into bf16 hi + lo
+// and issued as two MFMAs (~16 significant bits).  Decays are exp2 of
+// differences of prefix sums (exactly 1 on the diagonal); off-diagonal 32x32
+// blocks use exp2(cs_i - cs_e) * exp2(cs_e - cs_j) about the block's last token
+// e -- both factors <= 1, so nothing overflows.
 //
-// Data movement.  B and x tiles are staged row-major in LDS, double-buffered:
-// the next chunk's tiles stream in with direct global->LDS loads
-// (global_load_lds_dwordx4, no registers) while the current chunk computes.
-// Only the wave that owns a token tile reads its rows of C, so C goes straight
-// from global memory into that wave's MFMA operand registers (prefetched one
-// chunk ahead).  Operands that contract over tokens are read with
-// ds_read_b64_tr_b16 (LDS transpose read), so no transposed copies are kept.
-// Per-token decay vectors are built once per chunk by the wave with the fewest
-// MFMAs.  Workgroups are numbered so that the heads sharing a B/C group sit on
-// one XCD (its L2 then serves their common B and C).
+// Data movement.  Tiles are row-major and unpadded in LDS with the 16-byte
+// chunks of each row XOR-permuted by a key of the row, so that 16-byte row reads
+// and LDS transpose reads (ds_read_b64_tr_b16) are free of bank conflicts.
+// Operands that contract over tokens use the transpose reads, so no transposed
+// copies exist.  Workgroups are numbered so that the heads sharing a B/C group
+// sit on one XCD.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -53,14 +59,14 @@ namespace scan32 {
 constexpr int Q = 128;    // tokens per chunk
 constexpr int P = 64;     // head_dim
 constexpr int NS = 128;   // d_state
-constexpr int BS = 144;   // LDS row stride (bf16) of the [.][128] tiles: 72 dwords, 8-bank shift per row
-constexpr int XS = 80;    // LDS row stride (bf16) of the x tile: 40 dwords
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kRowB = NS * 2;   // bytes per row of the B and H tiles
+constexpr int kRowX = P * 2;    // bytes per row of the x tiles
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBInstr = Q * BS * 2 / 1024;   // 1-KB direct-load instructions per B tile (36)
-constexpr int kXInstr = Q * XS * 2 / 1024;   // per x tile (20)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -71,18 +77,35 @@ struct Vec {            // per-token quantities of one chunk
     float wS[Q];        // exp2(cs_last - cs_j) * dt_j for real tokens, 0 for padding
     float eY[Q];        // exp2(cs_i)
     float csE[4];       // cs at the end of each 32-token tile
-    float pad[4];
+    float dec;          // exp2(cs at the last real token): the chunk's decay of H
+    float pad[3];
 };
 
+constexpr int kStage = 16 * kRowB;      // per y wave: 16 C rows, or its 32 bf16 y rows
+
 struct Smem {
-    bf16 B[2][Q][BS];   // B[j][n], double-buffered over chunks
-    bf16 X[2][Q][XS];   // x[j][p], double-buffered over chunks
-    bf16 Hhi[P][BS];    // H[p][n], high and low bf16 parts
-    bf16 Hlo[P][BS];
-    Vec vec[2];         // the current chunk's and the next one's
+    unsigned char B[2][Q * kRowB];       // B[j][n], double-buffered
+    unsigned char X[2][Q * kRowX];       // x[j][p], double-buffered
+    unsigned char Hh[P * kRowB];         // H[p][n], high bf16 part
+    unsigned char Hl[P * kRowB];         //          low bf16 part
+    unsigned char stage[4][kStage];      // private to y wave t
+    Vec vec[2];
+    int hread;                           // y waves that have read the state (cumulative)
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-static_assert(Q * BS * 2 % 1024 == 0 && Q * XS * 2 % 1024 == 0, "tiles are whole 1-KB load blocks");
+
+// LDS swizzle.  The LDS has 64 four-byte banks (256 bytes per bank row).  A 256-byte
+// row (B, C, H) fills one bank row and has 16 chunks of 16 bytes; its chunks are
+// XOR-permuted by a 4-bit key of the row that is a bijection on any 16 consecutive
+// rows and gives 4 consecutive rows 4 different 4-chunk blocks.  A 128-byte row (x)
+// is half a bank row; a 3-bit key gives rows r and r + 2 different 4-chunk blocks.
+// Row reads (16 lanes per pass, 16 rows, one chunk each) and transpose reads (32
+// lanes per pass, 4 rows x 4 chunks) are then free of bank conflicts.
+__device__ __forceinline__ int key16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int key8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int RB> __device__ __forceinline__ int rkey(int r) { return RB == 256 ? key16(r) : key8(r); }
+// byte offset of logical 16-byte chunk c of row r in a tile of RB-byte rows
+template <int RB> __device__ __forceinline__ int soff(int r, int c) { return r * RB + ((c ^ rkey<RB>(r)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -95,57 +118,76 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 __device__ __forceinline__ bf16 bhi(float v) { return static_cast<bf16>(v); }
-__device__ __forceinline__ bf16 blo(float v, bf16 hi) { return static_cast<bf16>(v - static_cast<float>(hi)); }
 
-// MFMA operand whose k runs over tokens, read from a row-major [token][col] LDS
-// tile with two transpose reads.  Lane (c32 = lane%32, hf = lane/32) receives
-// column col_base + c32 at tokens j0 + 4hf + {0..3} (slots 0..3) and
-// j0 + 8 + 4hf + {0..3} (slots 4..7) -- the row order of a 32x32 accumulator
-// used as an operand.  Within each 16-lane group, lane m supplies the address
-// of row (first + m/4), columns col0 + 4(m%4) .. +3.
-__device__ __forceinline__ bf16x8 tr_frag(const bf16* mat, int rs, int j0, int col_base, int lane) {
-    const int m = lane & 15;
-    const int col = col_base + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
-    const int row = j0 + 4 * (lane >> 5) + (m >> 2);
-    const bf16* p0 = mat + row * rs + col;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)p0);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(p0 + 8 * rs));
+// Two-term bf16 split of 8 fp32 values: hi = v with the low 16 bits cleared (exact),
+// lo = RNE_bf16(v - hi); hi + lo carries ~16 significant bits.  Three VALU ops per
+// value: and, sub and half each of a byte permute and a packed convert.
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned u0 = __float_as_uint(v[2 * k]), u1 = __float_as_uint(v[2 * k + 1]);
+        const float r0 = v[2 * k] - __uint_as_float(u0 & 0xFFFF0000u);
+        const float r1 = v[2 * k + 1] - __uint_as_float(u1 & 0xFFFF0000u);
+        h[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);    // upper halves of u0 (low) and u1 (high)
+        l[k] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// RNE bf16 pair packed in one dword (low half = a)
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their maximum), as
+// the builtin so that the compiler's own wait insertion knows the loads are complete.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Lane-dependent byte offsets, computed once; every LDS access below is one of
+// these plus a compile-time constant (row block), so the compiler keeps only a
+// handful of address registers.
+//  * row reads: lane (c32, hf) reads row base + c32, 16-byte chunk 2ks + hf;
+//    the row key depends on c32 only (bases are multiples of 16 rows).
+//  * transpose reads (MFMA operands whose k runs over tokens): within each
+//    16-lane group, lane m supplies the address of row first + 4hf + m/4,
+//    columns col0 + 16g + 4(m%4) .. +3 (g = (lane/16)%2).  The receiving lane
+//    (c32, hf) then holds column col0 + c32 at tokens first + 4hf + {0..3};
+//    two reads (first and first + 8) give the 8 slots of an operand in the row
+//    order of a 32x32 accumulator.  first is a multiple of 16, so the key of a
+//    row read depends on rl (first read) or rl + 8 (second read) only.
+struct LaneOff {
+    int row[8];     // row reads of a 256-byte-row tile: c32 * 256 + swizzled chunk (2ks + hf)
+    int rl, cl, hb;
+    __device__ __forceinline__ LaneOff(int lane) {
+        const int c32 = lane & 31, hf = lane >> 5, rk = key16(c32);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) row[ks] = c32 * 256 + (((2 * ks + hf) ^ rk) << 4);
+        const int m = lane & 15;
+        rl = 4 * hf + (m >> 2);
+        cl = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+        hb = (m & 1) << 3;
+    }
+    // transpose-read base for a tile with RB-byte rows, columns from col0 (a multiple of 32),
+    // rows rl + 8h (h = 0 for the first read of an operand, 1 for the second)
+    template <int RB> __device__ __forceinline__ int tr(int col0, int h) const {
+        return rl * RB + ((((col0 >> 3) + cl) ^ rkey<RB>(rl + 8 * h)) << 4) + hb;
+    }
+};
+
+__device__ __forceinline__ bf16x8 ld16(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// operand from two transpose reads at rows j0 (base b0) and j0 + 8 (base b8), j0 % 16 == 0
+template <int RB>
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* t, int b0, int b8, int j0) {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(t + b0 + j0 * RB));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(t + b8 + (j0 + 8) * RB));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-struct Ctx {
-    const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
-    int64_t xs, bcs, b, L;
-    int H, h, grp;
-};
-
-// Direct global->LDS copy of one chunk's row-major tile into a padded LDS tile.
-// The tile is a sequence of 1-KB blocks; block k is written by wave k % 4 with
-// lane l storing LDS bytes [1024k + 16l, +16).  A lane whose bytes fall in a row's
-// padding, or in a row past the sequence end, re-reads a real row instead (the
-// padding is never read and rows past the end only meet zero weights).
-template <int RS, int DC, int NBLK>
-__device__ __forceinline__ void copy_tile(bf16* lds_tile, const bf16* g, int64_t row_stride, int64_t first_row,
-                                          int valid, int col_off, int W, int lane) {
-    constexpr int RB = RS * 2;            // LDS row bytes
-#pragma unroll
-    for (int m = 0; m < (NBLK + 3) / 4; ++m) {
-        const int k = W + 4 * m;
-        if (k < NBLK) {
-            const int o = 1024 * k + 16 * lane;
-            const int row = o / RB;
-            const int cb = o - row * RB;
-            const int r = row < valid ? row : valid - 1;
-            const int col = cb < 2 * DC ? cb / 2 : 0;    // DC real columns, the rest is padding
-            const bf16* src = g + (first_row + r) * row_stride + col_off + col;
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)((unsigned char*)lds_tile + 1024 * k),
-                                             16, 0, 0);
-        }
-    }
-}
-
 // Per-token vectors of a chunk from its dt (two tokens per lane of one wave).
+// r0, r1 are the raw dt of tokens 2*lane and 2*lane+1 (read from in-range rows);
+// tokens at or past `valid` count as dt = 0.
 __device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, int valid, int lane) {
     const float d0 = 2 * lane < valid ? static_cast<float>(r0) : 0.f;
     const float d1 = 2 * lane + 1 < valid ? static_cast<float>(r1) : 0.f;
@@ -173,154 +215,146 @@ __device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, in
     v.eY[j0] = fexp2(c0);
     v.eY[j1] = fexp2(c1);
     if ((lane & 15) == 15) v.csE[lane >> 4] = c1;
+    if (lane == 0) v.dec = fexp2(csl);
 }
 
-// Owned chunk-state tiles of wave W: tile k is H[p-tile pt][n-tile nt(k)].
-template <int W> struct Own {
-    static constexpr int n = W == 0 ? 4 : (W == 3 ? 0 : 2);
-    static constexpr int pt = W == 0 ? 0 : 1;
-    static constexpr int nt(int k) { return W == 2 ? 2 + k : k; }
+struct Ctx {
+    const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
+    int64_t xs, bcs, b, L, row0, nchunks;
+    int H, h, grp;
+    __device__ __forceinline__ int valid(int64_t c) const {
+        const int64_t r = L - c * Q;
+        return static_cast<int>(r < Q ? r : Q);
+    }
 };
 
-template <int W, typename TY>
-__device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
-    constexpr int IT = W;                       // this wave's token tile
-    constexpr int NO = Own<W>::n;
-    constexpr int NOA = NO > 0 ? NO : 1;
-    constexpr int PT = Own<W>::pt;
+// ---------------------------------------------------------------------------
+// Direct global->LDS copies of RB-byte rows: copy instruction k writes LDS bytes
+// [1024k, +1024) of dst, lane l the 16 bytes at 1024k + 16l.  The lane picks its
+// source so that the tile comes out swizzled: LDS chunk position cp of tile row r
+// receives logical chunk cp ^ rkey(r).  Copy k covers tile rows r_lo + RPK k + ...;
+// rows at or past `valid` re-read row valid - 1 (in range; such rows only meet zero
+// weights or are never stored).
+//
+// When every row is real the lane's part of the address is one of a few offsets
+// precomputed per lane (the key of row 4k + lane/16 depends on lane and k % 4 only;
+// that of row 8k + lane/8 on the lane only), added to a wave-uniform row base.
+template <int RB, int K0, int K1>
+__device__ __forceinline__ void dma_rows(unsigned char* dst, const bf16* src0, int64_t row_stride, int64_t row0,
+                                         int r_lo, int valid, int lane) {
+    constexpr int RPK = 1024 / RB;                 // rows per copy instruction
+    constexpr int LPR = RB / 16;                   // lanes per row
+    const unsigned char* g0 = reinterpret_cast<const unsigned char*>(src0 + (row0 + r_lo) * row_stride);
+    const int64_t sb = row_stride * 2;             // row stride in bytes
+    if (r_lo + RPK * K1 <= valid) {
+        const int lr = lane / LPR, cp = lane % LPR;
+        unsigned off[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            off[v] = static_cast<unsigned>(lr * sb) + 16u * static_cast<unsigned>(cp ^ rkey<RB>(r_lo + lr + RPK * v));
+#pragma unroll
+        for (int k = K0; k < K1; ++k) {
+            const unsigned char* src = g0 + k * RPK * sb + off[k & 3];
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int k = K0; k < K1; ++k) {
+            const int o = 1024 * k + 16 * lane;
+            const int row = o / RB, cp = (o % RB) >> 4;       // tile row r_lo + row
+            const int r = r_lo + row < valid ? row : valid - 1 - r_lo;
+            const unsigned char* src = g0 + r * sb + 16 * (cp ^ rkey<RB>(r_lo + row));
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+        }
+    }
+}
+
+// s_waitcnt lgkmcnt(0) (gfx9 encoding), before a copy overwrites LDS this wave just read
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// ---------------------------------------------------------------------------
+// y wave: token tile IT (tokens 32IT .. 32IT+31 of each chunk), both p tiles.
+template <typename TY, int IT>
+__device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
-    const int64_t L = cx.L;
-    const float A2 = a.A[cx.h] * kLog2e;
+    const int i = 32 * IT + c32;                     // this lane's token within the chunk
     const float Dh = a.D ? a.D[cx.h] : 0.f;
     TY* yg = static_cast<TY*>(a.y);
-    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
-    const int64_t nchunks = (L + Q - 1) / Q;
-    const int64_t row0 = cx.b * L;                                  // first token row of the sequence
-    const int bc_col = cx.grp * NS, x_col = cx.h * P;
-    const bf16* crow = cx.Cg + bc_col + 8 * hf;                     // + row * bcs + 16 ks
-    const int i = 32 * IT + c32;                                    // this lane's token in the chunk
+    const LaneOff lo(lane);
+    const int trX0 = lo.tr<kRowX>(0, 0), trX1 = lo.tr<kRowX>(32, 0);   // 128-byte rows: key period 8
+    unsigned char* st = sm.stage[IT];
+    const bf16* csrc = cx.Cg + static_cast<int64_t>(cx.grp) * NS;
 
-    auto load_c = [&](bf16x8 (&cf)[8], int64_t t0, int valid) {
-        const int r = i < valid ? i : valid - 1;
-        const bf16* src = crow + (row0 + t0 + r) * cx.bcs;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+    // C rows of token tile IT of chunk c, in two rounds of 16 rows through the staging
+    // area: copy round R (rows 32IT + 16R ..), then (after the copy lands) lanes with
+    // c32 / 16 == R take their row, 16-byte chunks 2ks + hf: k = n = 16ks + 8hf + s,
+    // the B operand (column i) of both H C^T and B C^T.
+    auto c_copy = [&](int64_t c, int R) {
+        dma_rows<kRowB, 0, 4>(st, csrc, cx.bcs, cx.row0 + c * Q, 32 * IT + 16 * R, cx.valid(c), lane);
     };
-    // dt of tokens 2*lane and 2*lane+1, read unconditionally from in-range rows; tokens past
-    // the sequence end are zeroed later, in build_vec, so nothing waits on these loads early
-    auto load_dt = [&](bf16& d0, bf16& d1, int64_t t0, int valid) {
-        const int r0 = 2 * lane < valid ? 2 * lane : valid - 1;
-        const int r1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
-        d0 = cx.dtg[(row0 + t0 + r0) * cx.H + cx.h];
-        d1 = cx.dtg[(row0 + t0 + r1) * cx.H + cx.h];
-    };
-
-    // ---- owned state tiles: Hs[k][4j + r] = H[p = 32PT + c32][n = 32nt + 8j + 4hf + r]
-    f32x16 Hs[NOA];
+    auto c_take = [&](bf16x8 (&cr)[8], int R) {
+        wait_vmem();
+        if ((c32 >> 4) == R) {
 #pragma unroll
-    for (int k = 0; k < NO; ++k) {
-        const int p = 32 * PT + c32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p * NS + n);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Hs[k][4 * j + r] = v[r];
+            for (int ks = 0; ks < 8; ++ks) cr[ks] = ld16(st + lo.row[ks] - R * kStage);
         }
+        wait_lds();
+    };
+
+    bf16x8 cn[8];
+    if (cx.nchunks > 0) {
+        c_copy(0, 0);
+        c_take(cn, 0);
+        c_copy(0, 1);
+        c_take(cn, 1);
     }
-    auto write_h = [&]() {
-#pragma unroll
-        for (int k = 0; k < NO; ++k) {
-            const int p = 32 * PT + c32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
-                bf16x4 hh, hl;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    hh[r] = bhi(Hs[k][4 * j + r]);
-                    hl[r] = blo(Hs[k][4 * j + r], hh[r]);
-                }
-                *reinterpret_cast<bf16x4*>(&sm.Hhi[p][n]) = hh;
-                *reinterpret_cast<bf16x4*>(&sm.Hlo[p][n]) = hl;
-            }
-        }
-    };
+    __syncthreads();                                            // chunk 0
 
-    bf16x8 cf[8];
-    if (nchunks > 0) {
-        const int valid0 = static_cast<int>(L < Q ? L : Q);
-        copy_tile<BS, NS, kBInstr>(&sm.B[0][0][0], cx.Bg, cx.bcs, row0, valid0, bc_col, W, lane);
-        copy_tile<XS, P, kXInstr>(&sm.X[0][0][0], cx.xg, cx.xs, row0, valid0, x_col, W, lane);
-        load_c(cf, 0, valid0);
-        if (W == 3) {
-            bf16 d0, d1;
-            load_dt(d0, d1, 0, valid0);
-            build_vec(sm.vec[0], d0, d1, A2, valid0, lane);
-        }
-        write_h();
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-
-    for (int64_t c = 0; c < nchunks; ++c) {
+    for (int64_t c = 0; c < cx.nchunks; ++c) {
         const int64_t t0 = c * Q;
-        const int valid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
-        const bool has_next = c + 1 < nchunks;
-        const int valid1 = has_next ? static_cast<int>((L - t0 - Q) < Q ? (L - t0 - Q) : Q) : 0;
-        const int cur = static_cast<int>(c & 1), nxt = cur ^ 1;
-        const Vec& v = sm.vec[cur];
-        const bf16* sB = &sm.B[cur][0][0];
-        const bf16* sX = &sm.X[cur][0][0];
+        const int valid = cx.valid(c);
+        const bool has_next = c + 1 < cx.nchunks;
+        const int buf = static_cast<int>(c & 1);
+        const Vec& v = sm.vec[buf];
+        const unsigned char* Bt = sm.B[buf];
+        const unsigned char* Xt = sm.X[buf];
+        bf16x8 cf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) cf[ks] = cn[ks];
+        if (has_next) c_copy(c + 1, 0);
 
-        // ---- stream the next chunk in: B and x straight to LDS, C rows and dt to registers
-        bf16x8 cfn[8];
-        bf16 nd0 = bf16(0.f), nd1 = bf16(0.f);
-        if (has_next) {
-            if (W == 3) load_dt(nd0, nd1, t0 + Q, valid1);
-            copy_tile<BS, NS, kBInstr>(&sm.B[nxt][0][0], cx.Bg, cx.bcs, row0 + t0 + Q, valid1, bc_col, W, lane);
-            copy_tile<XS, P, kXInstr>(&sm.X[nxt][0][0], cx.xg, cx.xs, row0 + t0 + Q, valid1, x_col, W, lane);
-            load_c(cfn, t0 + Q, valid1);
-        }
-
-        // ---- carried state: yo^T[p][i] = sum_n H[p][n] C[i][n]  (hi and lo of H, one chain per p tile)
-        f32x16 yo[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                const bf16x8 hh = *reinterpret_cast<const bf16x8*>(&sm.Hhi[32 * pt + c32][16 * ks + 8 * hf]);
-                const bf16x8 hl = *reinterpret_cast<const bf16x8*>(&sm.Hlo[32 * pt + c32][16 * ks + 8 * hf]);
-                yo[pt] = mfma32(hh, cf[ks], yo[pt]);
-                yo[pt] = mfma32(hl, cf[ks], yo[pt]);
-            }
-
-        // ---- C.B^T tiles (jt, IT), jt <= IT: acc rows = tokens j, cols = tokens i
-        constexpr int KP = IT == 0 ? 2 : 1;  // independent partial sums per tile
-        f32x16 cb[IT + 1][KP];
-#pragma unroll
-        for (int jt = 0; jt <= IT; ++jt)
-#pragma unroll
-            for (int kp = 0; kp < KP; ++kp) cb[jt][kp] = zero16();
+        // carried state: y^T[p][i] = sum_n H[p][n] C[i][n], p tiles 0 and 1
+        f32x16 y0 = zero16(), y1 = zero16();
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int jt = 0; jt <= IT; ++jt) {
-                const bf16x8 bf = *reinterpret_cast<const bf16x8*>(sB + (32 * jt + c32) * BS + 16 * ks + 8 * hf);
-                cb[jt][ks % KP] = mfma32(bf, cf[ks], cb[jt][ks % KP]);
-            }
+            y0 = mfma32(ld16(sm.Hh + lo.row[ks]), cf[ks], y0);
+            y1 = mfma32(ld16(sm.Hh + 32 * kRowB + lo.row[ks]), cf[ks], y1);
+            y0 = mfma32(ld16(sm.Hl + lo.row[ks]), cf[ks], y0);
+            y1 = mfma32(ld16(sm.Hl + 32 * kRowB + lo.row[ks]), cf[ks], y1);
         }
+        wait_lds();                                             // the state has been read
+        if (lane == 0) __hip_atomic_fetch_add(&sm.hread, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const float ey = v.eY[i];
+        y0 *= ey;
+        y1 *= ey;
 
-        // ---- per j tile: M = C.B^T * decay * dt (+ D on the diagonal) as bf16 hi/lo,
-        //      then y^T[p][i] += sum_j X^T[p][j] M^T[j][i]
+        // per causal key tile jt <= IT: the C.B^T tile (acc rows = tokens j, cols = tokens i),
+        // M = C.B^T * decay * dt (+ D on the diagonal) as bf16 hi/lo operands, and
+        // y^T[p][i] += sum_j X^T[p][j] M^T[j][i]
+        auto cbt = [&](int jt) {
+            f32x16 acc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) acc = mfma32(ld16(Bt + 32 * jt * kRowB + lo.row[ks]), cf[ks], acc);
+            return acc;
+        };
         const float csi = v.cs[i];
-        f32x16 yd[2] = {zero16(), zero16()};
+        f32x16 cbn = cbt(0);
 #pragma unroll
         for (int jt = 0; jt <= IT; ++jt) {
-            f32x16 m = cb[jt][0];
-#pragma unroll
-            for (int kp = 1; kp < KP; ++kp) m += cb[jt][kp];
+            f32x16 m = cbn;          // m[4j + r] = C_i . B_jj,  jj = 32jt + 8j + 4hf + r
+            if (jt < IT) cbn = cbt(jt + 1);   // the next tile's MFMAs overlap this tile's VALU work
             if (jt < IT) {
                 const float ai = fexp2(csi - v.csE[jt]);
 #pragma unroll
@@ -345,92 +379,228 @@ __device__ void run_wave(Smem& sm, const ScanArgs& a, const Ctx& cx, int lane) {
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                bf16x8 mh, ml;
+                float mv[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    mh[s] = bhi(m[8 * q + s]);
-                    ml[s] = blo(m[8 * q + s], mh[s]);
-                }
+                for (int s = 0; s < 8; ++s) mv[s] = m[8 * q + s];
+                bf16x8 mh, ml;
+                split8(mv, mh, ml);
+                const bf16x8 x0 = tr_frag<kRowX>(Xt, trX0, trX0, 32 * jt + 16 * q);
+                const bf16x8 x1 = tr_frag<kRowX>(Xt, trX1, trX1, 32 * jt + 16 * q);
+                y0 = mfma32(x0, mh, y0);
+                y1 = mfma32(x1, mh, y1);
+                y0 = mfma32(x0, ml, y0);
+                y1 = mfma32(x1, ml, y1);
+            }
+            if (jt == 0 && has_next) {         // first C round has landed by now
+                c_take(cn, 0);
+                c_copy(c + 1, 1);
+            }
+        }
+        if (has_next) c_take(cn, 1);
+
+        // y[token i][p]: lane (c32, hf) holds p = 32pt + 8j + 4hf + r in y_pt[4j + r].  Swapping
+        // j = 1 of the low half-wave with j = 0 of the high half-wave (and j = 3 with j = 2) leaves
+        // each lane with p = 32pt + 16g + 8hf + {0..7} (g = 0, 1): two 16-byte pieces per p tile.
+        TY* yrow = yg + ((cx.row0 + t0) * cx.H + cx.h) * static_cast<int64_t>(P);   // token 0, p 0
+        const int64_t ystr = static_cast<int64_t>(cx.H) * P;                         // token stride
+        if constexpr (sizeof(TY) == 4) {
+            if (i < valid) {
+                TY* dst = yrow + i * ystr + 8 * hf;
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    const bf16x8 xf = tr_frag(sX, XS, 32 * jt + 16 * q, 32 * pt, lane);
-                    yd[pt] = mfma32(xf, mh, yd[pt]);
-                    yd[pt] = mfma32(xf, ml, yd[pt]);
+                    const f32x16& yv = pt ? y1 : y0;
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        u32x4 lo4, hi4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float a0 = yv[8 * g + r], b0 = yv[8 * g + 4 + r];
+                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(b0),
+                                                                             false, false);
+                            lo4[r] = sw[0];
+                            hi4[r] = sw[1];
+                        }
+                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g) = lo4;
+                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g + 4) = hi4;
+                    }
                 }
             }
-        }
-
-        // ---- owned state tiles: H^T[n][p] = exp2(cs_last) H^T + sum_j B^T[n][j] (w_j x_j)[p]
-        if constexpr (NO > 0) {
-            const float alpha = fexp2(v.cs[valid - 1]);
-#pragma unroll
-            for (int k = 0; k < NO; ++k) Hs[k] *= alpha;
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int j0 = 32 * jt + 16 * q;
-                    const f32x4 w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
-                    const f32x4 w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
-                    const bf16x8 xf = tr_frag(sX, XS, j0, 32 * PT, lane);
-                    bf16x8 xh, xl;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const float e = static_cast<float>(xf[s]) * (s < 4 ? w0[s] : w1[s - 4]);
-                        xh[s] = bhi(e);
-                        xl[s] = blo(e, xh[s]);
-                    }
-#pragma unroll
-                    for (int k = 0; k < NO; ++k) {
-                        const bf16x8 bt = tr_frag(sB, BS, j0, 32 * Own<W>::nt(k), lane);
-                        Hs[k] = mfma32(bt, xh, Hs[k]);
-                        Hs[k] = mfma32(bt, xl, Hs[k]);
-                    }
-                }
-        }
-
-        // ---- y = y_diag + exp2(cs_i) * y_off for this wave's 32 tokens (lane = token i)
-        const float ey = v.eY[i];
-        if (i < valid) {
-            TY* dst = yg + ((row0 + t0 + i) * cx.H + cx.h) * static_cast<int64_t>(P);
+        } else {
+            // bf16: the 32 x 128-byte tile goes through the staging area (row c32, 16-byte
+            // chunk 4pt + 2g + hf, key of 128-byte rows by row pair), then out as whole rows:
+            // read k gives lane l row 8k + l/8, chunk l%8.
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const f32x16 yv = yd[pt] + ey * yo[pt];
+                const f32x16& yv = pt ? y1 : y0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = 32 * pt + 8 * j + 4 * hf;
-                    if constexpr (sizeof(TY) == 4) {
-                        *reinterpret_cast<f32x4*>(dst + p) = f32x4{yv[4 * j], yv[4 * j + 1], yv[4 * j + 2], yv[4 * j + 3]};
-                    } else {
-                        *reinterpret_cast<bf16x4*>(dst + p) =
-                            bf16x4{bf16(yv[4 * j]), bf16(yv[4 * j + 1]), bf16(yv[4 * j + 2]), bf16(yv[4 * j + 3])};
+                for (int g = 0; g < 2; ++g) {
+                    u32x4 o;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const unsigned pa = pack_bf16(yv[8 * g + 2 * h2], yv[8 * g + 2 * h2 + 1]);
+                        const unsigned pb = pack_bf16(yv[8 * g + 4 + 2 * h2], yv[8 * g + 4 + 2 * h2 + 1]);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(pa, pb, false, false);
+                        o[h2] = sw[0];
+                        o[2 + h2] = sw[1];
                     }
+                    const int ch = 4 * pt + 2 * g + hf;
+                    *reinterpret_cast<u32x4*>(st + c32 * kRowX + ((ch ^ ((c32 >> 1) & 7)) << 4)) = o;
                 }
             }
-        }
-
-        if (W == 3 && has_next) build_vec(sm.vec[nxt], nd0, nd1, A2, valid1, lane);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next chunk's tiles have landed
-        __syncthreads();   // ... and every wave is done with this chunk's LDS and H
-        write_h();
-        __syncthreads();
-        if (has_next) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) cf[ks] = cfn[ks];
+            for (int k = 0; k < 4; ++k) {
+                const int r = 8 * k + (lane >> 3), ch = lane & 7;
+                const u32x4 o = *reinterpret_cast<const u32x4*>(st + r * kRowX + ((ch ^ ((r >> 1) & 7)) << 4));
+                if (32 * IT + r < valid) *reinterpret_cast<u32x4*>(yrow + (32 * IT + r) * ystr + 8 * ch) = o;
+            }
+            wait_lds();                                         // staging free for the next copy
         }
+        __syncthreads();                                        // chunk c + 1
+    }
+}
+
+// ---------------------------------------------------------------------------
+// state wave: NT tiles of H^T, n tiles SN0 .. SN0+NT-1 of p tile SP.  Tile t holds
+// Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].  With DMA the
+// wave also copies the lower half of the next chunk's B tile.
+constexpr int kSpinMax = 1 << 20;
+
+template <int NT, int SP, int SN0, bool DMA>
+__device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    const int c32 = lane & 31, hf = lane >> 5;
+    const int hp = 32 * SP + c32;
+    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    const LaneOff lo(lane);
+    const int trW = lo.tr<kRowX>(32 * SP, 0);            // x^T fragments of the p tile
+    int trB0[NT], trB8[NT];                              // B^T fragments of the n tiles
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        trB0[t] = lo.tr<kRowB>(32 * (SN0 + t), 0);
+        trB8[t] = lo.tr<kRowB>(32 * (SN0 + t), 1);
+    }
+
+    f32x16 Hs[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Hs[t][4 * j + r] = v[r];
+        }
+    auto write_h = [&]() {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 hh, hl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hh[r] = bhi(Hs[t][4 * j + r]);
+                    hl[r] = static_cast<bf16>(Hs[t][4 * j + r] - static_cast<float>(hh[r]));
+                }
+                const int o = soff<kRowB>(hp, 4 * (SN0 + t) + j) + 8 * hf;
+                *reinterpret_cast<bf16x4*>(sm.Hh + o) = hh;
+                *reinterpret_cast<bf16x4*>(sm.Hl + o) = hl;
+            }
+    };
+
+    write_h();
+    __syncthreads();                                            // chunk 0
+
+    for (int64_t c = 0; c < cx.nchunks; ++c) {
+        const int buf = static_cast<int>(c & 1);
+        const Vec& v = sm.vec[buf];
+        const unsigned char* Bt = sm.B[buf];
+        const unsigned char* Xt = sm.X[buf];
+        if (DMA && c + 1 < cx.nchunks)
+            dma_rows<kRowB, 0, 16>(sm.B[buf ^ 1], cx.Bg + static_cast<int64_t>(cx.grp) * NS, cx.bcs,
+                                   cx.row0 + (c + 1) * Q, 0, cx.valid(c + 1), lane);
+        const float dec = v.dec;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) Hs[t] *= dec;
+
+        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B^T[n][j] (w_j x_j)[p]
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int j0 = 16 * k;
+            const bf16x8 xf = tr_frag<kRowX>(Xt, trW, trW, j0);
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
+            float e[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) e[s] = static_cast<float>(xf[s]) * (s < 4 ? w0[s] : w1[s - 4]);
+            bf16x8 wh, wl;
+            split8(e, wh, wl);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bf16x8 bt = tr_frag<kRowB>(Bt, trB0[t], trB8[t], j0);
+                Hs[t] = mfma32(bt, wh, Hs[t]);
+                Hs[t] = mfma32(bt, wl, Hs[t]);
+            }
+        }
+        // the y waves must have read the previous state before it is overwritten
+        const int target = 4 * static_cast<int>(c + 1);
+        for (int n = 0; n < kSpinMax; ++n) {
+            if (__hip_atomic_load(&sm.hread, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        write_h();
+        if (DMA) wait_vmem();
+        __syncthreads();                                        // chunk c + 1
     }
 
     if (a.final_state) {
 #pragma unroll
-        for (int k = 0; k < NO; ++k) {
-            const int p = 32 * PT + c32;
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = 32 * Own<W>::nt(k) + 8 * j + 4 * hf;
-                *reinterpret_cast<f32x4*>(a.final_state + sbase + p * NS + n) =
-                    f32x4{Hs[k][4 * j], Hs[k][4 * j + 1], Hs[k][4 * j + 2], Hs[k][4 * j + 3]};
+                const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
+                *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
+                    f32x4{Hs[t][4 * j], Hs[t][4 * j + 1], Hs[t][4 * j + 2], Hs[t][4 * j + 3]};
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// loader wave: x and the upper half of B of the next chunk, and its per-token vectors.
+__device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    const float A2 = a.A[cx.h] * kLog2e;
+    const bf16* bsrc = cx.Bg + static_cast<int64_t>(cx.grp) * NS;
+    const bf16* xsrc = cx.xg + static_cast<int64_t>(cx.h) * P;
+    auto load_dt = [&](bf16& d0, bf16& d1, int64_t t0, int valid) {
+        const int r0 = 2 * lane < valid ? 2 * lane : valid - 1;
+        const int r1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
+        d0 = cx.dtg[(cx.row0 + t0 + r0) * cx.H + cx.h];
+        d1 = cx.dtg[(cx.row0 + t0 + r1) * cx.H + cx.h];
+    };
+    if (lane == 0) sm.hread = 0;
+    if (cx.nchunks > 0) {
+        bf16 d0, d1;
+        const int v0 = cx.valid(0);
+        load_dt(d0, d1, 0, v0);
+        dma_rows<kRowX, 0, 16>(sm.X[0], xsrc, cx.xs, cx.row0, 0, v0, lane);
+        dma_rows<kRowB, 0, 32>(sm.B[0], bsrc, cx.bcs, cx.row0, 0, v0, lane);
+        build_vec(sm.vec[0], d0, d1, A2, v0, lane);
+    }
+    wait_vmem();
+    __syncthreads();                                            // chunk 0
+
+    for (int64_t c = 0; c < cx.nchunks; ++c) {
+        const int buf = static_cast<int>(c & 1);
+        if (c + 1 < cx.nchunks) {
+            const int64_t r0 = cx.row0 + (c + 1) * Q;
+            const int vn = cx.valid(c + 1);
+            bf16 d0, d1;
+            load_dt(d0, d1, (c + 1) * Q, vn);
+            dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
+            dma_rows<kRowB, 16, 32>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
+            build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane);
         }
+        wait_vmem();
+        __syncthreads();                                        // chunk c + 1
     }
 }
 
@@ -453,16 +623,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     cx.b = id / a.nheads;
     cx.h = static_cast<int>(id % a.nheads);
     cx.L = a.seqlen;
+    cx.row0 = cx.b * a.seqlen;
+    cx.nchunks = (a.seqlen + Q - 1) / Q;
     cx.H = a.nheads;
     cx.grp = cx.h / (a.nheads / a.ngroups);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    switch (wave) {
-        case 0: run_wave<0, TY>(sm, a, cx, lane); break;
-        case 1: run_wave<1, TY>(sm, a, cx, lane); break;
-        case 2: run_wave<2, TY>(sm, a, cx, lane); break;
-        default: run_wave<3, TY>(sm, a, cx, lane); break;
-    }
+    // wave w runs on SIMD w % 4; the role split balances MFMAs per SIMD
+    if (wave == 0) run_y<TY, 0>(sm, a, cx, lane);
+    else if (wave == 1) run_y<TY, 1>(sm, a, cx, lane);
+    else if (wave == 2) run_y<TY, 2>(sm, a, cx, lane);
+    else if (wave == 3) run_y<TY, 3>(sm, a, cx, lane);
+    else if (wave == 4) run_s<4, 0, 0, false>(sm, a, cx, lane);
+    else if (wave == 5) run_s<3, 1, 0, false>(sm, a, cx, lane);
+    else if (wave == 6) run_s<1, 1, 3, true>(sm, a, cx, lane);
+    else run_l(sm, a, cx, lane);
 }
 
 }  // namespace scan32
