@@ -16,17 +16,19 @@
 // goes to HBM between chunks.  The waves have fixed roles:
 //   * y waves 0..3: wave t owns the 32 tokens of token tile t and both 32-wide
 //     p tiles.  It keeps its tokens' C rows in registers (the B operand of both
-//     C.H and C.B^T) and fetches the next chunk's rows itself, through a private
-//     LDS staging area, in two direct-copy rounds.  Per chunk it computes
-//     y^T = H C^T, scales by exp2(cs_i), then for each causal key tile the C.B^T
-//     tile, turns it into score-matrix operands M (bf16 hi + lo) in registers and
-//     accumulates y^T += X^T M^T; y goes out through the same staging area as
-//     whole 128-byte rows.
+//     C.H and C.B^T) and loads the next chunk's rows itself, straight into
+//     registers.  Per chunk it computes y^T = H C^T, scales by exp2(cs_i), then
+//     for each causal key tile the C.B^T tile, turns it into score-matrix operands
+//     M (bf16 hi + lo) in registers and accumulates y^T += X^T M^T; y goes out
+//     through a private LDS staging area as whole 128-byte rows.
 //   * state waves 4..6 own the 8 [n-tile][p-tile] tiles of H^T (4, 3 and 1 of
 //     them) and add B^T (w x) per chunk; the decay-weighted x is formed in
 //     registers from x^T fragments.
-//   * wave 7 (with state wave 6) streams the next chunk's B and x tiles into the
-//     other half of double-buffered LDS and builds its per-token decay vectors.
+//   * wave 7 copies the next chunk's B and x tiles into the other half of
+//     double-buffered LDS and builds its per-token decay vectors.  It is the only
+//     wave that issues direct global->LDS copies: the compiler makes every LDS
+//     transpose read or LDS atomic wait for all copies in flight, and the other
+//     waves use those.
 // MFMAs per SIMD and chunk (wave w and wave w + 4 share SIMD w): 48 + 64,
 // 64 + 48, 80 + 16, 96 + 0.  The C.B^T accumulator is used directly as the
 // B operand of X^T M^T: accumulator rows are that MFMA's k, and k is permuted
@@ -81,7 +83,7 @@ struct Vec {            // per-token quantities of one chunk
     float pad[3];
 };
 
-constexpr int kStage = 16 * kRowB;      // per y wave: 16 C rows, or its 32 bf16 y rows
+constexpr int kStage = 32 * kRowX;      // per y wave: its 32 bf16 y rows
 
 struct Smem {
     unsigned char B[2][Q * kRowB];       // B[j][n], double-buffered
@@ -287,29 +289,20 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     unsigned char* st = sm.stage[IT];
     const bf16* csrc = cx.Cg + static_cast<int64_t>(cx.grp) * NS;
 
-    // C rows of token tile IT of chunk c, in two rounds of 16 rows through the staging
-    // area: copy round R (rows 32IT + 16R ..), then (after the copy lands) lanes with
-    // c32 / 16 == R take their row, 16-byte chunks 2ks + hf: k = n = 16ks + 8hf + s,
-    // the B operand (column i) of both H C^T and B C^T.
-    auto c_copy = [&](int64_t c, int R) {
-        dma_rows<kRowB, 0, 4>(st, csrc, cx.bcs, cx.row0 + c * Q, 32 * IT + 16 * R, cx.valid(c), lane);
-    };
-    auto c_take = [&](bf16x8 (&cr)[8], int R) {
-        wait_vmem();
-        if ((c32 >> 4) == R) {
+    // C row of token i of chunk c, 16-byte chunks 2ks + hf: k = n = 16ks + 8hf + s, the
+    // B operand (column i) of both H C^T and B C^T; loaded straight into registers (an
+    // LDS copy would make the compiler wait for it before every later transpose read).
+    // Rows past the end re-read the last real row.
+    auto c_load = [&](bf16x8 (&cr)[8], int64_t c, int k0, int k1) {
+        const int valid = cx.valid(c);
+        const int r = i < valid ? i : valid - 1;
+        const bf16* p = csrc + (cx.row0 + c * Q + r) * cx.bcs + 8 * hf;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) cr[ks] = ld16(st + lo.row[ks] - R * kStage);
-        }
-        wait_lds();
+        for (int ks = k0; ks < k1; ++ks) cr[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
     };
 
     bf16x8 cn[8];
-    if (cx.nchunks > 0) {
-        c_copy(0, 0);
-        c_take(cn, 0);
-        c_copy(0, 1);
-        c_take(cn, 1);
-    }
+    if (cx.nchunks > 0) c_load(cn, 0, 0, 8);
     __syncthreads();                                            // chunk 0
 
     for (int64_t c = 0; c < cx.nchunks; ++c) {
@@ -323,19 +316,39 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         bf16x8 cf[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) cf[ks] = cn[ks];
-        if (has_next) c_copy(c + 1, 0);
 
-        // carried state: y^T[p][i] = sum_n H[p][n] C[i][n], p tiles 0 and 1
+        // carried state: y^T[p][i] = sum_n H[p][n] C[i][n], p tiles 0 and 1.  The 32 state
+        // fragments are read in batches of 8, one batch ahead of the MFMAs that use them
+        // (scheduling barriers keep the compiler from sinking each read to its use).
         f32x16 y0 = zero16(), y1 = zero16();
+        {
+            auto hfrag = [&](int k) {   // k = 4ks + 2hl + pt
+                const unsigned char* hb = (k & 2) ? sm.Hl : sm.Hh;
+                return ld16(hb + (k & 1) * 32 * kRowB + lo.row[k >> 2]);
+            };
+            bf16x8 hf[32];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            y0 = mfma32(ld16(sm.Hh + lo.row[ks]), cf[ks], y0);
-            y1 = mfma32(ld16(sm.Hh + 32 * kRowB + lo.row[ks]), cf[ks], y1);
-            y0 = mfma32(ld16(sm.Hl + lo.row[ks]), cf[ks], y0);
-            y1 = mfma32(ld16(sm.Hl + 32 * kRowB + lo.row[ks]), cf[ks], y1);
+            for (int k = 0; k < 8; ++k) hf[k] = hfrag(k);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (g < 3) {
+#pragma unroll
+                    for (int k = 8 * (g + 1); k < 8 * (g + 2); ++k) hf[k] = hfrag(k);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 8 * g; k < 8 * (g + 1); ++k) {
+                    if (k & 1) y1 = mfma32(hf[k], cf[k >> 2], y1);
+                    else y0 = mfma32(hf[k], cf[k >> 2], y0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        wait_lds();                                             // the state has been read
-        if (lane == 0) __hip_atomic_fetch_add(&sm.hread, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the state has been read: LDS executes a wave's operations in issue order, so the
+        // counter update lands after this wave's state reads (no fence, which would also
+        // wait for the C copy in flight)
+        if (lane == 0) __hip_atomic_fetch_add(&sm.hread, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (has_next) c_load(cn, c + 1, 0, 4);
         const float ey = v.eY[i];
         y0 *= ey;
         y1 *= ey;
@@ -391,12 +404,8 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 y0 = mfma32(x0, ml, y0);
                 y1 = mfma32(x1, ml, y1);
             }
-            if (jt == 0 && has_next) {         // first C round has landed by now
-                c_take(cn, 0);
-                c_copy(c + 1, 1);
-            }
+            if (jt == 0 && has_next) c_load(cn, c + 1, 4, 8);
         }
-        if (has_next) c_take(cn, 1);
 
         // y[token i][p]: lane (c32, hf) holds p = 32pt + 8j + 4hf + r in y_pt[4j + r].  Swapping
         // j = 1 of the low half-wave with j = 0 of the high half-wave (and j = 3 with j = 2) leaves
@@ -453,7 +462,6 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 const u32x4 o = *reinterpret_cast<const u32x4*>(st + r * kRowX + ((ch ^ ((r >> 1) & 7)) << 4));
                 if (32 * IT + r < valid) *reinterpret_cast<u32x4*>(yrow + (32 * IT + r) * ystr + 8 * ch) = o;
             }
-            wait_lds();                                         // staging free for the next copy
         }
         __syncthreads();                                        // chunk c + 1
     }
@@ -461,11 +469,10 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 
 // ---------------------------------------------------------------------------
 // state wave: NT tiles of H^T, n tiles SN0 .. SN0+NT-1 of p tile SP.  Tile t holds
-// Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].  With DMA the
-// wave also copies the lower half of the next chunk's B tile.
+// Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].
 constexpr int kSpinMax = 1 << 20;
 
-template <int NT, int SP, int SN0, bool DMA>
+template <int NT, int SP, int SN0>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int hp = 32 * SP + c32;
@@ -515,9 +522,6 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         const Vec& v = sm.vec[buf];
         const unsigned char* Bt = sm.B[buf];
         const unsigned char* Xt = sm.X[buf];
-        if (DMA && c + 1 < cx.nchunks)
-            dma_rows<kRowB, 0, 16>(sm.B[buf ^ 1], cx.Bg + static_cast<int64_t>(cx.grp) * NS, cx.bcs,
-                                   cx.row0 + (c + 1) * Q, 0, cx.valid(c + 1), lane);
         const float dec = v.dec;
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hs[t] *= dec;
@@ -544,11 +548,11 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         // the y waves must have read the previous state before it is overwritten
         const int target = 4 * static_cast<int>(c + 1);
         for (int n = 0; n < kSpinMax; ++n) {
-            if (__hip_atomic_load(&sm.hread, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+            if (__hip_atomic_load(&sm.hread, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
             __builtin_amdgcn_s_sleep(1);
         }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the state writes stay after the wait
         write_h();
-        if (DMA) wait_vmem();
         __syncthreads();                                        // chunk c + 1
     }
 
@@ -565,7 +569,7 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 }
 
 // ---------------------------------------------------------------------------
-// loader wave: x and the upper half of B of the next chunk, and its per-token vectors.
+// loader wave: the next chunk's B and x tiles, and its per-token vectors.
 __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const float A2 = a.A[cx.h] * kLog2e;
     const bf16* bsrc = cx.Bg + static_cast<int64_t>(cx.grp) * NS;
@@ -596,7 +600,7 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
             bf16 d0, d1;
             load_dt(d0, d1, (c + 1) * Q, vn);
             dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
-            dma_rows<kRowB, 16, 32>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
+            dma_rows<kRowB, 0, 32>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
             build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane);
         }
         wait_vmem();
@@ -634,9 +638,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     else if (wave == 1) run_y<TY, 1>(sm, a, cx, lane);
     else if (wave == 2) run_y<TY, 2>(sm, a, cx, lane);
     else if (wave == 3) run_y<TY, 3>(sm, a, cx, lane);
-    else if (wave == 4) run_s<4, 0, 0, false>(sm, a, cx, lane);
-    else if (wave == 5) run_s<3, 1, 0, false>(sm, a, cx, lane);
-    else if (wave == 6) run_s<1, 1, 3, true>(sm, a, cx, lane);
+    else if (wave == 4) run_s<4, 0, 0>(sm, a, cx, lane);
+    else if (wave == 5) run_s<3, 1, 0>(sm, a, cx, lane);
+    else if (wave == 6) run_s<1, 1, 3>(sm, a, cx, lane);
     else run_l(sm, a, cx, lane);
 }
 
