@@ -30,24 +30,33 @@ METRIC = "SSD prefill tokens/s per layer + decode state-update GB/s (frac. of ro
 
 
 COPY_BYTES = 1 << 30         # plain device copy used as the practical HBM ceiling and counter calibration
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_scan_traffic.json")
-SCAN_SRC = os.path.join(ROOT, "selective_state_space_conv1d_amd", "csrc", "chunk_scan_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "selective_state_space_conv1d_amd", "csrc")
+KERNEL_SRC = {"chunk_scan": "chunk_scan_mfma.hip", "state_update": "state_update.hip", "conv1d_fwd": "conv1d.hip"}
 
 
-def scan_source_sha():
-    with open(SCAN_SRC, "rb") as f:
+def source_sha(kernel):
+    with open(os.path.join(CSRC, KERNEL_SRC[kernel]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per chunk-scan launch from FETCH_SIZE/WRITE_SIZE counters (scaled by the same
-    counters on the plain copy), if they were taken on the current kernel source; else None."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE/WRITE_SIZE counter runs (each
+    scaled by the same counter on a plain 1 GiB copy), if they were taken on the current
+    kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = json.load(f)["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
         return None
-    return t.get("bytes_per_launch") if t.get("kernel_source_sha") == scan_source_sha() else None
+    return t.get("bytes_per_launch") if t.get("source_sha") == source_sha(kernel) else None
+
+
+def traffic_rate(kernel, seconds):
+    """measured HBM bytes per launch over the launch's average duration, GB/s (the unit of
+    `achieved`), or None when no counter data exists for the current source"""
+    b = measured_traffic(kernel)
+    return None if b is None else b / seconds / 1e9
 
 
 def scan_bytes(d):
@@ -243,15 +252,19 @@ def main():
                     "conv_GBps": cb / avg["conv1d_fwd"] / 1e9,
                     "conv_frac": cb / avg["conv1d_fwd"] / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": "chunk_scan", "achieved": scan_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "algorithmic_bytes_per_launch": sb, "kernel_source_sha": scan_source_sha()},
+                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_rate("chunk_scan", avg["chunk_scan"]),
+                     "traffic_bytes_per_launch": measured_traffic("chunk_scan"),
+                     "algorithmic_bytes_per_launch": sb, "kernel_source_sha": source_sha("chunk_scan")},
         "copy_GBps": copy_gbs,
         "decode": {"value": upd_gbs, "unit": "GB/s", "kernel": "state_update",
                    "frac": upd_gbs / HBM_PEAK_GBS, "tokens_per_s": dd.batch / avg["state_update"],
                    "step_tokens_per_s": dd.batch / (avg["state_update"] + avg["conv1d_update"]),
                    "algorithmic_bytes_per_launch": ub,
                    "roofline": {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": upd_gbs / HBM_PEAK_GBS, "traffic": None},
+                                "frac": upd_gbs / HBM_PEAK_GBS,
+                                "traffic": traffic_rate("state_update", avg["state_update"]),
+                                "traffic_bytes_per_launch": measured_traffic("state_update")},
                    "conv_update_GBps": cub / avg["conv1d_update"] / 1e9},
     }
     if not args.no_cpu_baseline:
