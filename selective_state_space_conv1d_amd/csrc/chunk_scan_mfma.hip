@@ -24,11 +24,13 @@
 //   * state waves 4..6 own the 8 [n-tile][p-tile] tiles of H^T (4, 3 and 1 of
 //     them) and add B^T (w x) per chunk; the decay-weighted x is formed in
 //     registers from x^T fragments.
-//   * wave 7 copies the next chunk's B and x tiles into the other half of
-//     double-buffered LDS and builds its per-token decay vectors.  It is the only
-//     wave that issues direct global->LDS copies: the compiler makes every LDS
-//     transpose read or LDS atomic wait for all copies in flight, and the other
-//     waves use those.
+//   * wave 7 copies the next chunk's x tile and the lower half of its B tile into
+//     the other half of double-buffered LDS early in the chunk (x comes from HBM)
+//     and builds its per-token decay vectors.  y wave 0, the lightest, copies the
+//     upper half of B (L2-resident) once its single causal tile is done.  The
+//     compiler makes every LDS transpose read or LDS atomic wait for all copies in
+//     flight, so a wave copies only after its last transpose read and atomic of
+//     the chunk.
 // MFMAs per SIMD and chunk (wave w and wave w + 4 share SIMD w): 48 + 64,
 // 64 + 48, 80 + 16, 96 + 0.  The C.B^T accumulator is used directly as the
 // B operand of X^T M^T: accumulator rows are that MFMA's k, and k is permuted
@@ -84,6 +86,7 @@ struct Vec {            // per-token quantities of one chunk
 };
 
 constexpr int kStage = 32 * kRowX;      // per y wave: its 32 bf16 y rows
+constexpr int kYB = 16;                 // B copy units [kYB, 32) are moved by y wave 0, the rest by the loader
 
 struct Smem {
     unsigned char B[2][Q * kRowB];       // B[j][n], double-buffered
@@ -406,6 +409,15 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
             }
             if (jt == 0 && has_next) c_load(cn, c + 1, 4, 8);
         }
+        if constexpr (IT == 0) {
+            // the lightest y wave copies the upper half of the next chunk's B tile (L2-resident:
+            // the group's heads share it), after its last transpose read of the chunk
+            if (has_next) {
+                const int64_t r0 = cx.row0 + (c + 1) * Q;
+                dma_rows<kRowB, kYB, 32>(sm.B[buf ^ 1], cx.Bg + static_cast<int64_t>(cx.grp) * NS, cx.bcs, r0, 0,
+                                         cx.valid(c + 1), lane);
+            }
+        }
 
         // y[token i][p]: lane (c32, hf) holds p = 32pt + 8j + 4hf + r in y_pt[4j + r].  Swapping
         // j = 1 of the low half-wave with j = 0 of the high half-wave (and j = 3 with j = 2) leaves
@@ -463,6 +475,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 if (32 * IT + r < valid) *reinterpret_cast<u32x4*>(yrow + (32 * IT + r) * ystr + 8 * ch) = o;
             }
         }
+        if constexpr (IT == 0) wait_vmem();
         __syncthreads();                                        // chunk c + 1
     }
 }
@@ -569,7 +582,8 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 }
 
 // ---------------------------------------------------------------------------
-// loader wave: the next chunk's B and x tiles, and its per-token vectors.
+// loader wave: the next chunk's x tile and the lower half of its B tile, and its
+// per-token vectors.
 __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const float A2 = a.A[cx.h] * kLog2e;
     const bf16* bsrc = cx.Bg + static_cast<int64_t>(cx.grp) * NS;
@@ -600,7 +614,7 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
             bf16 d0, d1;
             load_dt(d0, d1, (c + 1) * Q, vn);
             dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
-            dma_rows<kRowB, 0, 32>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
+            dma_rows<kRowB, 0, kYB>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
             build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane);
         }
         wait_vmem();
