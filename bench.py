@@ -13,6 +13,10 @@ by HIP events on the launch stream; averages per kernel feed the roofline.
 
 Prints ONE JSON line.  value = prefill tokens/s per layer (conv + scan time);
 the decode state-update GB/s and its roofline fraction sit under "decode".
+"serving" times the packed-batch forms on their own: a prefill of 8192 tokens in 24
+requests of mixed lengths (ssd_conv1d_fwd_varlen + ssd_chunk_scan_varlen on the request
+slots of conv- and ssm-state pools), and the decode update of 64 requests on a 96-slot
+state pool (ssd_state_update_slots).
 """
 import argparse
 import hashlib
@@ -89,6 +93,77 @@ def update_bytes(d):
 
 def conv_update_bytes(d):
     return d.batch * d.conv_dim * (2 + 2 + 4 * 2 * 2) + d.conv_dim * 5 * 2
+
+
+def varlen_scan_bytes(d, T, n_init, n_final):
+    """Algorithmic bytes of a packed scan: the per-token traffic of scan_bytes over T rows, the
+    initial states of the requests that continue one, and every request's final state."""
+    per_token = 2 * (d.nheads * d.head_dim) * 2 + 2 * d.ngroups * d.d_state * 2 + d.nheads * 2
+    return T * per_token + (n_init + n_final) * d.nheads * d.head_dim * d.d_state * 4
+
+
+def varlen_conv_bytes(d, T, n_init, n_final):
+    """Packed conv: T rows in and out (bf16), taps and bias, conv states read and written."""
+    return T * d.conv_dim * 2 * 2 + d.conv_dim * 5 * 2 + (n_init + n_final) * d.conv_dim * 4 * 2
+
+
+def serving_leg(ssd, torch, dev, steps, warmup):
+    """Packed prefill and slot-pool decode, each launch bracketed by HIP events."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, scan_inputs, varlen_inputs, varlen_lengths
+    dv = WORKLOADS["varlen_ultra_8k"]
+    lens = varlen_lengths(dv.seqlen, dv.batch, 1006)
+    nslots = 32
+    vin = varlen_inputs(dv, lens, nslots, 1006, device=dev)
+    T = dv.seqlen
+    vout = torch.empty(T, dv.conv_dim, dtype=dv.dtype, device=dev)
+    xv, Bv, Cv = ssd.split_xbc(vout, dv.nheads, dv.head_dim, dv.ngroups, dv.d_state)
+    yv = torch.empty(T, dv.nheads, dv.head_dim, dtype=dv.dtype, device=dev)
+    n_init = int(vin["has_initial_state"].sum().item())
+    dd = WORKLOADS["decode_ultra_b64"]
+    npool = 96
+    pool = torch.randn(npool, dd.nheads, dd.head_dim, dd.d_state, device=dev) * 0.1
+    sin = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(dd, 1012, seqlen=1).items()}
+    g = torch.Generator(device="cpu").manual_seed(1013)
+    slot = torch.randperm(npool, generator=g)[:dd.batch].to(torch.int32).to(dev)
+    yd = torch.empty(dd.batch, dd.nheads, dd.head_dim, dtype=dd.dtype, device=dev)
+    torch.cuda.synchronize()
+
+    def one(ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record()
+        mark(0)
+        ssd.ssd_conv1d_fwd_varlen(vin["xbc"], vin["w"], vin["bias"], vin["cu_seqlens"], vin["conv_pool"],
+                                  vin["slot_idx"], vin["has_initial_state"], out=vout)
+        mark(1)
+        ssd.ssd_chunk_scan_varlen(xv, Bv, Cv, vin["dt"], vin["A"], vin["D"], vin["cu_seqlens"], vin["state_pool"],
+                                  vin["slot_idx"], vin["has_initial_state"], y=yv, chunk=dv.chunk)
+        mark(2)
+        ssd.ssd_state_update_slots(pool, slot, sin["x"][:, 0], sin["Bm"][:, 0], sin["Cm"][:, 0], sin["dt"][:, 0],
+                                   sin["A"], sin["D"], y=yd)
+        mark(3)
+
+    for _ in range(warmup):
+        one()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    t = [[e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs] for j in range(3)]
+    conv_s, scan_s, upd_s = (sum(v) / len(v) for v in t)
+    sb = varlen_scan_bytes(dv, T, n_init, dv.batch)
+    cb = varlen_conv_bytes(dv, T, n_init, dv.batch)
+    ub = update_bytes(dd)
+    return {
+        "prefill_varlen": {"requests": dv.batch, "tokens": T, "min_len": min(lens), "max_len": max(lens),
+                           "nslots": nslots, "requests_with_initial_state": n_init,
+                           "tokens_per_s": T / (conv_s + scan_s), "conv_us": conv_s * 1e6, "scan_us": scan_s * 1e6,
+                           "scan_GBps": sb / scan_s / 1e9, "scan_frac": sb / scan_s / 1e9 / HBM_PEAK_GBS,
+                           "scan_algorithmic_bytes": sb, "conv_GBps": cb / conv_s / 1e9,
+                           "conv_frac": cb / conv_s / 1e9 / HBM_PEAK_GBS},
+        "decode_slots": {"batch": dd.batch, "nslots": npool, "us": upd_s * 1e6, "GBps": ub / upd_s / 1e9,
+                         "frac": ub / upd_s / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": ub},
+    }
 
 
 def cpu_baseline(orc, inp, d, n_heads=256):
@@ -267,6 +342,9 @@ def main():
                                 "traffic_bytes_per_launch": measured_traffic("state_update")},
                    "conv_update_GBps": cub / avg["conv1d_update"] / 1e9},
     }
+    del v, x, Bm, Cm, y, state
+    print("[bench] serving forms (packed prefill, slot-pool decode)", file=sys.stderr, flush=True)
+    out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

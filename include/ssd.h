@@ -9,6 +9,9 @@
  *   ssd_chunk_scan     the SSD chunked scan of a prefill: y and the fp32 final
  *                      state from x, dt, A, B, C, D and an optional initial state
  *   ssd_state_update   the single-token selective state update (decode)
+ * and their serving forms on packed variable-length batches and state pools:
+ *   ssd_conv1d_fwd_varlen, ssd_chunk_scan_varlen, ssd_conv1d_update_slots,
+ *   ssd_state_update_slots
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
@@ -153,6 +156,81 @@ ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state,
                               const void* B, const void* C, int64_t bc_row_stride,
                               const void* dt, const float* A, const float* D, void* y,
                               hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Packed variable-length batches and state pools (serving).  [P2] "Mamba SSM 缓存详解" and
+ * "Prefill 阶段": the conv and SSM states live in per-request cache slots that the
+ * prefill writes in place.  [P3] 5.4: the kernels read and write the pool slots directly,
+ * with no gather or scatter around them.  [P1] "状态契约": decode advances one token per
+ * request.
+ *
+ * For the prefill calls, d->batch is the number of sequences S and d->seqlen is the
+ * number of packed token rows T.  Sequence s covers rows [cu_seqlens[s], cu_seqlens[s+1])
+ * of every packed tensor.
+ *  cu_seqlens         [S + 1] int32, device memory, nondecreasing from 0 to T.  Values
+ *                     outside [0, T] are clamped, so a malformed table cannot address
+ *                     outside the buffers, but its results are unspecified.
+ *  slot_idx           [S] int32 device memory, or NULL for slot s.  A negative slot, or
+ *                     one >= nslots, marks padding: the sequence starts from zeros and its
+ *                     final state is not stored.  Slots of one call must be distinct.
+ *  has_initial_state  [S] int32 device memory, or NULL for all zero.  Nonzero starts
+ *                     sequence s from its slot's state; zero starts from zeros.
+ *  nslots             Pool entries, >= 0.  A pool may be NULL only when nslots is 0.
+ * The tables and pools belong to the caller and are read on the device, in stream order.
+ */
+
+/*
+ * Varlen prefill conv.
+ *  xbc              [T, CD] act dtype, rows xbc_row_stride elements apart.
+ *  conv_state_pool  [nslots, CD, 4] act dtype, updated in place.  Each sequence with a
+ *                   slot gets its last 4 inputs, taking earlier columns from its old
+ *                   state (or zeros) when it has fewer than 4 tokens.
+ *  out              [T, CD] contiguous act dtype.  Rows outside every sequence are not written.
+ * w, bias and the other rules are as for ssd_conv1d_fwd.  The call makes two launches on
+ * `stream`: the per-token pass, then the pass that writes the pool.
+ */
+ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                   const void* w, const void* bias, const int32_t* cu_seqlens,
+                                   const int32_t* slot_idx, const int32_t* has_initial_state,
+                                   void* conv_state_pool, int64_t nslots, void* out, hipStream_t stream);
+
+/*
+ * Varlen SSD chunked scan.  Each sequence is scanned on its own, with chunks starting at
+ * its first row.  The result equals ssd_chunk_scan run per sequence.
+ *  x, B, C, dt   packed [T, ...] rows with the strides of ssd_chunk_scan (batch stride unused).
+ *  state_pool    [nslots, H, P, N] fp32, updated in place: the initial state is read as
+ *                has_initial_state says, and the final state is written to every sequence's slot.
+ *  y             [T, H, P] contiguous y dtype.
+ * chunk, A, D and workspace as for ssd_chunk_scan.
+ */
+ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                   const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                   const float* A, const float* D, const int32_t* cu_seqlens,
+                                   const int32_t* slot_idx, const int32_t* has_initial_state,
+                                   float* state_pool, int64_t nslots, void* y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One-token conv update on a conv-state pool.  Batch entry b uses slot slot_idx[b] of
+ * conv_state_pool [nslots, CD, 4].  slot_idx is [B] int32 device memory and required.
+ * A padding entry (slot < 0 or >= nslots) is convolved against a zero window and stores no
+ * state.  The rest is as for ssd_conv1d_update.
+ */
+ssd_status_t ssd_conv1d_update_slots(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                     const void* w, const void* bias, const int32_t* slot_idx,
+                                     void* conv_state_pool, int64_t nslots, void* out, hipStream_t stream);
+
+/*
+ * Single-token state update on a state pool.  Batch entry b updates slot slot_idx[b] of
+ * state_pool [nslots, H, P, N] fp32 in place.  slot_idx is [B] int32 device memory and
+ * required.  A padding entry starts from a zero state and stores nothing; its y is still
+ * written.  The rest is as for ssd_state_update.
+ */
+ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int64_t nslots,
+                                    const int32_t* slot_idx, const void* x, int64_t x_row_stride,
+                                    const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                    const float* A, const float* D, void* y, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

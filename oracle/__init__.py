@@ -8,6 +8,8 @@ module only marshals numpy arrays into it.
 Parity pins (see ``tests/test_oracle_pins.py``): brute-force semiseparable
 form, the d_state=1 closed form, ``torch.nn.functional.conv1d``, and the
 invariants dt=0, reset, prefill-then-decode, split prefill, group
-equivalence, linearity and zero-B/C.
+equivalence, linearity and zero-B/C.  The packed-batch (varlen) and
+state-pool forms run those routines per sequence; their indexing is pinned by
+``tests/test_oracle_varlen.py``.
 """
 from .oracle import Oracle, load  # noqa: F401

@@ -99,6 +99,80 @@ class Oracle:
                                      _ptr(dt), _ptr(A), _ptr(D), _ptr(y))
         return y, st
 
+    # ------------------------------------------------------------------ packed batches
+    # The plain per-sequence definition of the packed calls: sequence s is rows
+    # [cu[s], cu[s+1]) of the packed [T, ...] tensors and is run on its own by the routines
+    # above.  Its states are slot slot[s] (s when slot is None) of the pools; has_init[s] != 0
+    # starts it from that slot, else from zeros.  A slot outside [0, nslots) is padding: zero
+    # start, nothing stored.  Pools are returned as updated copies.
+    @staticmethod
+    def _slot(slot, s, nslots):
+        v = s if slot is None else int(slot[s])
+        return v if 0 <= v < nslots else -1
+
+    # u [T,CD], pool [nslots,CD,K]|None -> v [T,CD], new pool
+    def conv1d_fwd_varlen(self, u, w, bias, cu, pool=None, slot=None, has_init=None):
+        u = _f64(u)
+        cu = [int(c) for c in cu]
+        v = np.zeros_like(u)
+        new = None if pool is None else np.array(pool, dtype=np.float64, order="C", copy=True)
+        nslots = 0 if pool is None else new.shape[0]
+        for s in range(len(cu) - 1):
+            a, b = cu[s], cu[s + 1]
+            k = self._slot(slot, s, nslots)
+            start = k >= 0 and has_init is not None and int(has_init[s]) != 0
+            vs, s_out = self.conv1d_fwd(u[None, a:b], w, bias, new[k][None] if start else None)
+            v[a:b] = vs[0]
+            if k >= 0:
+                new[k] = s_out[0]
+        return v, new
+
+    # x [T,H,P], Bm/Cm [T,G,N], dt [T,H], pool [nslots,H,P,N]|None -> y [T,H,P], new pool
+    def scan_varlen(self, x, Bm, Cm, dt, A, D, cu, pool=None, slot=None, has_init=None):
+        x, Bm, Cm, dt = map(_f64, (x, Bm, Cm, dt))
+        cu = [int(c) for c in cu]
+        y = np.zeros_like(x)
+        new = None if pool is None else np.array(pool, dtype=np.float64, order="C", copy=True)
+        nslots = 0 if pool is None else new.shape[0]
+        for s in range(len(cu) - 1):
+            a, b = cu[s], cu[s + 1]
+            k = self._slot(slot, s, nslots)
+            start = k >= 0 and has_init is not None and int(has_init[s]) != 0
+            ys, fin = self.scan(x[None, a:b], Bm[None, a:b], Cm[None, a:b], dt[None, a:b], A, D,
+                                new[k][None] if start else None)
+            y[a:b] = ys[0]
+            if k >= 0:
+                new[k] = fin[0]
+        return y, new
+
+    # u [B,CD], pool [nslots,CD,K], slot [B] -> v [B,CD], new pool
+    def conv1d_update_slots(self, u, w, bias, pool, slot):
+        u = _f64(u)
+        new = np.array(pool, dtype=np.float64, order="C", copy=True)
+        v = np.zeros_like(u)
+        for b in range(u.shape[0]):
+            k = self._slot(slot, b, new.shape[0])
+            win = new[k][None] if k >= 0 else np.zeros((1,) + new.shape[1:])
+            vb, wb = self.conv1d_update(u[b:b + 1], w, bias, win)
+            v[b] = vb[0]
+            if k >= 0:
+                new[k] = wb[0]
+        return v, new
+
+    # pool [nslots,H,P,N], slot [B], x [B,H,P], Bm/Cm [B,G,N], dt [B,H] -> y [B,H,P], new pool
+    def state_update_slots(self, pool, slot, x, Bm, Cm, dt, A, D=None):
+        x, Bm, Cm, dt = map(_f64, (x, Bm, Cm, dt))
+        new = np.array(pool, dtype=np.float64, order="C", copy=True)
+        y = np.zeros_like(x)
+        for b in range(x.shape[0]):
+            k = self._slot(slot, b, new.shape[0])
+            st = new[k][None] if k >= 0 else np.zeros((1,) + new.shape[1:])
+            yb, sb = self.state_update(st, x[b:b + 1], Bm[b:b + 1], Cm[b:b + 1], dt[b:b + 1], A, D)
+            y[b] = yb[0]
+            if k >= 0:
+                new[k] = sb[0]
+        return y, new
+
 
 _DEFAULT = None
 

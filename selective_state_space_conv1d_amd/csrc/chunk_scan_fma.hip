@@ -37,8 +37,16 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
     FmaSmem& sm = *reinterpret_cast<FmaSmem*>(smem_raw);
     const int tid = threadIdx.x;
     const int H = a.nheads, P = a.head_dim, N = a.d_state;
-    const int64_t L = a.seqlen;
-    const int64_t b = blockIdx.x / H;
+    const int64_t b = blockIdx.x / H;   // batch entry, or sequence of a packed batch
+    int64_t L = a.seqlen, row0 = b * a.seqlen, sidx = b;
+    bool use_init = true, write_final = true;
+    if (a.seq.cu_seqlens) {
+        seq_span(a.seq.cu_seqlens, b, a.seqlen, row0, L);
+        const int64_t slot = seq_slot(a.seq.slot_idx, b, a.seq.nslots);
+        sidx = slot < 0 ? 0 : slot;
+        use_init = slot >= 0 && a.seq.has_init && a.seq.has_init[b] != 0;
+        write_final = slot >= 0;
+    }
     const int h = static_cast<int>(blockIdx.x % H);
     const int g = h / (H / a.ngroups);
     const float Ah = a.A[h];
@@ -48,11 +56,11 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
     const T* Cg = static_cast<const T*>(a.C);
     const T* dtg = static_cast<const T*>(a.dt);
     TY* yg = static_cast<TY*>(a.y);
-    const int64_t sbase = (b * H + h) * static_cast<int64_t>(P) * N;
+    const int64_t sbase = (sidx * H + h) * static_cast<int64_t>(P) * N;
 
     for (int e = tid; e < P * N; e += kFmaThreads) {
         const int p = e / N, n = e - p * N;
-        sm.H[p][n] = a.init_state ? a.init_state[sbase + e] : 0.f;
+        sm.H[p][n] = (a.init_state && use_init) ? a.init_state[sbase + e] : 0.f;
     }
 
     for (int64_t t0 = 0; t0 < L; t0 += kT) {
@@ -60,18 +68,18 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
         __syncthreads();
         for (int e = tid; e < kT * P; e += kFmaThreads) {
             const int j = e / P, p = e - j * P;
-            sm.X[j][p] = j < valid ? static_cast<float>(xg[(b * L + t0 + j) * a.x_row_stride +
+            sm.X[j][p] = j < valid ? static_cast<float>(xg[(row0 + t0 + j) * a.x_row_stride +
                                                          static_cast<int64_t>(h) * P + p])
                                    : 0.f;
         }
         for (int e = tid; e < kT * N; e += kFmaThreads) {
             const int j = e / N, n = e - j * N;
-            const int64_t o = (b * L + t0 + j) * a.bc_row_stride + static_cast<int64_t>(g) * N + n;
+            const int64_t o = (row0 + t0 + j) * a.bc_row_stride + static_cast<int64_t>(g) * N + n;
             sm.B[j][n] = j < valid ? static_cast<float>(Bg[o]) : 0.f;
             sm.C[j][n] = j < valid ? static_cast<float>(Cg[o]) : 0.f;
         }
         if (tid < kT) {
-            const float d = tid < valid ? static_cast<float>(dtg[(b * L + t0 + tid) * H + h]) : 0.f;
+            const float d = tid < valid ? static_cast<float>(dtg[(row0 + t0 + tid) * H + h]) : 0.f;
             sm.dt[tid] = d;
             // inclusive prefix sum of dt*A over the block (lanes 0..31 of wave 0)
             float v = d * Ah;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
             for (int j = 0; j <= i; ++j) yd = fmaf(sm.M[i][j], sm.X[j][p], yd);
             float yo = 0.f;
             for (int n = 0; n < N; ++n) yo = fmaf(sm.C[i][n], sm.H[p][n], yo);
-            yg[((b * L + t0 + i) * H + h) * static_cast<int64_t>(P) + p] =
+            yg[((row0 + t0 + i) * H + h) * static_cast<int64_t>(P) + p] =
                 static_cast<TY>(yd + expf(sm.cs[i]) * yo);
         }
         __syncthreads();
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
         }
     }
     __syncthreads();
-    if (a.final_state)
+    if (a.final_state && write_final)
         for (int e = tid; e < P * N; e += kFmaThreads) {
             const int p = e / N, n = e - p * N;
             a.final_state[sbase + e] = sm.H[p][n];

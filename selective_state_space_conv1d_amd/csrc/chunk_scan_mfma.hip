@@ -226,6 +226,8 @@ __device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, in
 struct Ctx {
     const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
     int64_t xs, bcs, b, L, row0, nchunks;
+    int64_t sidx;                 // state index (batch entry, or the sequence's pool slot)
+    bool use_init, write_final;   // read the initial state / write the final state
     int H, h, grp;
     __device__ __forceinline__ int valid(int64_t c) const {
         const int64_t r = L - c * Q;
@@ -489,7 +491,7 @@ template <int NT, int SP, int SN0>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int hp = 32 * SP + c32;
-    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    const int64_t sbase = (cx.sidx * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
     const LaneOff lo(lane);
     const int trW = lo.tr<kRowX>(32 * SP, 0);            // x^T fragments of the p tile
     int trB0[NT], trB8[NT];                              // B^T fragments of the n tiles
@@ -506,7 +508,7 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         for (int j = 0; j < 4; ++j) {
             const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
+            if (a.init_state && cx.use_init) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
 #pragma unroll
             for (int r = 0; r < 4; ++r) Hs[t][4 * j + r] = v[r];
         }
@@ -569,7 +571,7 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         __syncthreads();                                        // chunk c + 1
     }
 
-    if (a.final_state) {
+    if (a.final_state && cx.write_final) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -626,11 +628,15 @@ template <typename TY>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-    // XCD-aware numbering: workgroup id % 8 picks the XCD, so give each XCD a
-    // contiguous run of (batch, head) -- heads of one group share B and C in its L2.
-    const int64_t nb = a.batch * a.nheads;
+    // XCD-aware numbering: workgroup id % 8 picks the XCD.  XCD k takes heads
+    // [k H/8, (k+1) H/8) of every batch entry / sequence: heads of one group share B
+    // and C in that XCD's L2, and every XCD gets an equal share of each sequence
+    // (packed batches mix short and long ones).
     int64_t id = blockIdx.x;
-    if (nb % 8 == 0) id = (id % 8) * (nb / 8) + id / 8;
+    if (a.nheads % 8 == 0) {
+        const int64_t hpx = a.nheads / 8, j = id / 8;
+        id = (j / hpx) * a.nheads + (id % 8) * hpx + j % hpx;
+    }
     Ctx cx;
     cx.xg = static_cast<const bf16*>(a.x);
     cx.Bg = static_cast<const bf16*>(a.B);
@@ -640,9 +646,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     cx.bcs = a.bc_row_stride;
     cx.b = id / a.nheads;
     cx.h = static_cast<int>(id % a.nheads);
-    cx.L = a.seqlen;
-    cx.row0 = cx.b * a.seqlen;
-    cx.nchunks = (a.seqlen + Q - 1) / Q;
+    if (a.seq.cu_seqlens) {   // packed sequences: rows and state slot from the caller's tables
+        seq_span(a.seq.cu_seqlens, cx.b, a.seqlen, cx.row0, cx.L);
+        const int64_t slot = seq_slot(a.seq.slot_idx, cx.b, a.seq.nslots);
+        cx.sidx = slot < 0 ? 0 : slot;
+        cx.use_init = slot >= 0 && a.seq.has_init && a.seq.has_init[cx.b] != 0;
+        cx.write_final = slot >= 0;
+    } else {
+        cx.L = a.seqlen;
+        cx.row0 = cx.b * a.seqlen;
+        cx.sidx = cx.b;
+        cx.use_init = cx.write_final = true;
+    }
+    cx.nchunks = (cx.L + Q - 1) / Q;
     cx.H = a.nheads;
     cx.grp = cx.h / (a.nheads / a.ngroups);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

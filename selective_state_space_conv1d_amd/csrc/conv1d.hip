@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
 template <typename T>
 __global__ __launch_bounds__(kConvThreads) void conv1d_update_kernel(
     const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w, const T* __restrict__ bias,
-    T* __restrict__ state, T* __restrict__ out, int64_t CD, int64_t total) {
+    T* __restrict__ state, T* __restrict__ out, int64_t CD, int64_t total, const int32_t* __restrict__ slot_idx,
+    int64_t nslots) {
     constexpr int V = Vec16<T>::n;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x;
     if (idx >= total) return;
@@ -141,9 +142,16 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_update_kernel(
     const int64_t c0 = (idx - b * per_b) * V;
 
     float s[4 * V], wt[4 * V], u[V], bs[V], o[V];
-    T* sp = state + (b * CD + c0) * 4;
+    // the window of batch entry b (its pool slot with a slot table; none for padding)
+    const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    T* sp = state + (slot < 0 ? 0 : slot * CD + c0) * 4;
+    if (slot >= 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load16_f32(sp + q * V, s + q * V);
+        for (int q = 0; q < 4; ++q) load16_f32(sp + q * V, s + q * V);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4 * V; ++k) s[k] = 0.f;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) load16_f32(w + c0 * 4 + q * V, wt + q * V);
     load16_f32(xbc + b * xs + c0, u);
@@ -163,9 +171,207 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_update_kernel(
         for (int k = 0; k < 4; ++k) acc = fmaf(wt[v * 4 + k], sv[k], acc);
         o[v] = silu_f(acc);
     }
+    if (slot >= 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store16_f32(sp + q * V, s + q * V);
+        for (int q = 0; q < 4; ++q) store16_f32(sp + q * V, s + q * V);
+    }
     store16_f32(out + b * CD + c0, o);
+}
+
+// ---------------------------------------------------------------------------
+// Packed variable-length prefill: token rows [cu[s], cu[s+1]) belong to sequence s, whose halo
+// comes from its conv-state slot (zeros without an initial state).  Token tiles run over the
+// packed rows and may straddle sequences; the window restarts at each sequence's first token.
+// Rows outside every sequence (only with a malformed table) are not written.
+struct SeqView {
+    const int32_t* cu; const int32_t* slot; const int32_t* init; int64_t nseq, nslots, total;
+    __device__ __forceinline__ void span(int64_t s, int64_t& start, int64_t& end) const {
+        int64_t len;
+        seq_span(cu, s, total, start, len);
+        end = start + len;
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
+    const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w, const T* __restrict__ bias,
+    const T* pool, T* __restrict__ out, int64_t CD, int64_t cblocks, SeqView sv) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t cb = blockIdx.x % cblocks;
+    const int64_t tile = blockIdx.x / cblocks;
+    const int64_t c0 = (cb * kConvThreads + threadIdx.x) * V;
+    if (c0 >= CD) return;
+    const int64_t t0 = tile * kConvTokens;
+    const int64_t t1 = (t0 + kConvTokens < sv.total) ? t0 + kConvTokens : sv.total;
+
+    float wt[4][V], bs[V];
+    {
+        float tmp[4 * V];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load16_f32(w + c0 * 4 + q * V, tmp + q * V);
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wt[k][v] = tmp[v * 4 + k];
+    }
+    if (bias) load16_f32(bias + c0, bs);
+    else
+#pragma unroll
+        for (int v = 0; v < V; ++v) bs[v] = 0.f;
+
+    // the last sequence whose first row is <= t0 (binary search; the table is nondecreasing)
+    int64_t lo = 0, hi = sv.nseq - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        int64_t st, en;
+        sv.span(mid, st, en);
+        if (st <= t0) lo = mid;
+        else hi = mid - 1;
+    }
+    int64_t s = lo, start, end;
+    sv.span(s, start, end);
+    bool have = false;
+    float win[3][V];
+    for (int64_t t = t0; t < t1; ++t) {
+        while (t >= end && s + 1 < sv.nseq) {
+            ++s;
+            sv.span(s, start, end);
+            have = false;
+        }
+        if (t < start || t >= end) continue;
+        if (!have) {   // window at the tile's first row in s, or at s's first row
+            const int64_t slot = seq_slot(sv.slot, s, sv.nslots);
+            const bool from_state = slot >= 0 && sv.init && sv.init[s] != 0;
+            float st[4][V];
+            if (from_state && t - start < 3) {
+                float tmp[4 * V];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) load16_f32(pool + (slot * CD + c0) * 4 + q * V, tmp + q * V);
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) st[k][v] = tmp[v * 4 + k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int v = 0; v < V; ++v) st[k][v] = 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int64_t tau = t - 3 + k;   // input row of window slot k
+                if (tau >= start) {
+                    load16_f32(xbc + tau * xs + c0, win[k]);
+                } else {
+                    const int j = 4 + static_cast<int>(tau - start);   // state column 1..3
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        float x = st[1][v];
+                        if (j == 2) x = st[2][v];
+                        if (j == 3) x = st[3][v];
+                        win[k][v] = x;
+                    }
+                }
+            }
+            have = true;
+        }
+        float u[V], o[V];
+        load16_f32(xbc + t * xs + c0, u);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float acc = bs[v];
+            acc = fmaf(wt[0][v], win[0][v], acc);
+            acc = fmaf(wt[1][v], win[1][v], acc);
+            acc = fmaf(wt[2][v], win[2][v], acc);
+            acc = fmaf(wt[3][v], u[v], acc);
+            o[v] = silu_f(acc);
+            win[0][v] = win[1][v];
+            win[1][v] = win[2][v];
+            win[2][v] = u[v];
+        }
+        store16_f32(out + t * CD + c0, o);
+    }
+}
+
+// New conv state of every sequence with a slot: column k = input row end - 4 + k, from the old
+// state (or zeros) where that is before the sequence's first row.  Runs after the per-token pass,
+// which reads the old states; each thread reads its own old columns before writing them.
+template <typename T>
+__global__ __launch_bounds__(kConvThreads) void conv_state_varlen_kernel(const T* __restrict__ xbc, int64_t xs,
+                                                                         T* pool, int64_t CD, SeqView sv) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x) * V;
+    if (c0 >= CD) return;
+    const int64_t s = blockIdx.y;
+    const int64_t slot = seq_slot(sv.slot, s, sv.nslots);
+    if (slot < 0) return;
+    int64_t start, end;
+    sv.span(s, start, end);
+    T* sp = pool + (slot * CD + c0) * 4;
+    float old[4][V];
+    const bool from_state = sv.init && sv.init[s] != 0;
+    {
+        float tmp[4 * V];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (from_state) load16_f32(sp + q * V, tmp + q * V);
+            else
+#pragma unroll
+                for (int v = 0; v < V; ++v) tmp[q * V + v] = 0.f;
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) old[k][v] = tmp[v * 4 + k];
+    }
+    float ns[4][V];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t tau = end - 4 + k;
+        if (tau >= start) {
+            load16_f32(xbc + tau * xs + c0, ns[k]);
+        } else {
+            const int64_t j = 4 + (tau - start);   // old column 0..3 (at least k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float x = old[0][v];
+                if (j == 1) x = old[1][v];
+                if (j == 2) x = old[2][v];
+                if (j == 3) x = old[3][v];
+                ns[k][v] = x;
+            }
+        }
+    }
+    float tmp[4 * V];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tmp[v * 4 + k] = ns[k][v];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store16_f32(sp + q * V, tmp + q * V);
+}
+
+template <typename T>
+static hipError_t conv_fwd_varlen_t(const ConvFwdArgs& a, hipStream_t s) {
+    constexpr int V = Vec16<T>::n;
+    if (a.batch == 0 || a.channels == 0) return hipSuccess;
+    const int64_t cblocks = (a.channels / V + kConvThreads - 1) / kConvThreads;
+    SeqView sv{a.seq.cu_seqlens, a.seq.slot_idx, a.seq.has_init, a.batch, a.seq.nslots, a.seqlen};
+    T* pool = static_cast<T*>(a.state_out);
+    if (a.seqlen > 0) {
+        const int64_t tiles = (a.seqlen + kConvTokens - 1) / kConvTokens;
+        hipLaunchKernelGGL(conv1d_fwd_varlen_kernel<T>, dim3(static_cast<uint32_t>(cblocks * tiles)),
+                           dim3(kConvThreads), 0, s, static_cast<const T*>(a.xbc), a.xbc_row_stride,
+                           static_cast<const T*>(a.w), static_cast<const T*>(a.bias), pool,
+                           static_cast<T*>(a.out), a.channels, cblocks, sv);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (pool == nullptr || a.seq.nslots == 0) return hipSuccess;
+    hipLaunchKernelGGL(conv_state_varlen_kernel<T>, dim3(static_cast<uint32_t>(cblocks), static_cast<uint32_t>(a.batch)),
+                       dim3(kConvThreads), 0, s, static_cast<const T*>(a.xbc), a.xbc_row_stride, pool,
+                       a.channels, sv);
+    return hipGetLastError();
 }
 
 template <typename T>
@@ -193,12 +399,16 @@ static hipError_t conv_update_t(const ConvUpdateArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(conv1d_update_kernel<T>, dim3(static_cast<uint32_t>(blocks)), dim3(kConvThreads),
                        0, s, static_cast<const T*>(a.xbc), a.xbc_row_stride, static_cast<const T*>(a.w),
                        static_cast<const T*>(a.bias), static_cast<T*>(a.state), static_cast<T*>(a.out),
-                       a.channels, total);
+                       a.channels, total, a.slot_idx, a.nslots);
     return hipGetLastError();
 }
 
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, Dt act, hipStream_t s) {
     return act == Dt::BF16 ? conv_fwd_t<bf16>(a, s) : conv_fwd_t<float>(a, s);
+}
+
+hipError_t launch_conv1d_fwd_varlen(const ConvFwdArgs& a, Dt act, hipStream_t s) {
+    return act == Dt::BF16 ? conv_fwd_varlen_t<bf16>(a, s) : conv_fwd_varlen_t<float>(a, s);
 }
 
 hipError_t launch_conv1d_update(const ConvUpdateArgs& a, Dt act, hipStream_t s) {

@@ -28,6 +28,15 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
 
 ssd_status_t hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// Packed variable-length calls: tables and pool present as the sizes require.
+ssd_status_t check_seq_tables(const ssd_dims_t* d, const int32_t* cu_seqlens, const void* pool, int64_t nslots) {
+    if (nslots < 0) return SSD_ERR_SHAPE;
+    if (d->batch > 0 && !cu_seqlens) return SSD_ERR_NULL;
+    if (nslots > 0 && !pool) return SSD_ERR_NULL;
+    if (pool && !aligned16(pool)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +95,45 @@ ssd_status_t ssd_conv1d_update(const ssd_dims_t* d, const void* xbc, int64_t xbc
     return hip_status(ssd::launch_conv1d_update(a, static_cast<Dt>(d->act_dtype), stream));
 }
 
+ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                   const void* w, const void* bias, const int32_t* cu_seqlens,
+                                   const int32_t* slot_idx, const int32_t* has_initial_state,
+                                   void* conv_state_pool, int64_t nslots, void* out, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    st = check_seq_tables(d, cu_seqlens, conv_state_pool, nslots);
+    if (st != SSD_OK) return st;
+    const int64_t CD = ssd_conv_dim(d);
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if ((tokens || (d->batch > 0 && nslots > 0)) && (!w || (tokens && (!xbc || !out)))) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (tokens && xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, w, bias, static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::ConvFwdArgs a{xbc, xbc_row_stride, w, bias, conv_state_pool, conv_state_pool, out,
+                       d->batch, d->seqlen, CD, {cu_seqlens, slot_idx, has_initial_state, nslots}};
+    return hip_status(ssd::launch_conv1d_fwd_varlen(a, static_cast<Dt>(d->act_dtype), stream));
+}
+
+ssd_status_t ssd_conv1d_update_slots(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                     const void* w, const void* bias, const int32_t* slot_idx,
+                                     void* conv_state_pool, int64_t nslots, void* out, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    const int64_t CD = ssd_conv_dim(d);
+    if (nslots < 0) return SSD_ERR_SHAPE;
+    if (d->batch > 0 && (!xbc || !w || !out || !slot_idx)) return SSD_ERR_NULL;
+    if (nslots > 0 && !conv_state_pool) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, w, bias, static_cast<const void*>(conv_state_pool), static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::ConvUpdateArgs a{xbc, xbc_row_stride, w, bias, conv_state_pool, out, d->batch, CD, slot_idx, nslots};
+    return hip_status(ssd::launch_conv1d_update(a, static_cast<Dt>(d->act_dtype), stream));
+}
+
 size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
     (void)d;
     (void)chunk;
@@ -118,6 +166,59 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
     return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
+}
+
+ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                  const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                  const float* A, const float* D, const int32_t* cu_seqlens,
+                                  const int32_t* slot_idx, const int32_t* has_initial_state, float* state_pool,
+                                  int64_t nslots, void* y, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    st = check_seq_tables(d, cu_seqlens, state_pool, nslots);
+    if (st != SSD_OK) return st;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return SSD_ERR_UNSUPPORTED;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (tokens && (x_row_stride < I || bc_row_stride < GN)) return SSD_ERR_SHAPE;
+    if (!stride_ok(x_row_stride, d->act_dtype) || !stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {x, B, C, static_cast<const void*>(y)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
+    if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
+    (void)workspace;
+    if (d->batch > 0 && !tokens && nslots == 0) return SSD_OK;   // nothing to compute or store
+    ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,
+                    d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
+                    {cu_seqlens, slot_idx, has_initial_state, nslots}};
+    const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
+    if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
+        return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
+    return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
+}
+
+ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int64_t nslots, const int32_t* slot_idx,
+                                    const void* x, int64_t x_row_stride, const void* B, const void* C,
+                                    int64_t bc_row_stride, const void* dt, const float* A, const float* D, void* y,
+                                    hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    if (nslots < 0) return SSD_ERR_SHAPE;
+    if (d->batch > 0 && (!x || !B || !C || !dt || !A || !y || !slot_idx)) return SSD_ERR_NULL;
+    if (nslots > 0 && !state_pool) return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
+    if (state_pool && !aligned16(state_pool)) return SSD_ERR_ALIGN;
+    ssd::UpdateArgs a{state_pool, x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, slot_idx, nslots};
+    return hip_status(ssd::launch_state_update(a, static_cast<Dt>(d->act_dtype),
+                                               static_cast<Dt>(d->y_dtype), stream));
 }
 
 ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state, const void* x, int64_t x_row_stride,

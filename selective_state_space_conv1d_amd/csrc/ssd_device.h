@@ -42,4 +42,22 @@ __device__ __forceinline__ void store16_f32(T* p, const float* in) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Token rows [start, start + len) of packed sequence s, with the table's values clamped into
+// [0, total] so that a malformed table cannot address outside the packed tensors.
+__device__ __forceinline__ void seq_span(const int32_t* cu, int64_t s, int64_t total, int64_t& start,
+                                         int64_t& len) {
+    int64_t a = cu[s], b = cu[s + 1];
+    a = a < 0 ? 0 : (a > total ? total : a);
+    b = b < a ? a : (b > total ? total : b);
+    start = a;
+    len = b - a;
+}
+
+// State slot of batch entry / sequence s, or -1 (padding: no state read or written) when the
+// table says so (negative) or names a slot outside the pool.
+__device__ __forceinline__ int64_t seq_slot(const int32_t* slot_idx, int64_t s, int64_t nslots) {
+    const int64_t v = slot_idx ? static_cast<int64_t>(slot_idx[s]) : s;
+    return (v >= 0 && v < nslots) ? v : -1;
+}
+
 }  // namespace ssd

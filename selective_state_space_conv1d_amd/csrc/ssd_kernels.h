@@ -8,12 +8,24 @@ namespace ssd {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
+// Packed variable-length batches (all NULL / 0 for the fixed-length calls): "batch" counts
+// sequences, sequence s covers token rows [cu_seqlens[s], cu_seqlens[s+1]) of the packed
+// tensors, and its states are slot slot_idx[s] (NULL: slot s) of the caller's state pools of
+// nslots entries.  has_init[s] != 0 (NULL: never) starts sequence s from its slot's state.
+struct SeqMap {
+    const int32_t* cu_seqlens;
+    const int32_t* slot_idx;
+    const int32_t* has_init;
+    int64_t nslots;
+};
+
 struct ConvFwdArgs {
     const void* xbc; int64_t xbc_row_stride;
     const void* w; const void* bias;
     const void* state_in; void* state_out;
     void* out;
     int64_t batch, seqlen, channels;
+    SeqMap seq;   // varlen: state_in / state_out are the conv-state pool
 };
 
 struct ConvUpdateArgs {
@@ -21,6 +33,8 @@ struct ConvUpdateArgs {
     const void* w; const void* bias;
     void* state; void* out;
     int64_t batch, channels;
+    const int32_t* slot_idx;   // NULL: batch entry b uses state b; else slot slot_idx[b] of nslots
+    int64_t nslots;
 };
 
 struct ScanArgs {
@@ -31,6 +45,7 @@ struct ScanArgs {
     void* y;
     int64_t batch, seqlen;
     int nheads, head_dim, ngroups, d_state, chunk;
+    SeqMap seq;   // varlen: init_state / final_state are the state pool
 };
 
 struct UpdateArgs {
@@ -41,9 +56,13 @@ struct UpdateArgs {
     void* y;
     int64_t batch;
     int nheads, head_dim, ngroups, d_state;
+    const int32_t* slot_idx;   // NULL: batch entry b uses state b; else slot slot_idx[b] of nslots
+    int64_t nslots;
 };
 
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, Dt act, hipStream_t s);
+// varlen prefill conv: the per-token pass, then the conv-state pass
+hipError_t launch_conv1d_fwd_varlen(const ConvFwdArgs& a, Dt act, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs& a, Dt act, hipStream_t s);
 hipError_t launch_state_update(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).

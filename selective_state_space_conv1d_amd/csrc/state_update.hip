@@ -21,20 +21,54 @@ namespace ssd {
 constexpr int kUpdThreads = 128;
 constexpr int kUpdPerThread = 4;
 
-template <typename T, typename TY, int N>
+// SLOTS: batch entry b's state is slot slot_idx[b] of a pool (none for padding: it starts from
+// zeros and is not stored); the walk is still over [B, H, P, N], so each wave-wide access stays
+// 1 KB contiguous inside one slot.
+template <typename T, typename TY, int N, bool SLOTS>
 __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
     const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, TY* __restrict__ y, int64_t total4, int H, int P, int hpg) {
+    const float* __restrict__ D, TY* __restrict__ y, int64_t total4, int H, int P, int hpg,
+    const int32_t* __restrict__ slot_idx, int64_t nslots) {
     constexpr int QPR = N / 4;  // float4 per state row
     f32x4* st4 = reinterpret_cast<f32x4*>(state);
     const int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread) + threadIdx.x;
 
     f32x4 s[kUpdPerThread];
+    int64_t sf[kUpdPerThread];   // float4 index of the state (in the pool with SLOTS), -1: padding
+    int64_t bu = -1, shift = 0;  // with SLOTS: the block's one batch entry and its pool offset, if uniform
+    bool upad = false;           // that entry is padding
+    if constexpr (SLOTS) {
+        const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
+        const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread);
+        const int64_t fl = (f0 + kUpdThreads * kUpdPerThread < total4 ? f0 + kUpdThreads * kUpdPerThread : total4) - 1;
+        if (f0 / per_b == fl / per_b) {   // the usual case: one slot lookup per block
+            bu = f0 / per_b;
+            const int64_t slot = seq_slot(slot_idx, bu, nslots);
+            upad = slot < 0;
+            shift = (slot - bu) * per_b;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kUpdPerThread; ++i) {
         const int64_t f = base + i * kUpdThreads;
-        if (f < total4) s[i] = __builtin_nontemporal_load(st4 + f);
+        sf[i] = f;
+        if constexpr (SLOTS) {
+            if (bu >= 0) {
+                sf[i] = upad ? -1 : f + shift;
+            } else if (f < total4) {
+                const int64_t row = f / QPR;
+                const int64_t bh = row / P;
+                const int64_t b = bh / H;
+                const int64_t slot = seq_slot(slot_idx, b, nslots);
+                sf[i] = slot < 0 ? -1 : f + (slot - b) * static_cast<int64_t>(H) * P * QPR;
+            }
+        }
+        if constexpr (SLOTS) {
+            if (f < total4) s[i] = sf[i] >= 0 ? __builtin_nontemporal_load(st4 + sf[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            if (f < total4) s[i] = __builtin_nontemporal_load(st4 + f);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kUpdPerThread; ++i) {
@@ -71,23 +105,29 @@ __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
         for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
         if (ok) {
             if (q == 0) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
-            __builtin_nontemporal_store(v, st4 + f);
+            if (!SLOTS || sf[i] >= 0) __builtin_nontemporal_store(v, st4 + sf[i]);
         }
     }
 }
 
-template <typename T, typename TY, int N>
-static hipError_t upd_n(const UpdateArgs& a, hipStream_t s) {
+template <typename T, typename TY, int N, bool SLOTS>
+static hipError_t upd_launch(const UpdateArgs& a, hipStream_t s) {
     const int64_t total4 = a.batch * a.nheads * static_cast<int64_t>(a.head_dim) * (N / 4);
     if (total4 == 0) return hipSuccess;
     const int64_t per_block = kUpdThreads * kUpdPerThread;
     const int64_t blocks = (total4 + per_block - 1) / per_block;
-    hipLaunchKernelGGL((state_update_kernel<T, TY, N>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((state_update_kernel<T, TY, N, SLOTS>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kUpdThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
                        static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), total4, a.nheads,
-                       a.head_dim, a.nheads / a.ngroups);
+                       a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots);
     return hipGetLastError();
+}
+
+template <typename T, typename TY, int N>
+static hipError_t upd_n(const UpdateArgs& a, hipStream_t s) {
+    if (a.slot_idx) return upd_launch<T, TY, N, true>(a, s);
+    return upd_launch<T, TY, N, false>(a, s);
 }
 
 template <typename T, typename TY>

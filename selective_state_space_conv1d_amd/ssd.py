@@ -20,7 +20,8 @@ _DT = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_DTYPE", "SSD_ERR_ALIGN",
           "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
 EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan_workspace_size",
-           "ssd_chunk_scan", "ssd_state_update", "ssd_status_string"]
+           "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
+           "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots"]
 
 
 class SsdDims(ctypes.Structure):
@@ -59,7 +60,15 @@ def _lib():
         lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP,
                                        _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
-        for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update"):
+        lib.ssd_conv1d_fwd_varlen.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
+        lib.ssd_conv1d_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
+        lib.ssd_chunk_scan_varlen.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP,
+                                              _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
+        lib.ssd_state_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
+                                               _VP, _VP]
+        for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
+                  "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
+                  "ssd_state_update_slots"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -208,6 +217,137 @@ def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream
     _check(_lib().ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), x.stride(0), _ptr(B), _ptr(C),
                                    B.stride(0), _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(stream)),
            "ssd_state_update")
+    return y
+
+
+# --------------------------------------------------------------------------- packed batches
+def _table(t, n, name):
+    """An int32 sequence table on the device ([n], contiguous), or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or tuple(t.shape) != (n,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape [{n}]")
+    return t
+
+
+def ssd_conv1d_fwd_varlen(xbc, w, bias, cu_seqlens, conv_state_pool=None, slot_idx=None,
+                          has_initial_state=None, out=None, nheads=None, head_dim=None, ngroups=None,
+                          d_state=None, stream=None):
+    """Prefill conv of a packed batch.  xbc [T, CD] (token rows may be strided, channels packed),
+    cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, conv_state_pool
+    [nslots, CD, 4]|None, updated in place.  Returns out [T, CD]."""
+    T, CD = xbc.shape
+    S = cu_seqlens.numel() - 1
+    if S < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if xbc.stride(1) != 1 and CD > 1:
+        raise ValueError("xbc channels must be packed")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    nslots = 0
+    if conv_state_pool is not None:
+        if conv_state_pool.dim() != 3 or conv_state_pool.shape[1:] != (CD, 4) or not conv_state_pool.is_contiguous():
+            raise ValueError("conv_state_pool must be contiguous [nslots, CD, 4]")
+        nslots = conv_state_pool.shape[0]
+    if out is None:
+        out = torch.empty((T, CD), dtype=xbc.dtype, device=xbc.device)
+    d = _dims(S, T, H, P, G, N, xbc.dtype, xbc.dtype)
+    xs = CD if T == 0 else xbc.stride(0)
+    _check(_lib().ssd_conv1d_fwd_varlen(ctypes.byref(d), _ptr(xbc if T else None), xs, _ptr(w), _ptr(bias),
+                                        _ptr(_table(cu_seqlens, S + 1, "cu_seqlens")),
+                                        _ptr(_table(slot_idx, S, "slot_idx")),
+                                        _ptr(_table(has_initial_state, S, "has_initial_state")),
+                                        _ptr(conv_state_pool), nslots, _ptr(out), _stream(stream)),
+           "ssd_conv1d_fwd_varlen")
+    return out
+
+
+def ssd_conv1d_update_slots(xbc, w, bias, conv_state_pool, slot_idx, out=None, nheads=None, head_dim=None,
+                            ngroups=None, d_state=None, stream=None):
+    """One-token conv for B requests whose windows live in conv_state_pool [nslots, CD, 4]
+    (updated in place) at slot_idx [B] int32.  xbc [B, CD] (rows may be strided).  Returns out [B, CD]."""
+    Bt, CD = xbc.shape
+    if xbc.stride(1) != 1:
+        raise ValueError("xbc channels must be packed")
+    if conv_state_pool.dim() != 3 or conv_state_pool.shape[1:] != (CD, 4) or not conv_state_pool.is_contiguous():
+        raise ValueError("conv_state_pool must be contiguous [nslots, CD, 4]")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    if out is None:
+        out = torch.empty((Bt, CD), dtype=xbc.dtype, device=xbc.device)
+    d = _dims(Bt, 1, H, P, G, N, xbc.dtype, xbc.dtype)
+    _check(_lib().ssd_conv1d_update_slots(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias),
+                                          _ptr(_table(slot_idx, Bt, "slot_idx")), _ptr(conv_state_pool),
+                                          conv_state_pool.shape[0], _ptr(out), _stream(stream)),
+           "ssd_conv1d_update_slots")
+    return out
+
+
+def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None,
+                          has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None):
+    """SSD chunked scan of a packed batch.  x [T, H, P], B/C [T, G, N] (token rows may be strided,
+    e.g. views into the varlen conv output), dt [T, H], A [H] fp32, D [H] fp32|None,
+    cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, state_pool
+    [nslots, H, P, N] fp32|None, updated in place.  Returns y [T, H, P] in y_dtype (default x's)."""
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    S = cu_seqlens.numel() - 1
+    if S < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if T > 0 and (x.stride(2) != 1 or x.stride(1) != P):
+        raise ValueError("x must be [T, H, P] with packed (H, P)")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (T, G, N) or (T > 0 and (t.stride(2) != 1 or t.stride(1) != N)):
+            raise ValueError(f"{nm} must be [T, G, N] with packed (G, N)")
+    if B.stride(0) != C.stride(0):
+        raise ValueError("B and C must share a token stride")
+    if dt.shape != (T, H) or not dt.is_contiguous():
+        raise ValueError("dt must be contiguous [T, H]")
+    nslots = 0
+    if state_pool is not None:
+        if state_pool.shape[1:] != (H, P, N) or state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
+            raise ValueError("state_pool must be contiguous fp32 [nslots, H, P, N]")
+        nslots = state_pool.shape[0]
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((T, H, P), dtype=ydt, device=x.device)
+    d = _dims(S, T, H, P, G, N, x.dtype, y.dtype)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    xs, bcs = (P * H, G * N) if T == 0 else (x.stride(0), B.stride(0))
+    if T == 0:
+        x = B = C = dt = None
+    _check(_lib().ssd_chunk_scan_varlen(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
+                                        _ptr(A), _ptr(D), _ptr(_table(cu_seqlens, S + 1, "cu_seqlens")),
+                                        _ptr(_table(slot_idx, S, "slot_idx")),
+                                        _ptr(_table(has_initial_state, S, "has_initial_state")),
+                                        _ptr(state_pool), nslots, _ptr(y), _ptr(workspace), ws, _stream(stream)),
+           "ssd_chunk_scan_varlen")
+    return y
+
+
+def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None):
+    """One decode token for B requests whose states live in state_pool [nslots, H, P, N] fp32
+    (updated in place) at slot_idx [B] int32.  x [B, H, P], B/C [B, G, N], dt [B, H].
+    Returns y [B, H, P]."""
+    nslots, H, P, N = state_pool.shape
+    Bt = x.shape[0]
+    G = B.shape[1]
+    if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
+        raise ValueError("x must be [B, H, P] with packed (H, P)")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, G, N) or t.stride(2) != 1 or t.stride(1) != N:
+            raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
+    if B.stride(0) != C.stride(0):
+        raise ValueError("B and C must share a batch stride")
+    if dt.shape != (Bt, H) or not dt.is_contiguous() or not state_pool.is_contiguous():
+        raise ValueError("dt [B, H] and state_pool must be contiguous")
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
+    _check(_lib().ssd_state_update_slots(ctypes.byref(d), _ptr(state_pool), nslots,
+                                         _ptr(_table(slot_idx, Bt, "slot_idx")), _ptr(x), x.stride(0),
+                                         _ptr(B), _ptr(C), B.stride(0), _ptr(dt), _ptr(A), _ptr(D), _ptr(y),
+                                         _stream(stream)),
+           "ssd_state_update_slots")
     return y
 
 

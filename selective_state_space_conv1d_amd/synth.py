@@ -13,11 +13,17 @@ Distributions (one recipe for every workload):
   ssm state          N(0, 0.1^2)    fp32     (decode workload)
   slow decay variant A = -exp(U(-3, -1)), dt = softplus(N(-4, 1))
 
+Packed serving batches (varlen): S request lengths >= 1 drawn as round(T * w_s / sum(w)) with
+w_s ~ LogNormal(0, 1) (a mix of short and long prompts), adjusted to sum exactly to T tokens;
+slots are a seeded random choice of distinct pool entries; every other sequence continues from
+an initial state (pool states N(0, 0.1^2) fp32, conv-state pool N(0, 1)).
+
 Layer shapes follow the Ultra-family Mamba layer (256 heads x head_dim 64,
 d_state 128, 8 groups, conv width 4, conv_dim 18432).
 """
 from dataclasses import dataclass, replace
 
+import numpy as np
 import torch
 
 
@@ -58,6 +64,8 @@ WORKLOADS = {
     "continuation_h128_b8": LayerDims(8, 4096, 128, 64, 8, 128),
     # long context: batch 1 x 262144 tokens, Ultra layer
     "long_ultra_256k": LayerDims(1, 262144, 256, 64, 8, 128),
+    # packed serving prefill: 8192 tokens in 24 requests (batch = requests), Ultra layer
+    "varlen_ultra_8k": LayerDims(24, 8192, 256, 64, 8, 128),
 }
 
 
@@ -145,3 +153,44 @@ def decode_state(dims, seed, device="cpu"):
         "state": _randn((B, H, P, N), g, device, 0.1),
         "conv_state": _randn((B, CD, K), g, device).to(dims.dtype),
     }
+
+
+def varlen_lengths(total, nseq, seed):
+    """nseq request lengths >= 1 summing to total (total >= nseq), log-normal mix."""
+    r = np.random.default_rng(int(seed))
+    w = r.lognormal(0.0, 1.0, nseq)
+    lens = np.maximum(1, np.round(total * w / w.sum())).astype(np.int64)
+    while lens.sum() != total:               # move the rounding error onto the longest / shortest
+        if lens.sum() > total:
+            i = int(np.argmax(lens))
+            lens[i] -= min(lens[i] - 1, lens.sum() - total)
+        else:
+            lens[int(np.argmin(lens))] += total - lens.sum()
+    return [int(v) for v in lens]
+
+
+def varlen_tables(lens, nslots, seed, device="cpu"):
+    """cu_seqlens [S+1], slot_idx [S] (distinct slots of an nslots pool) and has_initial_state [S]
+    (every other request), all int32."""
+    r = np.random.default_rng(int(seed))
+    S = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slot = r.permutation(nslots)[:S].astype(np.int32)
+    has_init = (np.arange(S) % 2).astype(np.int32)
+    t = lambda a: torch.from_numpy(a).to(device)
+    return t(cu), t(slot), t(has_init)
+
+
+def varlen_inputs(dims, lens, nslots, seed, device="cpu"):
+    """A packed prefill: mixer inputs for T = sum(lens) token rows (xbc [T,CD], dt [T,H], taps,
+    A, D), the tables, and the pools: conv states [nslots,CD,K] and ssm states [nslots,H,P,N]."""
+    T = int(sum(lens))
+    inp = mixer_inputs(dims.with_(batch=1, seqlen=T), seed, device)
+    inp["xbc"] = inp["xbc"][0]
+    inp["dt"] = inp["dt"][0]
+    g = _gen(int(seed) + 7919, device)
+    H, P, N, CD, K = dims.nheads, dims.head_dim, dims.d_state, dims.conv_dim, dims.conv_width
+    inp["conv_pool"] = _randn((nslots, CD, K), g, device).to(dims.dtype)
+    inp["state_pool"] = _randn((nslots, H, P, N), g, device, 0.1)
+    inp["cu_seqlens"], inp["slot_idx"], inp["has_initial_state"] = varlen_tables(lens, nslots, seed, device)
+    return inp

@@ -140,6 +140,50 @@ def test_state_update_validation(ssd, lib):
     assert call(dims(ssd, nheads=5, ngroups=2)) == E["SSD_ERR_SHAPE"]
 
 
+def test_varlen_and_slot_validation(ssd, lib):
+    """The packed-batch and state-pool entry points reject bad host arguments before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=3, seqlen=300)   # 3 sequences, 300 packed rows; CD = 768
+
+    def scan_v(dd=d, cu=fp(8), slot=None, hi=None, pool=fp(9), nslots=4, x=fp(1), y=fp(6), chunk=128):
+        return lib.ssd_chunk_scan_varlen(ctypes.byref(dd), chunk, x, 256, fp(2), fp(3), 256, fp(4), fp(5), None,
+                                         cu, slot, hi, pool, nslots, y, None, 0, None)
+    assert scan_v(cu=None) == E["SSD_ERR_NULL"]
+    assert scan_v(pool=None) == E["SSD_ERR_NULL"]                     # nslots > 0 needs a pool
+    assert scan_v(nslots=-1) == E["SSD_ERR_SHAPE"]
+    assert scan_v(pool=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert scan_v(x=None) == E["SSD_ERR_NULL"]
+    assert scan_v(chunk=32) == E["SSD_ERR_UNSUPPORTED"]
+    assert scan_v(dims(ssd, batch=3, seqlen=300, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
+
+    def conv_v(dd=d, cu=fp(8), pool=fp(9), nslots=4, xbc=fp(1), xs=768, w=fp(2), out=fp(3)):
+        return lib.ssd_conv1d_fwd_varlen(ctypes.byref(dd), xbc, xs, w, None, cu, None, None, pool, nslots, out,
+                                         None)
+    assert conv_v(cu=None) == E["SSD_ERR_NULL"]
+    assert conv_v(pool=None) == E["SSD_ERR_NULL"]
+    assert conv_v(nslots=-2) == E["SSD_ERR_SHAPE"]
+    assert conv_v(w=None) == E["SSD_ERR_NULL"]
+    assert conv_v(xs=700) == E["SSD_ERR_SHAPE"]
+    assert conv_v(xs=772) == E["SSD_ERR_ALIGN"]
+
+    dd = dims(ssd, batch=2)
+    assert lib.ssd_conv1d_update_slots(ctypes.byref(dd), fp(1), 768, fp(2), None, None, fp(3), 4, fp(4),
+                                       None) == E["SSD_ERR_NULL"]        # slot_idx is required
+    assert lib.ssd_conv1d_update_slots(ctypes.byref(dd), fp(1), 768, fp(2), None, fp(5), None, 4, fp(4),
+                                       None) == E["SSD_ERR_NULL"]
+    assert lib.ssd_conv1d_update_slots(ctypes.byref(dd), fp(1), 768, fp(2), None, fp(5), fp(3), -1, fp(4),
+                                       None) == E["SSD_ERR_SHAPE"]
+
+    def upd(pool=fp(1), nslots=4, slot=fp(8), y=fp(7)):
+        return lib.ssd_state_update_slots(ctypes.byref(dd), pool, nslots, slot, fp(2), 256, fp(3), fp(4), 256,
+                                          fp(5), fp(6), None, y, None)
+    assert upd(slot=None) == E["SSD_ERR_NULL"]
+    assert upd(pool=None) == E["SSD_ERR_NULL"]
+    assert upd(nslots=-3) == E["SSD_ERR_SHAPE"]
+    assert upd(pool=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert upd(y=None) == E["SSD_ERR_NULL"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
