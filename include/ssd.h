@@ -83,6 +83,21 @@ typedef struct {
     int32_t y_dtype;    /* ssd_dtype_t */
 } ssd_dims_t;
 
+/*
+ * Optional dt prologue ([P2] plugin inputs: dt_bias with softplus; the configs
+ * draw dt = softplus(N(-2, 1)) directly).  NULL, or all fields zero, uses dt as
+ * given.  Otherwise, in fp32, per token and head h:
+ *   v = dt + bias[h]                      (bias NULL: + 0)
+ *   v = softplus ? log(1 + exp(v)) : v    (returns v itself for v > 20)
+ *   v = lo < hi ? min(max(v, lo), hi) : v
+ * and the scan or update uses v as dt.
+ */
+typedef struct {
+    const float* bias;  /* [H] fp32 device memory, or NULL */
+    int32_t softplus;   /* nonzero: apply softplus after the bias */
+    float lo, hi;       /* clamp range; lo >= hi disables the clamp */
+} ssd_dt_params_t;
+
 /* Conv channels CD = H*P + 2*G*N. */
 int64_t ssd_conv_dim(const ssd_dims_t* d);
 
@@ -129,6 +144,7 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
  *               x, B and C may be views into the conv output (row stride CD).
  *  dt           [B, L, H] act dtype, already positive (no bias, no softplus).
  *  A            [H] fp32 (negative decay rates).  D: [H] fp32 or NULL (no skip).
+ *  dt_params    optional dt prologue (see ssd_dt_params_t), or NULL.
  *  init_state   [B, H, P, N] fp32, or NULL (zeros).
  *  final_state  [B, H, P, N] fp32, or NULL (not written).  May alias init_state.
  *  y            [B, L, H, P] contiguous, y dtype.
@@ -139,6 +155,7 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
                             const void* x, int64_t x_row_stride,
                             const void* B, const void* C, int64_t bc_row_stride,
                             const void* dt, const float* A, const float* D,
+                            const ssd_dt_params_t* dt_params,
                             const float* init_state, float* final_state, void* y,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -148,14 +165,15 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
  *  state  [B, H, P, N] fp32, updated in place.
  *  x      x[b,h,p] at x[b*x_row_stride + h*P + p]; B, C: B[b,g,n] at
  *         B[b*bc_row_stride + g*N + n]; act dtype.
- *  dt     [B, H] act dtype.  A [H] fp32; D [H] fp32 or NULL.
+ *  dt     [B, H] act dtype.  A [H] fp32; D [H] fp32 or NULL.  dt_params: optional
+ *         dt prologue (see ssd_dt_params_t), or NULL.
  *  y      [B, H, P] contiguous, y dtype.
  */
 ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state,
                               const void* x, int64_t x_row_stride,
                               const void* B, const void* C, int64_t bc_row_stride,
-                              const void* dt, const float* A, const float* D, void* y,
-                              hipStream_t stream);
+                              const void* dt, const float* A, const float* D,
+                              const ssd_dt_params_t* dt_params, void* y, hipStream_t stream);
 
 /*
  * ---------------------------------------------------------------------------
@@ -202,11 +220,12 @@ ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t
  *  state_pool    [nslots, H, P, N] fp32, updated in place: the initial state is read as
  *                has_initial_state says, and the final state is written to every sequence's slot.
  *  y             [T, H, P] contiguous y dtype.
- * chunk, A, D and workspace as for ssd_chunk_scan.
+ * chunk, A, D, dt_params and workspace as for ssd_chunk_scan.
  */
 ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                    const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                                   const float* A, const float* D, const int32_t* cu_seqlens,
+                                   const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                   const int32_t* cu_seqlens,
                                    const int32_t* slot_idx, const int32_t* has_initial_state,
                                    float* state_pool, int64_t nslots, void* y, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
@@ -230,7 +249,8 @@ ssd_status_t ssd_conv1d_update_slots(const ssd_dims_t* d, const void* xbc, int64
 ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int64_t nslots,
                                     const int32_t* slot_idx, const void* x, int64_t x_row_stride,
                                     const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                                    const float* A, const float* D, void* y, hipStream_t stream);
+                                    const float* A, const float* D, const ssd_dt_params_t* dt_params, void* y,
+                                    hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

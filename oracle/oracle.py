@@ -99,6 +99,19 @@ class Oracle:
                                      _ptr(dt), _ptr(A), _ptr(D), _ptr(y))
         return y, st
 
+    # dt prologue (fp64), applied to dt [..., H] before the routines above: v = dt + bias[h];
+    # softplus v = log(1 + e^v); clamp to [lo, hi] when lo < hi.
+    @staticmethod
+    def dt_prologue(dt, bias=None, softplus=False, limit=None):
+        v = np.array(dt, dtype=np.float64)
+        if bias is not None:
+            v = v + np.asarray(bias, dtype=np.float64)
+        if softplus:
+            v = np.logaddexp(0.0, v)
+        if limit is not None and limit[0] < limit[1]:
+            v = np.clip(v, limit[0], limit[1])
+        return v
+
     # ------------------------------------------------------------------ packed batches
     # The plain per-sequence definition of the packed calls: sequence s is rows
     # [cu[s], cu[s+1]) of the packed [T, ...] tensors and is run on its own by the routines

@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
             sm.C[j][n] = j < valid ? static_cast<float>(Cg[o]) : 0.f;
         }
         if (tid < kT) {
-            const float d = tid < valid ? static_cast<float>(dtg[(row0 + t0 + tid) * H + h]) : 0.f;
+            const float d = tid < valid ? dt_prologue(static_cast<float>(dtg[(row0 + t0 + tid) * H + h]), a.dtp, h)
+                                        : 0.f;
             sm.dt[tid] = d;
             // inclusive prefix sum of dt*A over the block (lanes 0..31 of wave 0)
             float v = d * Ah;

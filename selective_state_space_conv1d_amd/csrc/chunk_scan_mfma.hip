@@ -191,11 +191,12 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* t, int b0, int b8
 }
 
 // Per-token vectors of a chunk from its dt (two tokens per lane of one wave).
-// r0, r1 are the raw dt of tokens 2*lane and 2*lane+1 (read from in-range rows);
-// tokens at or past `valid` count as dt = 0.
-__device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, int valid, int lane) {
-    const float d0 = 2 * lane < valid ? static_cast<float>(r0) : 0.f;
-    const float d1 = 2 * lane + 1 < valid ? static_cast<float>(r1) : 0.f;
+// r0, r1 are the raw dt of tokens 2*lane and 2*lane+1 (read from in-range rows), put
+// through the dt prologue of head h; tokens at or past `valid` count as dt = 0.
+__device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, int valid, int lane,
+                                          const DtParams& dtp, int h) {
+    const float d0 = 2 * lane < valid ? dt_prologue(static_cast<float>(r0), dtp, h) : 0.f;
+    const float d1 = 2 * lane + 1 < valid ? dt_prologue(static_cast<float>(r1), dtp, h) : 0.f;
     const float a0 = d0 * A2, a1 = d1 * A2;
     float s = a0 + a1;
 #pragma unroll
@@ -603,7 +604,7 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         load_dt(d0, d1, 0, v0);
         dma_rows<kRowX, 0, 16>(sm.X[0], xsrc, cx.xs, cx.row0, 0, v0, lane);
         dma_rows<kRowB, 0, 32>(sm.B[0], bsrc, cx.bcs, cx.row0, 0, v0, lane);
-        build_vec(sm.vec[0], d0, d1, A2, v0, lane);
+        build_vec(sm.vec[0], d0, d1, A2, v0, lane, a.dtp, cx.h);
     }
     wait_vmem();
     __syncthreads();                                            // chunk 0
@@ -617,7 +618,7 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
             load_dt(d0, d1, (c + 1) * Q, vn);
             dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
             dma_rows<kRowB, 0, kYB>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
-            build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane);
+            build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane, a.dtp, cx.h);
         }
         wait_vmem();
         __syncthreads();                                        // chunk c + 1

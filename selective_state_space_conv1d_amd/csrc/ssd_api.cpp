@@ -28,6 +28,14 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
 
 ssd_status_t hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+ssd::DtParams dt_params_of(const ssd_dt_params_t* p) {
+    if (!p) return ssd::DtParams{nullptr, 0, 0.f, 0.f};
+    return ssd::DtParams{p->bias, p->softplus, p->lo, p->hi};
+}
+bool dt_params_ok(const ssd_dt_params_t* p) {
+    return !p || !p->bias || (reinterpret_cast<uintptr_t>(p->bias) & 3u) == 0;
+}
+
 // Packed variable-length calls: tables and pool present as the sizes require.
 ssd_status_t check_seq_tables(const ssd_dims_t* d, const int32_t* cu_seqlens, const void* pool, int64_t nslots) {
     if (nslots < 0) return SSD_ERR_SHAPE;
@@ -142,7 +150,8 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
 
 ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                             const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                            const float* A, const float* D, const float* init_state,
+                            const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                            const float* init_state,
                             float* final_state, void* y, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
     ssd_status_t st = check_dims(d, true);
@@ -160,8 +169,10 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
     if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
     if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
     (void)workspace;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, init_state, final_state, y,
-                    d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk};
+                    d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
+                    {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params)};
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
@@ -170,7 +181,8 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
 
 ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                   const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                                  const float* A, const float* D, const int32_t* cu_seqlens,
+                                  const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                  const int32_t* cu_seqlens,
                                   const int32_t* slot_idx, const int32_t* has_initial_state, float* state_pool,
                                   int64_t nslots, void* y, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
@@ -192,9 +204,10 @@ ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const voi
     if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
     (void)workspace;
     if (d->batch > 0 && !tokens && nslots == 0) return SSD_OK;   // nothing to compute or store
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
-                    {cu_seqlens, slot_idx, has_initial_state, nslots}};
+                    {cu_seqlens, slot_idx, has_initial_state, nslots}, dt_params_of(dt_params)};
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
@@ -203,8 +216,8 @@ ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const voi
 
 ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int64_t nslots, const int32_t* slot_idx,
                                     const void* x, int64_t x_row_stride, const void* B, const void* C,
-                                    int64_t bc_row_stride, const void* dt, const float* A, const float* D, void* y,
-                                    hipStream_t stream) {
+                                    int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                    const ssd_dt_params_t* dt_params, void* y, hipStream_t stream) {
     ssd_status_t st = check_dims(d, false);
     if (st != SSD_OK) return st;
     if (nslots < 0) return SSD_ERR_SHAPE;
@@ -215,15 +228,18 @@ ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int6
     const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
     if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
     if (state_pool && !aligned16(state_pool)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::UpdateArgs a{state_pool, x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,
-                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, slot_idx, nslots};
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, slot_idx, nslots,
+                      dt_params_of(dt_params)};
     return hip_status(ssd::launch_state_update(a, static_cast<Dt>(d->act_dtype),
                                                static_cast<Dt>(d->y_dtype), stream));
 }
 
 ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state, const void* x, int64_t x_row_stride,
                               const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                              const float* A, const float* D, void* y, hipStream_t stream) {
+                              const float* A, const float* D, const ssd_dt_params_t* dt_params, void* y,
+                              hipStream_t stream) {
     ssd_status_t st = check_dims(d, false);
     if (st != SSD_OK) return st;
     if (d->batch > 0 && (!state || !x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
@@ -232,8 +248,10 @@ ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state, const void* x, 
     const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
     if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
     if (!aligned16(state)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::UpdateArgs a{state, x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,
-                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state};
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, nullptr, 0,
+                      dt_params_of(dt_params)};
     return hip_status(ssd::launch_state_update(a, static_cast<Dt>(d->act_dtype),
                                                static_cast<Dt>(d->y_dtype), stream));
 }

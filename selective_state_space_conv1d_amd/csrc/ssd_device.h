@@ -42,6 +42,16 @@ __device__ __forceinline__ void store16_f32(T* p, const float* in) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// dt prologue of head h (fp32): + bias, softplus (the identity above 20, where log(1 + e^v)
+// rounds to v), clamp.  With every step off it returns v unchanged.
+template <class DP>
+__device__ __forceinline__ float dt_prologue(float v, const DP& p, int h) {
+    if (p.bias) v += p.bias[h];
+    if (p.softplus) v = v > 20.f ? v : log1pf(expf(v));
+    if (p.lo < p.hi) v = fminf(fmaxf(v, p.lo), p.hi);
+    return v;
+}
+
 // Token rows [start, start + len) of packed sequence s, with the table's values clamped into
 // [0, total] so that a malformed table cannot address outside the packed tensors.
 __device__ __forceinline__ void seq_span(const int32_t* cu, int64_t s, int64_t total, int64_t& start,

@@ -19,6 +19,14 @@ struct SeqMap {
     int64_t nslots;
 };
 
+// dt prologue: dt <- clamp(softplus(dt + bias[h])) with each step optional (bias NULL,
+// softplus 0, lo >= hi skip it).
+struct DtParams {
+    const float* bias;
+    int softplus;
+    float lo, hi;
+};
+
 struct ConvFwdArgs {
     const void* xbc; int64_t xbc_row_stride;
     const void* w; const void* bias;
@@ -46,6 +54,7 @@ struct ScanArgs {
     int64_t batch, seqlen;
     int nheads, head_dim, ngroups, d_state, chunk;
     SeqMap seq;   // varlen: init_state / final_state are the state pool
+    DtParams dtp;
 };
 
 struct UpdateArgs {
@@ -58,6 +67,7 @@ struct UpdateArgs {
     int nheads, head_dim, ngroups, d_state;
     const int32_t* slot_idx;   // NULL: batch entry b uses state b; else slot slot_idx[b] of nslots
     int64_t nslots;
+    DtParams dtp;
 };
 
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, Dt act, hipStream_t s);

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
     const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ D, TY* __restrict__ y, int64_t total4, int H, int P, int hpg,
-    const int32_t* __restrict__ slot_idx, int64_t nslots) {
+    const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp) {
     constexpr int QPR = N / 4;  // float4 per state row
     f32x4* st4 = reinterpret_cast<f32x4*>(state);
     const int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread) + threadIdx.x;
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
         const int64_t b = bh / H;
         const int h = static_cast<int>(bh - b * H);
         const int g = h / hpg;
-        const float dtv = static_cast<float>(dt[bh]);
+        const float dtv = dt_prologue(static_cast<float>(dt[bh]), dtp, h);
         const float a = __expf(dtv * A[h]);
         const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
         const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 4 * q;
@@ -120,7 +120,7 @@ static hipError_t upd_launch(const UpdateArgs& a, hipStream_t s) {
                        dim3(kUpdThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
                        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
                        static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), total4, a.nheads,
-                       a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots);
+                       a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots, a.dtp);
     return hipGetLastError();
 }
 

@@ -38,6 +38,11 @@ class SsdError(RuntimeError):
 
 
 _LIB = None
+class SsdDtParams(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("softplus", ctypes.c_int32), ("lo", ctypes.c_float),
+                ("hi", ctypes.c_float)]
+
+
 _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -57,15 +62,16 @@ def _lib():
         lib.ssd_conv1d_update.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
         lib.ssd_chunk_scan_workspace_size.argtypes = [_PD, _I32]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_size_t
-        lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP,
-                                       _VP, _VP, ctypes.c_size_t, _VP]
-        lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        _PDT = ctypes.POINTER(SsdDtParams)
+        lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP, _VP,
+                                       _VP, ctypes.c_size_t, _VP]
+        lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP]
         lib.ssd_conv1d_fwd_varlen.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
         lib.ssd_conv1d_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
-        lib.ssd_chunk_scan_varlen.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP,
-                                              _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
+        lib.ssd_chunk_scan_varlen.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
+                                              _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
-                                               _VP, _VP]
+                                               _PDT, _VP, _VP]
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots"):
@@ -99,6 +105,20 @@ def _uniform_rows(t, L):
 def _check(code, where):
     if code != 0:
         raise SsdError(code, where)
+
+
+def _dt_params(dt_bias, dt_softplus, dt_limit):
+    """ssd_dt_params_t for the optional dt prologue, or None (dt used as given).  dt_bias [H] fp32
+    on the device; dt_limit (lo, hi) clamps after the softplus."""
+    if dt_bias is None and not dt_softplus and dt_limit is None:
+        return None
+    if dt_bias is not None and (dt_bias.dtype != torch.float32 or not dt_bias.is_contiguous()):
+        raise ValueError("dt_bias must be a contiguous fp32 [H] tensor")
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    if dt_limit is not None and not lo < hi:
+        raise ValueError("dt_limit needs lo < hi")
+    return ctypes.byref(SsdDtParams(None if dt_bias is None else dt_bias.data_ptr(), int(bool(dt_softplus)),
+                                    lo, hi))
 
 
 def _dims(batch, seqlen, H, P, G, N, act, ydt):
@@ -164,11 +184,11 @@ def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, head_dim, ngroups, d_st
 
 
 def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=None, chunk=128,
-                   y_dtype=None, workspace=None, stream=None):
+                   y_dtype=None, workspace=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
     """SSD chunked scan.  x [B, L, H, P], B/C [B, L, G, N] (token rows may be strided, e.g.
     views into the conv output), dt [B, L, H], A [H] fp32, D [H] fp32|None,
-    init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).
-    Returns y [B, L, H, P] in y_dtype (default: x's dtype)."""
+    init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).  Optional dt prologue:
+    dt <- clamp(softplus(dt + dt_bias), *dt_limit).  Returns y [B, L, H, P] in y_dtype (default x's)."""
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if L > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, L)):
@@ -190,12 +210,14 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     if L == 0:
         x = B = C = dt = None
     _check(_lib().ssd_chunk_scan(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
-                                 _ptr(dt), _ptr(A), _ptr(D), _ptr(init_state), _ptr(final_state), _ptr(y),
+                                 _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                 _ptr(init_state), _ptr(final_state), _ptr(y),
                                  _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
     return y
 
 
-def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None):
+def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None, dt_bias=None,
+                     dt_softplus=False, dt_limit=None):
     """One decode token, in place on state [B, H, P, N] fp32.  x [B, H, P], B/C [B, G, N]
     (batch rows may be strided, e.g. views into the conv-update output), dt [B, H].
     Returns y [B, H, P]."""
@@ -215,7 +237,8 @@ def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream
         y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
     d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
     _check(_lib().ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), x.stride(0), _ptr(B), _ptr(C),
-                                   B.stride(0), _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(stream)),
+                                   B.stride(0), _ptr(dt), _ptr(A), _ptr(D),
+                                   _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(y), _stream(stream)),
            "ssd_state_update")
     return y
 
@@ -282,7 +305,8 @@ def ssd_conv1d_update_slots(xbc, w, bias, conv_state_pool, slot_idx, out=None, n
 
 
 def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None,
-                          has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None):
+                          has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None,
+                          dt_bias=None, dt_softplus=False, dt_limit=None):
     """SSD chunked scan of a packed batch.  x [T, H, P], B/C [T, G, N] (token rows may be strided,
     e.g. views into the varlen conv output), dt [T, H], A [H] fp32, D [H] fp32|None,
     cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, state_pool
@@ -315,7 +339,8 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     if T == 0:
         x = B = C = dt = None
     _check(_lib().ssd_chunk_scan_varlen(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
-                                        _ptr(A), _ptr(D), _ptr(_table(cu_seqlens, S + 1, "cu_seqlens")),
+                                        _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                        _ptr(_table(cu_seqlens, S + 1, "cu_seqlens")),
                                         _ptr(_table(slot_idx, S, "slot_idx")),
                                         _ptr(_table(has_initial_state, S, "has_initial_state")),
                                         _ptr(state_pool), nslots, _ptr(y), _ptr(workspace), ws, _stream(stream)),
@@ -323,7 +348,8 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     return y
 
 
-def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None):
+def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None,
+                           dt_bias=None, dt_softplus=False, dt_limit=None):
     """One decode token for B requests whose states live in state_pool [nslots, H, P, N] fp32
     (updated in place) at slot_idx [B] int32.  x [B, H, P], B/C [B, G, N], dt [B, H].
     Returns y [B, H, P]."""
@@ -345,8 +371,8 @@ def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None,
     d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
     _check(_lib().ssd_state_update_slots(ctypes.byref(d), _ptr(state_pool), nslots,
                                          _ptr(_table(slot_idx, Bt, "slot_idx")), _ptr(x), x.stride(0),
-                                         _ptr(B), _ptr(C), B.stride(0), _ptr(dt), _ptr(A), _ptr(D), _ptr(y),
-                                         _stream(stream)),
+                                         _ptr(B), _ptr(C), B.stride(0), _ptr(dt), _ptr(A), _ptr(D),
+                                         _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(y), _stream(stream)),
            "ssd_state_update_slots")
     return y
 

@@ -59,7 +59,7 @@ def fp(i=0):
 
 def scan(lib, d, chunk=128, x=fp(1), xs=256, B=fp(2), C=fp(3), bcs=256, dt=fp(4), A=fp(5), D=None,
          init=None, fin=None, y=fp(6), ws=None, wsb=0):
-    return lib.ssd_chunk_scan(ctypes.byref(d), chunk, x, xs, B, C, bcs, dt, A, D, init, fin, y, ws, wsb, None)
+    return lib.ssd_chunk_scan(ctypes.byref(d), chunk, x, xs, B, C, bcs, dt, A, D, None, init, fin, y, ws, wsb, None)
 
 
 def test_status_strings(ssd, lib):
@@ -76,7 +76,7 @@ def test_conv_dim(ssd, lib):
 
 def test_scan_validation(ssd, lib):
     E = {n: i for i, n in enumerate(ssd.STATUS)}
-    assert lib.ssd_chunk_scan(None, 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None, None, None,
+    assert lib.ssd_chunk_scan(None, 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None, None, None, None,
                               fp(6), None, 0, None) == E["SSD_ERR_NULL"]
     assert scan(lib, dims(ssd, act_dtype=7)) == E["SSD_ERR_DTYPE"]
     assert scan(lib, dims(ssd, y_dtype=-1)) == E["SSD_ERR_DTYPE"]
@@ -131,7 +131,7 @@ def test_state_update_validation(ssd, lib):
     d = dims(ssd)
 
     def call(dd=d, state=fp(1), x=fp(2), xs=256, B=fp(3), C=fp(4), bcs=256, dt=fp(5), A=fp(6), y=fp(7)):
-        return lib.ssd_state_update(ctypes.byref(dd), state, x, xs, B, C, bcs, dt, A, None, y, None)
+        return lib.ssd_state_update(ctypes.byref(dd), state, x, xs, B, C, bcs, dt, A, None, None, y, None)
     assert call(state=None) == E["SSD_ERR_NULL"]
     assert call(y=None) == E["SSD_ERR_NULL"]
     assert call(dims(ssd, head_dim=24)) == E["SSD_ERR_UNSUPPORTED"]
@@ -147,7 +147,7 @@ def test_varlen_and_slot_validation(ssd, lib):
 
     def scan_v(dd=d, cu=fp(8), slot=None, hi=None, pool=fp(9), nslots=4, x=fp(1), y=fp(6), chunk=128):
         return lib.ssd_chunk_scan_varlen(ctypes.byref(dd), chunk, x, 256, fp(2), fp(3), 256, fp(4), fp(5), None,
-                                         cu, slot, hi, pool, nslots, y, None, 0, None)
+                                         None, cu, slot, hi, pool, nslots, y, None, 0, None)
     assert scan_v(cu=None) == E["SSD_ERR_NULL"]
     assert scan_v(pool=None) == E["SSD_ERR_NULL"]                     # nslots > 0 needs a pool
     assert scan_v(nslots=-1) == E["SSD_ERR_SHAPE"]
@@ -176,7 +176,7 @@ def test_varlen_and_slot_validation(ssd, lib):
 
     def upd(pool=fp(1), nslots=4, slot=fp(8), y=fp(7)):
         return lib.ssd_state_update_slots(ctypes.byref(dd), pool, nslots, slot, fp(2), 256, fp(3), fp(4), 256,
-                                          fp(5), fp(6), None, y, None)
+                                          fp(5), fp(6), None, None, y, None)
     assert upd(slot=None) == E["SSD_ERR_NULL"]
     assert upd(pool=None) == E["SSD_ERR_NULL"]
     assert upd(nslots=-3) == E["SSD_ERR_SHAPE"]

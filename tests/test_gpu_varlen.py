@@ -243,3 +243,73 @@ def test_varlen_ultra_serving_mix(orc):
                                   f64(spool0[:, h:h + 1]), slots, hinit)
         assert_close(y[:, h], yr[:, 0], BF16_BAR, f"y head {h}")
         assert_close(spool[:, h], spr[:, 0], BF16_BAR, f"state pool head {h}")
+
+
+# --------------------------------------------------------------------------- dt prologue
+DT_OPTS = [dict(dt_bias=True, dt_softplus=True, dt_limit=(0.0, 0.5)), dict(dt_bias=True, dt_softplus=True),
+           dict(dt_bias=False, dt_softplus=False, dt_limit=(0.05, 0.2))]
+
+
+def dt_args(H, opts, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    bias = (torch.randn(H, generator=g) - 1.0).to(DEV) if opts.get("dt_bias") else None
+    kw = dict(dt_bias=bias, dt_softplus=opts.get("dt_softplus", False), dt_limit=opts.get("dt_limit"))
+    okw = dict(bias=None if bias is None else f64(bias), softplus=kw["dt_softplus"], limit=kw["dt_limit"])
+    return kw, okw
+
+
+@pytest.mark.parametrize("opts", DT_OPTS)
+@pytest.mark.parametrize("P,N,dtype,chunk", [(64, 128, torch.bfloat16, 128), (16, 32, torch.float32, 64)])
+def test_scan_dt_prologue(orc, opts, P, N, dtype, chunk):
+    d = LayerDims(2, 300, 4, P, 2, N, dtype=dtype)
+    s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 280).items()}
+    raw = (torch.randn(2, 300, 4, device=DEV) * 2.0 - 1.0).to(dtype)   # pre-softplus values
+    kw, okw = dt_args(4, opts, 281)
+    fin = torch.empty_like(s["init_state"])
+    y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], raw, s["A"], s["D"], s["init_state"], fin, chunk=chunk,
+                           y_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    dt_eff = orc.dt_prologue(f64(raw), **okw)
+    yr, fr = orc.scan(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), dt_eff, f64(s["A"]), f64(s["D"]), f64(s["init_state"]))
+    bar = BF16_BAR if dtype == torch.bfloat16 else F32_BAR
+    assert_close(y, yr, bar, "y")
+    assert_close(fin, fr, bar, "final state")
+
+
+@pytest.mark.parametrize("opts", DT_OPTS)
+def test_state_update_and_slots_dt_prologue(orc, opts):
+    d = LayerDims(5, 1, 8, 64, 2, 128)
+    s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 290, seqlen=1).items()}
+    raw = (torch.randn(5, 8, device=DEV) * 2.0 - 1.0).to(torch.bfloat16)
+    kw, okw = dt_args(8, opts, 291)
+    dt_eff = orc.dt_prologue(f64(raw), **okw)
+    args = (s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], raw, s["A"], s["D"])
+    st = s["init_state"].clone()
+    y = ssd.ssd_state_update(st, *args, y_dtype=torch.float32, **kw)
+    pool = s["init_state"][[4, 2, 0, 3, 1]].clone()
+    slot = torch.tensor([2, 4, 1, 3, 0], dtype=torch.int32, device=DEV)
+    y2 = ssd.ssd_state_update_slots(pool, slot, *args, y_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    yr, sr = orc.state_update(f64(s["init_state"]), f64(s["x"][:, 0]), f64(s["Bm"][:, 0]), f64(s["Cm"][:, 0]),
+                              dt_eff, f64(s["A"]), f64(s["D"]))
+    assert_close(y, yr, F32_BAR, "y")
+    assert_close(st, sr, F32_BAR, "state")
+    assert torch.equal(y2, y) and torch.equal(pool[slot.long()], st)
+
+
+def test_scan_varlen_dt_prologue_matches_batched():
+    d = LayerDims(2, 200, 4, 64, 2, 128)
+    s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 300).items()}
+    raw = (torch.randn(2, 200, 4, device=DEV) - 1.0).to(torch.bfloat16)
+    bias = torch.randn(4, device=DEV)
+    kw = dict(dt_bias=bias, dt_softplus=True, dt_limit=(0.0, 1.0))
+    fin = torch.empty_like(s["init_state"])
+    yb = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], raw, s["A"], s["D"], s["init_state"], fin,
+                            y_dtype=torch.float32, **kw)
+    pool = s["init_state"].clone()
+    flat = lambda t: t.reshape((t.shape[0] * t.shape[1],) + tuple(t.shape[2:]))
+    cu = torch.tensor([0, 200, 400], dtype=torch.int32, device=DEV)
+    y = ssd.ssd_chunk_scan_varlen(flat(s["x"]), flat(s["Bm"]), flat(s["Cm"]), flat(raw), s["A"], s["D"], cu, pool,
+                                  None, torch.ones(2, dtype=torch.int32, device=DEV), y_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(2, 200, 4, 64), yb) and torch.equal(pool, fin)

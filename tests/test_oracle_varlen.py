@@ -164,5 +164,20 @@ def test_state_update_slots_matches_bruteforce(orc):
         assert np.array_equal(new[k], pool[k])
 
 
+def test_dt_prologue_matches_torch_softplus(orc):
+    """The dt prologue against torch's softplus and clamp in fp64 (the page's plugin takes dt_bias
+    with softplus)."""
+    r = np.random.default_rng(8)
+    dt = r.normal(-1.0, 6.0, (3, 50, 4))                 # spans both tails of the softplus
+    bias = r.normal(0.0, 2.0, 4)
+    v = orc.dt_prologue(dt, bias, True, (0.001, 3.0))
+    t = torch.nn.functional.softplus(torch.from_numpy(dt + bias), beta=1.0, threshold=1e9)
+    ref = torch.clamp(t, 0.001, 3.0).numpy()
+    assert rel_err(v, ref) < 1e-14
+    assert np.array_equal(orc.dt_prologue(dt), dt)
+    assert np.array_equal(orc.dt_prologue(dt, bias), dt + bias)
+    assert np.array_equal(orc.dt_prologue(dt, None, False, (1.0, 1.0)), dt)   # lo >= hi: no clamp
+
+
 def test_torch_is_cpu_only_here():
     assert torch.tensor([1.0]).device.type == "cpu"
