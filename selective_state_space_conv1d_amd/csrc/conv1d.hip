@@ -20,6 +20,44 @@ namespace ssd {
 constexpr int kConvThreads = 256;
 constexpr int kConvTokens = 32;  // tokens per thread in the prefill conv
 
+// Rows [ta, tb) of one thread's channel vector: out[t] = silu(bias + sum_k w[k] * in[t-3+k]), with
+// win holding the inputs at ta-3..ta-1 on entry.  Four rows are loaded before any is used, so each
+// thread keeps four 16-byte loads in flight.
+template <typename T, int V>
+__device__ __forceinline__ void conv_rows(const T* __restrict__ xr, int64_t xs, T* __restrict__ orow, int64_t os,
+                                          int64_t ta, int64_t tb, const float (&wt)[4][V], const float (&bs)[V],
+                                          float (&win)[3][V]) {
+    auto step = [&](const float (&u)[V], int64_t t) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float acc = bs[v];
+            acc = fmaf(wt[0][v], win[0][v], acc);
+            acc = fmaf(wt[1][v], win[1][v], acc);
+            acc = fmaf(wt[2][v], win[2][v], acc);
+            acc = fmaf(wt[3][v], u[v], acc);
+            o[v] = silu_f(acc);
+            win[0][v] = win[1][v];
+            win[1][v] = win[2][v];
+            win[2][v] = u[v];
+        }
+        store16_f32(orow + t * os, o);
+    };
+    int64_t t = ta;
+    for (; t + 4 <= tb; t += 4) {
+        float u[4][V];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) load16_f32(xr + (t + r) * xs, u[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) step(u[r], t + r);
+    }
+    for (; t < tb; ++t) {
+        float u[V];
+        load16_f32(xr + t * xs, u);
+        step(u, t);
+    }
+}
+
 // Grid: x = channel blocks * token tiles (channel block fastest), y = batch.
 // The thread of token tile 0 reads the incoming state before it writes the
 // outgoing one, so conv_state_out may alias conv_state_in.
@@ -79,24 +117,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
         for (int k = 0; k < 3; ++k) load16_f32(xb + (t0 - 3 + k) * xs + c0, win[k]);
     }
 
-    T* ob = out + b * L * CD;
-    for (int64_t t = t0; t < t1; ++t) {
-        float u[V], o[V];
-        load16_f32(xb + t * xs + c0, u);
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            float acc = bs[v];
-            acc = fmaf(wt[0][v], win[0][v], acc);
-            acc = fmaf(wt[1][v], win[1][v], acc);
-            acc = fmaf(wt[2][v], win[2][v], acc);
-            acc = fmaf(wt[3][v], u[v], acc);
-            o[v] = silu_f(acc);
-            win[0][v] = win[1][v];
-            win[1][v] = win[2][v];
-            win[2][v] = u[v];
-        }
-        store16_f32(ob + t * CD + c0, o);
-    }
+    conv_rows<T, V>(xb + c0, xs, out + b * L * CD + c0, CD, t0, t1, wt, bs, win);
 
     if (tile == 0 && s_out) {
         // new state column k = input at token L-4+k (from the old state when negative)
@@ -228,22 +249,22 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
         if (st <= t0) lo = mid;
         else hi = mid - 1;
     }
-    int64_t s = lo, start, end;
-    sv.span(s, start, end);
-    bool have = false;
-    float win[3][V];
-    for (int64_t t = t0; t < t1; ++t) {
-        while (t >= end && s + 1 < sv.nseq) {
-            ++s;
-            sv.span(s, start, end);
-            have = false;
-        }
-        if (t < start || t >= end) continue;
-        if (!have) {   // window at the tile's first row in s, or at s's first row
+    // One segment per sequence that overlaps the tile; inside a segment the row loop is the plain
+    // sliding window of the batched kernel, with no per-row sequence test.
+    for (int64_t s = lo; s < sv.nseq; ++s) {
+        int64_t start, end;
+        sv.span(s, start, end);
+        if (start >= t1) break;
+        const int64_t ta = start > t0 ? start : t0;
+        const int64_t tb = end < t1 ? end : t1;
+        if (ta >= tb) continue;
+        // window at row ta: inputs ta-3..ta-1, from the slot's state (or zeros) before the sequence
+        float win[3][V];
+        {
             const int64_t slot = seq_slot(sv.slot, s, sv.nslots);
             const bool from_state = slot >= 0 && sv.init && sv.init[s] != 0;
             float st[4][V];
-            if (from_state && t - start < 3) {
+            if (from_state && ta - start < 3) {
                 float tmp[4 * V];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) load16_f32(pool + (slot * CD + c0) * 4 + q * V, tmp + q * V);
@@ -259,7 +280,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
             }
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const int64_t tau = t - 3 + k;   // input row of window slot k
+                const int64_t tau = ta - 3 + k;   // input row of window slot k
                 if (tau >= start) {
                     load16_f32(xbc + tau * xs + c0, win[k]);
                 } else {
@@ -273,23 +294,8 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
                     }
                 }
             }
-            have = true;
         }
-        float u[V], o[V];
-        load16_f32(xbc + t * xs + c0, u);
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            float acc = bs[v];
-            acc = fmaf(wt[0][v], win[0][v], acc);
-            acc = fmaf(wt[1][v], win[1][v], acc);
-            acc = fmaf(wt[2][v], win[2][v], acc);
-            acc = fmaf(wt[3][v], u[v], acc);
-            o[v] = silu_f(acc);
-            win[0][v] = win[1][v];
-            win[1][v] = win[2][v];
-            win[2][v] = u[v];
-        }
-        store16_f32(out + t * CD + c0, o);
+        conv_rows<T, V>(xbc + c0, xs, out + c0, CD, ta, tb, wt, bs, win);
     }
 }
 
