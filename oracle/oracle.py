@@ -186,6 +186,58 @@ class Oracle:
                 new[k] = sb[0]
         return y, new
 
+    # ------------------------------------------------------------------ speculative decode
+    # ("Mamba 与 Nemotron 系列模型深度调研", 状态契约, MTP / speculative decoding: each candidate
+    # token leaves an intermediate recurrent and conv state; the accepted length selects the one
+    # written back to the request's state.)
+    # The plain definition of multi-token decode: the k candidate tokens of request b run one
+    # after another through the single-token routines above, starting from slot slot[b] of the
+    # pool (b when slot is None; zeros for padding), and the state after every token is kept.
+    # The pool itself is not changed.  accept_states then copies the state after token n
+    # (n = accept_len[b], clamped to [0, k]; n = 0 keeps the slot) back into the slot.
+
+    # pool [nslots,H,P,N], x [B,k,H,P], Bm/Cm [B,k,G,N], dt [B,k,H] -> y [B,k,H,P], inter [B,k,H,P,N]
+    def state_update_multi(self, pool, slot, x, Bm, Cm, dt, A, D=None):
+        x, Bm, Cm, dt, pool = map(_f64, (x, Bm, Cm, dt, pool))
+        Bt, k = x.shape[:2]
+        y = np.zeros_like(x)
+        inter = np.zeros((Bt, k) + pool.shape[1:])
+        for b in range(Bt):
+            s = self._slot(slot, b, pool.shape[0])
+            st = pool[s][None] if s >= 0 else np.zeros((1,) + pool.shape[1:])
+            for j in range(k):
+                yj, st = self.state_update(st, x[b:b + 1, j], Bm[b:b + 1, j], Cm[b:b + 1, j], dt[b:b + 1, j], A, D)
+                y[b, j] = yj[0]
+                inter[b, j] = st[0]
+        return y, inter
+
+    # u [B,k,CD], pool [nslots,CD,K] -> v [B,k,CD], inter [B,k,CD,K]
+    def conv1d_update_multi(self, u, w, bias, pool, slot):
+        u, pool = _f64(u), _f64(pool)
+        Bt, k = u.shape[:2]
+        v = np.zeros_like(u)
+        inter = np.zeros((Bt, k) + pool.shape[1:])
+        for b in range(Bt):
+            s = self._slot(slot, b, pool.shape[0])
+            st = pool[s][None] if s >= 0 else np.zeros((1,) + pool.shape[1:])
+            for j in range(k):
+                vj, st = self.conv1d_update(u[b:b + 1, j], w, bias, st)
+                v[b, j] = vj[0]
+                inter[b, j] = st[0]
+        return v, inter
+
+    # pool [nslots, ...], inter [B, k, ...], accept_len [B] -> updated copy of the pool
+    @classmethod
+    def accept_states(cls, pool, inter, accept_len, slot=None):
+        new = np.array(pool, dtype=np.float64, order="C", copy=True)
+        k = inter.shape[1]
+        for b in range(inter.shape[0]):
+            s = cls._slot(slot, b, new.shape[0])
+            n = min(max(int(accept_len[b]), 0), k)
+            if s >= 0 and n >= 1:
+                new[s] = inter[b, n - 1]
+        return new
+
 
 _DEFAULT = None
 

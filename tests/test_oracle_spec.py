@@ -1,0 +1,84 @@
+"""The oracle's multi-token (speculative) decode forms against independent references (CPU).
+
+The intermediate state after token j must be the final state of the brute-force semiseparable
+scan over the first j+1 tokens, and the intermediate conv state the final window of torch's
+conv1d over those rows; accepting n tokens must leave the slot at the state after n tokens.
+Source: "Mamba 与 Nemotron 系列模型深度调研", 状态契约 / "MTP / speculative decoding" (candidate tokens leave
+intermediate recurrent and conv states; the accepted length picks the one scattered back).
+"""
+import numpy as np
+
+from oracle_pins import rel_err, semiseparable_scan, softplus, torch_conv
+
+
+def spec_inputs(seed, Bt=4, k=5, H=4, P=3, G=2, N=5, nslots=7):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((Bt, k, H, P))
+    Bm = r.standard_normal((Bt, k, G, N))
+    Cm = r.standard_normal((Bt, k, G, N))
+    dt = softplus(r.normal(-2.0, 1.0, (Bt, k, H)))
+    A = -np.exp(r.uniform(0, 1, H))
+    D = r.standard_normal(H)
+    pool = r.standard_normal((nslots, H, P, N))
+    return x, Bm, Cm, dt, A, D, pool
+
+
+def test_state_update_multi_matches_bruteforce_prefixes(orc):
+    x, Bm, Cm, dt, A, D, pool = spec_inputs(11)
+    slot = np.array([5, -1, 0, 3])                   # -1 is padding: starts from zeros
+    y, inter = orc.state_update_multi(pool, slot, x, Bm, Cm, dt, A, D)
+    Bt, k = x.shape[:2]
+    for b in range(Bt):
+        S0 = pool[slot[b]][None] if slot[b] >= 0 else np.zeros((1,) + pool.shape[1:])
+        yr, _ = semiseparable_scan(x[b:b + 1], Bm[b:b + 1], Cm[b:b + 1], dt[b:b + 1], A, D, S0)
+        assert rel_err(y[b], yr[0]) < 1e-12, b
+        for j in range(k):
+            _, fr = semiseparable_scan(x[b:b + 1, :j + 1], Bm[b:b + 1, :j + 1], Cm[b:b + 1, :j + 1],
+                                       dt[b:b + 1, :j + 1], A, D, S0)
+            assert rel_err(inter[b, j], fr[0]) < 1e-12, (b, j)
+
+
+def test_conv_update_multi_matches_torch_conv_prefixes(orc):
+    r = np.random.default_rng(12)
+    Bt, k, CD, K, nslots = 3, 6, 10, 4, 5
+    u = r.standard_normal((Bt, k, CD))
+    w = r.uniform(-0.5, 0.5, (CD, K))
+    bias = r.uniform(-0.5, 0.5, CD)
+    pool = r.standard_normal((nslots, CD, K))
+    slot = np.array([4, 1, -1])
+    v, inter = orc.conv1d_update_multi(u, w, bias, pool, slot)
+    for b in range(Bt):
+        s_in = pool[slot[b]][None] if slot[b] >= 0 else np.zeros((1, CD, K))
+        vr, _ = torch_conv(u[b:b + 1], w, bias, s_in)
+        assert rel_err(v[b], vr[0]) < 1e-12, b
+        for j in range(k):
+            _, sr = torch_conv(u[b:b + 1, :j + 1], w, bias, s_in)
+            assert np.array_equal(inter[b, j], sr[0]), (b, j)
+
+
+def test_accept_is_the_state_after_n_tokens(orc):
+    x, Bm, Cm, dt, A, D, pool = spec_inputs(13)
+    slot = np.array([6, 2, 0, -1])
+    _, inter = orc.state_update_multi(pool, slot, x, Bm, Cm, dt, A, D)
+    acc = np.array([3, 0, 9, 2])                      # 0 keeps the slot; 9 > k clamps to k
+    new = orc.accept_states(pool, inter, acc, slot)
+    k = x.shape[1]
+    for b, n in enumerate(acc):
+        if slot[b] < 0:
+            continue
+        n = min(n, k)
+        if n == 0:
+            assert np.array_equal(new[slot[b]], pool[slot[b]])
+            continue
+        _, fr = semiseparable_scan(x[b:b + 1, :n], Bm[b:b + 1, :n], Cm[b:b + 1, :n], dt[b:b + 1, :n], A, D,
+                                   pool[slot[b]][None])
+        assert rel_err(new[slot[b]], fr[0]) < 1e-12, b
+    for s in (1, 3, 4, 5):                            # slots no request names are untouched
+        assert np.array_equal(new[s], pool[s])
+
+
+def test_single_candidate_is_the_plain_update(orc):
+    x, Bm, Cm, dt, A, D, pool = spec_inputs(14, k=1, nslots=4)
+    y, inter = orc.state_update_multi(pool, None, x, Bm, Cm, dt, A, D)
+    yr, sr = orc.state_update(pool, x[:, 0], Bm[:, 0], Cm[:, 0], dt[:, 0], A, D)
+    assert np.array_equal(y[:, 0], yr) and np.array_equal(inter[:, 0], sr)
