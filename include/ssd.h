@@ -12,6 +12,8 @@
  * and their serving forms on packed variable-length batches and state pools:
  *   ssd_conv1d_fwd_varlen, ssd_chunk_scan_varlen, ssd_conv1d_update_slots,
  *   ssd_state_update_slots
+ * and multi-token (speculative) decode with the accept step:
+ *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
@@ -251,6 +253,65 @@ ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int6
                                     const void* B, const void* C, int64_t bc_row_stride, const void* dt,
                                     const float* A, const float* D, const ssd_dt_params_t* dt_params, void* y,
                                     hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Multi-token decode for speculative decoding.  [P1] 状态契约, "MTP / speculative decoding":
+ * each candidate token of a request leaves an intermediate recurrent state and conv state;
+ * after verification, the state at the request's accepted length has to be written back into
+ * its main state, or later decode steps continue from the wrong history.
+ *
+ * d->batch = B requests, d->seqlen = k candidate tokens per request (0 <= k < 2^31).  Token j
+ * of request b is row b*k + j of every per-token tensor.  The multi-token calls only read the
+ * main states; ssd_accept_states then writes them.
+ *  slot_idx  [B] int32 device memory, or NULL: request b uses entry b of the main states.
+ *            With a table, the main states are pools of nslots entries and request b uses
+ *            slot slot_idx[b]; a slot < 0 or >= nslots is padding (starts from zeros, and
+ *            accept stores nothing for it).
+ * A k-token step with every token accepted equals k single-token calls (bitwise, for the same
+ * dtypes): the arithmetic per token is that of ssd_conv1d_update and ssd_state_update.
+ */
+
+/*
+ * k-token SSM update from the request's state (read only).
+ *  state         [B or nslots, H, P, N] fp32.  May be NULL only with a slot table and nslots 0.
+ *  x             x[b,j,h,p] at x[(b*k + j)*x_row_stride + h*P + p]; B, C: B[b,j,g,n] at
+ *                B[(b*k + j)*bc_row_stride + g*N + n]; act dtype.
+ *  dt            [B, k, H] act dtype, contiguous.  A, D, dt_params as ssd_state_update.
+ *  inter_states  [B, k, H, P, N] fp32: the state after each token, or NULL (not written).
+ *  y             [B, k, H, P] contiguous y dtype.
+ */
+ssd_status_t ssd_state_update_multi(const ssd_dims_t* d, const float* state, const int32_t* slot_idx,
+                                    int64_t nslots, const void* x, int64_t x_row_stride, const void* B,
+                                    const void* C, int64_t bc_row_stride, const void* dt, const float* A,
+                                    const float* D, const ssd_dt_params_t* dt_params, float* inter_states,
+                                    void* y, hipStream_t stream);
+
+/*
+ * k-token conv update from the request's conv state (read only).
+ *  xbc                [B*k, CD] act dtype, rows xbc_row_stride elements apart (>= CD).
+ *  w, bias            as ssd_conv1d_fwd.
+ *  conv_state         [B or nslots, CD, 4] act dtype.  NULL only with a slot table and nslots 0.
+ *  inter_conv_states  [B, k, CD, 4] act dtype: the window after each token, or NULL.
+ *  out                [B, k, CD] contiguous act dtype.
+ */
+ssd_status_t ssd_conv1d_update_multi(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                     const void* w, const void* bias, const void* conv_state,
+                                     const int32_t* slot_idx, int64_t nslots, void* inter_conv_states,
+                                     void* out, hipStream_t stream);
+
+/*
+ * Accept step.  accept_len [B] int32 device memory: request b keeps its first n tokens, with n
+ * clamped to [0, k].  For n >= 1, inter_states[b, n-1] is copied into its state (entry b or
+ * slot slot_idx[b]) and inter_conv_states[b, n-1] into its conv state; n = 0 and padding
+ * requests leave them unchanged.  Either pair (state, inter_states) or (conv_state,
+ * inter_conv_states) may be NULL, not one pointer of a pair.  Slots of one call must be
+ * distinct, and the intermediate buffers must not overlap the main states.  B <= 65535.
+ * Two launches on `stream` (SSM state, then conv state).
+ */
+ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, const int32_t* slot_idx,
+                               int64_t nslots, float* state, const float* inter_states, void* conv_state,
+                               const void* inter_conv_states, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

@@ -1,0 +1,240 @@
+// Multi-token decode for speculative decoding ("Mamba 与 Nemotron 系列模型深度调研", 状态契约,
+// MTP / speculative decoding): the k candidate tokens of a request advance its conv and SSM
+// states one token at a time, every intermediate state is kept, and once the verifier has fixed
+// how many tokens a request accepts, the state after the last accepted token is copied back into
+// the request's state.  The request's own state is only read here until that copy.
+//
+// All three kernels are HBM streams with no reuse across threads:
+//  * the SSM update reads each fp32 state element once and writes it k times (one intermediate
+//    state per candidate), with the single-token update's walk of the state as flat float4 and
+//    its arithmetic, in the same order, so k = 1 reproduces it bitwise;
+//  * the conv update keeps one 16-byte channel vector's 4-column window in registers across
+//    the k tokens and writes the window after each;
+//  * accept copies one intermediate state per request in 16-byte units.
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+constexpr int kMultiThreads = 128;
+constexpr int kMultiPerThread = 4;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyPerThread = 4;
+
+// Grid: one thread per kMultiPerThread float4 of the [B, H, P, N] state, 128-thread strides.
+// Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.
+template <typename T, typename TY, int N>
+__global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
+    const float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, TY* __restrict__ y, float* __restrict__ inter, int64_t total4, int k, int H,
+    int P, int hpg, const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp) {
+    constexpr int QPR = N / 4;  // float4 per state row
+    const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
+    const f32x4* st4 = reinterpret_cast<const f32x4*>(state);
+    f32x4* in4 = reinterpret_cast<f32x4*>(inter);
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread) + threadIdx.x;
+
+    // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g
+    f32x4 s[kMultiPerThread];
+    int64_t bb[kMultiPerThread], rem[kMultiPerThread];
+    int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
+#pragma unroll
+    for (int i = 0; i < kMultiPerThread; ++i) {
+        const int64_t f = base + i * kMultiThreads;
+        const int64_t ff = f < total4 ? f : 0;
+        bb[i] = ff / per_b;
+        rem[i] = ff - bb[i] * per_b;
+        rw[i] = static_cast<int>(rem[i] / QPR);
+        qq[i] = static_cast<int>(rem[i] - static_cast<int64_t>(rw[i]) * QPR);
+        hh[i] = rw[i] / P;
+        pp[i] = rw[i] - hh[i] * P;
+        gg[i] = hh[i] / hpg;
+        const int64_t slot = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
+        s[i] = (f < total4 && slot >= 0) ? __builtin_nontemporal_load(st4 + slot * per_b + rem[i])
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j = 0; j < k; ++j) {
+#pragma unroll
+        for (int i = 0; i < kMultiPerThread; ++i) {
+            const bool ok = base + i * kMultiThreads < total4;
+            const int64_t row = rw[i];
+            const int q = qq[i], h = hh[i], p = pp[i], g = gg[i];
+            const int64_t tok = bb[i] * k + j;
+            const float dtv = dt_prologue(static_cast<float>(dt[tok * H + h]), dtp, h);
+            const float a = __expf(dtv * A[h]);
+            const float xv = static_cast<float>(x[tok * xs + static_cast<int64_t>(h) * P + p]);
+            const int64_t bo = tok * bcs + static_cast<int64_t>(g) * N + 4 * q;
+            float bv[4], cv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bv[e] = static_cast<float>(Bm[bo + e]);
+                cv[e] = static_cast<float>(Cm[bo + e]);
+            }
+            const float dx = dtv * xv;
+            f32x4 v = s[i];
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = fmaf(a, v[e], dx * bv[e]);
+                part = fmaf(v[e], cv[e], part);
+            }
+            s[i] = v;
+            if (!ok) part = 0.f;
+#pragma unroll
+            for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+            if (ok) {
+                if (q == 0) y[tok * H * static_cast<int64_t>(P) + row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+                if (inter) __builtin_nontemporal_store(v, in4 + tok * per_b + rem[i]);
+            }
+        }
+    }
+}
+
+template <typename T, typename TY, int N>
+static hipError_t multi_launch(const UpdateArgs& a, hipStream_t s) {
+    const int64_t total4 = a.batch * a.nheads * static_cast<int64_t>(a.head_dim) * (N / 4);
+    if (total4 == 0 || a.k == 0) return hipSuccess;
+    const int64_t per_block = kMultiThreads * kMultiPerThread;
+    const int64_t blocks = (total4 + per_block - 1) / per_block;
+    hipLaunchKernelGGL((state_update_multi_kernel<T, TY, N>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kMultiThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
+                       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
+                       static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), a.inter, total4, a.k,
+                       a.nheads, a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots, a.dtp);
+    return hipGetLastError();
+}
+
+template <typename T, typename TY>
+static hipError_t multi_t(const UpdateArgs& a, hipStream_t s) {
+    switch (a.d_state) {
+        case 16: return multi_launch<T, TY, 16>(a, s);
+        case 32: return multi_launch<T, TY, 32>(a, s);
+        case 64: return multi_launch<T, TY, 64>(a, s);
+        case 128: return multi_launch<T, TY, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_state_update_multi(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s) {
+    if (act == Dt::BF16)
+        return ydt == Dt::BF16 ? multi_t<bf16, bf16>(a, s) : multi_t<bf16, float>(a, s);
+    return ydt == Dt::BF16 ? multi_t<float, bf16>(a, s) : multi_t<float, float>(a, s);
+}
+
+// One thread per (request, 16-byte channel vector).  The window of request b starts from its
+// conv state (its pool slot with a slot table; zeros for padding) and rolls by one per token,
+// with the single-token conv update's arithmetic.
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void conv1d_update_multi_kernel(
+    const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w, const T* __restrict__ bias,
+    const T* __restrict__ state, const int32_t* __restrict__ slot_idx, int64_t nslots, T* __restrict__ inter,
+    T* __restrict__ out, int64_t CD, int64_t total, int k) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t per_b = CD / V;
+    const int64_t b = idx / per_b;
+    const int64_t c0 = (idx - b * per_b) * V;
+
+    float s[4 * V], wt[4 * V], bs[V];
+    const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    if (slot >= 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load16_f32(state + (slot * CD + c0) * 4 + q * V, s + q * V);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4 * V; ++e) s[e] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load16_f32(w + c0 * 4 + q * V, wt + q * V);
+    if (bias) load16_f32(bias + c0, bs);
+    else
+#pragma unroll
+        for (int v = 0; v < V; ++v) bs[v] = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const int64_t tok = b * k + j;
+        float u[V], o[V];
+        load16_f32(xbc + tok * xs + c0, u);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float* sv = s + v * 4;
+            sv[0] = sv[1];
+            sv[1] = sv[2];
+            sv[2] = sv[3];
+            sv[3] = u[v];
+            float acc = bs[v];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(wt[v * 4 + e], sv[e], acc);
+            o[v] = silu_f(acc);
+        }
+        store16_f32(out + tok * CD + c0, o);
+        if (inter) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) store16_f32(inter + (tok * CD + c0) * 4 + q * V, s + q * V);
+        }
+    }
+}
+
+template <typename T>
+static hipError_t conv_multi_t(const ConvUpdateArgs& a, hipStream_t s) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t total = a.batch * (a.channels / V);
+    if (total == 0 || a.k == 0) return hipSuccess;
+    const int64_t blocks = (total + kCopyThreads - 1) / kCopyThreads;
+    hipLaunchKernelGGL(conv1d_update_multi_kernel<T>, dim3(static_cast<uint32_t>(blocks)), dim3(kCopyThreads), 0,
+                       s, static_cast<const T*>(a.xbc), a.xbc_row_stride, static_cast<const T*>(a.w),
+                       static_cast<const T*>(a.bias), static_cast<const T*>(a.state), a.slot_idx, a.nslots,
+                       static_cast<T*>(a.inter), static_cast<T*>(a.out), a.channels, total, a.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s) {
+    return act == Dt::BF16 ? conv_multi_t<bf16>(a, s) : conv_multi_t<float>(a, s);
+}
+
+// Request blockIdx.y: with n = accept_len clamped to [0, k] and n >= 1, copy its intermediate
+// state n-1 (units 16-byte vectors) into its slot.  Each thread moves kCopyPerThread vectors,
+// all loads before the stores.
+__global__ __launch_bounds__(kCopyThreads) void accept_copy_kernel(const int32_t* __restrict__ accept_len,
+                                                                   const int32_t* __restrict__ slot_idx,
+                                                                   int64_t nslots, int k, u32x4* __restrict__ dst,
+                                                                   const u32x4* __restrict__ src, int64_t units) {
+    const int64_t b = blockIdx.y;
+    int n = accept_len[b];
+    n = n < 0 ? 0 : (n > k ? k : n);
+    const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    if (n == 0 || slot < 0) return;
+    const u32x4* from = src + (b * k + n - 1) * units;
+    u32x4* to = dst + slot * units;
+    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * (kCopyThreads * kCopyPerThread) + threadIdx.x;
+    u32x4 v[kCopyPerThread];
+#pragma unroll
+    for (int r = 0; r < kCopyPerThread; ++r) {
+        const int64_t u = u0 + r * kCopyThreads;
+        if (u < units) v[r] = __builtin_nontemporal_load(from + u);
+    }
+#pragma unroll
+    for (int r = 0; r < kCopyPerThread; ++r) {
+        const int64_t u = u0 + r * kCopyThreads;
+        if (u < units) __builtin_nontemporal_store(v[r], to + u);
+    }
+}
+
+static hipError_t accept_copy(const AcceptArgs& a, void* dst, const void* src, int64_t bytes, hipStream_t s) {
+    const int64_t units = bytes / 16;
+    if (!dst || units == 0 || a.batch == 0 || a.k == 0) return hipSuccess;
+    const int64_t per_block = kCopyThreads * kCopyPerThread;
+    dim3 grid(static_cast<uint32_t>((units + per_block - 1) / per_block), static_cast<uint32_t>(a.batch));
+    hipLaunchKernelGGL(accept_copy_kernel, grid, dim3(kCopyThreads), 0, s, a.accept_len, a.slot_idx, a.nslots, a.k,
+                       static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), units);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s) {
+    hipError_t e = accept_copy(a, a.state, a.inter, a.state_bytes, s);
+    if (e != hipSuccess) return e;
+    return accept_copy(a, a.conv_state, a.inter_conv, a.conv_bytes, s);
+}
+
+}  // namespace ssd

@@ -256,4 +256,74 @@ ssd_status_t ssd_state_update(const ssd_dims_t* d, float* state, const void* x, 
                                                static_cast<Dt>(d->y_dtype), stream));
 }
 
+ssd_status_t ssd_state_update_multi(const ssd_dims_t* d, const float* state, const int32_t* slot_idx,
+                                    int64_t nslots, const void* x, int64_t x_row_stride, const void* B,
+                                    const void* C, int64_t bc_row_stride, const void* dt, const float* A,
+                                    const float* D, const ssd_dt_params_t* dt_params, float* inter_states,
+                                    void* y, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (nslots < 0 || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (tokens && !state && (!slot_idx || nslots > 0)) return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (tokens && (x_row_stride < I || bc_row_stride < GN)) return SSD_ERR_SHAPE;
+    for (const void* p : {static_cast<const void*>(state), static_cast<const void*>(inter_states)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
+    ssd::UpdateArgs a{const_cast<float*>(state), x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, slot_idx, nslots,
+                      dt_params_of(dt_params), inter_states, static_cast<int>(d->seqlen)};
+    return hip_status(ssd::launch_state_update_multi(a, static_cast<Dt>(d->act_dtype),
+                                                     static_cast<Dt>(d->y_dtype), stream));
+}
+
+ssd_status_t ssd_conv1d_update_multi(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride,
+                                     const void* w, const void* bias, const void* conv_state,
+                                     const int32_t* slot_idx, int64_t nslots, void* inter_conv_states,
+                                     void* out, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (nslots < 0 || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    const int64_t CD = ssd_conv_dim(d);
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!xbc || !w || !out)) return SSD_ERR_NULL;
+    if (tokens && !conv_state && (!slot_idx || nslots > 0)) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (tokens && xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, w, bias, conv_state, static_cast<const void*>(inter_conv_states),
+                          static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::ConvUpdateArgs a{xbc, xbc_row_stride, w, bias, const_cast<void*>(conv_state), out, d->batch, CD,
+                          slot_idx, nslots, inter_conv_states, static_cast<int>(d->seqlen)};
+    return hip_status(ssd::launch_conv1d_update_multi(a, static_cast<Dt>(d->act_dtype), stream));
+}
+
+ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, const int32_t* slot_idx,
+                               int64_t nslots, float* state, const float* inter_states, void* conv_state,
+                               const void* inter_conv_states, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (nslots < 0 || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    if (d->batch > 65535) return SSD_ERR_UNSUPPORTED;   // one grid row per request
+    if ((state == nullptr) != (inter_states == nullptr)) return SSD_ERR_NULL;
+    if ((conv_state == nullptr) != (inter_conv_states == nullptr)) return SSD_ERR_NULL;
+    const bool work = d->batch > 0 && d->seqlen > 0 && (state || conv_state) && (!slot_idx || nslots > 0);
+    if (work && !accept_len) return SSD_ERR_NULL;
+    if (ssd_conv_dim(d) % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    for (const void* p : {static_cast<const void*>(state), static_cast<const void*>(inter_states),
+                          static_cast<const void*>(conv_state), inter_conv_states})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if (!work) return SSD_OK;
+    const int64_t state_bytes = static_cast<int64_t>(d->nheads) * d->head_dim * d->d_state * 4;
+    const int64_t conv_bytes = ssd_conv_dim(d) * 4 * elem_size(d->act_dtype);
+    ssd::AcceptArgs a{accept_len, slot_idx, nslots, d->batch, static_cast<int>(d->seqlen),
+                      state, inter_states, state_bytes, conv_state, inter_conv_states, conv_bytes};
+    return hip_status(ssd::launch_accept_states(a, stream));
+}
+
 }  // extern "C"

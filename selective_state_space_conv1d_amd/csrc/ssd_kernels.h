@@ -43,6 +43,8 @@ struct ConvUpdateArgs {
     int64_t batch, channels;
     const int32_t* slot_idx;   // NULL: batch entry b uses state b; else slot slot_idx[b] of nslots
     int64_t nslots;
+    void* inter;   // multi-token: [B, k, CD, 4] window after each token, or NULL
+    int k;         // multi-token: tokens per request (the state is then read only)
 };
 
 struct ScanArgs {
@@ -68,6 +70,20 @@ struct UpdateArgs {
     const int32_t* slot_idx;   // NULL: batch entry b uses state b; else slot slot_idx[b] of nslots
     int64_t nslots;
     DtParams dtp;
+    float* inter;   // multi-token: [B, k, H, P, N] state after each token, or NULL
+    int k;          // multi-token: tokens per request (the state is then read only)
+};
+
+// Accept step of speculative decoding: request b with n = clamp(accept_len[b], 0, k) >= 1 gets
+// intermediate state b*k + n - 1 copied into its slot (b without a slot table), for the SSM
+// state (state_bytes per request) and the conv state (conv_bytes); NULL pointers skip one.
+struct AcceptArgs {
+    const int32_t* accept_len;
+    const int32_t* slot_idx;
+    int64_t nslots, batch;
+    int k;
+    void* state; const void* inter; int64_t state_bytes;
+    void* conv_state; const void* inter_conv; int64_t conv_bytes;
 };
 
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, Dt act, hipStream_t s);
@@ -75,6 +91,10 @@ hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, Dt act, hipStream_t s);
 hipError_t launch_conv1d_fwd_varlen(const ConvFwdArgs& a, Dt act, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs& a, Dt act, hipStream_t s);
 hipError_t launch_state_update(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
+// speculative decode: k tokens per request from a read-only state, then the accept copy
+hipError_t launch_state_update_multi(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
+hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s);
+hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);
 hipError_t launch_chunk_scan_mfma(const ScanArgs& a, Dt ydt, hipStream_t s);

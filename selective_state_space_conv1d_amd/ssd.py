@@ -21,7 +21,8 @@ STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_DTYPE", "SSD_ERR_A
           "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
 EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
-           "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots"]
+           "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
+           "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states"]
 
 
 class SsdDims(ctypes.Structure):
@@ -72,9 +73,14 @@ def _lib():
                                               _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
                                                _PDT, _VP, _VP]
+        lib.ssd_state_update_multi.argtypes = [_PD, _VP, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
+                                               _PDT, _VP, _VP, _VP]
+        lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
+        lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
-                  "ssd_state_update_slots"):
+                  "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
+                  "ssd_accept_states"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -375,6 +381,133 @@ def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None,
                                          _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(y), _stream(stream)),
            "ssd_state_update_slots")
     return y
+
+
+# --------------------------------------------------------------------------- speculative decode
+def _state_pool_args(state, slot_idx, Bt):
+    """(pointer tensor, nslots, slot table) of a main state given per request or as a slot pool."""
+    if slot_idx is None:
+        if state.shape[0] != Bt:
+            raise ValueError("without slot_idx the state needs one entry per request")
+        return state, 0, None
+    return state, state.shape[0], _table(slot_idx, Bt, "slot_idx")
+
+
+def ssd_state_update_multi(state, x, B, C, dt, A, D=None, slot_idx=None, inter_states=True, y=None,
+                           y_dtype=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
+    """k candidate tokens per request from state [B or nslots, H, P, N] fp32 (read only; with
+    slot_idx [B] int32 it is a pool).  x [B, k, H, P], B/C [B, k, G, N] (token rows may be
+    strided, e.g. views into the multi-token conv output), dt [B, k, H].  inter_states: True
+    allocates [B, k, H, P, N] fp32, a tensor is written, None/False skips it.
+    Returns (y [B, k, H, P], inter_states or None)."""
+    Bt, k, H, P = x.shape
+    N = state.shape[3]
+    G = B.shape[2]
+    if state.dim() != 4 or state.shape[1:] != (H, P, N) or not state.is_contiguous():
+        raise ValueError("state must be contiguous [B or nslots, H, P, N]")
+    if k > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, k)):
+        raise ValueError("x must be [B, k, H, P] with packed (H, P) and uniform token stride")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, k, G, N) or (k > 0 and (t.stride(3) != 1 or t.stride(2) != N
+                                                    or not _uniform_rows(t, k))):
+            raise ValueError(f"{nm} must be [B, k, G, N] with packed (G, N) and uniform token stride")
+    if B.stride(1) != C.stride(1):
+        raise ValueError("B and C must share a token stride")
+    if dt.shape != (Bt, k, H) or not dt.is_contiguous():
+        raise ValueError("dt must be contiguous [B, k, H]")
+    st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
+    if inter_states is True:
+        inter_states = torch.empty((Bt, k, H, P, N), dtype=torch.float32, device=x.device)
+    elif inter_states is False:
+        inter_states = None
+    if inter_states is not None and (inter_states.shape != (Bt, k, H, P, N) or not inter_states.is_contiguous()
+                                     or inter_states.dtype != torch.float32):
+        raise ValueError("inter_states must be contiguous fp32 [B, k, H, P, N]")
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((Bt, k, H, P), dtype=ydt, device=x.device)
+    d = _dims(Bt, k, H, P, G, N, x.dtype, y.dtype)
+    xs, bcs = (P * H, G * N) if k == 0 else (x.stride(1), B.stride(1))
+    _check(_lib().ssd_state_update_multi(ctypes.byref(d), _ptr(st), _ptr(tab), nslots, _ptr(x), xs, _ptr(B),
+                                         _ptr(C), bcs, _ptr(dt), _ptr(A), _ptr(D),
+                                         _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(inter_states), _ptr(y),
+                                         _stream(stream)), "ssd_state_update_multi")
+    return y, inter_states
+
+
+def ssd_conv1d_update_multi(xbc, w, bias, conv_state, slot_idx=None, inter_conv_states=True, out=None,
+                            nheads=None, head_dim=None, ngroups=None, d_state=None, stream=None):
+    """k candidate tokens per request through the conv from conv_state [B or nslots, CD, 4]
+    (read only).  xbc [B, k, CD] (token rows may be strided, uniform).  inter_conv_states: True
+    allocates [B, k, CD, 4], a tensor is written, None/False skips it.
+    Returns (out [B, k, CD], inter_conv_states or None)."""
+    Bt, k, CD = xbc.shape
+    if k > 0 and (xbc.stride(2) != 1 or not _uniform_rows(xbc, k)):
+        raise ValueError("xbc must be [B, k, CD] with packed channels and uniform token stride")
+    if conv_state.dim() != 3 or conv_state.shape[1:] != (CD, 4) or not conv_state.is_contiguous():
+        raise ValueError("conv_state must be contiguous [B or nslots, CD, 4]")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    st, nslots, tab = _state_pool_args(conv_state, slot_idx, Bt)
+    if inter_conv_states is True:
+        inter_conv_states = torch.empty((Bt, k, CD, 4), dtype=xbc.dtype, device=xbc.device)
+    elif inter_conv_states is False:
+        inter_conv_states = None
+    if inter_conv_states is not None and (inter_conv_states.shape != (Bt, k, CD, 4)
+                                          or not inter_conv_states.is_contiguous()
+                                          or inter_conv_states.dtype != xbc.dtype):
+        raise ValueError("inter_conv_states must be contiguous [B, k, CD, 4] in xbc's dtype")
+    if out is None:
+        out = torch.empty((Bt, k, CD), dtype=xbc.dtype, device=xbc.device)
+    d = _dims(Bt, k, H, P, G, N, xbc.dtype, xbc.dtype)
+    xs = CD if k == 0 else xbc.stride(1)
+    _check(_lib().ssd_conv1d_update_multi(ctypes.byref(d), _ptr(xbc), xs, _ptr(w), _ptr(bias), _ptr(st),
+                                          _ptr(tab), nslots, _ptr(inter_conv_states), _ptr(out),
+                                          _stream(stream)), "ssd_conv1d_update_multi")
+    return out, inter_conv_states
+
+
+def ssd_accept_states(accept_len, state=None, inter_states=None, conv_state=None, inter_conv_states=None,
+                      slot_idx=None, stream=None):
+    """Write back the state after each request's last accepted token: accept_len [B] int32
+    (clamped to [0, k]; 0 keeps the state).  state [B or nslots, H, P, N] fp32 with inter_states
+    [B, k, H, P, N]; conv_state [B or nslots, CD, 4] with inter_conv_states [B, k, CD, 4]; either
+    pair may be None.  Slots as for the multi-token calls."""
+    if inter_states is None and inter_conv_states is None:
+        raise ValueError("nothing to accept")
+    ref = inter_states if inter_states is not None else inter_conv_states
+    Bt, k = ref.shape[:2]
+    # the call's dims: (H, P, N) from the SSM states, CD = H*P + 2*G*N from the conv states
+    G, N, dtype = 1, 16, torch.float32
+    if inter_states is not None:
+        H, P, N = inter_states.shape[2:]
+    if inter_conv_states is not None:
+        CD, dtype = inter_conv_states.shape[2], inter_conv_states.dtype
+        if inter_states is None:
+            H, P, G, N = _split_cd(CD, None, None, None, None)
+        else:
+            G = (CD - H * P) // (2 * N)
+            if G <= 0 or H * P + 2 * G * N != CD or H % G:
+                raise ValueError("conv channels do not match the state's (H, P, N)")
+    for main, inter, nm in ((state, inter_states, "state"), (conv_state, inter_conv_states, "conv_state")):
+        if (main is None) != (inter is None):
+            raise ValueError(f"{nm} and its intermediate states go together")
+        if main is not None:
+            if not main.is_contiguous() or not inter.is_contiguous() or main.shape[1:] != inter.shape[2:]:
+                raise ValueError(f"{nm} [.., {tuple(inter.shape[2:])}] and its intermediates must be contiguous")
+            if inter.shape[:2] != (Bt, k) or main.dtype != inter.dtype:
+                raise ValueError(f"intermediate {nm}s must be [B, k, ...] in the state's dtype")
+            if slot_idx is None and main.shape[0] != Bt:
+                raise ValueError(f"without slot_idx {nm} needs one entry per request")
+    nslots = 0
+    if slot_idx is not None:
+        nslots = (state if state is not None else conv_state).shape[0]
+        if state is not None and conv_state is not None and conv_state.shape[0] != nslots:
+            raise ValueError("state and conv_state pools must have the same number of slots")
+    d = _dims(Bt, k, H, P, G, N, dtype, dtype)
+    _check(_lib().ssd_accept_states(ctypes.byref(d), _ptr(_table(accept_len, Bt, "accept_len")),
+                                    _ptr(_table(slot_idx, Bt, "slot_idx")), nslots, _ptr(state),
+                                    _ptr(inter_states), _ptr(conv_state), _ptr(inter_conv_states),
+                                    _stream(stream)), "ssd_accept_states")
 
 
 def split_xbc(v, nheads, head_dim, ngroups, d_state):

@@ -184,6 +184,48 @@ def test_varlen_and_slot_validation(ssd, lib):
     assert upd(y=None) == E["SSD_ERR_NULL"]
 
 
+def test_multi_token_and_accept_validation(ssd, lib):
+    """The speculative-decode entry points reject bad host arguments before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=3)   # 2 requests x 3 candidate tokens; CD = 768
+
+    def upd(dd=d, state=fp(1), slot=None, nslots=0, x=fp(2), xs=256, inter=fp(9), y=fp(7)):
+        return lib.ssd_state_update_multi(ctypes.byref(dd), state, slot, nslots, x, xs, fp(3), fp(4), 256, fp(5),
+                                          fp(6), None, None, inter, y, None)
+    assert upd(state=None) == E["SSD_ERR_NULL"]                   # no state without a slot table
+    assert upd(state=None, slot=fp(8), nslots=2) == E["SSD_ERR_NULL"]
+    assert upd(x=None) == E["SSD_ERR_NULL"]
+    assert upd(y=None) == E["SSD_ERR_NULL"]
+    assert upd(nslots=-1) == E["SSD_ERR_SHAPE"]
+    assert upd(xs=100) == E["SSD_ERR_SHAPE"]
+    assert upd(inter=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert upd(dims(ssd, batch=2, seqlen=3, head_dim=24)) == E["SSD_ERR_UNSUPPORTED"]
+    assert upd(dims(ssd, batch=2, seqlen=-1)) == E["SSD_ERR_SHAPE"]
+
+    def conv(dd=d, xbc=fp(1), xs=768, state=fp(2), slot=None, nslots=0, inter=fp(3), out=fp(4)):
+        return lib.ssd_conv1d_update_multi(ctypes.byref(dd), xbc, xs, fp(5), None, state, slot, nslots, inter, out,
+                                           None)
+    assert conv(state=None) == E["SSD_ERR_NULL"]
+    assert conv(out=None) == E["SSD_ERR_NULL"]
+    assert conv(xs=700) == E["SSD_ERR_SHAPE"]
+    assert conv(xs=772) == E["SSD_ERR_ALIGN"]
+    assert conv(inter=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert conv(nslots=-5) == E["SSD_ERR_SHAPE"]
+
+    def acc(dd=d, alen=fp(1), slot=None, nslots=0, st=fp(2), ist=fp(3), cs=fp(4), ics=fp(5)):
+        return lib.ssd_accept_states(ctypes.byref(dd), alen, slot, nslots, st, ist, cs, ics, None)
+    assert acc(alen=None) == E["SSD_ERR_NULL"]
+    assert acc(ist=None) == E["SSD_ERR_NULL"]                     # a pair is both or neither
+    assert acc(cs=None) == E["SSD_ERR_NULL"]
+    assert acc(st=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert acc(nslots=-1) == E["SSD_ERR_SHAPE"]
+    assert acc(dims(ssd, batch=70000, seqlen=3)) == E["SSD_ERR_UNSUPPORTED"]
+    # nothing to do: no states, no tokens, or an empty pool -- no launch, no table read
+    assert acc(st=None, ist=None, cs=None, ics=None, alen=None) == E["SSD_OK"]
+    assert acc(dims(ssd, batch=2, seqlen=0), alen=None) == E["SSD_OK"]
+    assert acc(slot=fp(8), nslots=0, alen=None) == E["SSD_OK"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
