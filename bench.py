@@ -166,6 +166,69 @@ def serving_leg(ssd, torch, dev, steps, warmup):
     }
 
 
+def spec_leg(ssd, torch, dev, steps, warmup, k=4):
+    """One speculative-decode step of the Ultra decode layer: batch 64 requests of a 96-slot pool,
+    k candidate tokens each: the k-token conv, the k-token SSM update with every intermediate
+    state, and the accept copy at seeded accept lengths in [0, k].  Each launch bracketed by
+    HIP events."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, scan_inputs
+    dd = WORKLOADS["decode_ultra_b64"]
+    B, H, P, N, G, CD = dd.batch, dd.nheads, dd.head_dim, dd.d_state, dd.ngroups, dd.conv_dim
+    npool = 96
+    g = torch.Generator(device="cpu").manual_seed(1020)
+    slot = torch.randperm(npool, generator=g)[:B].to(torch.int32).to(dev)
+    acc = torch.randint(0, k + 1, (B,), generator=g).to(torch.int32)
+    n_acc = int((acc > 0).sum())
+    acc = acc.to(dev)
+    xbc = (torch.randn(B, k, CD, generator=g) * 1.0).to(dd.dtype).to(dev)
+    w = (torch.rand(CD, 4, generator=g) - 0.5).to(dd.dtype).to(dev)
+    bias = (torch.rand(CD, generator=g) - 0.5).to(dd.dtype).to(dev)
+    cpool = torch.randn(npool, CD, 4, generator=g).to(dd.dtype).to(dev)
+    spool = (torch.randn(npool, H, P, N, generator=g) * 0.1).to(dev)
+    sin = scan_inputs(dd, 1021, seqlen=k, init_state=False)
+    dt, A, D = sin["dt"].to(dev), sin["A"].to(dev), sin["D"].to(dev)
+    del sin
+    cout = torch.empty(B, k, CD, dtype=dd.dtype, device=dev)
+    cinter = torch.empty(B, k, CD, 4, dtype=dd.dtype, device=dev)
+    inter = torch.empty(B, k, H, P, N, dtype=torch.float32, device=dev)
+    y = torch.empty(B, k, H, P, dtype=dd.dtype, device=dev)
+    xv, Bv, Cv = ssd.split_xbc(cout, H, P, G, N)
+    torch.cuda.synchronize()
+
+    def one(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ssd.ssd_conv1d_update_multi(xbc, w, bias, cpool, slot_idx=slot, inter_conv_states=cinter, out=cout)
+        mark(1)
+        ssd.ssd_state_update_multi(spool, xv, Bv, Cv, dt, A, D, slot_idx=slot, inter_states=inter, y=y)
+        mark(2)
+        ssd.ssd_accept_states(acc, spool, inter, cpool, cinter, slot_idx=slot)
+        mark(3)
+
+    for _ in range(warmup):
+        one()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    conv_s, upd_s, acc_s = (sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1e-3 for j in range(3))
+    S = H * P * N * 4
+    upd_b = B * (1 + k) * S + B * k * (2 * H * P * 2 + 2 * G * N * 2 + H * 2)
+    conv_b = B * CD * 4 * 2 + B * k * CD * 2 * 2 + B * k * CD * 4 * 2 + CD * 5 * 2
+    acc_b = n_acc * 2 * (S + CD * 4 * 2)
+    tot = conv_s + upd_s + acc_s
+    return {"batch": B, "candidates": k, "nslots": npool, "requests_accepting": n_acc,
+            "accepted_tokens": int(acc.clamp(0, k).sum()),
+            "candidate_tokens_per_s": B * k / tot, "accepted_tokens_per_s": int(acc.clamp(0, k).sum()) / tot,
+            "conv_multi_us": conv_s * 1e6, "conv_multi_GBps": conv_b / conv_s / 1e9,
+            "state_multi_us": upd_s * 1e6, "state_multi_GBps": upd_b / upd_s / 1e9,
+            "state_multi_frac": upd_b / upd_s / 1e9 / HBM_PEAK_GBS, "state_multi_algorithmic_bytes": upd_b,
+            "accept_us": acc_s * 1e6, "accept_GBps": acc_b / acc_s / 1e9,
+            "accept_frac": acc_b / acc_s / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(orc, inp, d, n_heads=256):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
     over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
@@ -345,6 +408,8 @@ def main():
     del v, x, Bm, Cm, y, state
     print("[bench] serving forms (packed prefill, slot-pool decode)", file=sys.stderr, flush=True)
     out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
+    print("[bench] speculative decode (k-token updates, accept)", file=sys.stderr, flush=True)
+    out["spec_decode"] = spec_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -276,7 +276,8 @@ ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int6
  * k-token SSM update from the request's state (read only).
  *  state         [B or nslots, H, P, N] fp32.  May be NULL only with a slot table and nslots 0.
  *  x             x[b,j,h,p] at x[(b*k + j)*x_row_stride + h*P + p]; B, C: B[b,j,g,n] at
- *                B[(b*k + j)*bc_row_stride + g*N + n]; act dtype.
+ *                B[(b*k + j)*bc_row_stride + g*N + n]; act dtype.  B and C 16-byte aligned and
+ *                bc_row_stride a multiple of 8 (bf16) or 4 (fp32) elements.
  *  dt            [B, k, H] act dtype, contiguous.  A, D, dt_params as ssd_state_update.
  *  inter_states  [B, k, H, P, N] fp32: the state after each token, or NULL (not written).
  *  y             [B, k, H, P] contiguous y dtype.

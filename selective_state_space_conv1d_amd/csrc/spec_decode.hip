@@ -17,12 +17,26 @@
 namespace ssd {
 
 constexpr int kMultiThreads = 128;
-constexpr int kMultiPerThread = 4;
+constexpr int kMultiPerThread = 2;   // measured best at batch 64, k = 4 (4 per thread: 30 % slower)
 constexpr int kCopyThreads = 256;
 constexpr int kCopyPerThread = 4;
 
+// Four consecutive elements of T (8 bytes of bf16, 16 of fp32) in one load.
+template <typename T> struct Quad;
+template <> struct Quad<bf16> { typedef bf16x4 type; };
+template <> struct Quad<float> { typedef f32x4 type; };
+
+// Per element and token: the raw inputs, kept in their storage type until used.
+template <typename T>
+struct TokIn {
+    T dt, x;
+    typename Quad<T>::type b, c;
+};
+
 // Grid: one thread per kMultiPerThread float4 of the [B, H, P, N] state, 128-thread strides.
-// Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.
+// Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.  The
+// per-head constants are read once; each token's inputs for all of a thread's elements are
+// loaded one token ahead of their use, so the loads overlap the previous token's stores.
 template <typename T, typename TY, int N>
 __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     const float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
@@ -30,64 +44,90 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     const float* __restrict__ D, TY* __restrict__ y, float* __restrict__ inter, int64_t total4, int k, int H,
     int P, int hpg, const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp) {
     constexpr int QPR = N / 4;  // float4 per state row
+    typedef typename Quad<T>::type Q;
     const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
     const f32x4* st4 = reinterpret_cast<const f32x4*>(state);
     f32x4* in4 = reinterpret_cast<f32x4*>(inter);
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread) + threadIdx.x;
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread);
+    const int64_t base = f0 + threadIdx.x;
+    // The block's elements almost always lie in one request: then its index and slot are looked
+    // up once for the block, so no state load waits on a per-thread table read.
+    const int64_t fl = (f0 + kMultiThreads * kMultiPerThread < total4 ? f0 + kMultiThreads * kMultiPerThread
+                                                                       : total4) - 1;
+    const int64_t ub = f0 / per_b;
+    const bool uni = ub == fl / per_b;
+    const int64_t uslot = uni ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
 
-    // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g
+    // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g,
+    // and the head's A, D and dt bias
     f32x4 s[kMultiPerThread];
     int64_t bb[kMultiPerThread], rem[kMultiPerThread];
     int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
+    float Ah[kMultiPerThread], Dh[kMultiPerThread], biash[kMultiPerThread];
 #pragma unroll
     for (int i = 0; i < kMultiPerThread; ++i) {
         const int64_t f = base + i * kMultiThreads;
         const int64_t ff = f < total4 ? f : 0;
-        bb[i] = ff / per_b;
+        bb[i] = uni ? ub : ff / per_b;
         rem[i] = ff - bb[i] * per_b;
         rw[i] = static_cast<int>(rem[i] / QPR);
         qq[i] = static_cast<int>(rem[i] - static_cast<int64_t>(rw[i]) * QPR);
         hh[i] = rw[i] / P;
         pp[i] = rw[i] - hh[i] * P;
         gg[i] = hh[i] / hpg;
-        const int64_t slot = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
+        const int64_t slot = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
         s[i] = (f < total4 && slot >= 0) ? __builtin_nontemporal_load(st4 + slot * per_b + rem[i])
                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        Ah[i] = A[hh[i]];
+        Dh[i] = D ? D[hh[i]] : 0.f;
+        biash[i] = dtp.bias ? dtp.bias[hh[i]] : 0.f;
     }
+    auto load_tok = [&](int j, TokIn<T> (&in)[kMultiPerThread]) {
+#pragma unroll
+        for (int i = 0; i < kMultiPerThread; ++i) {
+            const int64_t tok = bb[i] * k + j;
+            in[i].dt = dt[tok * H + hh[i]];
+            in[i].x = x[tok * xs + static_cast<int64_t>(hh[i]) * P + pp[i]];
+            const int64_t bo = tok * bcs + static_cast<int64_t>(gg[i]) * N + 4 * qq[i];
+            in[i].b = *reinterpret_cast<const Q*>(Bm + bo);
+            in[i].c = *reinterpret_cast<const Q*>(Cm + bo);
+        }
+    };
+    TokIn<T> cur[kMultiPerThread], nxt[kMultiPerThread];
+    load_tok(0, cur);
     for (int j = 0; j < k; ++j) {
+        if (j + 1 < k) load_tok(j + 1, nxt);
 #pragma unroll
         for (int i = 0; i < kMultiPerThread; ++i) {
             const bool ok = base + i * kMultiThreads < total4;
-            const int64_t row = rw[i];
-            const int q = qq[i], h = hh[i], p = pp[i], g = gg[i];
             const int64_t tok = bb[i] * k + j;
-            const float dtv = dt_prologue(static_cast<float>(dt[tok * H + h]), dtp, h);
-            const float a = __expf(dtv * A[h]);
-            const float xv = static_cast<float>(x[tok * xs + static_cast<int64_t>(h) * P + p]);
-            const int64_t bo = tok * bcs + static_cast<int64_t>(g) * N + 4 * q;
-            float bv[4], cv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bv[e] = static_cast<float>(Bm[bo + e]);
-                cv[e] = static_cast<float>(Cm[bo + e]);
-            }
+            // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
+            float dtv = static_cast<float>(cur[i].dt);
+            if (dtp.bias) dtv += biash[i];
+            if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
+            if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
+            const float a = __expf(dtv * Ah[i]);
+            const float xv = static_cast<float>(cur[i].x);
             const float dx = dtv * xv;
             f32x4 v = s[i];
             float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[e] = fmaf(a, v[e], dx * bv[e]);
-                part = fmaf(v[e], cv[e], part);
+                v[e] = fmaf(a, v[e], dx * static_cast<float>(cur[i].b[e]));
+                part = fmaf(v[e], static_cast<float>(cur[i].c[e]), part);
             }
             s[i] = v;
             if (!ok) part = 0.f;
 #pragma unroll
             for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
             if (ok) {
-                if (q == 0) y[tok * H * static_cast<int64_t>(P) + row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
-                if (inter) __builtin_nontemporal_store(v, in4 + tok * per_b + rem[i]);
+                if (qq[i] == 0)
+                    y[tok * H * static_cast<int64_t>(P) + rw[i]] = static_cast<TY>(part + (D ? Dh[i] * xv : 0.f));
+                if (inter) in4[tok * per_b + rem[i]] = v;   // plain stores measured faster here
             }
         }
+#pragma unroll
+        for (int i = 0; i < kMultiPerThread; ++i) cur[i] = nxt[i];
     }
 }
 

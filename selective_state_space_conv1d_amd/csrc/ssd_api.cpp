@@ -271,7 +271,8 @@ ssd_status_t ssd_state_update_multi(const ssd_dims_t* d, const float* state, con
     const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
     const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
     if (tokens && (x_row_stride < I || bc_row_stride < GN)) return SSD_ERR_SHAPE;
-    for (const void* p : {static_cast<const void*>(state), static_cast<const void*>(inter_states)})
+    if (!stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;   // B/C are read 4 elements at a time
+    for (const void* p : {static_cast<const void*>(state), static_cast<const void*>(inter_states), B, C})
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
     if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::UpdateArgs a{const_cast<float*>(state), x, x_row_stride, B, C, bc_row_stride, dt, A, D, y,

@@ -199,6 +199,10 @@ def test_multi_token_and_accept_validation(ssd, lib):
     assert upd(nslots=-1) == E["SSD_ERR_SHAPE"]
     assert upd(xs=100) == E["SSD_ERR_SHAPE"]
     assert upd(inter=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert lib.ssd_state_update_multi(ctypes.byref(d), fp(1), None, 0, fp(2), 256, fp(3), fp(4), 260, fp(5), fp(6),
+                                      None, None, None, fp(7), None) == E["SSD_ERR_ALIGN"]   # B/C row stride
+    assert lib.ssd_state_update_multi(ctypes.byref(d), fp(1), None, 0, fp(2), 256, ctypes.c_void_p(P0 + 8), fp(4),
+                                      256, fp(5), fp(6), None, None, None, fp(7), None) == E["SSD_ERR_ALIGN"]
     assert upd(dims(ssd, batch=2, seqlen=3, head_dim=24)) == E["SSD_ERR_UNSUPPORTED"]
     assert upd(dims(ssd, batch=2, seqlen=-1)) == E["SSD_ERR_SHAPE"]
 
