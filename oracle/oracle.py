@@ -8,7 +8,7 @@ import os
 
 import numpy as np
 
-from . import build_oracle
+from . import build_oracle, lowprec
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.c_int64
@@ -237,6 +237,47 @@ class Oracle:
             if s >= 0 and n >= 1:
                 new[s] = inter[b, n - 1]
         return new
+
+    # ------------------------------------------------------------------ reduced-precision state
+    # The state is stored as uint16 codes of fmt ('f16' or 'bf16', see lowprec) and decoded for
+    # the fp64 update above; the new state before rounding is returned, since which of the two
+    # neighbouring codes stores it depends on the fp32 value the kernel rounds.
+    # codes [nslots, H, P, N] uint16, slot [B]|None -> y [B,H,P], new state [B,H,P,N] (fp64, unrounded)
+    def state_update_lp(self, codes, fmt, slot, x, Bm, Cm, dt, A, D=None):
+        vals = lowprec.decode(codes, fmt)
+        Bt = np.asarray(x).shape[0]
+        st = np.zeros((Bt,) + vals.shape[1:])
+        for b in range(Bt):
+            s = self._slot(slot, b, vals.shape[0])
+            if s >= 0:
+                st[b] = vals[s]
+        return self.state_update(st, x, Bm, Cm, dt, A, D)
+
+    # With A = 0 for every head the update of an element is s + (dt*x)*B with the product dt*x,
+    # its product with B and the sum each rounded to fp32: the exact value the fp32 kernels
+    # compute.  Rounding it to fmt (round-to-nearest-even, or stochastically with
+    # sr = (seed, offset, rounds), the element index being its flat index in the pool) gives the
+    # codes that must be stored.  Returns the new pool of codes.
+    @classmethod
+    def state_update_lp_codes_a0(cls, codes, fmt, slot, x, Bm, Cm, dt, sr=None):
+        codes = np.array(codes, dtype=np.uint16, copy=True)
+        nslots, H, P, N = codes.shape
+        x, Bm, Cm, dt = (np.asarray(t, dtype=np.float32) for t in (x, Bm, Cm, dt))
+        G = Bm.shape[1]
+        vals = lowprec.decode(codes, fmt).astype(np.float32)
+        for b in range(x.shape[0]):
+            s = cls._slot(slot, b, nslots)
+            if s < 0:
+                continue
+            Bh = np.repeat(Bm[b], H // G, axis=0)                               # [H, N], group of each head
+            dx = (dt[b][:, None] * x[b]).astype(np.float32)                      # [H, P]
+            v = (vals[s] + (dx[:, :, None] * Bh[:, None, :]).astype(np.float32)).astype(np.float32)
+            r16 = None
+            if sr is not None:
+                e = s * H * P * N + np.arange(H * P * N, dtype=np.int64).reshape(H, P, N)
+                r16 = lowprec.random16(e, sr[0], sr[1], sr[2])
+            codes[s] = lowprec.round_state(v, fmt, r16)
+        return codes
 
 
 _DEFAULT = None
