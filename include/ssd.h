@@ -14,6 +14,7 @@
  *   ssd_state_update_slots
  * and multi-token (speculative) decode with the accept step:
  *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states
+ * and the decode update on a 16-bit state with stochastic rounding: ssd_state_update_lp
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
@@ -68,7 +69,7 @@ typedef enum {
     SSD_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } ssd_status_t;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 /* stored SSM state only */ } ssd_dtype_t;
 
 /* Sizes of one mixer layer.  act_dtype is the element type of the conv input,
  * taps, bias, conv state and output, and of x, B, C and dt.  y_dtype is the
@@ -313,6 +314,47 @@ ssd_status_t ssd_conv1d_update_multi(const ssd_dims_t* d, const void* xbc, int64
 ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, const int32_t* slot_idx,
                                int64_t nslots, float* state, const float* inter_states, void* conv_state,
                                const void* inter_conv_states, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Reduced-precision state storage.  [P2] 部署时如何调这些缓存: inference engines store the
+ * Mamba state cache in fp16 with stochastic rounding driven by a Philox generator (5 rounds).
+ * [P3] 5.4: the state pool may be stored in a narrower type while the update accumulates in
+ * fp32.  The state is read as 16-bit codes, updated in fp32 exactly as ssd_state_update does,
+ * and rounded back:
+ *  sr == NULL  round to nearest even.
+ *  sr != NULL  stochastic rounding.  Element e of the state array (its flat index in the pool
+ *              with a slot table) draws r16 = the 16-bit half (e mod 2), low half first, of word
+ *              (e mod 8) / 2 of Philox4x32-R (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
+ *              (o mod 2^32, o / 2^32, offset mod 2^32, offset / 2^32), o = e / 8, and key
+ *              (seed mod 2^32, seed / 2^32).  With lo the code next to the fp32 value v toward
+ *              zero (v itself when representable) and spacing the distance from lo to the next
+ *              code away from zero, v is stored as that next code iff
+ *              r16 < 65536 * (|v| - |lo|) / spacing, else as lo.  Past the largest finite value
+ *              the next code is infinity and the spacing that of the last binade; fp16 values
+ *              of magnitude 65536 or more become infinities; NaN and infinite v round to
+ *              nearest even.  Use a new offset for every call, or the same numbers repeat.
+ */
+typedef struct {
+    uint64_t seed;     /* Philox key */
+    uint64_t offset;   /* Philox counter words 2 and 3 */
+    int32_t rounds;    /* Philox rounds, 1..16 */
+} ssd_sr_params_t;
+
+/*
+ * Single-token state update on a 16-bit state.
+ *  state        [B or nslots, H, P, N] codes of state_dtype (SSD_F16 or SSD_BF16), updated in
+ *               place, 16-byte aligned.
+ *  slot_idx     [B] int32 device memory or NULL, as ssd_state_update_slots (NULL: entry b).
+ *  sr           rounding (above); NULL rounds to nearest even.
+ *  B, C         16-byte aligned, bc_row_stride a multiple of 8 (bf16) or 4 (fp32) elements.
+ * The rest is as for ssd_state_update.
+ */
+ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state_dtype, const int32_t* slot_idx,
+                                 int64_t nslots, const void* x, int64_t x_row_stride, const void* B, const void* C,
+                                 int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                 const ssd_dt_params_t* dt_params, const ssd_sr_params_t* sr, void* y,
+                                 hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

@@ -327,4 +327,32 @@ ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, c
     return hip_status(ssd::launch_accept_states(a, stream));
 }
 
+ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state_dtype, const int32_t* slot_idx,
+                                 int64_t nslots, const void* x, int64_t x_row_stride, const void* B, const void* C,
+                                 int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                 const ssd_dt_params_t* dt_params, const ssd_sr_params_t* sr, void* y,
+                                 hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    if (state_dtype != SSD_F16 && state_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (nslots < 0) return SSD_ERR_SHAPE;
+    if (sr && (sr->rounds < 1 || sr->rounds > 16)) return SSD_ERR_UNSUPPORTED;
+    if (d->batch > 0 && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (d->batch > 0 && !state && (!slot_idx || nslots > 0)) return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
+    if (!stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;   // B/C are read 8 elements at a time
+    for (const void* p : {static_cast<const void*>(state), B, C})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
+    ssd::LpUpdateArgs a{{nullptr, x, x_row_stride, B, C, bc_row_stride, dt, A, D, y, d->batch, d->nheads,
+                         d->head_dim, d->ngroups, d->d_state, slot_idx, slot_idx ? nslots : d->batch,
+                         dt_params_of(dt_params)},
+                        state, state_dtype == SSD_F16, sr ? sr->seed : 0, sr ? sr->offset : 0, sr ? sr->rounds : 0};
+    return hip_status(ssd::launch_state_update_lp(a, static_cast<Dt>(d->act_dtype), static_cast<Dt>(d->y_dtype),
+                                                  stream));
+}
+
 }  // extern "C"

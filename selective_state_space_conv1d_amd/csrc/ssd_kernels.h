@@ -74,6 +74,15 @@ struct UpdateArgs {
     int k;          // multi-token: tokens per request (the state is then read only)
 };
 
+// Decode update on a 16-bit state (fp16 or bf16 codes): u carries everything but the state.
+struct LpUpdateArgs {
+    UpdateArgs u;
+    void* state;
+    bool f16;          // fp16 codes, else bf16
+    uint64_t seed, offset;
+    int rounds;        // Philox rounds for stochastic rounding; 0: round to nearest even
+};
+
 // Accept step of speculative decoding: request b with n = clamp(accept_len[b], 0, k) >= 1 gets
 // intermediate state b*k + n - 1 copied into its slot (b without a slot table), for the SSM
 // state (state_bytes per request) and the conv state (conv_bytes); NULL pointers skip one.
@@ -94,6 +103,7 @@ hipError_t launch_state_update(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t 
 // speculative decode: k tokens per request from a read-only state, then the accept copy
 hipError_t launch_state_update_multi(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s);
+hipError_t launch_state_update_lp(const LpUpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);

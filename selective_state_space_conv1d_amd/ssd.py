@@ -22,7 +22,7 @@ STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_DTYPE", "SSD_ERR_A
 EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
-           "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states"]
+           "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp"]
 
 
 class SsdDims(ctypes.Structure):
@@ -48,6 +48,11 @@ _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _PD = ctypes.POINTER(SsdDims)
+
+
+class SsdSrParams(ctypes.Structure):
+    """Stochastic rounding of a 16-bit state: Philox key, counter offset and rounds."""
+    _fields_ = [("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64), ("rounds", ctypes.c_int32)]
 
 
 def _lib():
@@ -77,10 +82,12 @@ def _lib():
                                                _PDT, _VP, _VP, _VP]
         lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
         lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_state_update_lp.argtypes = [_PD, _VP, _I32, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
+                                            _PDT, ctypes.POINTER(SsdSrParams), _VP, _VP]
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
-                  "ssd_accept_states"):
+                  "ssd_accept_states", "ssd_state_update_lp"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -508,6 +515,44 @@ def ssd_accept_states(accept_len, state=None, inter_states=None, conv_state=None
                                     _ptr(_table(slot_idx, Bt, "slot_idx")), nslots, _ptr(state),
                                     _ptr(inter_states), _ptr(conv_state), _ptr(inter_conv_states),
                                     _stream(stream)), "ssd_accept_states")
+
+
+# --------------------------------------------------------------------------- 16-bit state
+SSD_F16 = 2
+_STATE_DT = {torch.float16: SSD_F16, torch.bfloat16: SSD_BF16}
+
+
+def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y=None, y_dtype=None, stream=None,
+                        dt_bias=None, dt_softplus=False, dt_limit=None):
+    """One decode token on a 16-bit state [B or nslots, H, P, N] (float16 or bfloat16, updated in
+    place; with slot_idx [B] int32 it is a pool).  The update runs in fp32 and is rounded back to
+    nearest even, or stochastically with sr = (seed, offset, rounds) (Philox4x32; use a new offset
+    per call).  x [B, H, P], B/C [B, G, N] (16-byte aligned rows), dt [B, H].  Returns y [B, H, P]."""
+    if state.dtype not in _STATE_DT or state.dim() != 4 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float16 or bfloat16 [B or nslots, H, P, N] tensor")
+    _, H, P, N = state.shape
+    Bt = x.shape[0]
+    G = B.shape[1]
+    if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
+        raise ValueError("x must be [B, H, P] with packed (H, P)")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, G, N) or t.stride(2) != 1 or t.stride(1) != N:
+            raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
+    if B.stride(0) != C.stride(0):
+        raise ValueError("B and C must share a batch stride")
+    if dt.shape != (Bt, H) or not dt.is_contiguous():
+        raise ValueError("dt [B, H] must be contiguous")
+    st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
+    srp = None if sr is None else ctypes.byref(SsdSrParams(int(sr[0]), int(sr[1]), int(sr[2])))
+    _check(_lib().ssd_state_update_lp(ctypes.byref(d), _ptr(st), _STATE_DT[state.dtype], _ptr(tab), nslots,
+                                      _ptr(x), x.stride(0), _ptr(B), _ptr(C), B.stride(0), _ptr(dt), _ptr(A),
+                                      _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), srp, _ptr(y),
+                                      _stream(stream)), "ssd_state_update_lp")
+    return y
 
 
 def split_xbc(v, nheads, head_dim, ngroups, d_state):

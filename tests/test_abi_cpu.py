@@ -230,6 +230,27 @@ def test_multi_token_and_accept_validation(ssd, lib):
     assert acc(slot=fp(8), nslots=0, alen=None) == E["SSD_OK"]
 
 
+def test_lowprec_state_validation(ssd, lib):
+    """The 16-bit state update rejects bad host arguments before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=1)
+
+    def upd(dd=d, state=fp(1), sdt=2, slot=None, nslots=0, B=fp(3), bcs=256, sr=None, y=fp(7)):
+        return lib.ssd_state_update_lp(ctypes.byref(dd), state, sdt, slot, nslots, fp(2), 256, B, fp(4), bcs, fp(5),
+                                       fp(6), None, None, sr, y, None)
+    assert upd(sdt=0) == E["SSD_ERR_DTYPE"]                 # fp32 is not a 16-bit state
+    assert upd(sdt=7) == E["SSD_ERR_DTYPE"]
+    assert upd(state=None) == E["SSD_ERR_NULL"]
+    assert upd(y=None) == E["SSD_ERR_NULL"]
+    assert upd(nslots=-1) == E["SSD_ERR_SHAPE"]
+    assert upd(state=ctypes.c_void_p(P0 + 2)) == E["SSD_ERR_ALIGN"]
+    assert upd(B=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert upd(bcs=260) == E["SSD_ERR_ALIGN"]
+    assert upd(sr=ctypes.byref(ssd.SsdSrParams(1, 2, 0))) == E["SSD_ERR_UNSUPPORTED"]
+    assert upd(sr=ctypes.byref(ssd.SsdSrParams(1, 2, 17))) == E["SSD_ERR_UNSUPPORTED"]
+    assert upd(dims(ssd, batch=2, seqlen=1, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")

@@ -1,0 +1,150 @@
+"""Parity of the 16-bit-state decode update (fp16/bf16 storage, stochastic or nearest-even
+rounding) with the oracle, on the GPU.
+
+* With A = 0 for every head the fp32 value each element is rounded from is reproducible exactly
+  (oracle.state_update_lp_codes_a0), so the stored codes -- the Philox stream and the rounding
+  decision included -- must match the oracle bit for bit.
+* With general A the stored state must be within one spacing of the format (half a spacing when
+  rounding to nearest) of the fp64 update, and y within the fp32 bar.
+* Over many Philox offsets the mean stored value approaches the fp32 value (unbiased rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import F32_BAR, assert_close, f64
+from oracle import lowprec as lp
+from selective_state_space_conv1d_amd import ssd
+from selective_state_space_conv1d_amd.synth import WORKLOADS, LayerDims, scan_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMT = {torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+def codes_of(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def lp_inputs(d, seed, nstate, sdt):
+    s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, seed, seqlen=1).items()}
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    state = (torch.randn(nstate, d.nheads, d.head_dim, d.d_state, generator=g) * 0.1).to(sdt).to(DEV)
+    args = (s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], s["dt"][:, 0].contiguous())
+    return state, args, s["A"], s["D"]
+
+
+def spacing_of(v, fmt):
+    """Spacing of the format's codes at |v| (fp64 arrays)."""
+    av = np.abs(v)
+    if fmt == "f16":
+        e = np.floor(np.log2(np.maximum(av, 2.0 ** -14)))
+        return 2.0 ** (e - 10)
+    e = np.floor(np.log2(np.maximum(av, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("sdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("sr", [None, (0x1234ABCD5678, 3, 5), (7, 2 ** 40 + 9, 10)])
+@pytest.mark.parametrize("use_slots", [False, True])
+def test_lp_codes_bitwise_when_a_is_zero(orc, sdt, sr, use_slots):
+    d = LayerDims(5, 1, 8, 64, 2, 128)
+    nstate = 9 if use_slots else 5
+    state0, args, A, D = lp_inputs(d, 500, nstate, sdt)
+    A0 = torch.zeros_like(A)
+    slots = [8, 0, -1, 4, 2] if use_slots else None
+    slot = None if slots is None else torch.tensor(slots, dtype=torch.int32, device=DEV)
+    state = state0.clone()
+    y = ssd.ssd_state_update_lp(state, *args, A0, D, slot_idx=slot, sr=sr, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    fmt = FMT[sdt]
+    want = orc.state_update_lp_codes_a0(codes_of(state0), fmt, None if slots is None else np.array(slots),
+                                        *(f64(t) for t in args), sr)
+    got = codes_of(state)
+    assert np.array_equal(got, want), f"{(got != want).sum()} codes differ"
+    yr, _ = orc.state_update_lp(codes_of(state0), fmt, None if slots is None else np.array(slots),
+                                *(f64(t) for t in args), f64(A0), f64(D))
+    assert_close(y, yr, F32_BAR, "y")
+
+
+@pytest.mark.parametrize("sdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("sr", [None, (99, 1, 5)])
+@pytest.mark.parametrize("P,N,act", [(64, 128, torch.bfloat16), (16, 32, torch.float32)])
+def test_lp_state_within_one_spacing(orc, sdt, sr, P, N, act):
+    d = LayerDims(4, 1, 8, P, 2, N, dtype=act)
+    state0, args, A, D = lp_inputs(d, 510, 4, sdt)
+    state = state0.clone()
+    y = ssd.ssd_state_update_lp(state, *args, A, D, sr=sr, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    fmt = FMT[sdt]
+    x, Bm, Cm, dt = (f64(t) for t in args)
+    yr, exact = orc.state_update_lp(codes_of(state0), fmt, None, x, Bm, Cm, dt, f64(A), f64(D))
+    assert_close(y, yr, F32_BAR, "y")
+    got = lp.decode(codes_of(state), fmt)
+    # fp32 evaluation error of a*s + (dt*x)*b, bounded by a few ulps of its two terms
+    s0 = lp.decode(codes_of(state0), fmt)
+    hpg = d.nheads // d.ngroups
+    Bh = np.repeat(Bm, hpg, axis=1)
+    scale = np.abs(np.exp(dt * f64(A))[:, :, None, None] * s0) + np.abs((dt[:, :, None] * x)[..., None] * Bh[:, :, None, :])
+    bound = spacing_of(exact, fmt) * (0.5 if sr is None else 1.0) + 4 * 2.0 ** -24 * scale + 1e-30
+    bad = np.abs(got - exact) > bound
+    assert not bad.any(), f"{bad.sum()} elements outside one spacing"
+
+
+def test_lp_stochastic_rounding_is_unbiased_on_gpu():
+    d = LayerDims(2, 1, 4, 16, 1, 32, dtype=torch.float32)
+    sdt = torch.float16
+    state0, args, A, D = lp_inputs(d, 520, 2, sdt)
+    A0 = torch.zeros_like(A)
+    n = 256
+    acc = torch.zeros(state0.shape, dtype=torch.float64, device=DEV)
+    for off in range(n):
+        st = state0.clone()
+        ssd.ssd_state_update_lp(st, *args, A0, D, sr=(11, off, 5))
+        acc += st.double()
+    torch.cuda.synchronize()
+    # the fp32 values being rounded (A = 0: s + (dt*x)*B, each step rounded to fp32)
+    x, Bm, Cm, dt = (t.float().cpu() for t in args)
+    dx = dt[:, :, None] * x                                             # [B, H, P], one group
+    v32 = (state0.float().cpu() + (dx[..., None] * Bm[:, 0][:, None, None, :]).float()).double().numpy()
+    mean = (acc / n).cpu().numpy()
+    sp = spacing_of(v32, "f16")
+    z = (mean - v32) / sp
+    assert np.abs(z).max() < 0.25, np.abs(z).max()                      # 8 sigma of a 256-sample mean
+    assert abs(z.mean()) < 0.02
+
+
+def test_lp_full_size_pool(orc):
+    """Batch 64 of the Ultra decode layer on a 96-slot fp16 pool with stochastic rounding: the
+    A = 0 form bitwise on two requests, the general form within one spacing on one head per
+    group of one request."""
+    d = WORKLOADS["decode_ultra_b64"]
+    state0, args, A, D = lp_inputs(d, 530, 96, torch.float16)
+    g = torch.Generator(device="cpu").manual_seed(531)
+    slot = torch.randperm(96, generator=g)[:64].to(torch.int32).to(DEV)
+    sr = (2024, 17, 5)
+    st = state0.clone()
+    ssd.ssd_state_update_lp(st, *args, torch.zeros_like(A), D, slot_idx=slot, sr=sr)
+    torch.cuda.synchronize()
+    for b in (3, 60):
+        sl = int(slot[b])
+        # the values rounded (A = 0) and the random stream of slot sl's elements in the pool
+        x, Bm, Cm, dt = (np.asarray(f64(t[b:b + 1]), np.float32) for t in args)
+        vals = lp.decode(codes_of(state0[sl]), "f16").astype(np.float32)
+        Bh = np.repeat(Bm[0], d.nheads // d.ngroups, axis=0)
+        v = (vals + ((dt[0][:, None] * x[0]).astype(np.float32)[:, :, None] * Bh[:, None, :]).astype(np.float32))
+        e = sl * vals.size + np.arange(vals.size, dtype=np.int64).reshape(vals.shape)
+        want = lp.round_state(v.astype(np.float32), "f16", lp.random16(e, *sr))
+        assert np.array_equal(codes_of(st[sl]), want), b
+    st = state0.clone()
+    y = ssd.ssd_state_update_lp(st, *args, A, D, slot_idx=slot, sr=sr, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    b = 21
+    sl = int(slot[b])
+    heads = [gi * (d.nheads // d.ngroups) for gi in range(d.ngroups)]
+    x, Bm, Cm, dt = (f64(t[b:b + 1]) for t in args)
+    yr, exact = orc.state_update_lp(codes_of(state0[sl:sl + 1, heads]), "f16", None, x[:, heads], Bm, Cm,
+                                    dt[:, heads], f64(A)[heads], f64(D)[heads])
+    assert_close(y[b:b + 1, heads], yr, F32_BAR, "y sampled heads")
+    got = lp.decode(codes_of(st[sl, heads]), "f16")
+    assert np.all(np.abs(got - exact[0]) <= spacing_of(exact[0], "f16") + 1e-6 * np.abs(exact[0]) + 1e-30)
