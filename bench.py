@@ -229,6 +229,44 @@ def spec_leg(ssd, torch, dev, steps, warmup, k=4):
             "accept_frac": acc_b / acc_s / 1e9 / HBM_PEAK_GBS}
 
 
+def lowprec_leg(ssd, torch, dev, steps, warmup):
+    """The decode update of batch 64 on a 16-bit state: fp16 with Philox stochastic rounding
+    (5 rounds), fp16 rounded to nearest, bf16 with stochastic rounding.  Each launch bracketed by
+    HIP events; a new Philox offset per step."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, scan_inputs
+    dd = WORKLOADS["decode_ultra_b64"]
+    B, H, P, N = dd.batch, dd.nheads, dd.head_dim, dd.d_state
+    s = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(dd, 1030, seqlen=1).items()}
+    args = (s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], s["dt"][:, 0].contiguous(), s["A"], s["D"])
+    y = torch.empty(B, H, P, dtype=dd.dtype, device=dev)
+    io = B * (H * P * 2 + 2 * dd.ngroups * N + H + H * P) * 2
+    alg = B * H * P * N * 2 * 2 + io
+    out = {"batch": B, "state_bytes_per_request": H * P * N * 2, "algorithmic_bytes": alg}
+    for name, sdt, rounds in (("f16_sr5", torch.float16, 5), ("f16_rne", torch.float16, 0),
+                              ("bf16_sr5", torch.bfloat16, 5)):
+        st = (s["init_state"]).to(sdt)
+        step = [0]
+
+        def one():
+            sr = (2024, step[0], rounds) if rounds else None
+            step[0] += 1
+            ssd.ssd_state_update_lp(st, *args, sr=sr, y=y)
+
+        for _ in range(warmup):
+            one()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+        for i in range(steps):
+            ev[2 * i].record()
+            one()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        t = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps * 1e-3
+        out[name] = {"us": t * 1e6, "GBps": alg / t / 1e9, "frac": alg / t / 1e9 / HBM_PEAK_GBS,
+                     "tokens_per_s": B / t}
+        del st
+    return out
+
+
 def cpu_baseline(orc, inp, d, n_heads=256):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
     over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
@@ -410,6 +448,8 @@ def main():
     out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
     print("[bench] speculative decode (k-token updates, accept)", file=sys.stderr, flush=True)
     out["spec_decode"] = spec_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
+    print("[bench] 16-bit state decode (stochastic rounding)", file=sys.stderr, flush=True)
+    out["lowprec_decode"] = lowprec_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

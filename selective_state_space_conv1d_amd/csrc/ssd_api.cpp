@@ -343,6 +343,7 @@ ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state
     const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
     const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
     if (x_row_stride < I || bc_row_stride < GN) return SSD_ERR_SHAPE;
+    if (I * d->d_state >= (INT64_C(1) << 31)) return SSD_ERR_UNSUPPORTED;   // one state's offsets in 32 bits
     if (!stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;   // B/C are read 8 elements at a time
     for (const void* p : {static_cast<const void*>(state), B, C})
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;

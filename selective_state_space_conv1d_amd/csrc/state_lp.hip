@@ -48,10 +48,12 @@ struct Bf16Fmt {
     }
     // bf16 keeps fp32's exponent: the 16 dropped bits are the distance past the truncated code
     // in units of 2^-16 spacing, and the truncated code + 1 is the next code away from zero.
+    // Written with selects only: a branch per element would split the wave.
+    template <bool SUB = true>
     static __device__ __forceinline__ uint32_t sr(float v, uint32_t r16) {
         const uint32_t u = __float_as_uint(v);
-        if ((u & 0x7F800000u) == 0x7F800000u) return rne(v);
-        return (u >> 16) + (r16 < (u & 0xFFFFu) ? 1u : 0u);
+        const uint32_t t = (u >> 16) + (r16 < (u & 0xFFFFu) ? 1u : 0u);
+        return (u & 0x7F800000u) == 0x7F800000u ? rne(v) : t;
     }
 };
 
@@ -62,33 +64,27 @@ struct F16Fmt {
     static __device__ __forceinline__ uint32_t rne(float v) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
     }
+    // Selects only, as for bf16.  SUB: some value of the wave is in fp16's subnormal range (the
+    // caller tests that once per octet for the whole wave; the normal-range path alone is cheaper).
+    template <bool SUB = true>
     static __device__ __forceinline__ uint32_t sr(float v, uint32_t r16) {
         const uint32_t u = __float_as_uint(v);
         const uint32_t a = u & 0x7FFFFFFFu;
-        if (a >= 0x7F800000u) return rne(v);                  // inf, NaN
-        const uint32_t sgn = (u >> 16) & 0x8000u;
-        if (a >= 0x47800000u) return sgn | 0x7C00u;            // |v| >= 65536: infinity
-        const int e = a >= 0x00800000u ? static_cast<int>(a >> 23) - 127 : -126;
-        uint32_t code, up;
-        if (e >= -14) {
-            // fp16 normal range: the code keeps the top 10 mantissa bits, 13 are dropped
-            code = (static_cast<uint32_t>(e + 15) << 10) | ((a >> 13) & 0x3FFu);
-            up = r16 < ((a & 0x1FFFu) << 3) ? 1u : 0u;
-        } else {
-            // fp16 subnormals: |v| = m * 2^(e - 23) is (m >> s) units of 2^-24 plus m mod 2^s
-            // over 2^s of one, s = -(e + 1) >= 14
-            const uint32_t m = (a & 0x7FFFFFu) | (a >= 0x00800000u ? 0x800000u : 0u);
-            const int s = -(e + 1);
-            if (s >= 40) {                                     // m * 2^16 < 2^s: only r16 = 0 rounds up
-                code = 0;
-                up = (r16 == 0 && m != 0) ? 1u : 0u;
-            } else {
-                code = s >= 32 ? 0u : m >> s;
-                const uint64_t d = static_cast<uint64_t>(m) & ((1ull << s) - 1);
-                up = (static_cast<uint64_t>(r16) << s) < (d << 16) ? 1u : 0u;
-            }
+        // fp16 normal range (|v| >= 2^-14): the code is fp32's top 10 mantissa bits under the
+        // exponent rebiased from 127 to 15; 13 bits are dropped, so frac * 65536 = dropped << 3
+        const uint32_t cn = (a >> 13) - (112u << 10) + (r16 < ((a & 0x1FFFu) << 3) ? 1u : 0u);
+        // fp16 subnormals: q = |v| * 2^24 counts units of 2^-24 and is exact in fp32, as are its
+        // integer part (the code), its fraction and the fraction * 65536
+        uint32_t c = cn;   // +1 carries into the exponent, past 65504 into infinity
+        if constexpr (SUB) {
+            const float q = __uint_as_float(a < 0x38800000u ? a : 0u) * 16777216.0f;   // < 1024 (0 outside)
+            const uint32_t ci = static_cast<uint32_t>(q);
+            const uint32_t cs = ci + (static_cast<float>(r16) < (q - static_cast<float>(ci)) * 65536.0f ? 1u : 0u);
+            c = a < 0x38800000u ? cs : cn;
         }
-        return sgn | (code + up);   // + 1 carries into the exponent, and past 65504 into infinity
+        c = a >= 0x47800000u ? 0x7C00u : c;       // |v| >= 65536: infinity
+        const uint32_t r = ((u >> 16) & 0x8000u) | c;
+        return a >= 0x7F800000u ? rne(v) : r;     // inf, NaN
     }
 };
 
@@ -118,29 +114,32 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     const bool uni = ub == fl / per_b;
     const int64_t uslot = uni ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
 
+    // per octet: batch entry, offset inside its state (< 2^31: the ABI bounds H*P*N), octet index
+    // in the state array (-1: padding)
     u32x4 raw[kLpPerThread];
-    int64_t so[kLpPerThread];   // octet index in the state array, -1: padding
+    int64_t bb[kLpPerThread], so[kLpPerThread];
+    uint32_t rem[kLpPerThread];
 #pragma unroll
     for (int i = 0; i < kLpPerThread; ++i) {
         const int64_t f = base + i * kLpThreads;
         const int64_t ff = f < total8 ? f : 0;
-        const int64_t b = uni ? ub : ff / per_b;
-        const int64_t slot = uni ? uslot : (slot_idx ? seq_slot(slot_idx, b, nslots) : b);
-        so[i] = (f < total8 && slot >= 0) ? slot * per_b + (ff - b * per_b) : -1;
+        bb[i] = uni ? ub : ff / per_b;
+        rem[i] = static_cast<uint32_t>(ff - bb[i] * per_b);
+        const int64_t slot = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
+        so[i] = (f < total8 && slot >= 0) ? slot * per_b + rem[i] : -1;
         raw[i] = so[i] >= 0 ? __builtin_nontemporal_load(st + so[i]) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < kLpPerThread; ++i) {
-        const int64_t f = base + i * kLpThreads;
-        const bool ok = f < total8;
-        const int64_t ff = ok ? f : 0;
-        const int64_t row = ff / OPR;  // (b, h, p)
-        const int q = static_cast<int>(ff - row * OPR);
-        const int64_t bh = row / P;
-        const int p = static_cast<int>(row - bh * P);
-        const int64_t b = bh / H;
-        const int h = static_cast<int>(bh - b * H);
+        const bool ok = base + i * kLpThreads < total8;
+        const int64_t b = bb[i];
+        const uint32_t rin = rem[i] / OPR;  // h*P + p inside the batch entry
+        const int q = static_cast<int>(rem[i] % OPR);
+        const int h = static_cast<int>(rin / static_cast<uint32_t>(P));
+        const int p = static_cast<int>(rin) - h * P;
         const int g = h / hpg;
+        const int64_t bh = b * H + h;
+        const int64_t row = bh * P + p;
         const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
         const float a = __expf(dtv * A[h]);
         const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
@@ -167,9 +166,21 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
                 uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
                                  static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
                 philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
+                // values below 2^-14 (fp16's subnormal range) anywhere in the wave?
+                bool sub = false;
 #pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    rw[w] = F::sr(v[2 * w], c[w] & 0xFFFFu) | (F::sr(v[2 * w + 1], c[w] >> 16) << 16);
+                for (int e = 0; e < 8; ++e) sub |= (__float_as_uint(v[e]) & 0x7FFFFFFFu) < 0x38800000u;
+                if (__builtin_amdgcn_ballot_w64(sub)) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        rw[w] = F::template sr<true>(v[2 * w], c[w] & 0xFFFFu) |
+                                (F::template sr<true>(v[2 * w + 1], c[w] >> 16) << 16);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        rw[w] = F::template sr<false>(v[2 * w], c[w] & 0xFFFFu) |
+                                (F::template sr<false>(v[2 * w + 1], c[w] >> 16) << 16);
+                }
             } else {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
