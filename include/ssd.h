@@ -9,6 +9,7 @@
  *   ssd_chunk_scan     the SSD chunked scan of a prefill: y and the fp32 final
  *                      state from x, dt, A, B, C, D and an optional initial state
  *   ssd_state_update   the single-token selective state update (decode)
+ *   (ssd_chunk_scan_snapshots: the scan, also storing the state every N tokens)
  * and their serving forms on packed variable-length batches and state pools:
  *   ssd_conv1d_fwd_varlen, ssd_chunk_scan_varlen, ssd_conv1d_update_slots,
  *   ssd_state_update_slots
@@ -161,6 +162,24 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
                             const ssd_dt_params_t* dt_params,
                             const float* init_state, float* final_state, void* y,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_chunk_scan that also stores the state every `interval` tokens ([P2] 部署时如何调这些缓存:
+ * one engine's setting writes an SSM state snapshot every N tokens, for prefix caching).
+ *  snapshots  [B, L / interval, H, P, N] fp32, 16-byte aligned: entry k is the state after token
+ *             (k + 1) * interval - 1 of each batch entry (the same values the final state would
+ *             have if the sequence ended there).  May be NULL when L < interval.
+ *  interval   a positive multiple of 128.
+ * The rest is as for ssd_chunk_scan.
+ */
+ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk,
+                                      const void* x, int64_t x_row_stride,
+                                      const void* B, const void* C, int64_t bc_row_stride,
+                                      const void* dt, const float* A, const float* D,
+                                      const ssd_dt_params_t* dt_params,
+                                      const float* init_state, float* final_state, float* snapshots,
+                                      int64_t interval, void* y, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * Single-token selective state update, in place ([P2] "Decode 阶段"; [P1]

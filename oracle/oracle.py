@@ -99,6 +99,23 @@ class Oracle:
                                      _ptr(dt), _ptr(A), _ptr(D), _ptr(y))
         return y, st
 
+    # The state after every `interval` tokens: the scan run segment by segment, each segment
+    # starting from the previous one's final state.  -> y, final state, snapshots [B, L // interval, H, P, N]
+    def scan_snapshots(self, x, Bm, Cm, dt, A, D=None, init=None, interval=128):
+        x, Bm, Cm, dt = map(_f64, (x, Bm, Cm, dt))
+        Bt, L, H, P = x.shape
+        N = Bm.shape[3]
+        st = np.zeros((Bt, H, P, N)) if init is None else _f64(init)
+        ys, snaps = [], []
+        for a in range(0, L, interval):
+            b = min(a + interval, L)
+            yk, st = self.scan(x[:, a:b], Bm[:, a:b], Cm[:, a:b], dt[:, a:b], A, D, st)
+            ys.append(yk)
+            if b - a == interval:
+                snaps.append(st)
+        snaps = np.stack(snaps, 1) if snaps else np.zeros((Bt, 0, H, P, N))
+        return (np.concatenate(ys, 1) if ys else np.zeros((Bt, 0, H, P))), st, snaps
+
     # dt prologue (fp64), applied to dt [..., H] before the routines above: v = dt + bias[h];
     # softplus v = log(1 + e^v); clamp to [lo, hi] when lo < hi.
     @staticmethod

@@ -561,6 +561,22 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 Hs[t] = mfma32(bt, wl, Hs[t]);
             }
         }
+        // state snapshot after token (c + 1) * Q - 1 when that closes an interval
+        if (a.snapshots) {
+            const int64_t t_end = (c + 1) * Q;
+            if (t_end % a.snap_interval == 0 && t_end <= cx.L) {
+                const int64_t nsnap = cx.L / a.snap_interval, k = t_end / a.snap_interval - 1;
+                float* snap = a.snapshots + ((cx.b * nsnap + k) * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
+                        *reinterpret_cast<f32x4*>(snap + hp * NS + n) =
+                            f32x4{Hs[t][4 * j], Hs[t][4 * j + 1], Hs[t][4 * j + 2], Hs[t][4 * j + 3]};
+                    }
+            }
+        }
         // the y waves must have read the previous state before it is overwritten
         const int target = 4 * static_cast<int>(c + 1);
         for (int n = 0; n < kSpinMax; ++n) {

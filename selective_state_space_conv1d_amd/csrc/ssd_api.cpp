@@ -148,12 +148,12 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
     return 0;
 }
 
-ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
-                            const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                            const float* A, const float* D, const ssd_dt_params_t* dt_params,
-                            const float* init_state,
-                            float* final_state, void* y, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+// the batched scan, with optional state snapshots (internal linkage)
+static ssd_status_t chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                               const void* B, const void* C, int64_t bc_row_stride, const void* dt, const float* A,
+                               const float* D, const ssd_dt_params_t* dt_params, const float* init_state,
+                               float* final_state, float* snapshots, int64_t interval, void* y, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
     ssd_status_t st = check_dims(d, true);
     if (st != SSD_OK) return st;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
@@ -172,11 +172,35 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
     if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, init_state, final_state, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
-                    {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params)};
+                    {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params), snapshots, interval};
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
     return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
+}
+
+ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                            const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                            const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                            const float* init_state,
+                            float* final_state, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return chunk_scan(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, init_state, final_state,
+                      nullptr, 0, y, workspace, workspace_bytes, stream);
+}
+
+ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                      const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                      const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                      const float* init_state, float* final_state, float* snapshots,
+                                      int64_t interval, void* y, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    if (!d) return SSD_ERR_NULL;
+    if (interval <= 0 || interval % 128 != 0) return SSD_ERR_UNSUPPORTED;
+    if (d->batch > 0 && d->seqlen >= interval && !snapshots) return SSD_ERR_NULL;
+    if (snapshots && !aligned16(snapshots)) return SSD_ERR_ALIGN;
+    return chunk_scan(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, init_state, final_state,
+                      snapshots, interval, y, workspace, workspace_bytes, stream);
 }
 
 ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,

@@ -57,6 +57,8 @@ struct ScanArgs {
     int nheads, head_dim, ngroups, d_state, chunk;
     SeqMap seq;   // varlen: init_state / final_state are the state pool
     DtParams dtp;
+    float* snapshots;        // [B, L / snap_interval, H, P, N]: state after every snap_interval tokens, or NULL
+    int64_t snap_interval;   // a positive multiple of 128 when snapshots is set
 };
 
 struct UpdateArgs {

@@ -22,7 +22,8 @@ STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_DTYPE", "SSD_ERR_A
 EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
-           "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp"]
+           "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
+           "ssd_chunk_scan_snapshots"]
 
 
 class SsdDims(ctypes.Structure):
@@ -82,12 +83,14 @@ def _lib():
                                                _PDT, _VP, _VP, _VP]
         lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
         lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_chunk_scan_snapshots.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
+                                                 _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_lp.argtypes = [_PD, _VP, _I32, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
                                             _PDT, ctypes.POINTER(SsdSrParams), _VP, _VP]
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
-                  "ssd_accept_states", "ssd_state_update_lp"):
+                  "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -197,7 +200,8 @@ def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, head_dim, ngroups, d_st
 
 
 def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=None, chunk=128,
-                   y_dtype=None, workspace=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
+                   y_dtype=None, workspace=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None,
+                   snapshots=None, snapshot_interval=None):
     """SSD chunked scan.  x [B, L, H, P], B/C [B, L, G, N] (token rows may be strided, e.g.
     views into the conv output), dt [B, L, H], A [H] fp32, D [H] fp32|None,
     init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).  Optional dt prologue:
@@ -222,10 +226,21 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))
     if L == 0:
         x = B = C = dt = None
-    _check(_lib().ssd_chunk_scan(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
-                                 _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
-                                 _ptr(init_state), _ptr(final_state), _ptr(y),
-                                 _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
+    if snapshot_interval is None:
+        _check(_lib().ssd_chunk_scan(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
+                                     _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                     _ptr(init_state), _ptr(final_state), _ptr(y),
+                                     _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
+        return y
+    # state every snapshot_interval tokens into snapshots [B, L // interval, H, P, N] fp32
+    if snapshots is None or snapshots.shape != (Bt, L // snapshot_interval, H, P, N) or \
+            snapshots.dtype != torch.float32 or not snapshots.is_contiguous():
+        raise ValueError("snapshots must be contiguous fp32 [B, L // snapshot_interval, H, P, N]")
+    _check(_lib().ssd_chunk_scan_snapshots(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
+                                           _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                           _ptr(init_state), _ptr(final_state), _ptr(snapshots),
+                                           int(snapshot_interval), _ptr(y), _ptr(workspace), ws, _stream(stream)),
+           "ssd_chunk_scan_snapshots")
     return y
 
 

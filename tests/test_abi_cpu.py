@@ -251,6 +251,23 @@ def test_lowprec_state_validation(ssd, lib):
     assert upd(dims(ssd, batch=2, seqlen=1, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
 
 
+def test_snapshot_scan_validation(ssd, lib):
+    """The snapshot form of the scan rejects a bad interval or a missing buffer before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=300)
+
+    def snap(dd=d, buf=fp(9), iv=128, x=fp(1)):
+        return lib.ssd_chunk_scan_snapshots(ctypes.byref(dd), 128, x, 256, fp(2), fp(3), 256, fp(4), fp(5), None,
+                                            None, None, None, buf, iv, fp(6), None, 0, None)
+    assert snap(iv=0) == E["SSD_ERR_UNSUPPORTED"]
+    assert snap(iv=100) == E["SSD_ERR_UNSUPPORTED"]
+    assert snap(buf=None) == E["SSD_ERR_NULL"]
+    assert snap(buf=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert snap(x=None) == E["SSD_ERR_NULL"]                    # the scan's own checks still apply
+    assert lib.ssd_chunk_scan_snapshots(None, 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None, None, None,
+                                        None, fp(9), 128, fp(6), None, 0, None) == E["SSD_ERR_NULL"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import F32_BAR, assert_bf16_elementwise, assert_close, f64
+from gpu_util import BF16_BAR, F32_BAR, assert_bf16_elementwise, assert_close, f64
 from selective_state_space_conv1d_amd import ssd
 from selective_state_space_conv1d_amd.synth import WORKLOADS, LayerDims, scan_inputs
 
@@ -203,3 +203,27 @@ def test_full_size_speculative_step_sampled(orc):
                                     sub(s["Cm"]), sub(s["dt"])[:, :, heads], f64(s["A"])[heads], f64(s["D"])[heads])
     assert_close(y[b:b + 1, :, heads], yr, F32_BAR, "y sampled heads")
     assert_close(inter[b:b + 1, :, heads], ir, F32_BAR, "intermediate states sampled heads")
+
+
+# --------------------------------------------------------------------------- state snapshots
+@pytest.mark.parametrize("P,N,dtype,L,iv", [(64, 128, torch.bfloat16, 700, 128), (64, 128, torch.bfloat16, 1024, 256),
+                                            (16, 32, torch.float32, 300, 128), (16, 32, torch.float32, 256, 128)])
+def test_scan_snapshots(orc, P, N, dtype, L, iv):
+    d = LayerDims(2, L, 4, P, 2, N, dtype=dtype)
+    s = {n: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for n, v in scan_inputs(d, 470).items()}
+    fin = torch.empty_like(s["init_state"])
+    snaps = torch.full((2, L // iv, 4, P, N), float("nan"), device=DEV)
+    y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], s["init_state"], fin,
+                           y_dtype=torch.float32, snapshots=snaps, snapshot_interval=iv)
+    fin2 = torch.empty_like(fin)
+    y2 = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], s["init_state"], fin2,
+                            y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(fin, fin2), "snapshots must not change y or the final state"
+    if L % iv == 0:
+        assert torch.equal(snaps[:, -1], fin), "the last snapshot is the final state"
+    yr, fr, sr = orc.scan_snapshots(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), f64(s["dt"]), f64(s["A"]), f64(s["D"]),
+                                    f64(s["init_state"]), iv)
+    bar = BF16_BAR if dtype == torch.bfloat16 else F32_BAR
+    assert_close(y, yr, bar, "y")
+    assert_close(snaps, sr, bar, "snapshots")

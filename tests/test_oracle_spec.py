@@ -82,3 +82,27 @@ def test_single_candidate_is_the_plain_update(orc):
     y, inter = orc.state_update_multi(pool, None, x, Bm, Cm, dt, A, D)
     yr, sr = orc.state_update(pool, x[:, 0], Bm[:, 0], Cm[:, 0], dt[:, 0], A, D)
     assert np.array_equal(y[:, 0], yr) and np.array_equal(inter[:, 0], sr)
+
+
+def test_scan_snapshots_are_the_prefix_states(orc):
+    """State snapshots every `interval` tokens ("modeling_nemotron_h.py" walk-through page,
+    部署时如何调这些缓存: a state snapshot every N tokens): snapshot k equals the brute-force final
+    state of tokens [0, (k + 1) * interval), and the segmented scan's y and final state equal the
+    one-pass scan's."""
+    r = np.random.default_rng(15)
+    Bt, L, H, P, G, N, iv = 2, 23, 4, 3, 2, 5, 5
+    x = r.standard_normal((Bt, L, H, P))
+    Bm = r.standard_normal((Bt, L, G, N))
+    Cm = r.standard_normal((Bt, L, G, N))
+    dt = softplus(r.normal(-2.0, 1.0, (Bt, L, H)))
+    A = -np.exp(r.uniform(0, 1, H))
+    D = r.standard_normal(H)
+    S0 = r.standard_normal((Bt, H, P, N))
+    y, fin, snaps = orc.scan_snapshots(x, Bm, Cm, dt, A, D, S0, iv)
+    assert snaps.shape == (Bt, L // iv, H, P, N)
+    for k in range(L // iv):
+        e = (k + 1) * iv
+        _, fr = semiseparable_scan(x[:, :e], Bm[:, :e], Cm[:, :e], dt[:, :e], A, D, S0)
+        assert rel_err(snaps[:, k], fr) < 1e-12, k
+    yr, fr = orc.scan(x, Bm, Cm, dt, A, D, S0)
+    assert rel_err(y, yr) < 1e-12 and rel_err(fin, fr) < 1e-12
