@@ -116,6 +116,18 @@ class Oracle:
         snaps = np.stack(snaps, 1) if snaps else np.zeros((Bt, 0, H, P, N))
         return (np.concatenate(ys, 1) if ys else np.zeros((Bt, 0, H, P))), st, snaps
 
+    # Gated group RMSNorm after the scan, gate applied before the norm ("MAX 平台 Nemotron-H 混合架构解析",
+    # 5.4, item 4: silu gate in fp32, RMS norm over each group of channels, fp32 weight):
+    # v = y * silu(z); out = v / sqrt(mean over the group of v^2 + eps) * w.
+    # y, z [..., I] with I = ngroups * group size, w [I] -> out [..., I] (fp64)
+    @staticmethod
+    def gated_rmsnorm(y, z, w, ngroups, eps):
+        y, z, w = (np.asarray(t, dtype=np.float64) for t in (y, z, w))
+        v = y * (z / (1.0 + np.exp(-z)))
+        g = v.reshape(v.shape[:-1] + (ngroups, -1))
+        r = 1.0 / np.sqrt((g * g).mean(-1, keepdims=True) + eps)
+        return (g * r).reshape(v.shape) * w
+
     # dt prologue (fp64), applied to dt [..., H] before the routines above: v = dt + bias[h];
     # softplus v = log(1 + e^v); clamp to [lo, hi] when lo < hi.
     @staticmethod
