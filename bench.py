@@ -267,6 +267,31 @@ def lowprec_leg(ssd, torch, dev, steps, warmup):
     return out
 
 
+def norm_leg(ssd, torch, dev, steps, warmup, y):
+    """The gated group RMSNorm on the prefill output y [1, 8192, 256, 64] (bf16), with a seeded bf16
+    gate z and fp32 weight; each launch bracketed by HIP events."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS
+    dp = WORKLOADS["prefill_ultra_8k"]
+    I = dp.nheads * dp.head_dim
+    g = torch.Generator(device="cpu").manual_seed(1040)
+    z = torch.randn(dp.seqlen, I, generator=g).to(dp.dtype).to(dev)
+    w = (torch.rand(I, generator=g) + 0.5).to(dev)
+    yv = y.view(dp.seqlen, I)
+    out = torch.empty(dp.seqlen, I, dtype=dp.dtype, device=dev)
+    for _ in range(warmup):
+        ssd.ssd_gated_rmsnorm(yv, z, w, dp.ngroups, out=out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        ssd.ssd_gated_rmsnorm(yv, z, w, dp.ngroups, out=out)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    t = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps * 1e-3
+    alg = dp.seqlen * I * 2 * 3 + I * 4
+    return {"rows": dp.seqlen, "channels": I, "groups": dp.ngroups, "us": t * 1e6, "GBps": alg / t / 1e9,
+            "frac": alg / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
+
+
 def cpu_baseline(orc, inp, d, n_heads=256):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
     over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
@@ -443,6 +468,8 @@ def main():
                                 "traffic_bytes_per_launch": measured_traffic("state_update")},
                    "conv_update_GBps": cub / avg["conv1d_update"] / 1e9},
     }
+    print("[bench] gated group RMSNorm on the prefill output", file=sys.stderr, flush=True)
+    out["gated_norm"] = norm_leg(ssd, torch, dev, max(5, args.steps // 2), 2, y)
     del v, x, Bm, Cm, y, state
     print("[bench] serving forms (packed prefill, slot-pool decode)", file=sys.stderr, flush=True)
     out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))

@@ -15,7 +15,8 @@
  *   ssd_state_update_slots
  * and multi-token (speculative) decode with the accept step:
  *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states
- * and the decode update on a 16-bit state with stochastic rounding: ssd_state_update_lp
+ * and the decode update on a 16-bit state with stochastic rounding: ssd_state_update_lp,
+ * and the gated group RMSNorm of the mixer output: ssd_gated_rmsnorm
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
@@ -374,6 +375,21 @@ ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state
                                  int64_t bc_row_stride, const void* dt, const float* A, const float* D,
                                  const ssd_dt_params_t* dt_params, const ssd_sr_params_t* sr, void* y,
                                  hipStream_t stream);
+
+/*
+ * Gated group RMSNorm of the mixer output ([P3] 5.4, item 4: one fused kernel; the gate is applied
+ * before the norm, in fp32, with an fp32 weight).  Per row and group g of gs = H*P/G channels:
+ *   v = y * silu(z);  out = v / sqrt(mean over the group of v^2 + eps) * weight.
+ *  d          rows = batch * seqlen; the channels are H*P in G groups (gs a multiple of 8).
+ *  y          [rows, H*P] y dtype, rows y_row_stride elements apart.
+ *  z          [rows, H*P] act dtype, rows z_row_stride elements apart (may be a view into the
+ *             in_proj output).
+ *  weight     [H*P] fp32.  eps >= 0.
+ *  out        [rows, H*P] contiguous act dtype; must not overlap y or z.
+ * Row strides keep rows 16-byte aligned; all pointers 16-byte aligned.
+ */
+ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* d, const void* y, int64_t y_row_stride, const void* z,
+                               int64_t z_row_stride, const float* weight, float eps, void* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

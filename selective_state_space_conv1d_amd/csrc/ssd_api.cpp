@@ -380,4 +380,22 @@ ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state
                                                   stream));
 }
 
+ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* d, const void* y, int64_t y_row_stride, const void* z,
+                               int64_t z_row_stride, const float* weight, float eps, void* out, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    const int64_t rows = d->batch * d->seqlen;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    if (rows > 0 && (!y || !z || !weight || !out)) return SSD_ERR_NULL;
+    if ((I / d->ngroups) % 8 != 0 || rows * d->ngroups >= (INT64_C(1) << 32)) return SSD_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f)) return SSD_ERR_SHAPE;
+    if (rows > 0 && (y_row_stride < I || z_row_stride < I)) return SSD_ERR_SHAPE;
+    if (!stride_ok(y_row_stride, d->y_dtype) || !stride_ok(z_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {y, z, static_cast<const void*>(weight), static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::NormArgs a{y, y_row_stride, z, z_row_stride, weight, eps, out, rows, I, d->ngroups};
+    return hip_status(ssd::launch_gated_rmsnorm(a, static_cast<Dt>(d->act_dtype), static_cast<Dt>(d->y_dtype),
+                                                stream));
+}
+
 }  // extern "C"

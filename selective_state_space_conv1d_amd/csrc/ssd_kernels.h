@@ -85,6 +85,16 @@ struct LpUpdateArgs {
     int rounds;        // Philox rounds for stochastic rounding; 0: round to nearest even
 };
 
+// Gated group RMSNorm: rows x channels, ngroups groups of channels / ngroups.
+struct NormArgs {
+    const void* y; int64_t y_row_stride;
+    const void* z; int64_t z_row_stride;
+    const float* weight; float eps;
+    void* out;
+    int64_t rows, channels;
+    int ngroups;
+};
+
 // Accept step of speculative decoding: request b with n = clamp(accept_len[b], 0, k) >= 1 gets
 // intermediate state b*k + n - 1 copied into its slot (b without a slot table), for the SSM
 // state (state_bytes per request) and the conv state (conv_bytes); NULL pointers skip one.
@@ -106,6 +116,7 @@ hipError_t launch_state_update(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t 
 hipError_t launch_state_update_multi(const UpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s);
 hipError_t launch_state_update_lp(const LpUpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);

@@ -23,7 +23,7 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
-           "ssd_chunk_scan_snapshots"]
+           "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm"]
 
 
 class SsdDims(ctypes.Structure):
@@ -83,6 +83,7 @@ def _lib():
                                                _PDT, _VP, _VP, _VP]
         lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
         lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_gated_rmsnorm.argtypes = [_PD, _VP, _I64, _VP, _I64, _VP, ctypes.c_float, _VP, _VP]
         lib.ssd_chunk_scan_snapshots.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
                                                  _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_lp.argtypes = [_PD, _VP, _I32, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
@@ -90,7 +91,7 @@ def _lib():
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
-                  "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots"):
+                  "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -568,6 +569,31 @@ def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y
                                       _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), srp, _ptr(y),
                                       _stream(stream)), "ssd_state_update_lp")
     return y
+
+
+# --------------------------------------------------------------------------- gated norm
+def ssd_gated_rmsnorm(y, z, weight, ngroups, eps=1e-5, out=None, stream=None):
+    """out = rmsnorm over each of ngroups channel groups of y * silu(z), times weight (fp32
+    arithmetic).  y [..., I] (e.g. the scan output viewed as [B, L, H*P]; rows may be strided),
+    z [..., I] in the activation dtype (rows may be strided), weight [I] fp32.  Returns out
+    [..., I] in z's dtype."""
+    I = y.shape[-1]
+    if z.shape != y.shape or y.stride(-1) != 1 or z.stride(-1) != 1 or y.dim() < 2:
+        raise ValueError("y and z must have the same shape [..., I] with packed channels")
+    y2 = y.reshape(-1, I) if y.dim() > 2 else y
+    z2 = z.reshape(-1, I) if z.dim() > 2 else z
+    if weight.shape != (I,) or weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise ValueError("weight must be contiguous fp32 [I]")
+    if I % ngroups:
+        raise ValueError("ngroups must divide the channel count")
+    if out is None:
+        out = torch.empty(y.shape, dtype=z.dtype, device=y.device)
+    rows = y2.shape[0]
+    d = _dims(rows, 1, ngroups, I // ngroups, ngroups, 16, z.dtype, y.dtype)   # one "head" per group
+    _check(_lib().ssd_gated_rmsnorm(ctypes.byref(d), _ptr(y2), y2.stride(0) if rows else I, _ptr(z2),
+                                    z2.stride(0) if rows else I, _ptr(weight), float(eps), _ptr(out),
+                                    _stream(stream)), "ssd_gated_rmsnorm")
+    return out
 
 
 def split_xbc(v, nheads, head_dim, ngroups, d_state):

@@ -268,6 +268,23 @@ def test_snapshot_scan_validation(ssd, lib):
                                         None, fp(9), 128, fp(6), None, 0, None) == E["SSD_ERR_NULL"]
 
 
+def test_gated_rmsnorm_validation(ssd, lib):
+    """The gated norm rejects bad host arguments before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=4, seqlen=2)     # 8 rows, I = 256 channels in 2 groups of 128
+
+    def nrm(dd=d, y=fp(1), ys=256, z=fp(2), zs=256, w=fp(3), eps=1e-5, out=fp(4)):
+        return lib.ssd_gated_rmsnorm(ctypes.byref(dd), y, ys, z, zs, w, eps, out, None)
+    assert nrm(y=None) == E["SSD_ERR_NULL"]
+    assert nrm(w=None) == E["SSD_ERR_NULL"]
+    assert nrm(ys=200) == E["SSD_ERR_SHAPE"]
+    assert nrm(zs=260) == E["SSD_ERR_ALIGN"]
+    assert nrm(eps=-1.0) == E["SSD_ERR_SHAPE"]
+    assert nrm(out=ctypes.c_void_p(P0 + 2)) == E["SSD_ERR_ALIGN"]
+    assert nrm(dims(ssd, batch=4, seqlen=2, nheads=4, head_dim=20, ngroups=4)) == E["SSD_ERR_UNSUPPORTED"]   # group of 20
+    assert nrm(dims(ssd, batch=0, seqlen=2), y=None, z=None, w=None, out=None) == E["SSD_OK"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")

@@ -1,0 +1,49 @@
+"""Parity of the gated group RMSNorm with the oracle on the GPU (fp32 arithmetic; bf16 output
+within one bf16 ulp plus the fp32 evaluation, fp32 output within the fp32 bar)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import F32_BAR, assert_close, f64
+from selective_state_space_conv1d_amd import ssd
+from selective_state_space_conv1d_amd.synth import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def norm_inputs(rows, I, ydt, zdt, seed, zpad=0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    y = (torch.randn(rows, I, generator=g) * 2.0).to(ydt).to(DEV)
+    zbase = torch.randn(rows, I + zpad, generator=g).to(zdt).to(DEV)
+    w = (torch.rand(I, generator=g) + 0.5).to(DEV)
+    return y, zbase[:, :I], w
+
+
+@pytest.mark.parametrize("ydt,zdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
+                                     (torch.float32, torch.float32)])
+@pytest.mark.parametrize("I,G", [(256, 2), (2048, 8), (96, 4)])
+def test_gated_rmsnorm(orc, ydt, zdt, I, G):
+    y, z, w = norm_inputs(37, I, ydt, zdt, 600, zpad=64)     # z is a strided view (row stride I + 64)
+    out = ssd.ssd_gated_rmsnorm(y, z, w, G, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = orc.gated_rmsnorm(f64(y), f64(z), f64(w), G, 1e-5)
+    if zdt == torch.bfloat16:
+        o = f64(out)
+        bad = np.abs(o - ref) > np.abs(ref) * 2.0 ** -7 + 1e-5 * np.abs(ref).max()
+        assert not bad.any(), f"{bad.sum()} outputs off by more than one bf16 ulp"
+    else:
+        assert_close(out, ref, F32_BAR, "out")
+
+
+def test_gated_rmsnorm_full_size_prefill_sampled(orc):
+    """The prefill output of the Ultra layer (8192 tokens x 256 heads x 64, 8 groups), sampled rows."""
+    d = WORKLOADS["prefill_ultra_8k"]
+    I = d.nheads * d.head_dim
+    y, z, w = norm_inputs(d.seqlen, I, torch.bfloat16, torch.bfloat16, 610)
+    out = ssd.ssd_gated_rmsnorm(y.view(1, d.seqlen, I), z.view(1, d.seqlen, I), w, d.ngroups)
+    torch.cuda.synchronize()
+    rows = [0, 1, 4095, 8191]
+    ref = orc.gated_rmsnorm(f64(y[rows]), f64(z[rows]), f64(w), d.ngroups, 1e-5)
+    o = f64(out[0, rows])
+    assert np.all(np.abs(o - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-5 * np.abs(ref).max())
