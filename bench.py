@@ -292,6 +292,36 @@ def norm_leg(ssd, torch, dev, steps, warmup, y):
             "frac": alg / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
 
 
+def decode_step_leg(ssd, torch, dev, steps, warmup):
+    """One decode step of batch 64 (conv update + state update) in one launch, ping-ponging the
+    conv windows; each launch bracketed by HIP events."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, decode_state, decode_tokens, mixer_inputs
+    dd = WORKLOADS["decode_ultra_b64"]
+    dst = decode_state(dd, 1001, device=dev)
+    dpar = mixer_inputs(dd.with_(seqlen=1), 1001, device=dev)
+    ntok = 16
+    dtok = decode_tokens(dd, 1011, ntok, device=dev)
+    state, cs = dst["state"], [dst["conv_state"], torch.empty_like(dst["conv_state"])]
+    y = torch.empty(dd.batch, dd.nheads, dd.head_dim, dtype=dd.dtype, device=dev)
+
+    def one(i):
+        ssd.ssd_decode_step(dtok["xbc"][i % ntok], dpar["w"], dpar["bias"], cs[i % 2], cs[(i + 1) % 2], state,
+                            dtok["dt"][i % ntok], dpar["A"], dpar["D"], ngroups=dd.ngroups, y=y)
+
+    for i in range(warmup):
+        one(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        one(warmup + i)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    t = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps * 1e-3
+    alg = update_bytes(dd) + conv_update_bytes(dd) - dd.batch * dd.conv_dim * 2 * 2   # no x|B|C round trip
+    return {"batch": dd.batch, "us": t * 1e6, "tokens_per_s": dd.batch / t, "GBps": alg / t / 1e9,
+            "frac": alg / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
+
+
 def cpu_baseline(orc, inp, d, n_heads=256):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
     over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
@@ -475,6 +505,8 @@ def main():
     out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
     print("[bench] speculative decode (k-token updates, accept)", file=sys.stderr, flush=True)
     out["spec_decode"] = spec_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
+    print("[bench] one-launch decode step", file=sys.stderr, flush=True)
+    out["decode_step_fused"] = decode_step_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
     print("[bench] 16-bit state decode (stochastic rounding)", file=sys.stderr, flush=True)
     out["lowprec_decode"] = lowprec_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
     if not args.no_cpu_baseline:

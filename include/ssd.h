@@ -16,7 +16,8 @@
  * and multi-token (speculative) decode with the accept step:
  *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states
  * and the decode update on a 16-bit state with stochastic rounding: ssd_state_update_lp,
- * and the gated group RMSNorm of the mixer output: ssd_gated_rmsnorm
+ * and the gated group RMSNorm of the mixer output: ssd_gated_rmsnorm,
+ * and one decode step (conv update + state update) in one launch: ssd_decode_step
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "Mamba 与 Nemotron 系列模型深度调研": "Mamba 架构 / 1. Selective SSM 的直觉"
@@ -390,6 +391,23 @@ ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state
  */
 ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* d, const void* y, int64_t y_row_stride, const void* z,
                                int64_t z_row_stride, const float* weight, float eps, void* out, hipStream_t stream);
+
+/*
+ * One decode step of the mixer in one launch: ssd_conv1d_update followed by ssd_state_update
+ * ([P2] "Decode 阶段"), bitwise equal to the two calls (the conv outputs are rounded to the
+ * activation dtype as the conv call stores them).  The conv outputs x, B, C are not written.
+ *  xbc             [B, CD] act dtype, rows xbc_row_stride elements apart.
+ *  conv_state_in   [B, CD, 4] act dtype, read only.
+ *  conv_state_out  [B, CD, 4] act dtype: the rolled windows.  Must not overlap conv_state_in:
+ *                  the step reads every group's old window from many workgroups (swap the two
+ *                  buffers between steps).
+ *  state           [B, H, P, N] fp32, updated in place.
+ * w, bias, dt, A, D, dt_params and y as for ssd_conv1d_update and ssd_state_update.
+ */
+ssd_status_t ssd_decode_step(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride, const void* w,
+                             const void* bias, const void* conv_state_in, void* conv_state_out, float* state,
+                             const void* dt, const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                             void* y, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

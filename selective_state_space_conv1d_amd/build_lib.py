@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
-SOURCES = ["ssd_api.cpp", "conv1d.hip", "state_update.hip", "spec_decode.hip", "state_lp.hip", "norm.hip",
+SOURCES = ["ssd_api.cpp", "conv1d.hip", "state_update.hip", "spec_decode.hip", "state_lp.hip", "norm.hip", "decode_step.hip",
            "chunk_scan_fma.hip", "chunk_scan_mfma.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -398,4 +398,27 @@ ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* d, const void* y, int64_t y_row
                                                 stream));
 }
 
+ssd_status_t ssd_decode_step(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride, const void* w,
+                             const void* bias, const void* conv_state_in, void* conv_state_out, float* state,
+                             const void* dt, const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                             void* y, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, false);
+    if (st != SSD_OK) return st;
+    const int64_t CD = ssd_conv_dim(d);
+    if (d->batch > 0 && (!xbc || !w || !conv_state_in || !conv_state_out || !state || !dt || !A || !y))
+        return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    if (xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    // the old and new conv windows must be distinct buffers (every block reads the old ones)
+    const uintptr_t cb = static_cast<uintptr_t>(d->batch) * CD * 4 * elem_size(d->act_dtype);
+    const uintptr_t ci = reinterpret_cast<uintptr_t>(conv_state_in), co = reinterpret_cast<uintptr_t>(conv_state_out);
+    if (d->batch > 0 && ci < co + cb && co < ci + cb) return SSD_ERR_SHAPE;
+    if (state && !aligned16(state)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
+    ssd::DecodeStepArgs a{{state, nullptr, 0, nullptr, nullptr, 0, dt, A, D, y, d->batch, d->nheads, d->head_dim,
+                           d->ngroups, d->d_state, nullptr, 0, dt_params_of(dt_params)},
+                          xbc, xbc_row_stride, w, bias, conv_state_in, conv_state_out};
+    return hip_status(ssd::launch_decode_step(a, static_cast<Dt>(d->act_dtype), static_cast<Dt>(d->y_dtype), stream));
+}
+
 }  // extern "C"

@@ -85,6 +85,15 @@ struct LpUpdateArgs {
     int rounds;        // Philox rounds for stochastic rounding; 0: round to nearest even
 };
 
+// One decode step (conv update + state update) in one launch: u carries the state update's
+// arguments (x, B, C unused: they are the conv's outputs); the conv reads conv_in and writes conv_out.
+struct DecodeStepArgs {
+    UpdateArgs u;
+    const void* xbc; int64_t xbc_row_stride;
+    const void* w; const void* bias;
+    const void* conv_in; void* conv_out;
+};
+
 // Gated group RMSNorm: rows x channels, ngroups groups of channels / ngroups.
 struct NormArgs {
     const void* y; int64_t y_row_stride;
@@ -117,6 +126,7 @@ hipError_t launch_state_update_multi(const UpdateArgs& a, Dt act, Dt ydt, hipStr
 hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s);
 hipError_t launch_state_update_lp(const LpUpdateArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, Dt act, Dt ydt, hipStream_t s);
+hipError_t launch_decode_step(const DecodeStepArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);

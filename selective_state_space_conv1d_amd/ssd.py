@@ -23,7 +23,7 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
-           "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm"]
+           "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step"]
 
 
 class SsdDims(ctypes.Structure):
@@ -83,6 +83,7 @@ def _lib():
                                                _PDT, _VP, _VP, _VP]
         lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
         lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_decode_step.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _PDT, _VP, _VP]
         lib.ssd_gated_rmsnorm.argtypes = [_PD, _VP, _I64, _VP, _I64, _VP, ctypes.c_float, _VP, _VP]
         lib.ssd_chunk_scan_snapshots.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
                                                  _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
@@ -91,7 +92,8 @@ def _lib():
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
-                  "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm"):
+                  "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
+                  "ssd_decode_step"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -568,6 +570,35 @@ def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y
                                       _ptr(x), x.stride(0), _ptr(B), _ptr(C), B.stride(0), _ptr(dt), _ptr(A),
                                       _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), srp, _ptr(y),
                                       _stream(stream)), "ssd_state_update_lp")
+    return y
+
+
+# --------------------------------------------------------------------------- one-launch decode step
+def ssd_decode_step(xbc, w, bias, conv_state_in, conv_state_out, state, dt, A, D=None, nheads=None, head_dim=None,
+                    ngroups=None, y=None, y_dtype=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
+    """Conv update + state update in one launch.  xbc [B, CD] (rows may be strided); conv_state_in
+    [B, CD, 4] is read, conv_state_out [B, CD, 4] (a different buffer) receives the rolled windows;
+    state [B, H, P, N] fp32 is updated in place; dt [B, H].  Returns y [B, H, P]."""
+    Bt, CD = xbc.shape
+    _, H, P, N = state.shape
+    G = ngroups if ngroups is not None else (CD - H * P) // (2 * N)
+    if H * P + 2 * G * N != CD or (nheads is not None and nheads != H) or (head_dim is not None and head_dim != P):
+        raise ValueError("xbc channels must be H*P + 2*G*N for the state's (H, P, N)")
+    if xbc.stride(1) != 1:
+        raise ValueError("xbc channels must be packed")
+    for t, nm in ((conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+        if t.shape != (Bt, CD, 4) or not t.is_contiguous() or t.dtype != xbc.dtype:
+            raise ValueError(f"{nm} must be contiguous [B, CD, 4] in xbc's dtype")
+    if state.shape[0] != Bt or not state.is_contiguous() or dt.shape != (Bt, H) or not dt.is_contiguous():
+        raise ValueError("state [B, H, P, N] and dt [B, H] must be contiguous")
+    ydt = y_dtype or xbc.dtype
+    if y is None:
+        y = torch.empty((Bt, H, P), dtype=ydt, device=xbc.device)
+    d = _dims(Bt, 1, H, P, G, N, xbc.dtype, y.dtype)
+    _check(_lib().ssd_decode_step(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias), _ptr(conv_state_in),
+                                  _ptr(conv_state_out), _ptr(state), _ptr(dt), _ptr(A), _ptr(D),
+                                  _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(y), _stream(stream)),
+           "ssd_decode_step")
     return y
 
 

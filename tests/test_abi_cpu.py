@@ -285,6 +285,24 @@ def test_gated_rmsnorm_validation(ssd, lib):
     assert nrm(dims(ssd, batch=0, seqlen=2), y=None, z=None, w=None, out=None) == E["SSD_OK"]
 
 
+def test_decode_step_validation(ssd, lib):
+    """The one-launch decode step rejects bad host arguments, and overlapping conv windows, before any launch."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=1)     # CD = 768: conv windows of 2 * 768 * 4 bf16 = 12 KiB
+
+    def step(dd=d, xs=768, cin=fp(3), cout=fp(8), state=fp(5), y=fp(7)):
+        return lib.ssd_decode_step(ctypes.byref(dd), fp(1), xs, fp(2), None, cin, cout, state, fp(4), fp(6), None,
+                                   None, y, None)
+    assert step(cin=None) == E["SSD_ERR_NULL"]
+    assert step(state=None) == E["SSD_ERR_NULL"]
+    assert step(y=None) == E["SSD_ERR_NULL"]
+    assert step(xs=700) == E["SSD_ERR_SHAPE"]
+    assert step(cout=fp(3)) == E["SSD_ERR_SHAPE"]                           # same buffer
+    assert step(cout=ctypes.c_void_p(P0 + 0x3000 + 4096)) == E["SSD_ERR_SHAPE"]  # overlapping
+    assert step(state=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert step(dims(ssd, batch=2, seqlen=1, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
