@@ -14,7 +14,8 @@
  *   ssd_conv1d_fwd_varlen, ssd_chunk_scan_varlen, ssd_conv1d_update_slots,
  *   ssd_state_update_slots
  * and multi-token (speculative) decode with the accept step:
- *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states
+ *   ssd_state_update_multi, ssd_conv1d_update_multi, ssd_accept_states (or, by recomputation,
+ *   ssd_state_update_accept and ssd_conv1d_update_accept)
  * and the decode update on a 16-bit state with stochastic rounding: ssd_state_update_lp,
  * and the gated group RMSNorm of the mixer output: ssd_gated_rmsnorm,
  * and one decode step (conv update + state update) in one launch: ssd_decode_step
@@ -408,6 +409,27 @@ ssd_status_t ssd_decode_step(const ssd_dims_t* d, const void* xbc, int64_t xbc_r
                              const void* bias, const void* conv_state_in, void* conv_state_out, float* state,
                              const void* dt, const float* A, const float* D, const ssd_dt_params_t* dt_params,
                              void* y, hipStream_t stream);
+
+/*
+ * Accept step by recomputation: instead of keeping the k intermediate states, apply each request's
+ * first n = accept_len[b] (clamped to [0, k]) candidate tokens to its main state in place.  The
+ * per-token arithmetic is ssd_state_update_multi's, so the state equals the intermediate state
+ * n - 1 bitwise; n = 0 and padding requests are left unchanged.  The inputs are the multi-token
+ * call's: x, B, C, dt with its layout and strides (B and C 16-byte aligned).  With it, the
+ * multi-token call can run with inter_states NULL.
+ */
+ssd_status_t ssd_state_update_accept(const ssd_dims_t* d, float* state, const int32_t* slot_idx, int64_t nslots,
+                                     const void* x, int64_t x_row_stride, const void* B, const void* C,
+                                     int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                     const ssd_dt_params_t* dt_params, const int32_t* accept_len, hipStream_t stream);
+
+/*
+ * The conv counterpart: request b's window becomes the last 4 of (its old window, candidate rows
+ * 0 .. n-1 of xbc), in place.  xbc is the multi-token conv call's input [B*k, CD].
+ */
+ssd_status_t ssd_conv1d_update_accept(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride, void* conv_state,
+                                      const int32_t* slot_idx, int64_t nslots, const int32_t* accept_len,
+                                      hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* ssd_status_string(ssd_status_t s);

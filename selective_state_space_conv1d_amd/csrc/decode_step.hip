@@ -127,10 +127,9 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(
             part = fmaf(v[k], cc[4 * q + k], part);
         }
         if (!ok) part = 0.f;
-#pragma unroll
-        for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        part = group_sum_last<QPR>(part);
         if (ok) {
-            if (q == 0) y[bh * P + p0 + r] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+            if (q == QPR - 1) y[bh * P + p0 + r] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
             __builtin_nontemporal_store(v, st4 + f);
         }
     }

@@ -33,20 +33,26 @@ struct TokIn {
     typename Quad<T>::type b, c;
 };
 
+constexpr int kTokBlock = 1;   // tokens per y-reduction block (2 or 4 raise VGPRs to 100+ and run 15-30 % slower)
+
 // Grid: one thread per kMultiPerThread float4 of the [B, H, P, N] state, 128-thread strides.
 // Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.  The
 // per-head constants are read once; each token's inputs for all of a thread's elements are
-// loaded one token ahead of their use, so the loads overlap the previous token's stores.
-template <typename T, typename TY, int N>
+// loaded one token ahead of their use.  Each row's y dot product is a DPP reduction over its
+// lanes (no LDS round trip), kTokBlock tokens at a time.
+// REPLAY (the accept step by recomputation): request b applies its first
+// n = clamp(accept_len[b], 0, k) tokens and writes the state back in place; no y, no inter.
+template <typename T, typename TY, int N, bool REPLAY>
 __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
-    const float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
+    float* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
     const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ D, TY* __restrict__ y, float* __restrict__ inter, int64_t total4, int k, int H,
-    int P, int hpg, const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp) {
+    int P, int hpg, const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp,
+    const int32_t* __restrict__ accept_len) {
     constexpr int QPR = N / 4;  // float4 per state row
     typedef typename Quad<T>::type Q;
     const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
-    const f32x4* st4 = reinterpret_cast<const f32x4*>(state);
+    f32x4* st4 = reinterpret_cast<f32x4*>(state);
     f32x4* in4 = reinterpret_cast<f32x4*>(inter);
     const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread);
     const int64_t base = f0 + threadIdx.x;
@@ -57,12 +63,20 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     const int64_t ub = f0 / per_b;
     const bool uni = ub == fl / per_b;
     const int64_t uslot = uni ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
+    auto tokens_of = [&](int64_t b) {   // tokens to apply: k, or the accepted count when replaying
+        if constexpr (!REPLAY) return k;
+        const int n = accept_len[b];
+        return n < 0 ? 0 : (n > k ? k : n);
+    };
+    int kmax = uni ? tokens_of(ub) : k;
+    if (REPLAY && uni && (kmax == 0 || uslot < 0)) return;   // nothing accepted, or padding
 
     // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g,
-    // and the head's A, D and dt bias
+    // the head's A, D and dt bias, its slot and its token count
     f32x4 s[kMultiPerThread];
-    int64_t bb[kMultiPerThread], rem[kMultiPerThread];
+    int64_t bb[kMultiPerThread], rem[kMultiPerThread], sl[kMultiPerThread];
     int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
+    int nk[kMultiPerThread];
     float Ah[kMultiPerThread], Dh[kMultiPerThread], biash[kMultiPerThread];
 #pragma unroll
     for (int i = 0; i < kMultiPerThread; ++i) {
@@ -75,9 +89,10 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
         hh[i] = rw[i] / P;
         pp[i] = rw[i] - hh[i] * P;
         gg[i] = hh[i] / hpg;
-        const int64_t slot = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
-        s[i] = (f < total4 && slot >= 0) ? __builtin_nontemporal_load(st4 + slot * per_b + rem[i])
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        sl[i] = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
+        nk[i] = f < total4 ? (uni ? kmax : tokens_of(bb[i])) : 0;
+        s[i] = (f < total4 && sl[i] >= 0 && nk[i] > 0) ? __builtin_nontemporal_load(st4 + sl[i] * per_b + rem[i])
+                                                       : f32x4{0.f, 0.f, 0.f, 0.f};
         Ah[i] = A[hh[i]];
         Dh[i] = D ? D[hh[i]] : 0.f;
         biash[i] = dtp.bias ? dtp.bias[hh[i]] : 0.f;
@@ -85,7 +100,7 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     auto load_tok = [&](int j, TokIn<T> (&in)[kMultiPerThread]) {
 #pragma unroll
         for (int i = 0; i < kMultiPerThread; ++i) {
-            const int64_t tok = bb[i] * k + j;
+            const int64_t tok = bb[i] * k + (j < nk[i] ? j : 0);   // rows past a request's count: its first
             in[i].dt = dt[tok * H + hh[i]];
             in[i].x = x[tok * xs + static_cast<int64_t>(hh[i]) * P + pp[i]];
             const int64_t bo = tok * bcs + static_cast<int64_t>(gg[i]) * N + 4 * qq[i];
@@ -95,39 +110,66 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     };
     TokIn<T> cur[kMultiPerThread], nxt[kMultiPerThread];
     load_tok(0, cur);
-    for (int j = 0; j < k; ++j) {
-        if (j + 1 < k) load_tok(j + 1, nxt);
+    for (int j0 = 0; j0 < kmax; j0 += kTokBlock) {
+        float part[kMultiPerThread][kTokBlock], xk[kMultiPerThread][kTokBlock];
 #pragma unroll
-        for (int i = 0; i < kMultiPerThread; ++i) {
-            const bool ok = base + i * kMultiThreads < total4;
-            const int64_t tok = bb[i] * k + j;
-            // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
-            float dtv = static_cast<float>(cur[i].dt);
-            if (dtp.bias) dtv += biash[i];
-            if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
-            if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
-            const float a = __expf(dtv * Ah[i]);
-            const float xv = static_cast<float>(cur[i].x);
-            const float dx = dtv * xv;
-            f32x4 v = s[i];
-            float part = 0.f;
+        for (int jj = 0; jj < kTokBlock; ++jj) {
+            const int j = j0 + jj;
+            if (j < kmax) {   // uniform
+                if (j + 1 < kmax) load_tok(j + 1, nxt);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = fmaf(a, v[e], dx * static_cast<float>(cur[i].b[e]));
-                part = fmaf(v[e], static_cast<float>(cur[i].c[e]), part);
-            }
-            s[i] = v;
-            if (!ok) part = 0.f;
+                for (int i = 0; i < kMultiPerThread; ++i) {
+                    // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
+                    float dtv = static_cast<float>(cur[i].dt);
+                    if (dtp.bias) dtv += biash[i];
+                    if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
+                    if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
+                    const float a = __expf(dtv * Ah[i]);
+                    const float xv = static_cast<float>(cur[i].x);
+                    const float dx = dtv * xv;
+                    f32x4 v = s[i];
+                    float pt = 0.f;
 #pragma unroll
-            for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-            if (ok) {
-                if (qq[i] == 0)
-                    y[tok * H * static_cast<int64_t>(P) + rw[i]] = static_cast<TY>(part + (D ? Dh[i] * xv : 0.f));
-                if (inter) in4[tok * per_b + rem[i]] = v;   // plain stores measured faster here
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = fmaf(a, v[e], dx * static_cast<float>(cur[i].b[e]));
+                        pt = fmaf(v[e], static_cast<float>(cur[i].c[e]), pt);
+                    }
+                    if (j < nk[i]) s[i] = v;
+                    part[i][jj] = (base + i * kMultiThreads < total4) ? pt : 0.f;
+                    xk[i][jj] = xv;
+                    if constexpr (!REPLAY) {
+                        if (inter && base + i * kMultiThreads < total4)
+                            in4[(bb[i] * k + j) * per_b + rem[i]] = v;   // plain stores measured faster here
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kMultiPerThread; ++i) cur[i] = nxt[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kMultiPerThread; ++i) part[i][jj] = 0.f, xk[i][jj] = 0.f;
             }
         }
+        if constexpr (!REPLAY) {
 #pragma unroll
-        for (int i = 0; i < kMultiPerThread; ++i) cur[i] = nxt[i];
+            for (int i = 0; i < kMultiPerThread; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < kTokBlock; ++jj) part[i][jj] = group_sum_last<QPR>(part[i][jj]);
+                if (base + i * kMultiThreads >= total4 || qq[i] != QPR - 1) continue;
+#pragma unroll
+                for (int jj = 0; jj < kTokBlock; ++jj) {
+                    const int64_t tok = bb[i] * k + j0 + jj;
+                    if (j0 + jj < kmax)
+                        y[tok * H * static_cast<int64_t>(P) + rw[i]] =
+                            static_cast<TY>(part[i][jj] + (D ? Dh[i] * xk[i][jj] : 0.f));
+                }
+            }
+        }
+    }
+    if constexpr (REPLAY) {
+#pragma unroll
+        for (int i = 0; i < kMultiPerThread; ++i)
+            if (base + i * kMultiThreads < total4 && sl[i] >= 0 && nk[i] > 0)
+                __builtin_nontemporal_store(s[i], st4 + sl[i] * per_b + rem[i]);
     }
 }
 
@@ -137,11 +179,18 @@ static hipError_t multi_launch(const UpdateArgs& a, hipStream_t s) {
     if (total4 == 0 || a.k == 0) return hipSuccess;
     const int64_t per_block = kMultiThreads * kMultiPerThread;
     const int64_t blocks = (total4 + per_block - 1) / per_block;
-    hipLaunchKernelGGL((state_update_multi_kernel<T, TY, N>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kMultiThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
-                       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
-                       static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), a.inter, total4, a.k,
-                       a.nheads, a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots, a.dtp);
+    if (a.accept_len)
+        hipLaunchKernelGGL((state_update_multi_kernel<T, TY, N, true>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kMultiThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
+                           static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
+                           static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), nullptr, total4, a.k,
+                           a.nheads, a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots, a.dtp, a.accept_len);
+    else
+        hipLaunchKernelGGL((state_update_multi_kernel<T, TY, N, false>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kMultiThreads), 0, s, a.state, static_cast<const T*>(a.x), a.x_row_stride,
+                           static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.bc_row_stride,
+                           static_cast<const T*>(a.dt), a.A, a.D, static_cast<TY*>(a.y), a.inter, total4, a.k,
+                           a.nheads, a.head_dim, a.nheads / a.ngroups, a.slot_idx, a.nslots, a.dtp, nullptr);
     return hipGetLastError();
 }
 
@@ -231,6 +280,57 @@ static hipError_t conv_multi_t(const ConvUpdateArgs& a, hipStream_t s) {
 
 hipError_t launch_conv1d_update_multi(const ConvUpdateArgs& a, Dt act, hipStream_t s) {
     return act == Dt::BF16 ? conv_multi_t<bf16>(a, s) : conv_multi_t<float>(a, s);
+}
+
+// Accept by recomputation for the conv: request b's window after its first n candidate rows
+// (n = accept_len clamped to [0, k]) is the last 4 of (old window, rows 0 .. n-1).  One thread
+// per (request, 16-byte channel vector); nothing to do for n = 0 or padding.
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void conv_accept_kernel(const T* __restrict__ xbc, int64_t xs,
+                                                                   T* __restrict__ state,
+                                                                   const int32_t* __restrict__ slot_idx, int64_t nslots,
+                                                                   const int32_t* __restrict__ accept_len, int64_t CD,
+                                                                   int64_t total, int k) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t per_b = CD / V;
+    const int64_t b = idx / per_b;
+    const int64_t c0 = (idx - b * per_b) * V;
+    int n = accept_len[b];
+    n = n < 0 ? 0 : (n > k ? k : n);
+    const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    if (n == 0 || slot < 0) return;
+    T* sp = state + (slot * CD + c0) * 4;
+    float s[4 * V], o[4 * V];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load16_f32(sp + q * V, s + q * V);
+#pragma unroll
+    for (int col = 0; col < 4; ++col) {
+        const int t = n - 4 + col;   // candidate row of window column col, or the old column 4 + t
+        float u[V];
+        if (t >= 0) load16_f32(xbc + (b * k + t) * xs + c0, u);
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v * 4 + col] = t >= 0 ? u[v] : s[v * 4 + 4 + t];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store16_f32(sp + q * V, o + q * V);
+}
+
+template <typename T>
+static hipError_t conv_accept_t(const ConvUpdateArgs& a, const int32_t* accept_len, hipStream_t s) {
+    constexpr int V = Vec16<T>::n;
+    const int64_t total = a.batch * (a.channels / V);
+    if (total == 0 || a.k == 0) return hipSuccess;
+    const int64_t blocks = (total + kCopyThreads - 1) / kCopyThreads;
+    hipLaunchKernelGGL(conv_accept_kernel<T>, dim3(static_cast<uint32_t>(blocks)), dim3(kCopyThreads), 0, s,
+                       static_cast<const T*>(a.xbc), a.xbc_row_stride, static_cast<T*>(a.state), a.slot_idx,
+                       a.nslots, accept_len, a.channels, total, a.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d_update_accept(const ConvUpdateArgs& a, const int32_t* accept_len, Dt act, hipStream_t s) {
+    return act == Dt::BF16 ? conv_accept_t<bf16>(a, accept_len, s) : conv_accept_t<float>(a, accept_len, s);
 }
 
 // Request blockIdx.y: with n = accept_len clamped to [0, k] and n >= 1, copy its intermediate

@@ -328,6 +328,51 @@ ssd_status_t ssd_conv1d_update_multi(const ssd_dims_t* d, const void* xbc, int64
     return hip_status(ssd::launch_conv1d_update_multi(a, static_cast<Dt>(d->act_dtype), stream));
 }
 
+ssd_status_t ssd_state_update_accept(const ssd_dims_t* d, float* state, const int32_t* slot_idx, int64_t nslots,
+                                     const void* x, int64_t x_row_stride, const void* B, const void* C,
+                                     int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                     const ssd_dt_params_t* dt_params, const int32_t* accept_len, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (nslots < 0 || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    const bool tokens = d->batch > 0 && d->seqlen > 0 && (!slot_idx || nslots > 0);
+    if (tokens && (!x || !B || !C || !dt || !A || !accept_len || !state)) return SSD_ERR_NULL;
+    if (!pow2_16_128(d->head_dim) || !pow2_16_128(d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (tokens && (x_row_stride < I || bc_row_stride < GN)) return SSD_ERR_SHAPE;
+    if (!stride_ok(bc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(state), B, C})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
+    if (!tokens) return SSD_OK;
+    ssd::UpdateArgs a{state, x, x_row_stride, B, C, bc_row_stride, dt, A, D, nullptr,
+                      d->batch, d->nheads, d->head_dim, d->ngroups, d->d_state, slot_idx, nslots,
+                      dt_params_of(dt_params), nullptr, static_cast<int>(d->seqlen), accept_len};
+    return hip_status(ssd::launch_state_update_multi(a, static_cast<Dt>(d->act_dtype), static_cast<Dt>(d->act_dtype),
+                                                     stream));
+}
+
+ssd_status_t ssd_conv1d_update_accept(const ssd_dims_t* d, const void* xbc, int64_t xbc_row_stride, void* conv_state,
+                                      const int32_t* slot_idx, int64_t nslots, const int32_t* accept_len,
+                                      hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (nslots < 0 || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    const int64_t CD = ssd_conv_dim(d);
+    const bool tokens = d->batch > 0 && d->seqlen > 0 && (!slot_idx || nslots > 0);
+    if (tokens && (!xbc || !conv_state || !accept_len)) return SSD_ERR_NULL;
+    if (CD % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (tokens && xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, static_cast<const void*>(conv_state)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if (!tokens) return SSD_OK;
+    ssd::ConvUpdateArgs a{xbc, xbc_row_stride, nullptr, nullptr, conv_state, nullptr, d->batch, CD,
+                          slot_idx, nslots, nullptr, static_cast<int>(d->seqlen)};
+    return hip_status(ssd::launch_conv1d_update_accept(a, accept_len, static_cast<Dt>(d->act_dtype), stream));
+}
+
 ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, const int32_t* slot_idx,
                                int64_t nslots, float* state, const float* inter_states, void* conv_state,
                                const void* inter_conv_states, hipStream_t stream) {

@@ -44,6 +44,26 @@ __device__ __forceinline__ void store16_f32(T* p, const float* in) {
 // activation dtype, and the division's exact rounding costs a dozen instructions per element.
 __device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// Sum of v over each aligned group of G consecutive lanes (G = 2, 4, 8, 16 or 32), valid in the
+// group's last lane.  DPP lane moves (VALU, a few cycles each) instead of LDS shuffles: quad
+// permutes for 2 and 4 lanes, the half-row and row mirrors for 8 and 16, and the row-15 broadcast
+// into rows 1 and 3 for 32 (the last lane of each 32-group is in those rows).  Lane semantics were
+// checked on the device for every G.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, RMASK, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum_last(float v) {
+    static_assert(G == 2 || G == 4 || G == 8 || G == 16 || G == 32, "group of 2..32 lanes");
+    if constexpr (G >= 2) v += dpp_f<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v += dpp_f<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_f<0x141, 0xF>(v);   // row_half_mirror
+    if constexpr (G >= 16) v += dpp_f<0x140, 0xF>(v);  // row_mirror
+    if constexpr (G >= 32) v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    return v;
+}
+
 // dt prologue of head h (fp32): + bias, softplus (the identity above 20, where log(1 + e^v)
 // rounds to v), clamp.  With every step off it returns v unchanged.
 template <class DP>

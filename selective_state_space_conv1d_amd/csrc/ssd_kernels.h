@@ -74,6 +74,7 @@ struct UpdateArgs {
     DtParams dtp;
     float* inter;   // multi-token: [B, k, H, P, N] state after each token, or NULL
     int k;          // multi-token: tokens per request (the state is then read only)
+    const int32_t* accept_len;   // multi-token replay: apply the first accept_len[b] tokens in place
 };
 
 // Decode update on a 16-bit state (fp16 or bf16 codes): u carries everything but the state.
@@ -128,6 +129,8 @@ hipError_t launch_state_update_lp(const LpUpdateArgs& a, Dt act, Dt ydt, hipStre
 hipError_t launch_gated_rmsnorm(const NormArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_decode_step(const DecodeStepArgs& a, Dt act, Dt ydt, hipStream_t s);
 hipError_t launch_accept_states(const AcceptArgs& a, hipStream_t s);
+// accept by recomputation: the multi-token update with u.accept_len set, and the conv windows
+hipError_t launch_conv1d_update_accept(const ConvUpdateArgs& a, const int32_t* accept_len, Dt act, hipStream_t s);
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);
 hipError_t launch_chunk_scan_mfma(const ScanArgs& a, Dt ydt, hipStream_t s);

@@ -156,9 +156,8 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
             part = fmaf(v[e], cv[e], part);
         }
         if (!ok) part = 0.f;
-#pragma unroll
-        for (int off = OPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (ok && q == 0) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+        part = group_sum_last<OPR>(part);
+        if (ok && q == OPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
         if (so[i] >= 0) {
             uint32_t rw[4];
             if constexpr (SR) {

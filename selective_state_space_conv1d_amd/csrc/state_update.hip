@@ -11,7 +11,7 @@
 // this step.  (Measured on MI355X at batch 64: 4 x 128 threads reaches ~98% of
 // an in-place read+write of the same buffer; 8 or 16 in flight per thread, or
 // cached accesses, are slower.)  One state row p (N floats) spans N/4 consecutive lanes; the
-// output y[p] is a butterfly reduction over those lanes.  No MFMA: the
+// output y[p] is a DPP reduction over those lanes.  No MFMA: the
 // arithmetic is 2 FMAs per 4-byte element.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
@@ -103,10 +103,9 @@ __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
             part = fmaf(v[k], cv[k], part);
         }
         if (!ok) part = 0.f;
-#pragma unroll
-        for (int off = QPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        part = group_sum_last<QPR>(part);   // the row's QPR lanes are consecutive and aligned
         if (ok) {
-            if (q == 0) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+            if (q == QPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
             if (!SLOTS || sf[i] >= 0) __builtin_nontemporal_store(v, st4 + sf[i]);
         }
     }

@@ -23,7 +23,8 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan", "ssd_state_update", "ssd_status_string", "ssd_conv1d_fwd_varlen",
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
-           "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step"]
+           "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
+           "ssd_conv1d_update_accept"]
 
 
 class SsdDims(ctypes.Structure):
@@ -83,6 +84,9 @@ def _lib():
                                                _PDT, _VP, _VP, _VP]
         lib.ssd_conv1d_update_multi.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]
         lib.ssd_accept_states.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
+        lib.ssd_state_update_accept.argtypes = [_PD, _VP, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
+                                                _PDT, _VP, _VP]
+        lib.ssd_conv1d_update_accept.argtypes = [_PD, _VP, _I64, _VP, _VP, _I64, _VP, _VP]
         lib.ssd_decode_step.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _PDT, _VP, _VP]
         lib.ssd_gated_rmsnorm.argtypes = [_PD, _VP, _I64, _VP, _I64, _VP, ctypes.c_float, _VP, _VP]
         lib.ssd_chunk_scan_snapshots.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
@@ -93,7 +97,7 @@ def _lib():
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
                   "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
-                  "ssd_decode_step"):
+                  "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -625,6 +629,51 @@ def ssd_gated_rmsnorm(y, z, weight, ngroups, eps=1e-5, out=None, stream=None):
                                     z2.stride(0) if rows else I, _ptr(weight), float(eps), _ptr(out),
                                     _stream(stream)), "ssd_gated_rmsnorm")
     return out
+
+
+def ssd_state_update_accept(state, x, B, C, dt, A, D, accept_len, slot_idx=None, stream=None, dt_bias=None,
+                            dt_softplus=False, dt_limit=None):
+    """Accept step by recomputation: apply each request's first accept_len[b] (clamped to [0, k])
+    candidate tokens to state [B or nslots, H, P, N] fp32 in place.  x, B, C, dt as given to
+    ssd_state_update_multi ([B, k, ...])."""
+    Bt, k, H, P = x.shape
+    N = state.shape[3]
+    G = B.shape[2]
+    if state.dim() != 4 or state.shape[1:] != (H, P, N) or not state.is_contiguous():
+        raise ValueError("state must be contiguous [B or nslots, H, P, N]")
+    if k > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, k)):
+        raise ValueError("x must be [B, k, H, P] with packed (H, P) and uniform token stride")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, k, G, N) or (k > 0 and (t.stride(3) != 1 or t.stride(2) != N
+                                                    or not _uniform_rows(t, k))):
+            raise ValueError(f"{nm} must be [B, k, G, N] with packed (G, N) and uniform token stride")
+    if dt.shape != (Bt, k, H) or not dt.is_contiguous():
+        raise ValueError("dt must be contiguous [B, k, H]")
+    st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
+    d = _dims(Bt, k, H, P, G, N, x.dtype, x.dtype)
+    xs, bcs = (P * H, G * N) if k == 0 else (x.stride(1), B.stride(1))
+    _check(_lib().ssd_state_update_accept(ctypes.byref(d), _ptr(st), _ptr(tab), nslots, _ptr(x), xs, _ptr(B), _ptr(C),
+                                          bcs, _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                          _ptr(_table(accept_len, Bt, "accept_len")), _stream(stream)),
+           "ssd_state_update_accept")
+
+
+def ssd_conv1d_update_accept(xbc, conv_state, accept_len, slot_idx=None, nheads=None, head_dim=None, ngroups=None,
+                             d_state=None, stream=None):
+    """Accept step by recomputation for the conv windows: request b's window in conv_state
+    [B or nslots, CD, 4] becomes the last 4 of (its old window, rows 0 .. n-1 of xbc [B, k, CD]),
+    n = accept_len[b] clamped to [0, k]."""
+    Bt, k, CD = xbc.shape
+    if k > 0 and (xbc.stride(2) != 1 or not _uniform_rows(xbc, k)):
+        raise ValueError("xbc must be [B, k, CD] with packed channels and uniform token stride")
+    if conv_state.dim() != 3 or conv_state.shape[1:] != (CD, 4) or not conv_state.is_contiguous():
+        raise ValueError("conv_state must be contiguous [B or nslots, CD, 4]")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    st, nslots, tab = _state_pool_args(conv_state, slot_idx, Bt)
+    d = _dims(Bt, k, H, P, G, N, xbc.dtype, xbc.dtype)
+    _check(_lib().ssd_conv1d_update_accept(ctypes.byref(d), _ptr(xbc), CD if k == 0 else xbc.stride(1), _ptr(st),
+                                           _ptr(tab), nslots, _ptr(_table(accept_len, Bt, "accept_len")),
+                                           _stream(stream)), "ssd_conv1d_update_accept")
 
 
 def split_xbc(v, nheads, head_dim, ngroups, d_state):

@@ -303,6 +303,32 @@ def test_decode_step_validation(ssd, lib):
     assert step(dims(ssd, batch=2, seqlen=1, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
 
 
+def test_accept_by_recomputation_validation(ssd, lib):
+    """The recomputing accept calls reject bad host arguments before any launch, and launch nothing
+    when there is nothing to apply."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=3)
+
+    def sacc(dd=d, state=fp(1), slot=None, nslots=0, alen=fp(9), B=fp(3), bcs=256):
+        return lib.ssd_state_update_accept(ctypes.byref(dd), state, slot, nslots, fp(2), 256, B, fp(4), bcs, fp(5),
+                                           fp(6), None, None, alen, None)
+    assert sacc(alen=None) == E["SSD_ERR_NULL"]
+    assert sacc(state=None) == E["SSD_ERR_NULL"]
+    assert sacc(nslots=-1) == E["SSD_ERR_SHAPE"]
+    assert sacc(B=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert sacc(bcs=260) == E["SSD_ERR_ALIGN"]
+    assert sacc(dims(ssd, batch=2, seqlen=0), alen=None, state=None) == E["SSD_OK"]
+    assert sacc(slot=fp(8), nslots=0, alen=None, state=None) == E["SSD_OK"]
+
+    def cacc(dd=d, xbc=fp(1), xs=768, cs=fp(2), alen=fp(9)):
+        return lib.ssd_conv1d_update_accept(ctypes.byref(dd), xbc, xs, cs, None, 0, alen, None)
+    assert cacc(alen=None) == E["SSD_ERR_NULL"]
+    assert cacc(cs=None) == E["SSD_ERR_NULL"]
+    assert cacc(xs=700) == E["SSD_ERR_SHAPE"]
+    assert cacc(xs=772) == E["SSD_ERR_ALIGN"]
+    assert cacc(dims(ssd, batch=0, seqlen=3), xbc=None, cs=None, alen=None) == E["SSD_OK"]
+
+
 def test_binding_raises_without_library(ssd, monkeypatch):
     monkeypatch.setattr(ssd, "_LIB", None)
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")

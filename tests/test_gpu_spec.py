@@ -227,3 +227,33 @@ def test_scan_snapshots(orc, P, N, dtype, L, iv):
     bar = BF16_BAR if dtype == torch.bfloat16 else F32_BAR
     assert_close(y, yr, bar, "y")
     assert_close(snaps, sr, bar, "snapshots")
+
+
+# --------------------------------------------------------------------------- accept by recomputation
+@pytest.mark.parametrize("use_slots", [False, True])
+@pytest.mark.parametrize("k", [4, 7])
+def test_accept_by_recomputation_is_the_stored_intermediate(use_slots, k):
+    d = LayerDims(6, 1, 8, 64, 2, 128)
+    s = ssm_inputs(d, k, 480)
+    xbc, w, bias, cpool0 = conv_inputs(d, k, 9 if use_slots else 6, 481)
+    if use_slots:
+        spool0 = torch.randn(9, 8, 64, 128, device=DEV) * 0.1
+        slots = [7, 2, -1, 0, 5, 8]
+        slot = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    else:
+        spool0, slots, slot = s["init_state"], list(range(6)), None
+    acc = torch.tensor([2, 0, 3, k, 9, 1], dtype=torch.int32, device=DEV)    # 9 > k clamps to k
+    # y with and without intermediate states: identical (the y reductions run in token blocks)
+    y1, inter = ssd.ssd_state_update_multi(spool0, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], slot_idx=slot)
+    y2, none = ssd.ssd_state_update_multi(spool0, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], slot_idx=slot,
+                                          inter_states=None)
+    _, cinter = ssd.ssd_conv1d_update_multi(xbc, w, bias, cpool0, slot_idx=slot)
+    sp_copy, cp_copy = spool0.clone(), cpool0.clone()
+    ssd.ssd_accept_states(acc, sp_copy, inter, cp_copy, cinter, slot_idx=slot)
+    sp_re, cp_re = spool0.clone(), cpool0.clone()
+    ssd.ssd_state_update_accept(sp_re, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], acc, slot_idx=slot)
+    ssd.ssd_conv1d_update_accept(xbc, cp_re, acc, slot_idx=slot)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(y1, y2)
+    assert torch.equal(sp_re, sp_copy), "recomputed states must equal the stored intermediate ones"
+    assert torch.equal(cp_re, cp_copy), "recomputed conv windows must equal the stored ones"
