@@ -157,6 +157,7 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
  *  y            [B, L, H, P] contiguous, y dtype.
  *  workspace    may be NULL when ssd_chunk_scan_workspace_size() is 0.
  * Row strides are in elements: >= the row's extent, multiples of 8 (bf16) or 4 (fp32).
+ * B and L above 2^31 - 1 are rejected (SSD_ERR_SHAPE).
  */
 ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
                             const void* x, int64_t x_row_stride,
@@ -245,7 +246,10 @@ ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t
  *  state_pool    [nslots, H, P, N] fp32, updated in place: the initial state is read as
  *                has_initial_state says, and the final state is written to every sequence's slot.
  *  y             [T, H, P] contiguous y dtype.
- * chunk, A, D, dt_params and workspace as for ssd_chunk_scan.
+ * chunk, A, D, dt_params and workspace as for ssd_chunk_scan; S and T above 2^31 - 1 are
+ * rejected (SSD_ERR_SHAPE).  When sequences x heads exceed what the device holds at once,
+ * one workgroup scans a range of consecutive sequences (balanced by tokens): sequence
+ * states must then sit in distinct slots, as for any in-place pool update.
  */
 ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                    const void* B, const void* C, int64_t bc_row_stride, const void* dt,

@@ -57,6 +57,8 @@
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
+#include <atomic>
+
 namespace ssd {
 namespace scan32 {
 
@@ -224,15 +226,69 @@ __device__ __forceinline__ void build_vec(Vec& v, bf16 r0, bf16 r1, float A2, in
     if (lane == 0) v.dec = fexp2(csl);
 }
 
+// A position in the chunk sequence a workgroup walks: chunk c of sequence s, whose rows are
+// [row0, row0 + L); ok is false past the last chunk.
+struct Cursor {
+    int64_t row0;
+    int s, c, L;
+    bool ok;
+    __device__ __forceinline__ int valid() const {
+        const int r = L - c * Q;
+        return r < Q ? r : Q;
+    }
+    __device__ __forceinline__ int64_t first_row() const { return row0 + static_cast<int64_t>(c) * Q; }
+};
+
+// A workgroup scans head h of sequences [s_begin, s_end) one after another (WALK), so that a
+// sequence's first chunk is loaded while the previous one's last chunk is computed, or of
+// sequence s_begin alone.
+template <bool WALK>
 struct Ctx {
     const bf16* xg; const bf16* Bg; const bf16* Cg; const bf16* dtg;
-    int64_t xs, bcs, b, L, row0, nchunks;
-    int64_t sidx;                 // state index (batch entry, or the sequence's pool slot)
-    bool use_init, write_final;   // read the initial state / write the final state
+    int64_t xs, bcs, seqlen;
+    int s_begin, s_end;
+    const SeqMap* seq;            // packed sequences (cu_seqlens set), else batch entries of seqlen rows
     int H, h, grp;
-    __device__ __forceinline__ int valid(int64_t c) const {
-        const int64_t r = L - c * Q;
-        return static_cast<int>(r < Q ? r : Q);
+    __device__ __forceinline__ void span(int64_t s, int64_t& row0, int64_t& L) const {
+        if (seq->cu_seqlens) seq_span(seq->cu_seqlens, s, seqlen, row0, L);
+        else { row0 = s * seqlen; L = seqlen; }
+    }
+    // state index of sequence s (-1: padding, nothing stored) and whether it starts from it
+    __device__ __forceinline__ int64_t slot(int64_t s) const {
+        return seq->cu_seqlens ? seq_slot(seq->slot_idx, s, seq->nslots) : s;
+    }
+    __device__ __forceinline__ bool use_init(int64_t s) const {
+        return seq->cu_seqlens ? (slot(s) >= 0 && seq->has_init && seq->has_init[s] != 0) : true;
+    }
+    // the first chunk of sequence s or of the next non-empty one
+    __device__ __forceinline__ Cursor at(int s) const {
+        Cursor u{0, s, 0, 0, false};
+        if (!WALK) {
+            if (s < s_end) {
+                int64_t L;
+                span(s, u.row0, L);
+                u.L = static_cast<int>(L);
+                u.ok = u.L > 0;
+            }
+            return u;
+        }
+        for (; u.s < s_end; ++u.s) {
+            int64_t L;
+            span(u.s, u.row0, L);
+            u.L = static_cast<int>(L);
+            if (u.L > 0) { u.ok = true; break; }
+        }
+        return u;
+    }
+    __device__ __forceinline__ Cursor first() const { return at(s_begin); }
+    __device__ __forceinline__ Cursor next(const Cursor& u) const {
+        Cursor n = u;
+        ++n.c;
+        if (!WALK || n.c * Q < u.L) {
+            n.ok = n.c * Q < u.L;
+            return n;
+        }
+        return at(u.s + 1);
     }
 };
 
@@ -284,8 +340,8 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 // ---------------------------------------------------------------------------
 // y wave: token tile IT (tokens 32IT .. 32IT+31 of each chunk), both p tiles.
-template <typename TY, int IT>
-__device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+template <typename TY, int IT, class CX>
+__device__ void run_y(Smem& sm, const ScanArgs& a, const CX& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int i = 32 * IT + c32;                     // this lane's token within the chunk
     const float Dh = a.D ? a.D[cx.h] : 0.f;
@@ -299,23 +355,33 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     // B operand (column i) of both H C^T and B C^T; loaded straight into registers (an
     // LDS copy would make the compiler wait for it before every later transpose read).
     // Rows past the end re-read the last real row.
-    auto c_load = [&](bf16x8 (&cr)[8], int64_t c, int k0, int k1) {
-        const int valid = cx.valid(c);
+    auto c_load = [&](bf16x8 (&cr)[8], const Cursor& u, int k0, int k1) {
+        const int valid = u.valid();
         const int r = i < valid ? i : valid - 1;
-        const bf16* p = csrc + (cx.row0 + c * Q + r) * cx.bcs + 8 * hf;
+        const bf16* p = csrc + (u.first_row() + r) * cx.bcs + 8 * hf;
 #pragma unroll
         for (int ks = k0; ks < k1; ++ks) cr[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
     };
 
     bf16x8 cn[8];
-    if (cx.nchunks > 0) c_load(cn, 0, 0, 8);
+    Cursor cur = cx.first();
+    if (cur.ok) c_load(cn, cur, 0, 8);
     __syncthreads();                                            // chunk 0
 
-    for (int64_t c = 0; c < cx.nchunks; ++c) {
-        const int64_t t0 = c * Q;
-        const int valid = cx.valid(c);
-        const bool has_next = c + 1 < cx.nchunks;
-        const int buf = static_cast<int>(c & 1);
+    for (int64_t gc = 0; cur.ok; ++gc) {
+        const Cursor nx = cx.next(cur);
+        const int valid = cur.valid();
+        const bool has_next = nx.ok;
+        const int buf = static_cast<int>(gc & 1);
+        if constexpr (IT > 0) {
+            if (32 * IT >= valid) {     // none of this wave's tokens is in the chunk: nothing to compute
+                if (lane == 0) __hip_atomic_fetch_add(&sm.hread, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (has_next) c_load(cn, nx, 0, 8);
+                __syncthreads();                                // chunk c + 1
+                cur = nx;
+                continue;
+            }
+        }
         const Vec& v = sm.vec[buf];
         const unsigned char* Bt = sm.B[buf];
         const unsigned char* Xt = sm.X[buf];
@@ -354,7 +420,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         // counter update lands after this wave's state reads (no fence, which would also
         // wait for the C copy in flight)
         if (lane == 0) __hip_atomic_fetch_add(&sm.hread, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (has_next) c_load(cn, c + 1, 0, 4);
+        if (has_next) c_load(cn, nx, 0, 4);
         const float ey = v.eY[i];
         y0 *= ey;
         y1 *= ey;
@@ -410,22 +476,20 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 y0 = mfma32(x0, ml, y0);
                 y1 = mfma32(x1, ml, y1);
             }
-            if (jt == 0 && has_next) c_load(cn, c + 1, 4, 8);
+            if (jt == 0 && has_next) c_load(cn, nx, 4, 8);
         }
         if constexpr (IT == 0) {
             // the lightest y wave copies the upper half of the next chunk's B tile (L2-resident:
             // the group's heads share it), after its last transpose read of the chunk
-            if (has_next) {
-                const int64_t r0 = cx.row0 + (c + 1) * Q;
-                dma_rows<kRowB, kYB, 32>(sm.B[buf ^ 1], cx.Bg + static_cast<int64_t>(cx.grp) * NS, cx.bcs, r0, 0,
-                                         cx.valid(c + 1), lane);
-            }
+            if (has_next)
+                dma_rows<kRowB, kYB, 32>(sm.B[buf ^ 1], cx.Bg + static_cast<int64_t>(cx.grp) * NS, cx.bcs,
+                                         nx.first_row(), 0, nx.valid(), lane);
         }
 
         // y[token i][p]: lane (c32, hf) holds p = 32pt + 8j + 4hf + r in y_pt[4j + r].  Swapping
         // j = 1 of the low half-wave with j = 0 of the high half-wave (and j = 3 with j = 2) leaves
         // each lane with p = 32pt + 16g + 8hf + {0..7} (g = 0, 1): two 16-byte pieces per p tile.
-        TY* yrow = yg + ((cx.row0 + t0) * cx.H + cx.h) * static_cast<int64_t>(P);   // token 0, p 0
+        TY* yrow = yg + (cur.first_row() * cx.H + cx.h) * static_cast<int64_t>(P);   // token 0, p 0
         const int64_t ystr = static_cast<int64_t>(cx.H) * P;                         // token stride
         if constexpr (sizeof(TY) == 4) {
             if (i < valid) {
@@ -480,6 +544,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         }
         if constexpr (IT == 0) wait_vmem();
         __syncthreads();                                        // chunk c + 1
+        cur = nx;
     }
 }
 
@@ -488,11 +553,12 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 // Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].
 constexpr int kSpinMax = 1 << 20;
 
-template <int NT, int SP, int SN0>
-__device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+template <int NT, int SP, int SN0, class CX>
+__device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int hp = 32 * SP + c32;
-    const int64_t sbase = (cx.sidx * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    // the state of sequence s lives at slot(s) (nothing read or stored for padding)
+    auto sbase = [&](int64_t sl) { return (sl * cx.H + cx.h) * static_cast<int64_t>(P) * NS; };
     const LaneOff lo(lane);
     const int trW = lo.tr<kRowX>(32 * SP, 0);            // x^T fragments of the p tile
     int trB0[NT], trB8[NT];                              // B^T fragments of the n tiles
@@ -503,16 +569,47 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     }
 
     f32x16 Hs[NT];
+    auto load_init = [&](int64_t s) {   // Hs = the initial state of sequence s (zeros without one)
+        const int64_t sl = cx.slot(s);
+        const bool from = a.init_state && sl >= 0 && cx.use_init(s);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (a.init_state && cx.use_init) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
+            for (int j = 0; j < 4; ++j) {
+                const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (from) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Hs[t][4 * j + r] = v[r];
+                for (int r = 0; r < 4; ++r) Hs[t][4 * j + r] = v[r];
+            }
+    };
+    auto store_final = [&](int64_t s) {   // Hs as the final state of sequence s
+        const int64_t sl = cx.slot(s);
+        if (!a.final_state || sl < 0) return;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
+                *reinterpret_cast<f32x4*>(a.final_state + sbase(sl) + hp * NS + n) =
+                    f32x4{Hs[t][4 * j], Hs[t][4 * j + 1], Hs[t][4 * j + 2], Hs[t][4 * j + 3]};
+            }
+    };
+    // empty sequences in [s0, s1) end with their initial state (zeros without one)
+    auto finish_empty = [&](int s0, int s1) {
+        for (int e = s0; e < s1; ++e) {
+            load_init(e);
+            store_final(e);
         }
+    };
+    Cursor cur = cx.first();
+    finish_empty(cx.s_begin, cur.ok ? cur.s : cx.s_end);
+    if (cur.ok) {
+        load_init(cur.s);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) Hs[t] = zero16();
+    }
     auto write_h = [&]() {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -533,8 +630,9 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     write_h();
     __syncthreads();                                            // chunk 0
 
-    for (int64_t c = 0; c < cx.nchunks; ++c) {
-        const int buf = static_cast<int>(c & 1);
+    for (int64_t gc = 0; cur.ok; ++gc) {
+        const Cursor nx = cx.next(cur);
+        const int buf = static_cast<int>(gc & 1);
         const Vec& v = sm.vec[buf];
         const unsigned char* Bt = sm.B[buf];
         const unsigned char* Xt = sm.X[buf];
@@ -542,10 +640,13 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hs[t] *= dec;
 
-        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B^T[n][j] (w_j x_j)[p]
+        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B^T[n][j] (w_j x_j)[p]; steps
+        // past the chunk's last token would only add zero weights
+        const int valid = cur.valid();
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int j0 = 16 * k;
+            if (k > 0 && j0 >= valid) break;
             const bf16x8 xf = tr_frag<kRowX>(Xt, trW, trW, j0);
             const f32x4 w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
             const f32x4 w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
@@ -561,12 +662,12 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 Hs[t] = mfma32(bt, wl, Hs[t]);
             }
         }
-        // state snapshot after token (c + 1) * Q - 1 when that closes an interval
+        // state snapshot after token (c + 1) * Q - 1 of the sequence when that closes an interval
         if (a.snapshots) {
-            const int64_t t_end = (c + 1) * Q;
-            if (t_end % a.snap_interval == 0 && t_end <= cx.L) {
-                const int64_t nsnap = cx.L / a.snap_interval, k = t_end / a.snap_interval - 1;
-                float* snap = a.snapshots + ((cx.b * nsnap + k) * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+            const int64_t t_end = (cur.c + 1) * Q;
+            if (t_end % a.snap_interval == 0 && t_end <= cur.L) {
+                const int64_t nsnap = cur.L / a.snap_interval, k = t_end / a.snap_interval - 1;
+                float* snap = a.snapshots + ((cur.s * nsnap + k) * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -577,8 +678,15 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                     }
             }
         }
+        // the sequence's last chunk: its final state, those of the empty sequences after it, and
+        // the next sequence's initial state, which the y waves then use as the carried state
+        if (!nx.ok || nx.s != cur.s) {
+            store_final(cur.s);
+            finish_empty(cur.s + 1, nx.ok ? nx.s : cx.s_end);
+            if (nx.ok) load_init(nx.s);
+        }
         // the y waves must have read the previous state before it is overwritten
-        const int target = 4 * static_cast<int>(c + 1);
+        const int target = 4 * static_cast<int>(gc + 1);
         for (int n = 0; n < kSpinMax; ++n) {
             if (__hip_atomic_load(&sm.hread, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
             __builtin_amdgcn_s_sleep(1);
@@ -586,67 +694,83 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the state writes stay after the wait
         write_h();
         __syncthreads();                                        // chunk c + 1
-    }
-
-    if (a.final_state && cx.write_final) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
-                *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
-                    f32x4{Hs[t][4 * j], Hs[t][4 * j + 1], Hs[t][4 * j + 2], Hs[t][4 * j + 3]};
-            }
+        cur = nx;
     }
 }
 
 // ---------------------------------------------------------------------------
 // loader wave: the next chunk's x tile and the lower half of its B tile, and its
 // per-token vectors.
-__device__ void run_l(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+template <class CX>
+__device__ void run_l(Smem& sm, const ScanArgs& a, const CX& cx, const int lane) {
     const float A2 = a.A[cx.h] * kLog2e;
     const bf16* bsrc = cx.Bg + static_cast<int64_t>(cx.grp) * NS;
     const bf16* xsrc = cx.xg + static_cast<int64_t>(cx.h) * P;
-    auto load_dt = [&](bf16& d0, bf16& d1, int64_t t0, int valid) {
-        const int r0 = 2 * lane < valid ? 2 * lane : valid - 1;
-        const int r1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
-        d0 = cx.dtg[(cx.row0 + t0 + r0) * cx.H + cx.h];
-        d1 = cx.dtg[(cx.row0 + t0 + r1) * cx.H + cx.h];
+    auto load_dt = [&](bf16& d0, bf16& d1, int64_t r0, int valid) {   // rows r0 .. r0 + valid - 1
+        const int q0 = 2 * lane < valid ? 2 * lane : valid - 1;
+        const int q1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
+        d0 = cx.dtg[(r0 + q0) * cx.H + cx.h];
+        d1 = cx.dtg[(r0 + q1) * cx.H + cx.h];
     };
     if (lane == 0) sm.hread = 0;
-    if (cx.nchunks > 0) {
+    Cursor cur = cx.first();
+    if (cur.ok) {
         bf16 d0, d1;
-        const int v0 = cx.valid(0);
-        load_dt(d0, d1, 0, v0);
-        dma_rows<kRowX, 0, 16>(sm.X[0], xsrc, cx.xs, cx.row0, 0, v0, lane);
-        dma_rows<kRowB, 0, 32>(sm.B[0], bsrc, cx.bcs, cx.row0, 0, v0, lane);
+        const int v0 = cur.valid();
+        const int64_t r0 = cur.first_row();
+        load_dt(d0, d1, r0, v0);
+        dma_rows<kRowX, 0, 16>(sm.X[0], xsrc, cx.xs, r0, 0, v0, lane);
+        dma_rows<kRowB, 0, 32>(sm.B[0], bsrc, cx.bcs, r0, 0, v0, lane);
         build_vec(sm.vec[0], d0, d1, A2, v0, lane, a.dtp, cx.h);
     }
     wait_vmem();
     __syncthreads();                                            // chunk 0
 
-    for (int64_t c = 0; c < cx.nchunks; ++c) {
-        const int buf = static_cast<int>(c & 1);
-        if (c + 1 < cx.nchunks) {
-            const int64_t r0 = cx.row0 + (c + 1) * Q;
-            const int vn = cx.valid(c + 1);
+    for (int64_t gc = 0; cur.ok; ++gc) {
+        const Cursor nx = cx.next(cur);
+        const int buf = static_cast<int>(gc & 1);
+        if (nx.ok) {
+            const int64_t r0 = nx.first_row();
+            const int vn = nx.valid();
             bf16 d0, d1;
-            load_dt(d0, d1, (c + 1) * Q, vn);
+            load_dt(d0, d1, r0, vn);
             dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
             dma_rows<kRowB, 0, kYB>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
             build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane, a.dtp, cx.h);
         }
         wait_vmem();
         __syncthreads();                                        // chunk c + 1
+        cur = nx;
     }
 }
 
-template <typename TY>
+// First sequence of range r of a.nranges: sequences split evenly for a batch of equal
+// sequences; for packed ones, the first sequence that starts at or after token r T / R (T the
+// packed rows), so that ranges hold about equal token counts.  Range 0 starts at 0 and range R
+// at the end; with a non-decreasing cu_seqlens the ranges partition the sequences.
+__device__ int64_t range_start(const ScanArgs& a, int64_t r) {
+    const int64_t S = a.batch, R = a.nranges;
+    if (r <= 0) return 0;
+    if (r >= R) return S;
+    if (!a.seq.cu_seqlens) return S * r / R;
+    const int64_t t = (a.seqlen * r + R - 1) / R;
+    int64_t lo = 0, hi = S;
+    while (lo < hi) {
+        const int64_t m = (lo + hi) / 2;
+        int64_t v = a.seq.cu_seqlens[m];
+        v = v < 0 ? 0 : (v > a.seqlen ? a.seqlen : v);
+        if (v >= t) hi = m;
+        else lo = m + 1;
+    }
+    return lo;
+}
+
+template <typename TY, bool WALK>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     // XCD-aware numbering: workgroup id % 8 picks the XCD.  XCD k takes heads
-    // [k H/8, (k+1) H/8) of every batch entry / sequence: heads of one group share B
+    // [k H/8, (k+1) H/8) of every batch entry / sequence range: heads of one group share B
     // and C in that XCD's L2, and every XCD gets an equal share of each sequence
     // (packed batches mix short and long ones).
     int64_t id = blockIdx.x;
@@ -654,28 +778,25 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
         const int64_t hpx = a.nheads / 8, j = id / 8;
         id = (j / hpx) * a.nheads + (id % 8) * hpx + j % hpx;
     }
-    Ctx cx;
+    Ctx<WALK> cx;
     cx.xg = static_cast<const bf16*>(a.x);
     cx.Bg = static_cast<const bf16*>(a.B);
     cx.Cg = static_cast<const bf16*>(a.C);
     cx.dtg = static_cast<const bf16*>(a.dt);
     cx.xs = a.x_row_stride;
     cx.bcs = a.bc_row_stride;
-    cx.b = id / a.nheads;
+    const int64_t r = id / a.nheads;
     cx.h = static_cast<int>(id % a.nheads);
-    if (a.seq.cu_seqlens) {   // packed sequences: rows and state slot from the caller's tables
-        seq_span(a.seq.cu_seqlens, cx.b, a.seqlen, cx.row0, cx.L);
-        const int64_t slot = seq_slot(a.seq.slot_idx, cx.b, a.seq.nslots);
-        cx.sidx = slot < 0 ? 0 : slot;
-        cx.use_init = slot >= 0 && a.seq.has_init && a.seq.has_init[cx.b] != 0;
-        cx.write_final = slot >= 0;
+    cx.seq = &a.seq;
+    cx.seqlen = a.seqlen;
+    if (!WALK) {                             // one sequence per workgroup
+        cx.s_begin = static_cast<int>(r);
+        cx.s_end = static_cast<int>(r + 1);
     } else {
-        cx.L = a.seqlen;
-        cx.row0 = cx.b * a.seqlen;
-        cx.sidx = cx.b;
-        cx.use_init = cx.write_final = true;
+        const int64_t b = range_start(a, r), e = range_start(a, r + 1);
+        cx.s_begin = static_cast<int>(b);
+        cx.s_end = static_cast<int>(e > b ? e : b);
     }
-    cx.nchunks = (cx.L + Q - 1) / Q;
     cx.H = a.nheads;
     cx.grp = cx.h / (a.nheads / a.ngroups);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -697,11 +818,42 @@ bool mfma_scan_supports(int head_dim, int d_state, int chunk) {
     return head_dim == scan32::P && d_state == scan32::NS && chunk == scan32::Q;
 }
 
+// Workgroups resident per CU times this: the sequence ranges per head are chosen so that one
+// launch has about this many rounds of workgroups.
+#ifndef SSD_SCAN_RANGE_ROUNDS
+#define SSD_SCAN_RANGE_ROUNDS 1
+#endif
+
+// Compute units of the current device (cached per device).
+static int64_t device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <typename TY>
-static hipError_t mfma_t(const ScanArgs& a, hipStream_t s) {
-    const int64_t blocks = a.batch * a.nheads;
-    if (blocks == 0) return hipSuccess;
-    auto kern = scan32::chunk_scan_kernel<TY>;
+static hipError_t mfma_t(const ScanArgs& args, hipStream_t s) {
+    if (args.batch * args.nheads == 0) return hipSuccess;
+    // One workgroup per (sequence, head) while that fills the chip, or while sequences average
+    // more than kWalkChunks chunks (the walking kernel's per-chunk cost is a little higher);
+    // past that, each workgroup walks a range of sequences (one CU holds one workgroup), so that
+    // a sequence's first chunk is fetched while the previous one's last chunk is computed.
+    constexpr int64_t kWalkChunks = 8;
+    ScanArgs a = args;
+    const int64_t want = (SSD_SCAN_RANGE_ROUNDS * device_cus() + a.nheads - 1) / a.nheads;
+    const int64_t rows = a.seq.cu_seqlens ? a.seqlen : a.batch * a.seqlen;   // all sequences' rows
+    const bool walk = a.batch > want && rows <= kWalkChunks * scan32::Q * a.batch;
+    a.nranges = walk ? want : a.batch;
+    const int64_t blocks = a.nranges * a.nheads;
+    auto kern = a.nranges < a.batch ? scan32::chunk_scan_kernel<TY, true> : scan32::chunk_scan_kernel<TY, false>;
     const size_t smem = sizeof(scan32::Smem);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));

@@ -156,6 +156,7 @@ static ssd_status_t chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x
                                size_t workspace_bytes, hipStream_t stream) {
     ssd_status_t st = check_dims(d, true);
     if (st != SSD_OK) return st;
+    if (d->batch > INT32_MAX || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
     if (tokens && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
     if (chunk != 64 && chunk != 128 && chunk != 256) return SSD_ERR_UNSUPPORTED;
@@ -214,6 +215,7 @@ ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const voi
     if (st != SSD_OK) return st;
     st = check_seq_tables(d, cu_seqlens, state_pool, nslots);
     if (st != SSD_OK) return st;
+    if (d->batch > INT32_MAX || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
     if (tokens && (!x || !B || !C || !dt || !A || !y)) return SSD_ERR_NULL;
     if (chunk != 64 && chunk != 128 && chunk != 256) return SSD_ERR_UNSUPPORTED;

@@ -59,6 +59,7 @@ struct ScanArgs {
     DtParams dtp;
     float* snapshots;        // [B, L / snap_interval, H, P, N]: state after every snap_interval tokens, or NULL
     int64_t snap_interval;   // a positive multiple of 128 when snapshots is set
+    int64_t nranges;         // set by the launcher: sequence ranges per head (workgroups = nranges * nheads)
 };
 
 struct UpdateArgs {
