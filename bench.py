@@ -7,7 +7,8 @@ One step = one pass of the whole hot path on synthetic Ultra-shaped layers:
   decode   batch 64, one token: ssd_conv1d_update, then ssd_state_update in place
            on the (64, 256, 64, 128) fp32 state.
 All inputs are resident in HBM before timing.  Every kernel launch is bracketed
-by HIP events on the launch stream; averages per kernel feed the roofline.
+by HIP events on the launch stream; averages per kernel feed the roofline.  The default
+warmup (50 steps) lets the GPU's clocks settle before the timed steps.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -387,8 +388,10 @@ def cpu_baseline(orc, inp, d, n_heads=256):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=40)
+    # the GPU's clocks settle after about 25 steps (15 ms) of this loop: the latency-bound scan
+    # runs about 20 % slower before that
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
