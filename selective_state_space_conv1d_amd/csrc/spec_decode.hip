@@ -14,6 +14,8 @@
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
+#include <type_traits>
+
 namespace ssd {
 
 constexpr int kMultiThreads = 128;
@@ -33,13 +35,12 @@ struct TokIn {
     typename Quad<T>::type b, c;
 };
 
-constexpr int kTokBlock = 1;   // tokens per y-reduction block (2 or 4 raise VGPRs to 100+ and run 15-30 % slower)
-
 // Grid: one thread per kMultiPerThread float4 of the [B, H, P, N] state, 128-thread strides.
 // Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.  The
 // per-head constants are read once; each token's inputs for all of a thread's elements are
 // loaded one token ahead of their use.  Each row's y dot product is a DPP reduction over its
-// lanes (no LDS round trip), kTokBlock tokens at a time.
+// lanes (no LDS round trip), one token at a time (reducing 2 or 4 tokens together raised VGPRs to
+// 100+ and ran 15-30 % slower).
 // REPLAY (the accept step by recomputation): request b applies its first
 // n = clamp(accept_len[b], 0, k) tokens and writes the state back in place; no y, no inter.
 template <typename T, typename TY, int N, bool REPLAY>
@@ -52,125 +53,125 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     constexpr int QPR = N / 4;  // float4 per state row
     typedef typename Quad<T>::type Q;
     const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
+    const int lp = __builtin_ctz(static_cast<unsigned>(P));   // head_dim is a power of two
     f32x4* st4 = reinterpret_cast<f32x4*>(state);
     f32x4* in4 = reinterpret_cast<f32x4*>(inter);
     const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread);
     const int64_t base = f0 + threadIdx.x;
-    // The block's elements almost always lie in one request: then its index and slot are looked
-    // up once for the block, so no state load waits on a per-thread table read.
-    const int64_t fl = (f0 + kMultiThreads * kMultiPerThread < total4 ? f0 + kMultiThreads * kMultiPerThread
-                                                                       : total4) - 1;
-    const int64_t ub = f0 / per_b;
-    const bool uni = ub == fl / per_b;
-    const int64_t uslot = uni ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
     auto tokens_of = [&](int64_t b) {   // tokens to apply: k, or the accepted count when replaying
         if constexpr (!REPLAY) return k;
         const int n = accept_len[b];
         return n < 0 ? 0 : (n > k ? k : n);
     };
-    int kmax = uni ? tokens_of(ub) : k;
-    if (REPLAY && uni && (kmax == 0 || uslot < 0)) return;   // nothing accepted, or padding
+    // The block's elements almost always lie in one request (UNI): its index, slot and token
+    // count are then block constants, held in scalar registers, and every token's row addresses
+    // are scalar too.  Otherwise each element finds its request with a 64-bit division.
+    const int64_t ub = f0 / per_b;
+    const int64_t r0 = f0 - ub * per_b;
+    const int64_t span = total4 - f0 < kMultiThreads * kMultiPerThread ? total4 - f0 : kMultiThreads * kMultiPerThread;
+    auto body = [&](auto uni_tag) {
+        constexpr bool UNI = decltype(uni_tag)::value;
+        const int64_t uslot = UNI ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
+        const int kmax = UNI ? tokens_of(ub) : k;
+        if (REPLAY && UNI && (kmax == 0 || uslot < 0)) return;   // nothing accepted, or padding
 
-    // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g,
-    // the head's A, D and dt bias, its slot and its token count
-    f32x4 s[kMultiPerThread];
-    int64_t bb[kMultiPerThread], rem[kMultiPerThread], sl[kMultiPerThread];
-    int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
-    int nk[kMultiPerThread];
-    float Ah[kMultiPerThread], Dh[kMultiPerThread], biash[kMultiPerThread];
-#pragma unroll
-    for (int i = 0; i < kMultiPerThread; ++i) {
-        const int64_t f = base + i * kMultiThreads;
-        const int64_t ff = f < total4 ? f : 0;
-        bb[i] = uni ? ub : ff / per_b;
-        rem[i] = ff - bb[i] * per_b;
-        rw[i] = static_cast<int>(rem[i] / QPR);
-        qq[i] = static_cast<int>(rem[i] - static_cast<int64_t>(rw[i]) * QPR);
-        hh[i] = rw[i] / P;
-        pp[i] = rw[i] - hh[i] * P;
-        gg[i] = hh[i] / hpg;
-        sl[i] = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
-        nk[i] = f < total4 ? (uni ? kmax : tokens_of(bb[i])) : 0;
-        s[i] = (f < total4 && sl[i] >= 0 && nk[i] > 0) ? __builtin_nontemporal_load(st4 + sl[i] * per_b + rem[i])
-                                                       : f32x4{0.f, 0.f, 0.f, 0.f};
-        Ah[i] = A[hh[i]];
-        Dh[i] = D ? D[hh[i]] : 0.f;
-        biash[i] = dtp.bias ? dtp.bias[hh[i]] : 0.f;
-    }
-    auto load_tok = [&](int j, TokIn<T> (&in)[kMultiPerThread]) {
+        // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g,
+        // the head's A, D and dt bias, its slot and its token count
+        f32x4 s[kMultiPerThread];
+        int64_t bb[kMultiPerThread], rem[kMultiPerThread], sl[kMultiPerThread];
+        int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
+        int nk[kMultiPerThread];
+        bool live[kMultiPerThread];
+        float Ah[kMultiPerThread], Dh[kMultiPerThread], biash[kMultiPerThread];
 #pragma unroll
         for (int i = 0; i < kMultiPerThread; ++i) {
-            const int64_t tok = bb[i] * k + (j < nk[i] ? j : 0);   // rows past a request's count: its first
-            in[i].dt = dt[tok * H + hh[i]];
-            in[i].x = x[tok * xs + static_cast<int64_t>(hh[i]) * P + pp[i]];
-            const int64_t bo = tok * bcs + static_cast<int64_t>(gg[i]) * N + 4 * qq[i];
-            in[i].b = *reinterpret_cast<const Q*>(Bm + bo);
-            in[i].c = *reinterpret_cast<const Q*>(Cm + bo);
-        }
-    };
-    TokIn<T> cur[kMultiPerThread], nxt[kMultiPerThread];
-    load_tok(0, cur);
-    for (int j0 = 0; j0 < kmax; j0 += kTokBlock) {
-        float part[kMultiPerThread][kTokBlock], xk[kMultiPerThread][kTokBlock];
-#pragma unroll
-        for (int jj = 0; jj < kTokBlock; ++jj) {
-            const int j = j0 + jj;
-            if (j < kmax) {   // uniform
-                if (j + 1 < kmax) load_tok(j + 1, nxt);
-#pragma unroll
-                for (int i = 0; i < kMultiPerThread; ++i) {
-                    // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
-                    float dtv = static_cast<float>(cur[i].dt);
-                    if (dtp.bias) dtv += biash[i];
-                    if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
-                    if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
-                    const float a = __expf(dtv * Ah[i]);
-                    const float xv = static_cast<float>(cur[i].x);
-                    const float dx = dtv * xv;
-                    f32x4 v = s[i];
-                    float pt = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[e] = fmaf(a, v[e], dx * static_cast<float>(cur[i].b[e]));
-                        pt = fmaf(v[e], static_cast<float>(cur[i].c[e]), pt);
-                    }
-                    if (j < nk[i]) s[i] = v;
-                    part[i][jj] = (base + i * kMultiThreads < total4) ? pt : 0.f;
-                    xk[i][jj] = xv;
-                    if constexpr (!REPLAY) {
-                        if (inter && base + i * kMultiThreads < total4)
-                            in4[(bb[i] * k + j) * per_b + rem[i]] = v;   // plain stores measured faster here
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < kMultiPerThread; ++i) cur[i] = nxt[i];
+            const int64_t f = base + i * kMultiThreads;
+            live[i] = f < total4;
+            if constexpr (UNI) {
+                bb[i] = ub;
+                rem[i] = live[i] ? r0 + threadIdx.x + i * kMultiThreads : 0;
+                sl[i] = uslot;
+                nk[i] = live[i] ? kmax : 0;
             } else {
-#pragma unroll
-                for (int i = 0; i < kMultiPerThread; ++i) part[i][jj] = 0.f, xk[i][jj] = 0.f;
+                const int64_t ff = live[i] ? f : 0;
+                bb[i] = ff / per_b;
+                rem[i] = ff - bb[i] * per_b;
+                sl[i] = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
+                nk[i] = live[i] ? tokens_of(bb[i]) : 0;
             }
+            rw[i] = static_cast<int>(static_cast<uint64_t>(rem[i]) / QPR);
+            qq[i] = static_cast<int>(static_cast<uint64_t>(rem[i]) % QPR);
+            hh[i] = rw[i] >> lp;
+            pp[i] = rw[i] & (P - 1);
+            gg[i] = static_cast<int>(static_cast<unsigned>(hh[i]) / static_cast<unsigned>(hpg));
+            s[i] = (live[i] && sl[i] >= 0 && nk[i] > 0) ? __builtin_nontemporal_load(st4 + sl[i] * per_b + rem[i])
+                                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            Ah[i] = A[hh[i]];
+            Dh[i] = D ? D[hh[i]] : 0.f;
+            biash[i] = dtp.bias ? dtp.bias[hh[i]] : 0.f;
         }
-        if constexpr (!REPLAY) {
+        // token row of element i's request: a block constant when UNI (j < kmax there); rows past a
+        // request's own count read its first
+        auto tok_of = [&](int i, int j) -> int64_t { return UNI ? ub * k + j : bb[i] * k + (j < nk[i] ? j : 0); };
+        auto load_tok = [&](int j, TokIn<T> (&in)[kMultiPerThread]) {
 #pragma unroll
             for (int i = 0; i < kMultiPerThread; ++i) {
+                const int64_t tok = tok_of(i, j);
+                in[i].dt = dt[tok * H + hh[i]];
+                in[i].x = x[tok * xs + rw[i]];
+                const int64_t bo = tok * bcs + static_cast<int64_t>(gg[i]) * N + 4 * qq[i];
+                in[i].b = *reinterpret_cast<const Q*>(Bm + bo);
+                in[i].c = *reinterpret_cast<const Q*>(Cm + bo);
+            }
+        };
+        // token j with its inputs: advance the state, store the intermediate state, reduce and store y
+        auto step = [&](int j, const TokIn<T> (&in)[kMultiPerThread]) {
 #pragma unroll
-                for (int jj = 0; jj < kTokBlock; ++jj) part[i][jj] = group_sum_last<QPR>(part[i][jj]);
-                if (base + i * kMultiThreads >= total4 || qq[i] != QPR - 1) continue;
+            for (int i = 0; i < kMultiPerThread; ++i) {
+                // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
+                float dtv = static_cast<float>(in[i].dt);
+                if (dtp.bias) dtv += biash[i];
+                if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
+                if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
+                const float a = __expf(dtv * Ah[i]);
+                const float xv = static_cast<float>(in[i].x);
+                const float dx = dtv * xv;
+                f32x4 v = s[i];
+                float pt = 0.f;
 #pragma unroll
-                for (int jj = 0; jj < kTokBlock; ++jj) {
-                    const int64_t tok = bb[i] * k + j0 + jj;
-                    if (j0 + jj < kmax)
-                        y[tok * H * static_cast<int64_t>(P) + rw[i]] =
-                            static_cast<TY>(part[i][jj] + (D ? Dh[i] * xk[i][jj] : 0.f));
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = fmaf(a, v[e], dx * static_cast<float>(in[i].b[e]));
+                    pt = fmaf(v[e], static_cast<float>(in[i].c[e]), pt);
+                }
+                if (j < nk[i]) s[i] = v;
+                if constexpr (!REPLAY) {
+                    const int64_t row = (UNI ? ub : bb[i]) * k + j;
+                    if (inter && live[i]) in4[row * per_b + rem[i]] = v;   // plain stores measured faster here
+                    pt = group_sum_last<QPR>(live[i] ? pt : 0.f);
+                    if (live[i] && qq[i] == QPR - 1)
+                        y[row * H * static_cast<int64_t>(P) + rw[i]] = static_cast<TY>(pt + (D ? Dh[i] * xv : 0.f));
                 }
             }
+        };
+        // the inputs of token j + 1 are loaded while token j is computed, into the other of two
+        // register sets (a copy between them would wait for the loads)
+        TokIn<T> ta[kMultiPerThread], tb[kMultiPerThread];
+        load_tok(0, ta);
+        for (int j = 0; j < kmax; j += 2) {
+            load_tok(j + 1 < kmax ? j + 1 : j, tb);   // past the last token: re-reads its rows
+            step(j, ta);
+            if (j + 1 >= kmax) break;
+            load_tok(j + 2 < kmax ? j + 2 : j + 1, ta);
+            step(j + 1, tb);
         }
-    }
-    if constexpr (REPLAY) {
+        if constexpr (REPLAY) {
 #pragma unroll
-        for (int i = 0; i < kMultiPerThread; ++i)
-            if (base + i * kMultiThreads < total4 && sl[i] >= 0 && nk[i] > 0)
-                __builtin_nontemporal_store(s[i], st4 + sl[i] * per_b + rem[i]);
-    }
+            for (int i = 0; i < kMultiPerThread; ++i)
+                if (live[i] && sl[i] >= 0 && nk[i] > 0) __builtin_nontemporal_store(s[i], st4 + sl[i] * per_b + rem[i]);
+        }
+    };
+    if (r0 + span <= per_b) body(std::true_type{});
+    else body(std::false_type{});
 }
 
 template <typename T, typename TY, int N>

@@ -15,6 +15,8 @@
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
+#include <type_traits>
+
 namespace ssd {
 
 constexpr int kLpThreads = 128;
@@ -104,89 +106,105 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp, uint64_t seed, uint64_t offset,
     int rounds) {
     constexpr int OPR = N / 8;  // octets per state row
+    constexpr int kSpan = kLpThreads * kLpPerThread;
     const int64_t per_b = static_cast<int64_t>(H) * P * OPR;
+    const int lp = __builtin_ctz(static_cast<unsigned>(P));   // head_dim is a power of two
     u32x4* st = reinterpret_cast<u32x4*>(state);
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kLpThreads * kLpPerThread);
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kSpan;
     const int64_t base = f0 + threadIdx.x;
-    // the block's octets almost always lie in one batch entry: one slot lookup for the block
-    const int64_t fl = (f0 + kLpThreads * kLpPerThread < total8 ? f0 + kLpThreads * kLpPerThread : total8) - 1;
+    // The block's octets almost always lie in one batch entry (UNI): its index and slot are then
+    // block constants (one slot lookup for the block) and each octet's offset in the entry is the
+    // block's plus the thread's; otherwise each octet divides its flat index.
     const int64_t ub = f0 / per_b;
-    const bool uni = ub == fl / per_b;
-    const int64_t uslot = uni ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
+    const int64_t r0 = f0 - ub * per_b;
+    const int64_t span = total8 - f0 < kSpan ? total8 - f0 : kSpan;
+    auto body = [&](auto uni_tag) {
+        constexpr bool UNI = decltype(uni_tag)::value;
+        const int64_t uslot = UNI ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
 
-    // per octet: batch entry, offset inside its state (< 2^31: the ABI bounds H*P*N), octet index
-    // in the state array (-1: padding)
-    u32x4 raw[kLpPerThread];
-    int64_t bb[kLpPerThread], so[kLpPerThread];
-    uint32_t rem[kLpPerThread];
+        // per octet: batch entry, offset inside its state (< 2^31: the ABI bounds H*P*N), octet index
+        // in the state array (-1: padding)
+        u32x4 raw[kLpPerThread];
+        int64_t bb[kLpPerThread], so[kLpPerThread];
+        uint32_t rem[kLpPerThread];
 #pragma unroll
-    for (int i = 0; i < kLpPerThread; ++i) {
-        const int64_t f = base + i * kLpThreads;
-        const int64_t ff = f < total8 ? f : 0;
-        bb[i] = uni ? ub : ff / per_b;
-        rem[i] = static_cast<uint32_t>(ff - bb[i] * per_b);
-        const int64_t slot = uni ? uslot : (slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i]);
-        so[i] = (f < total8 && slot >= 0) ? slot * per_b + rem[i] : -1;
-        raw[i] = so[i] >= 0 ? __builtin_nontemporal_load(st + so[i]) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < kLpPerThread; ++i) {
-        const bool ok = base + i * kLpThreads < total8;
-        const int64_t b = bb[i];
-        const uint32_t rin = rem[i] / OPR;  // h*P + p inside the batch entry
-        const int q = static_cast<int>(rem[i] % OPR);
-        const int h = static_cast<int>(rin / static_cast<uint32_t>(P));
-        const int p = static_cast<int>(rin) - h * P;
-        const int g = h / hpg;
-        const int64_t bh = b * H + h;
-        const int64_t row = bh * P + p;
-        const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
-        const float a = __expf(dtv * A[h]);
-        const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
-        const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 8 * q;
-        float bv[8], cv[8], v[8];
-        load8_f32(Bm + bo, bv);
-        load8_f32(Cm + bo, cv);
-        const float dx = dtv * xv;
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t word = raw[i][e >> 1];
-            v[e] = fmaf(a, F::dec((e & 1) ? word >> 16 : word & 0xFFFFu), dx * bv[e]);
-            part = fmaf(v[e], cv[e], part);
+        for (int i = 0; i < kLpPerThread; ++i) {
+            const int64_t f = base + i * kLpThreads;
+            const int64_t ff = f < total8 ? f : 0;
+            int64_t slot;
+            if constexpr (UNI) {
+                bb[i] = ub;
+                rem[i] = f < total8 ? static_cast<uint32_t>(r0) + threadIdx.x + i * kLpThreads : 0u;
+                slot = uslot;
+            } else {
+                bb[i] = ff / per_b;
+                rem[i] = static_cast<uint32_t>(ff - bb[i] * per_b);
+                slot = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
+            }
+            so[i] = (f < total8 && slot >= 0) ? slot * per_b + rem[i] : -1;
+            raw[i] = so[i] >= 0 ? __builtin_nontemporal_load(st + so[i]) : u32x4{0u, 0u, 0u, 0u};
         }
-        if (!ok) part = 0.f;
-        part = group_sum_last<OPR>(part);
-        if (ok && q == OPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
-        if (so[i] >= 0) {
-            uint32_t rw[4];
-            if constexpr (SR) {
-                const uint64_t o = static_cast<uint64_t>(so[i]);
-                uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
-                                 static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
-                philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
-                // values below 2^-14 (fp16's subnormal range) anywhere in the wave?
-                bool sub = false;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sub |= (__float_as_uint(v[e]) & 0x7FFFFFFFu) < 0x38800000u;
-                if (__builtin_amdgcn_ballot_w64(sub)) {
+        for (int i = 0; i < kLpPerThread; ++i) {
+            const bool ok = base + i * kLpThreads < total8;
+            const int64_t b = bb[i];
+            const uint32_t rin = rem[i] / OPR;  // h*P + p inside the batch entry
+            const int q = static_cast<int>(rem[i] % OPR);
+            const int h = static_cast<int>(rin >> lp);
+            const int p = static_cast<int>(rin & static_cast<uint32_t>(P - 1));
+            const int g = h / hpg;
+            const int64_t bh = b * H + h;
+            const int64_t row = bh * P + p;
+            const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
+            const float a = __expf(dtv * A[h]);
+            const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
+            const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 8 * q;
+            float bv[8], cv[8], v[8];
+            load8_f32(Bm + bo, bv);
+            load8_f32(Cm + bo, cv);
+            const float dx = dtv * xv;
+            float part = 0.f;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        rw[w] = F::template sr<true>(v[2 * w], c[w] & 0xFFFFu) |
-                                (F::template sr<true>(v[2 * w + 1], c[w] >> 16) << 16);
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t word = raw[i][e >> 1];
+                v[e] = fmaf(a, F::dec((e & 1) ? word >> 16 : word & 0xFFFFu), dx * bv[e]);
+                part = fmaf(v[e], cv[e], part);
+            }
+            if (!ok) part = 0.f;
+            part = group_sum_last<OPR>(part);
+            if (ok && q == OPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+            if (so[i] >= 0) {
+                uint32_t rw[4];
+                if constexpr (SR) {
+                    const uint64_t o = static_cast<uint64_t>(so[i]);
+                    uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
+                                     static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
+                    philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
+                    // values below 2^-14 (fp16's subnormal range) anywhere in the wave?
+                    bool sub = false;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sub |= (__float_as_uint(v[e]) & 0x7FFFFFFFu) < 0x38800000u;
+                    if (__builtin_amdgcn_ballot_w64(sub)) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            rw[w] = F::template sr<true>(v[2 * w], c[w] & 0xFFFFu) |
+                                    (F::template sr<true>(v[2 * w + 1], c[w] >> 16) << 16);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            rw[w] = F::template sr<false>(v[2 * w], c[w] & 0xFFFFu) |
+                                    (F::template sr<false>(v[2 * w + 1], c[w] >> 16) << 16);
+                    }
                 } else {
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        rw[w] = F::template sr<false>(v[2 * w], c[w] & 0xFFFFu) |
-                                (F::template sr<false>(v[2 * w + 1], c[w] >> 16) << 16);
+                    for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
                 }
-            } else {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
+                __builtin_nontemporal_store(u32x4{rw[0], rw[1], rw[2], rw[3]}, st + so[i]);
             }
-            __builtin_nontemporal_store(u32x4{rw[0], rw[1], rw[2], rw[3]}, st + so[i]);
         }
-    }
+    };
+    if (r0 + span <= per_b) body(std::true_type{});
+    else body(std::false_type{});
 }
 
 template <typename T, typename TY, class F, int N>

@@ -16,6 +16,8 @@
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
+#include <type_traits>
+
 namespace ssd {
 
 constexpr int kUpdThreads = 128;
@@ -33,82 +35,101 @@ __global__ __launch_bounds__(kUpdThreads) void state_update_kernel(
     const float* __restrict__ D, TY* __restrict__ y, int64_t total4, int H, int P, int hpg,
     const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp) {
     constexpr int QPR = N / 4;  // float4 per state row
+    constexpr int kSpan = kUpdThreads * kUpdPerThread;
     f32x4* st4 = reinterpret_cast<f32x4*>(state);
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread) + threadIdx.x;
-
-    f32x4 s[kUpdPerThread];
-    int64_t sf[kUpdPerThread];   // float4 index of the state (in the pool with SLOTS), -1: padding
-    int64_t bu = -1, shift = 0;  // with SLOTS: the block's one batch entry and its pool offset, if uniform
-    bool upad = false;           // that entry is padding
-    if constexpr (SLOTS) {
-        const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
-        const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kUpdThreads * kUpdPerThread);
-        const int64_t fl = (f0 + kUpdThreads * kUpdPerThread < total4 ? f0 + kUpdThreads * kUpdPerThread : total4) - 1;
-        if (f0 / per_b == fl / per_b) {   // the usual case: one slot lookup per block
-            bu = f0 / per_b;
-            const int64_t slot = seq_slot(slot_idx, bu, nslots);
+    const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
+    const int lp = __builtin_ctz(static_cast<unsigned>(P));   // head_dim is a power of two
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kSpan;
+    const int64_t base = f0 + threadIdx.x;
+    // The block's elements almost always lie in one batch entry (UNI): its index (and slot) are
+    // then block constants, and each element's row, head and q come from shifts of its offset in
+    // the entry; otherwise each element divides its flat index.
+    const int64_t ub = f0 / per_b;
+    const int64_t r0 = f0 - ub * per_b;
+    const int64_t span = total4 - f0 < kSpan ? total4 - f0 : kSpan;
+    auto body = [&](auto uni_tag) {
+        constexpr bool UNI = decltype(uni_tag)::value;
+        int64_t ushift = 0;   // with SLOTS and UNI: the entry's offset from its slot in the pool
+        bool upad = false;    // that entry is padding
+        if constexpr (SLOTS && UNI) {
+            const int64_t slot = seq_slot(slot_idx, ub, nslots);
             upad = slot < 0;
-            shift = (slot - bu) * per_b;
+            ushift = (slot - ub) * per_b;
         }
-    }
+        f32x4 s[kUpdPerThread];
+        int64_t sf[kUpdPerThread];   // float4 index of the state (in the pool with SLOTS), -1: padding
 #pragma unroll
-    for (int i = 0; i < kUpdPerThread; ++i) {
-        const int64_t f = base + i * kUpdThreads;
-        sf[i] = f;
-        if constexpr (SLOTS) {
-            if (bu >= 0) {
-                sf[i] = upad ? -1 : f + shift;
-            } else if (f < total4) {
-                const int64_t row = f / QPR;
-                const int64_t bh = row / P;
-                const int64_t b = bh / H;
-                const int64_t slot = seq_slot(slot_idx, b, nslots);
-                sf[i] = slot < 0 ? -1 : f + (slot - b) * static_cast<int64_t>(H) * P * QPR;
+        for (int i = 0; i < kUpdPerThread; ++i) {
+            const int64_t f = base + i * kUpdThreads;
+            sf[i] = f;
+            if constexpr (SLOTS) {
+                if (UNI) {
+                    sf[i] = upad ? -1 : f + ushift;
+                } else if (f < total4) {
+                    const int64_t b = f / per_b;
+                    const int64_t slot = seq_slot(slot_idx, b, nslots);
+                    sf[i] = slot < 0 ? -1 : f + (slot - b) * per_b;
+                }
+            }
+            if constexpr (SLOTS) {
+                if (f < total4) s[i] = sf[i] >= 0 ? __builtin_nontemporal_load(st4 + sf[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                if (f < total4) s[i] = __builtin_nontemporal_load(st4 + f);
             }
         }
-        if constexpr (SLOTS) {
-            if (f < total4) s[i] = sf[i] >= 0 ? __builtin_nontemporal_load(st4 + sf[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-            if (f < total4) s[i] = __builtin_nontemporal_load(st4 + f);
-        }
-    }
 #pragma unroll
-    for (int i = 0; i < kUpdPerThread; ++i) {
-        const int64_t f = base + i * kUpdThreads;
-        const bool ok = f < total4;
-        const int64_t ff = ok ? f : 0;
-        const int64_t row = ff / QPR;          // (b, h, p)
-        const int q = static_cast<int>(ff - row * QPR);
-        const int64_t bh = row / P;
-        const int p = static_cast<int>(row - bh * P);
-        const int64_t b = bh / H;
-        const int h = static_cast<int>(bh - b * H);
-        const int g = h / hpg;
-        const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
-        const float a = __expf(dtv * A[h]);
-        const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
-        const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 4 * q;
-        float bv[4], cv[4];
+        for (int i = 0; i < kUpdPerThread; ++i) {
+            const int64_t f = base + i * kUpdThreads;
+            const bool ok = f < total4;
+            int64_t b, row, bh;   // batch entry, state row (b, h, p), (b, h)
+            int q, h, p;
+            if constexpr (UNI) {
+                const int rem = ok ? static_cast<int>(r0) + static_cast<int>(threadIdx.x) + i * kUpdThreads : 0;
+                const int rw = rem / QPR;   // h * P + p
+                q = rem % QPR;
+                h = rw >> lp;
+                p = rw & (P - 1);
+                b = ub;
+                row = ub * H * P + rw;
+                bh = ub * H + h;
+            } else {
+                const int64_t ff = ok ? f : 0;
+                row = ff / QPR;
+                q = static_cast<int>(ff - row * QPR);
+                bh = row >> lp;
+                p = static_cast<int>(row & (P - 1));
+                b = bh / H;
+                h = static_cast<int>(bh - b * H);
+            }
+            const int g = h / hpg;
+            const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
+            const float a = __expf(dtv * A[h]);
+            const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
+            const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 4 * q;
+            float bv[4], cv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            bv[k] = static_cast<float>(Bm[bo + k]);
-            cv[k] = static_cast<float>(Cm[bo + k]);
-        }
-        const float dx = dtv * xv;
-        f32x4 v = s[i];
-        float part = 0.f;
+            for (int k = 0; k < 4; ++k) {
+                bv[k] = static_cast<float>(Bm[bo + k]);
+                cv[k] = static_cast<float>(Cm[bo + k]);
+            }
+            const float dx = dtv * xv;
+            f32x4 v = s[i];
+            float part = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[k] = fmaf(a, v[k], dx * bv[k]);
-            part = fmaf(v[k], cv[k], part);
+            for (int k = 0; k < 4; ++k) {
+                v[k] = fmaf(a, v[k], dx * bv[k]);
+                part = fmaf(v[k], cv[k], part);
+            }
+            if (!ok) part = 0.f;
+            part = group_sum_last<QPR>(part);   // the row's QPR lanes are consecutive and aligned
+            if (ok) {
+                if (q == QPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
+                if (!SLOTS || sf[i] >= 0) __builtin_nontemporal_store(v, st4 + sf[i]);
+            }
         }
-        if (!ok) part = 0.f;
-        part = group_sum_last<QPR>(part);   // the row's QPR lanes are consecutive and aligned
-        if (ok) {
-            if (q == QPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
-            if (!SLOTS || sf[i] >= 0) __builtin_nontemporal_store(v, st4 + sf[i]);
-        }
-    }
+    };
+    if (r0 + span <= per_b && per_b < (1LL << 30)) body(std::true_type{});   // offsets fit 32 bits
+    else body(std::false_type{});
 }
 
 template <typename T, typename TY, int N, bool SLOTS, bool DTP>
