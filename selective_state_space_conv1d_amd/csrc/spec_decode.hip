@@ -28,19 +28,23 @@ template <typename T> struct Quad;
 template <> struct Quad<bf16> { typedef bf16x4 type; };
 template <> struct Quad<float> { typedef f32x4 type; };
 
-// Per element and token: the raw inputs, kept in their storage type until used.
+// Per thread and token: the raw inputs of its row (dt, x) and of its kMultiPerThread float4
+// (B and C quads), kept in their storage type until used.
 template <typename T>
 struct TokIn {
     T dt, x;
-    typename Quad<T>::type b, c;
+    typename Quad<T>::type b[kMultiPerThread], c[kMultiPerThread];
 };
 
-// Grid: one thread per kMultiPerThread float4 of the [B, H, P, N] state, 128-thread strides.
+// Grid: each thread takes kMultiPerThread (V) float4 of one state row: float4 q = l + LPR*v of the
+// row, for lane l of the row's LPR = N/(4V) consecutive lanes, so the row's dt, x and decay are
+// computed once per thread.  A block covers 128 V consecutive float4 (whole rows).
 // Token j of request b is row b*k + j of x, B, C, dt and y, and entry b*k + j of inter.  The
-// per-head constants are read once; each token's inputs for all of a thread's elements are
-// loaded one token ahead of their use.  Each row's y dot product is a DPP reduction over its
-// lanes (no LDS round trip), one token at a time (reducing 2 or 4 tokens together raised VGPRs to
-// 100+ and ran 15-30 % slower).
+// per-head constants are read once; each token's inputs are loaded one token ahead of their use.
+// Each row's y dot product is a DPP reduction over its lanes, one token at a time (reducing 2 or
+// 4 tokens together raised VGPRs to 100+ and ran 15-30 % slower): the V partial sums go through
+// the same LPR-lane tree and are then added, which is the order of the single-token update's
+// 2 LPR-lane tree, so k = 1 reproduces it bitwise.
 // REPLAY (the accept step by recomputation): request b applies its first
 // n = clamp(accept_len[b], 0, k) tokens and writes the state back in place; no y, no inter.
 template <typename T, typename TY, int N, bool REPLAY>
@@ -50,112 +54,113 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
     const float* __restrict__ D, TY* __restrict__ y, float* __restrict__ inter, int64_t total4, int k, int H,
     int P, int hpg, const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp,
     const int32_t* __restrict__ accept_len) {
-    constexpr int QPR = N / 4;  // float4 per state row
+    constexpr int QPR = N / 4;                   // float4 per state row
+    constexpr int V = kMultiPerThread;
+    constexpr int LPR = QPR / V;                 // lanes per row
+    constexpr int kSpan = kMultiThreads * V;     // float4 per block
+    static_assert(QPR % V == 0 && LPR >= 2, "rows split over whole lanes");
     typedef typename Quad<T>::type Q;
     const int64_t per_b = static_cast<int64_t>(H) * P * QPR;
     const int lp = __builtin_ctz(static_cast<unsigned>(P));   // head_dim is a power of two
     f32x4* st4 = reinterpret_cast<f32x4*>(state);
     f32x4* in4 = reinterpret_cast<f32x4*>(inter);
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * (kMultiThreads * kMultiPerThread);
-    const int64_t base = f0 + threadIdx.x;
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kSpan;
+    const int l = static_cast<int>(threadIdx.x) % LPR;
+    const int64_t fr = f0 + (static_cast<int>(threadIdx.x) / LPR) * QPR;   // the thread's row, float4 0
+    const bool live = fr < total4;                                          // total4 is whole rows
     auto tokens_of = [&](int64_t b) {   // tokens to apply: k, or the accepted count when replaying
         if constexpr (!REPLAY) return k;
         const int n = accept_len[b];
         return n < 0 ? 0 : (n > k ? k : n);
     };
-    // The block's elements almost always lie in one request (UNI): its index, slot and token
-    // count are then block constants, held in scalar registers, and every token's row addresses
-    // are scalar too.  Otherwise each element finds its request with a 64-bit division.
+    // The block's rows almost always lie in one request (UNI): its index, slot and token count are
+    // then block constants, held in scalar registers, and every token's row addresses are scalar
+    // too.  Otherwise each thread finds its request with a 64-bit division.
     const int64_t ub = f0 / per_b;
     const int64_t r0 = f0 - ub * per_b;
-    const int64_t span = total4 - f0 < kMultiThreads * kMultiPerThread ? total4 - f0 : kMultiThreads * kMultiPerThread;
+    const int64_t span = total4 - f0 < kSpan ? total4 - f0 : kSpan;
     auto body = [&](auto uni_tag) {
         constexpr bool UNI = decltype(uni_tag)::value;
-        const int64_t uslot = UNI ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
-        const int kmax = UNI ? tokens_of(ub) : k;
-        if (REPLAY && UNI && (kmax == 0 || uslot < 0)) return;   // nothing accepted, or padding
-
-        // per element, fixed over the tokens: request, offset in its state, row h*P + p, q, h, p, g,
-        // the head's A, D and dt bias, its slot and its token count
-        f32x4 s[kMultiPerThread];
-        int64_t bb[kMultiPerThread], rem[kMultiPerThread], sl[kMultiPerThread];
-        int rw[kMultiPerThread], qq[kMultiPerThread], hh[kMultiPerThread], pp[kMultiPerThread], gg[kMultiPerThread];
-        int nk[kMultiPerThread];
-        bool live[kMultiPerThread];
-        float Ah[kMultiPerThread], Dh[kMultiPerThread], biash[kMultiPerThread];
-#pragma unroll
-        for (int i = 0; i < kMultiPerThread; ++i) {
-            const int64_t f = base + i * kMultiThreads;
-            live[i] = f < total4;
-            if constexpr (UNI) {
-                bb[i] = ub;
-                rem[i] = live[i] ? r0 + threadIdx.x + i * kMultiThreads : 0;
-                sl[i] = uslot;
-                nk[i] = live[i] ? kmax : 0;
-            } else {
-                const int64_t ff = live[i] ? f : 0;
-                bb[i] = ff / per_b;
-                rem[i] = ff - bb[i] * per_b;
-                sl[i] = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
-                nk[i] = live[i] ? tokens_of(bb[i]) : 0;
-            }
-            rw[i] = static_cast<int>(static_cast<uint64_t>(rem[i]) / QPR);
-            qq[i] = static_cast<int>(static_cast<uint64_t>(rem[i]) % QPR);
-            hh[i] = rw[i] >> lp;
-            pp[i] = rw[i] & (P - 1);
-            gg[i] = static_cast<int>(static_cast<unsigned>(hh[i]) / static_cast<unsigned>(hpg));
-            s[i] = (live[i] && sl[i] >= 0 && nk[i] > 0) ? __builtin_nontemporal_load(st4 + sl[i] * per_b + rem[i])
-                                                        : f32x4{0.f, 0.f, 0.f, 0.f};
-            Ah[i] = A[hh[i]];
-            Dh[i] = D ? D[hh[i]] : 0.f;
-            biash[i] = dtp.bias ? dtp.bias[hh[i]] : 0.f;
+        int64_t bb, rem, sl;   // request, offset of the thread's float4 0 in its state, slot
+        int nk;                // tokens the thread applies
+        if constexpr (UNI) {
+            bb = ub;
+            rem = live ? r0 + (fr - f0) + l : 0;
+            sl = slot_idx ? seq_slot(slot_idx, ub, nslots) : ub;
+            nk = tokens_of(ub);
+            if (REPLAY && (nk == 0 || sl < 0)) return;   // nothing accepted, or padding
+            if (!live) nk = 0;
+        } else {
+            const int64_t ff = live ? fr + l : 0;
+            bb = ff / per_b;
+            rem = ff - bb * per_b;
+            sl = slot_idx ? seq_slot(slot_idx, bb, nslots) : bb;
+            nk = live ? tokens_of(bb) : 0;
         }
-        // token row of element i's request: a block constant when UNI (j < kmax there); rows past a
-        // request's own count read its first
-        auto tok_of = [&](int i, int j) -> int64_t { return UNI ? ub * k + j : bb[i] * k + (j < nk[i] ? j : 0); };
-        auto load_tok = [&](int j, TokIn<T> (&in)[kMultiPerThread]) {
+        const int kmax = UNI ? tokens_of(ub) : k;
+        const int rw = static_cast<int>(static_cast<uint64_t>(rem) / QPR);   // h * P + p
+        const int h = rw >> lp;
+        const int g = static_cast<int>(static_cast<unsigned>(h) / static_cast<unsigned>(hpg));
+        const float Ah = A[h];
+        const float Dh = D ? D[h] : 0.f;
+        const float biash = dtp.bias ? dtp.bias[h] : 0.f;
+        f32x4 s[V];
 #pragma unroll
-            for (int i = 0; i < kMultiPerThread; ++i) {
-                const int64_t tok = tok_of(i, j);
-                in[i].dt = dt[tok * H + hh[i]];
-                in[i].x = x[tok * xs + rw[i]];
-                const int64_t bo = tok * bcs + static_cast<int64_t>(gg[i]) * N + 4 * qq[i];
-                in[i].b = *reinterpret_cast<const Q*>(Bm + bo);
-                in[i].c = *reinterpret_cast<const Q*>(Cm + bo);
+        for (int v = 0; v < V; ++v)
+            s[v] = (live && sl >= 0 && nk > 0) ? __builtin_nontemporal_load(st4 + sl * per_b + rem + LPR * v)
+                                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        // token row of the thread's request: a block constant when UNI (j < kmax there); rows past
+        // a request's own count read its first
+        auto tok_of = [&](int j) -> int64_t { return UNI ? ub * k + j : bb * k + (j < nk ? j : 0); };
+        auto load_tok = [&](int j, TokIn<T>& in) {
+            const int64_t tok = tok_of(j);
+            in.dt = dt[tok * H + h];
+            in.x = x[tok * xs + rw];
+            const int64_t bo = tok * bcs + static_cast<int64_t>(g) * N + 4 * l;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                in.b[v] = *reinterpret_cast<const Q*>(Bm + bo + 4 * LPR * v);
+                in.c[v] = *reinterpret_cast<const Q*>(Cm + bo + 4 * LPR * v);
             }
         };
         // token j with its inputs: advance the state, store the intermediate state, reduce and store y
-        auto step = [&](int j, const TokIn<T> (&in)[kMultiPerThread]) {
+        auto step = [&](int j, const TokIn<T>& in) {
+            // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
+            float dtv = static_cast<float>(in.dt);
+            if (dtp.bias) dtv += biash;
+            if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
+            if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
+            const float a = __expf(dtv * Ah);
+            const float xv = static_cast<float>(in.x);
+            const float dx = dtv * xv;
+            const int64_t row = (UNI ? ub : bb) * k + j;
+            float part[V];
 #pragma unroll
-            for (int i = 0; i < kMultiPerThread; ++i) {
-                // the dt prologue with the head's bias already loaded (same steps as dt_prologue)
-                float dtv = static_cast<float>(in[i].dt);
-                if (dtp.bias) dtv += biash[i];
-                if (dtp.softplus) dtv = dtv > 20.f ? dtv : log1pf(expf(dtv));
-                if (dtp.lo < dtp.hi) dtv = fminf(fmaxf(dtv, dtp.lo), dtp.hi);
-                const float a = __expf(dtv * Ah[i]);
-                const float xv = static_cast<float>(in[i].x);
-                const float dx = dtv * xv;
-                f32x4 v = s[i];
+            for (int v = 0; v < V; ++v) {
+                f32x4 u = s[v];
                 float pt = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = fmaf(a, v[e], dx * static_cast<float>(in[i].b[e]));
-                    pt = fmaf(v[e], static_cast<float>(in[i].c[e]), pt);
+                    u[e] = fmaf(a, u[e], dx * static_cast<float>(in.b[v][e]));
+                    pt = fmaf(u[e], static_cast<float>(in.c[v][e]), pt);
                 }
-                if (j < nk[i]) s[i] = v;
+                if (j < nk) s[v] = u;
                 if constexpr (!REPLAY) {
-                    const int64_t row = (UNI ? ub : bb[i]) * k + j;
-                    if (inter && live[i]) in4[row * per_b + rem[i]] = v;   // plain stores measured faster here
-                    pt = group_sum_last<QPR>(live[i] ? pt : 0.f);
-                    if (live[i] && qq[i] == QPR - 1)
-                        y[row * H * static_cast<int64_t>(P) + rw[i]] = static_cast<TY>(pt + (D ? Dh[i] * xv : 0.f));
+                    if (inter && live) in4[row * per_b + rem + LPR * v] = u;   // plain stores measured faster here
                 }
+                part[v] = live ? pt : 0.f;
+            }
+            if constexpr (!REPLAY) {
+                float sum = group_sum_last<LPR>(part[0]);
+#pragma unroll
+                for (int v = 1; v < V; ++v) sum = group_sum_last<LPR>(part[v]) + sum;
+                if (live && l == LPR - 1)
+                    y[row * H * static_cast<int64_t>(P) + rw] = static_cast<TY>(sum + (D ? Dh * xv : 0.f));
             }
         };
         // the inputs of token j + 1 are loaded while token j is computed, into the other of two
         // register sets (a copy between them would wait for the loads)
-        TokIn<T> ta[kMultiPerThread], tb[kMultiPerThread];
+        TokIn<T> ta, tb;
         load_tok(0, ta);
         for (int j = 0; j < kmax; j += 2) {
             load_tok(j + 1 < kmax ? j + 1 : j, tb);   // past the last token: re-reads its rows
@@ -165,9 +170,10 @@ __global__ __launch_bounds__(kMultiThreads) void state_update_multi_kernel(
             step(j + 1, tb);
         }
         if constexpr (REPLAY) {
+            if (live && sl >= 0 && nk > 0) {
 #pragma unroll
-            for (int i = 0; i < kMultiPerThread; ++i)
-                if (live[i] && sl[i] >= 0 && nk[i] > 0) __builtin_nontemporal_store(s[i], st4 + sl[i] * per_b + rem[i]);
+                for (int v = 0; v < V; ++v) __builtin_nontemporal_store(s[v], st4 + sl * per_b + rem + LPR * v);
+            }
         }
     };
     if (r0 + span <= per_b) body(std::true_type{});
