@@ -76,6 +76,26 @@ def test_lp_codes_bitwise_when_a_is_zero(orc, sdt, sr, use_slots, scale):
 
 
 @pytest.mark.parametrize("sdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("use_slots", [False, True])
+def test_lp_codes_bitwise_blocks_straddling_requests(orc, sdt, use_slots):
+    """H*P*N/8 = 96 octets per request: every 256-octet block spans several requests, and each
+    thread finds its own request and slot."""
+    d = LayerDims(7, 1, 3, 16, 1, 16)
+    nstate = 9 if use_slots else 7
+    state0, args, A, D = lp_inputs(d, 505, nstate, sdt)
+    slots = [8, 0, -1, 4, 2, 6, 1] if use_slots else None
+    slot = None if slots is None else torch.tensor(slots, dtype=torch.int32, device=DEV)
+    sr = (0xBEEF, 12, 5)
+    state = state0.clone()
+    ssd.ssd_state_update_lp(state, *args, torch.zeros_like(A), D, slot_idx=slot, sr=sr, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = orc.state_update_lp_codes_a0(codes_of(state0), FMT[sdt], None if slots is None else np.array(slots),
+                                        *(f64(t) for t in args), sr)
+    got = codes_of(state)
+    assert np.array_equal(got, want), f"{(got != want).sum()} codes differ"
+
+
+@pytest.mark.parametrize("sdt", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("sr", [None, (99, 1, 5)])
 @pytest.mark.parametrize("P,N,act", [(64, 128, torch.bfloat16), (16, 32, torch.float32)])
 def test_lp_state_within_one_spacing(orc, sdt, sr, P, N, act):

@@ -30,14 +30,15 @@ def conv_inputs(d, k, nstate, seed):
     return xbc, w, bias, pool
 
 
-@pytest.mark.parametrize("P,N,dtype", [(64, 128, torch.bfloat16), (16, 32, torch.float32)])
+@pytest.mark.parametrize("H,P,N,dtype", [(8, 64, 128, torch.bfloat16), (8, 16, 32, torch.float32),
+                                         (6, 16, 16, torch.bfloat16)])   # the last: blocks straddle requests
 @pytest.mark.parametrize("use_slots", [False, True])
-def test_state_update_multi_matches_oracle(orc, P, N, dtype, use_slots):
-    d = LayerDims(4, 1, 8, P, 2, N, dtype=dtype)
+def test_state_update_multi_matches_oracle(orc, H, P, N, dtype, use_slots):
+    d = LayerDims(4, 1, H, P, 2, N, dtype=dtype)
     k = 5
     s = ssm_inputs(d, k, 400)
     if use_slots:
-        pool0 = torch.randn(6, 8, P, N, device=DEV) * 0.1
+        pool0 = torch.randn(6, H, P, N, device=DEV) * 0.1
         slots = [5, -1, 0, 3]
         slot = torch.tensor(slots, dtype=torch.int32, device=DEV)
     else:
@@ -53,8 +54,14 @@ def test_state_update_multi_matches_oracle(orc, P, N, dtype, use_slots):
     assert_close(inter, ir, F32_BAR, "intermediate states")
 
 
-def test_state_update_multi_is_k_single_updates_bitwise():
-    d = WORKLOADS["decode_ultra_b64"].with_(batch=6)
+# (batch, H, P, G, N): the Ultra layer; blocks of 256 float4 that straddle requests (H*P*N/4 = 192
+# and 384) and so find each thread's request on their own; other row widths (N/8 lanes per row)
+STRADDLE = [(5, 3, 16, 1, 16), (4, 3, 16, 3, 32), (3, 5, 32, 5, 64)]
+
+
+@pytest.mark.parametrize("shape", [None] + STRADDLE)
+def test_state_update_multi_is_k_single_updates_bitwise(shape):
+    d = WORKLOADS["decode_ultra_b64"].with_(batch=6) if shape is None else LayerDims(shape[0], 1, *shape[1:])
     k = 4
     s = ssm_inputs(d, k, 410)
     y, inter = ssd.ssd_state_update_multi(s["init_state"], s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"])
@@ -231,13 +238,13 @@ def test_scan_snapshots(orc, P, N, dtype, L, iv):
 
 # --------------------------------------------------------------------------- accept by recomputation
 @pytest.mark.parametrize("use_slots", [False, True])
-@pytest.mark.parametrize("k", [4, 7])
-def test_accept_by_recomputation_is_the_stored_intermediate(use_slots, k):
-    d = LayerDims(6, 1, 8, 64, 2, 128)
+@pytest.mark.parametrize("k,H,P,N", [(4, 8, 64, 128), (7, 8, 64, 128), (4, 3, 16, 16)])   # the last: straddling blocks
+def test_accept_by_recomputation_is_the_stored_intermediate(use_slots, k, H, P, N):
+    d = LayerDims(6, 1, H, P, 1, N)
     s = ssm_inputs(d, k, 480)
     xbc, w, bias, cpool0 = conv_inputs(d, k, 9 if use_slots else 6, 481)
     if use_slots:
-        spool0 = torch.randn(9, 8, 64, 128, device=DEV) * 0.1
+        spool0 = torch.randn(9, H, P, N, device=DEV) * 0.1
         slots = [7, 2, -1, 0, 5, 8]
         slot = torch.tensor(slots, dtype=torch.int32, device=DEV)
     else:
