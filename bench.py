@@ -530,7 +530,7 @@ def main():
                    "conv_update_GBps": cub / avg["conv1d_update"] / 1e9},
     }
     print("[bench] gated group RMSNorm on the prefill output", file=sys.stderr, flush=True)
-    out["gated_norm"] = norm_leg(ssd, torch, dev, max(5, args.steps // 2), 2, y)
+    out["gated_norm"] = norm_leg(ssd, torch, dev, max(5, args.steps // 2), max(2, args.warmup // 5), y)
     del v, x, Bm, Cm, y, state
     print("[bench] serving forms (packed prefill, slot-pool decode)", file=sys.stderr, flush=True)
     out["serving"] = serving_leg(ssd, torch, dev, max(3, args.steps // 2), max(1, args.warmup // 2))
