@@ -569,7 +569,8 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
     }
 
     f32x16 Hs[NT];
-    auto load_init = [&](int64_t s) {   // Hs = the initial state of sequence s (zeros without one)
+    // dst = the initial state of sequence s (zeros without one)
+    auto load_init = [&](int64_t s, f32x16 (&dst)[NT]) {
         const int64_t sl = cx.slot(s);
         const bool from = a.init_state && sl >= 0 && cx.use_init(s);
 #pragma unroll
@@ -580,10 +581,10 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (from) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Hs[t][4 * j + r] = v[r];
+                for (int r = 0; r < 4; ++r) dst[t][4 * j + r] = v[r];
             }
     };
-    auto store_final = [&](int64_t s) {   // Hs as the final state of sequence s
+    auto store_final = [&](int64_t s, const f32x16 (&src)[NT]) {   // src as the final state of sequence s
         const int64_t sl = cx.slot(s);
         if (!a.final_state || sl < 0) return;
 #pragma unroll
@@ -592,20 +593,21 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
             for (int j = 0; j < 4; ++j) {
                 const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
                 *reinterpret_cast<f32x4*>(a.final_state + sbase(sl) + hp * NS + n) =
-                    f32x4{Hs[t][4 * j], Hs[t][4 * j + 1], Hs[t][4 * j + 2], Hs[t][4 * j + 3]};
+                    f32x4{src[t][4 * j], src[t][4 * j + 1], src[t][4 * j + 2], src[t][4 * j + 3]};
             }
     };
     // empty sequences in [s0, s1) end with their initial state (zeros without one)
     auto finish_empty = [&](int s0, int s1) {
         for (int e = s0; e < s1; ++e) {
-            load_init(e);
-            store_final(e);
+            f32x16 He[NT];
+            load_init(e, He);
+            store_final(e, He);
         }
     };
     Cursor cur = cx.first();
     finish_empty(cx.s_begin, cur.ok ? cur.s : cx.s_end);
     if (cur.ok) {
-        load_init(cur.s);
+        load_init(cur.s, Hs);
     } else {
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hs[t] = zero16();
@@ -679,11 +681,18 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
             }
         }
         // the sequence's last chunk: its final state, those of the empty sequences after it, and
-        // the next sequence's initial state, which the y waves then use as the carried state
+        // the next sequence's initial state, which the y waves then use as the carried state.  The
+        // next state's loads are issued before the final state's stores, so that waiting for them
+        // does not wait for the stores as well (one counter covers both).
         if (!nx.ok || nx.s != cur.s) {
-            store_final(cur.s);
+            f32x16 Hn[NT];
+            if (nx.ok) load_init(nx.s, Hn);
+            store_final(cur.s, Hs);
+            if (nx.ok) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) Hs[t] = Hn[t];
+            }
             finish_empty(cur.s + 1, nx.ok ? nx.s : cx.s_end);
-            if (nx.ok) load_init(nx.s);
         }
         // the y waves must have read the previous state before it is overwritten
         const int target = 4 * static_cast<int>(gc + 1);
