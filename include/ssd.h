@@ -9,7 +9,8 @@
  *   ssd_chunk_scan     the SSD chunked scan of a prefill: y and the fp32 final
  *                      state from x, dt, A, B, C, D and an optional initial state
  *   ssd_state_update   the single-token selective state update (decode)
- *   (ssd_chunk_scan_snapshots: the scan, also storing the state every N tokens)
+ *   (ssd_chunk_scan_snapshots: the scan, also storing the state every N tokens;
+ *    ssd_chunk_scan_varlen_snapshots: the same for packed sequences, into a snapshot pool)
  * and their serving forms on packed variable-length batches and state pools:
  *   ssd_conv1d_fwd_varlen, ssd_chunk_scan_varlen, ssd_conv1d_update_slots,
  *   ssd_state_update_slots
@@ -184,6 +185,29 @@ ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk,
                                       const float* init_state, float* final_state, float* snapshots,
                                       int64_t interval, void* y, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
+
+/*
+ * ssd_chunk_scan_varlen that also stores states at interval boundaries of each packed
+ * sequence into a snapshot pool ([P2] 部署时如何调这些缓存: a state snapshot every N tokens for
+ * prefix caching; here for the packed prefill that fills the cache).
+ *  snap_pool     [nsnap_slots, H, P, N] fp32, 16-byte aligned; may be NULL when nsnap_slots is 0.
+ *  snap_table    [S, max_snaps] int32 (device): entry (s, k) names the pool slot that receives the
+ *                state of sequence s after its token (k + 1) * interval - 1.  Negative entries,
+ *                entries naming no slot of the pool, and entries with k >= len_s / interval store
+ *                nothing.  May be NULL when max_snaps is 0.
+ *  interval      a positive multiple of 128.
+ * Slots named by the table must be distinct from one another.  y and the state pool are exactly
+ * those of ssd_chunk_scan_varlen; the rest is as there.
+ */
+ssd_status_t ssd_chunk_scan_varlen_snapshots(const ssd_dims_t* d, int32_t chunk, const void* x,
+                                             int64_t x_row_stride, const void* B, const void* C,
+                                             int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                             const ssd_dt_params_t* dt_params, const int32_t* cu_seqlens,
+                                             const int32_t* slot_idx, const int32_t* has_initial_state,
+                                             float* state_pool, int64_t nslots, float* snap_pool,
+                                             int64_t nsnap_slots, const int32_t* snap_table, int32_t max_snaps,
+                                             int64_t interval, void* y, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
 
 /*
  * Single-token selective state update, in place ([P2] "Decode 阶段"; [P1]

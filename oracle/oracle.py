@@ -187,6 +187,34 @@ class Oracle:
                 new[k] = fin[0]
         return y, new
 
+    # The packed scan with snapshots into a pool (the modeling_nemotron_h.py walk-through page,
+    # 部署时如何调这些缓存: a state snapshot every N tokens for prefix caching): each sequence is
+    # scanned with scan_snapshots, and its k-th snapshot goes to pool slot snap_table[s, k] when
+    # that names a slot.  -> y, new state pool, new snapshot pool
+    def scan_varlen_snapshots(self, x, Bm, Cm, dt, A, D, cu, pool, slot, has_init, snap_pool, snap_table,
+                              interval):
+        x, Bm, Cm, dt = map(_f64, (x, Bm, Cm, dt))
+        cu = [int(c) for c in cu]
+        y = np.zeros_like(x)
+        new = None if pool is None else np.array(pool, dtype=np.float64, order="C", copy=True)
+        snaps = np.array(snap_pool, dtype=np.float64, order="C", copy=True)
+        nslots = 0 if pool is None else new.shape[0]
+        table = np.asarray(snap_table)
+        for s in range(len(cu) - 1):
+            a, b = cu[s], cu[s + 1]
+            k = self._slot(slot, s, nslots)
+            start = k >= 0 and has_init is not None and int(has_init[s]) != 0
+            ys, fin, sn = self.scan_snapshots(x[None, a:b], Bm[None, a:b], Cm[None, a:b], dt[None, a:b], A, D,
+                                              new[k][None] if start else None, interval)
+            y[a:b] = ys[0]
+            if k >= 0:
+                new[k] = fin[0]
+            for j in range(min(sn.shape[1], table.shape[1])):
+                sl = int(table[s, j])
+                if 0 <= sl < snaps.shape[0]:
+                    snaps[sl] = sn[0, j]
+        return y, new, snaps
+
     # u [B,CD], pool [nslots,CD,K], slot [B] -> v [B,CD], new pool
     def conv1d_update_slots(self, u, w, bias, pool, slot):
         u = _f64(u)

@@ -126,10 +126,9 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
             sm.H[p][n] = fmaf(alpha, sm.H[p][n], s);
         }
         // state snapshot after token t0 + kT - 1 when that closes an interval (a multiple of kT)
-        if (a.snapshots && (t0 + kT) % a.snap_interval == 0 && t0 + kT <= L) {
+        float* snap = a.snapshots ? snapshot_dst(a, b, L, t0 + kT, h) : nullptr;
+        if (snap) {
             __syncthreads();
-            const int64_t nsnap = L / a.snap_interval, k = (t0 + kT) / a.snap_interval - 1;
-            float* snap = a.snapshots + ((b * nsnap + k) * H + h) * static_cast<int64_t>(P) * N;
             for (int e = tid; e < P * N; e += kFmaThreads) {
                 const int p = e / N, n = e - p * N;
                 snap[e] = sm.H[p][n];

@@ -666,10 +666,8 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
         }
         // state snapshot after token (c + 1) * Q - 1 of the sequence when that closes an interval
         if (a.snapshots) {
-            const int64_t t_end = (cur.c + 1) * Q;
-            if (t_end % a.snap_interval == 0 && t_end <= cur.L) {
-                const int64_t nsnap = cur.L / a.snap_interval, k = t_end / a.snap_interval - 1;
-                float* snap = a.snapshots + ((cur.s * nsnap + k) * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+            float* snap = snapshot_dst(a, cur.s, cur.L, (cur.c + 1) * static_cast<int64_t>(Q), cx.h);
+            if (snap) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll

@@ -204,13 +204,15 @@ ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk, const 
                       snapshots, interval, y, workspace, workspace_bytes, stream);
 }
 
-ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
-                                  const void* B, const void* C, int64_t bc_row_stride, const void* dt,
-                                  const float* A, const float* D, const ssd_dt_params_t* dt_params,
-                                  const int32_t* cu_seqlens,
-                                  const int32_t* slot_idx, const int32_t* has_initial_state, float* state_pool,
-                                  int64_t nslots, void* y, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
+// the packed scan, with optional snapshots into a pool (internal linkage)
+static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                      const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                      const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                      const int32_t* cu_seqlens, const int32_t* slot_idx,
+                                      const int32_t* has_initial_state, float* state_pool, int64_t nslots,
+                                      float* snap_pool, int64_t nsnap_slots, const int32_t* snap_table,
+                                      int32_t max_snaps, int64_t interval, void* y, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
     ssd_status_t st = check_dims(d, true);
     if (st != SSD_OK) return st;
     st = check_seq_tables(d, cu_seqlens, state_pool, nslots);
@@ -234,10 +236,49 @@ ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const voi
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
                     {cu_seqlens, slot_idx, has_initial_state, nslots}, dt_params_of(dt_params)};
+    if (snap_table && max_snaps > 0 && nsnap_slots > 0) {   // otherwise no snapshot can be stored
+        a.snapshots = snap_pool;
+        a.snap_interval = interval;
+        a.snap_table = snap_table;
+        a.snap_max = max_snaps;
+        a.snap_slots = nsnap_slots;
+    }
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
     return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
+}
+
+ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                   const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                   const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                   const int32_t* cu_seqlens,
+                                   const int32_t* slot_idx, const int32_t* has_initial_state,
+                                   float* state_pool, int64_t nslots, void* y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return chunk_scan_varlen(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, cu_seqlens,
+                             slot_idx, has_initial_state, state_pool, nslots, nullptr, 0, nullptr, 0, 0, y,
+                             workspace, workspace_bytes, stream);
+}
+
+ssd_status_t ssd_chunk_scan_varlen_snapshots(const ssd_dims_t* d, int32_t chunk, const void* x,
+                                             int64_t x_row_stride, const void* B, const void* C,
+                                             int64_t bc_row_stride, const void* dt, const float* A, const float* D,
+                                             const ssd_dt_params_t* dt_params, const int32_t* cu_seqlens,
+                                             const int32_t* slot_idx, const int32_t* has_initial_state,
+                                             float* state_pool, int64_t nslots, float* snap_pool,
+                                             int64_t nsnap_slots, const int32_t* snap_table, int32_t max_snaps,
+                                             int64_t interval, void* y, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+    if (!d) return SSD_ERR_NULL;
+    if (interval <= 0 || interval % 128 != 0) return SSD_ERR_UNSUPPORTED;
+    if (nsnap_slots < 0 || max_snaps < 0) return SSD_ERR_SHAPE;
+    if (nsnap_slots > 0 && !snap_pool) return SSD_ERR_NULL;
+    if (d->batch > 0 && max_snaps > 0 && !snap_table) return SSD_ERR_NULL;
+    if (snap_pool && !aligned16(snap_pool)) return SSD_ERR_ALIGN;
+    return chunk_scan_varlen(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, cu_seqlens,
+                             slot_idx, has_initial_state, state_pool, nslots, snap_pool, nsnap_slots, snap_table,
+                             max_snaps, interval, y, workspace, workspace_bytes, stream);
 }
 
 ssd_status_t ssd_state_update_slots(const ssd_dims_t* d, float* state_pool, int64_t nslots, const int32_t* slot_idx,

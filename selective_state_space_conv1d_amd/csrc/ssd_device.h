@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_kernels.h"
+
 namespace ssd {
 
 typedef __bf16 bf16;
@@ -90,6 +92,21 @@ __device__ __forceinline__ void seq_span(const int32_t* cu, int64_t s, int64_t t
 __device__ __forceinline__ int64_t seq_slot(const int32_t* slot_idx, int64_t s, int64_t nslots) {
     const int64_t v = slot_idx ? static_cast<int64_t>(slot_idx[s]) : s;
     return (v >= 0 && v < nslots) ? v : -1;
+}
+
+// Where the scan stores the snapshot of head h's state after token t_end of sequence (or batch
+// entry) s of length L, or NULL: t_end must close an interval.  Batched calls fill
+// [B, L / interval, H, P, N]; packed ones the pool slot their table names for (s, interval k).
+__device__ __forceinline__ float* snapshot_dst(const ScanArgs& a, int64_t s, int64_t L, int64_t t_end, int h) {
+    if (!a.snapshots || t_end % a.snap_interval != 0 || t_end > L) return nullptr;
+    const int64_t k = t_end / a.snap_interval - 1;
+    const int64_t pn = static_cast<int64_t>(a.head_dim) * a.d_state;
+    if (a.snap_table) {
+        if (k >= a.snap_max) return nullptr;
+        const int64_t sl = a.snap_table[s * a.snap_max + k];
+        return (sl >= 0 && sl < a.snap_slots) ? a.snapshots + (sl * a.nheads + h) * pn : nullptr;
+    }
+    return a.snapshots + ((s * (L / a.snap_interval) + k) * a.nheads + h) * pn;
 }
 
 }  // namespace ssd

@@ -57,8 +57,11 @@ struct ScanArgs {
     int nheads, head_dim, ngroups, d_state, chunk;
     SeqMap seq;   // varlen: init_state / final_state are the state pool
     DtParams dtp;
-    float* snapshots;        // [B, L / snap_interval, H, P, N]: state after every snap_interval tokens, or NULL
+    float* snapshots;        // [B, L / snap_interval, H, P, N]: state after every snap_interval tokens, or NULL;
+                             // with snap_table: the snapshot pool [snap_slots, H, P, N]
     int64_t snap_interval;   // a positive multiple of 128 when snapshots is set
+    const int32_t* snap_table;   // packed sequences: [S, snap_max] pool slot per (sequence, interval), or NULL
+    int64_t snap_max, snap_slots;
     int64_t nranges;         // set by the launcher: sequence ranges per head (workgroups = nranges * nheads)
 };
 

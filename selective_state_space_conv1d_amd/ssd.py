@@ -24,7 +24,7 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
            "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
-           "ssd_conv1d_update_accept"]
+           "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots"]
 
 
 class SsdDims(ctypes.Structure):
@@ -78,6 +78,9 @@ def _lib():
         lib.ssd_conv1d_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
         lib.ssd_chunk_scan_varlen.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
                                               _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
+        lib.ssd_chunk_scan_varlen_snapshots.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT,
+                                                        _VP, _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I32, _I64, _VP,
+                                                        _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
                                                _PDT, _VP, _VP]
         lib.ssd_state_update_multi.argtypes = [_PD, _VP, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
@@ -97,7 +100,8 @@ def _lib():
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
                   "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
-                  "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept"):
+                  "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept",
+                  "ssd_chunk_scan_varlen_snapshots"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -341,11 +345,15 @@ def ssd_conv1d_update_slots(xbc, w, bias, conv_state_pool, slot_idx, out=None, n
 
 def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None,
                           has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None,
-                          dt_bias=None, dt_softplus=False, dt_limit=None):
+                          dt_bias=None, dt_softplus=False, dt_limit=None, snapshot_pool=None, snapshot_table=None,
+                          snapshot_interval=None):
     """SSD chunked scan of a packed batch.  x [T, H, P], B/C [T, G, N] (token rows may be strided,
     e.g. views into the varlen conv output), dt [T, H], A [H] fp32, D [H] fp32|None,
     cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, state_pool
-    [nslots, H, P, N] fp32|None, updated in place.  Returns y [T, H, P] in y_dtype (default x's)."""
+    [nslots, H, P, N] fp32|None, updated in place.  With snapshot_table [S, max_snaps] int32 the
+    state after every snapshot_interval tokens of sequence s goes to snapshot_pool
+    [nsnap_slots, H, P, N] fp32 slot snapshot_table[s, k] (ssd_chunk_scan_varlen_snapshots).
+    Returns y [T, H, P] in y_dtype (default x's)."""
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     S = cu_seqlens.numel() - 1
@@ -373,13 +381,32 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     xs, bcs = (P * H, G * N) if T == 0 else (x.stride(0), B.stride(0))
     if T == 0:
         x = B = C = dt = None
-    _check(_lib().ssd_chunk_scan_varlen(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
-                                        _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
-                                        _ptr(_table(cu_seqlens, S + 1, "cu_seqlens")),
-                                        _ptr(_table(slot_idx, S, "slot_idx")),
-                                        _ptr(_table(has_initial_state, S, "has_initial_state")),
-                                        _ptr(state_pool), nslots, _ptr(y), _ptr(workspace), ws, _stream(stream)),
-           "ssd_chunk_scan_varlen")
+    tabs = (_ptr(_table(cu_seqlens, S + 1, "cu_seqlens")), _ptr(_table(slot_idx, S, "slot_idx")),
+            _ptr(_table(has_initial_state, S, "has_initial_state")))
+    if snapshot_table is None:
+        _check(_lib().ssd_chunk_scan_varlen(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
+                                            _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), *tabs,
+                                            _ptr(state_pool), nslots, _ptr(y), _ptr(workspace), ws, _stream(stream)),
+               "ssd_chunk_scan_varlen")
+        return y
+    if snapshot_interval is None:
+        raise ValueError("snapshot_table needs snapshot_interval")
+    if (snapshot_table.dim() != 2 or snapshot_table.shape[0] != S or snapshot_table.dtype != torch.int32
+            or not snapshot_table.is_contiguous() or snapshot_table.device != x.device):
+        raise ValueError("snapshot_table must be contiguous int32 [S, max_snaps] on the scan's device")
+    nsnap = 0
+    if snapshot_pool is not None:
+        if (snapshot_pool.dim() != 4 or snapshot_pool.shape[1:] != (H, P, N) or snapshot_pool.dtype != torch.float32
+                or not snapshot_pool.is_contiguous()):
+            raise ValueError("snapshot_pool must be contiguous fp32 [nsnap_slots, H, P, N]")
+        nsnap = snapshot_pool.shape[0]
+    _check(_lib().ssd_chunk_scan_varlen_snapshots(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
+                                                  _ptr(dt), _ptr(A), _ptr(D),
+                                                  _dt_params(dt_bias, dt_softplus, dt_limit), *tabs,
+                                                  _ptr(state_pool), nslots, _ptr(snapshot_pool), nsnap,
+                                                  _ptr(snapshot_table), snapshot_table.shape[1], snapshot_interval,
+                                                  _ptr(y), _ptr(workspace), ws, _stream(stream)),
+           "ssd_chunk_scan_varlen_snapshots")
     return y
 
 

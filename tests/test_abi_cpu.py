@@ -268,6 +268,30 @@ def test_snapshot_scan_validation(ssd, lib):
                                         None, fp(9), 128, fp(6), None, 0, None) == E["SSD_ERR_NULL"]
 
 
+def test_scan_varlen_snapshots_validation(ssd, lib):
+    """The packed scan with snapshots rejects a bad interval, a missing pool or table, negative
+    sizes and a misaligned pool before any launch; the packed scan's own checks still apply."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=3, seqlen=300)
+
+    def snap(dd=d, pool=fp(9), nsnap=4, table=fp(10), maxs=2, iv=128, x=fp(1), cu=fp(11)):
+        return lib.ssd_chunk_scan_varlen_snapshots(ctypes.byref(dd), 128, x, 256, fp(2), fp(3), 256, fp(4), fp(5),
+                                                   None, None, cu, None, None, None, 0, pool, nsnap, table, maxs, iv,
+                                                   fp(6), None, 0, None)
+    assert snap(iv=0) == E["SSD_ERR_UNSUPPORTED"]
+    assert snap(iv=192) == E["SSD_ERR_UNSUPPORTED"]
+    assert snap(pool=None) == E["SSD_ERR_NULL"]
+    assert snap(table=None) == E["SSD_ERR_NULL"]
+    assert snap(nsnap=-1) == E["SSD_ERR_SHAPE"]
+    assert snap(maxs=-1) == E["SSD_ERR_SHAPE"]
+    assert snap(pool=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert snap(cu=None) == E["SSD_ERR_NULL"]                   # the packed scan's own checks still apply
+    assert snap(x=None) == E["SSD_ERR_NULL"]
+    assert lib.ssd_chunk_scan_varlen_snapshots(None, 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None, None,
+                                               fp(11), None, None, None, 0, fp(9), 4, fp(10), 2, 128, fp(6), None, 0,
+                                               None) == E["SSD_ERR_NULL"]
+
+
 def test_gated_rmsnorm_validation(ssd, lib):
     """The gated norm rejects bad host arguments before any launch."""
     E = {n: i for i, n in enumerate(ssd.STATUS)}

@@ -52,7 +52,7 @@ def test_scan_varlen_mfma(orc, slow):
     pool = pool0.clone()
     y = run_scan_varlen(s, cu, slot, hi, pool)
     yr, pr = orc.scan_varlen(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), f64(s["dt"]), f64(s["A"]), f64(s["D"]),
-                             np.array(cu.cpu()), f64(pool0), np.array(slots), np.array(has_init))
+                             cu.cpu().numpy(), f64(pool0), np.array(slots), np.array(has_init))
     assert_close(y, yr, BF16_BAR, "y")
     named = [k for k in slots if 0 <= k < nslots]
     assert_close(pool[named], pr[named], BF16_BAR, "final states")
@@ -75,7 +75,7 @@ def test_scan_varlen_fp32_path(orc):
     pool = pool0.clone()
     y = run_scan_varlen(s, cu, slot, hi, pool, chunk=64)
     yr, pr = orc.scan_varlen(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), f64(s["dt"]), f64(s["A"]), f64(s["D"]),
-                             np.array(cu.cpu()), f64(pool0), np.array(slots), np.array(has_init))
+                             cu.cpu().numpy(), f64(pool0), np.array(slots), np.array(has_init))
     assert_close(y, yr, F32_BAR, "y")
     assert_close(pool, pr, F32_BAR, "pool")
 
@@ -110,6 +110,59 @@ def test_scan_varlen_no_tokens_copies_or_zeroes_states():
     assert not pool[0].any(), "an empty sequence without an initial state ends at zero"
 
 
+# (H, P, G, N, dtype, chunk, lens): the MFMA scan walking sequence ranges (64 heads, 14 requests),
+# and the FMA scan (fp32, chunk 64, one request per workgroup)
+SNAP_CASES = [(64, 64, 8, 128, torch.bfloat16, 128, [0, 300, 128, 1, 700, 256, 5, 129, 384, 2, 40, 511, 127, 260]),
+              (4, 16, 1, 16, torch.float32, 64, [130, 0, 256, 5, 400])]
+
+
+@pytest.mark.parametrize("case", range(len(SNAP_CASES)))
+def test_scan_varlen_snapshots(orc, case):
+    H, P, G, N, dtype, chunk, lens = SNAP_CASES[case]
+    d = LayerDims(1, 1, H, P, G, N, chunk=chunk, dtype=dtype)
+    s = packed_scan(d, lens, 240 + case)
+    S, iv = len(lens), 128
+    r = np.random.default_rng(241 + case)
+    nslots = S + 2
+    slots = r.permutation(nslots)[:S].astype(np.int32)
+    slots[3] = -1
+    has_init = (r.random(S) < 0.5).astype(np.int32)
+    cu, slot, hi = tables(lens, slots, has_init)
+    maxs = 5
+    nsnap = S * maxs // 2
+    table = np.full((S, maxs), -1, dtype=np.int32)
+    free = list(r.permutation(nsnap + 3))          # distinct slots, a few past the pool's end
+    for q in range(S):
+        for k in range(maxs):
+            if free and r.random() < 0.8:
+                table[q, k] = free.pop()
+    pool0 = torch.randn(nslots, H, P, N, device=DEV) * 0.1
+    snap0 = torch.randn(nsnap, H, P, N, device=DEV)
+    pool, snaps = pool0.clone(), snap0.clone()
+    tab = torch.tensor(table, device=DEV)
+    y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], cu, pool, slot, hi, chunk=chunk,
+                                  y_dtype=torch.float32, snapshot_pool=snaps, snapshot_table=tab,
+                                  snapshot_interval=iv)
+    pool2 = pool0.clone()
+    y2 = run_scan_varlen(s, cu, slot, hi, pool2, chunk=chunk)
+    assert torch.equal(y, y2) and torch.equal(pool, pool2), "snapshots must not change y or the states"
+    hpg = H // G
+    heads = list(range(H)) if H <= 4 else [g * hpg + (5 * g) % hpg for g in range(0, G, 3)]
+    bar = F32_BAR if dtype == torch.float32 else BF16_BAR
+    for h in heads:
+        g = h // hpg
+        yr, pr, sr = orc.scan_varlen_snapshots(
+            f64(s["x"][:, h:h + 1]), f64(s["Bm"][:, g:g + 1]), f64(s["Cm"][:, g:g + 1]), f64(s["dt"][:, h:h + 1]),
+            f64(s["A"][h:h + 1]), f64(s["D"][h:h + 1]), cu.cpu().numpy(), f64(pool0[:, h:h + 1]), slots, has_init,
+            f64(snap0[:, h:h + 1]), table, iv)
+        assert_close(y[:, h], yr[:, 0], bar, f"y head {h}")
+        assert_close(snaps[:, h], sr[:, 0], bar, f"snapshot pool head {h}")
+    written = {int(table[q, k]) for q in range(S) for k in range(min(lens[q] // iv, maxs))
+               if 0 <= table[q, k] < nsnap}
+    kept = [k for k in range(nsnap) if k not in written]
+    assert torch.equal(snaps[kept], snap0[kept]), "slots the table does not name for a reached interval are untouched"
+
+
 # --------------------------------------------------------------------------- conv
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_conv_varlen(orc, dtype):
@@ -127,7 +180,7 @@ def test_conv_varlen(orc, dtype):
     pool = pool0.clone()
     v = ssd.ssd_conv1d_fwd_varlen(xbc, w, bias, cu, pool, slot, hi)
     torch.cuda.synchronize()
-    vr, pr = orc.conv1d_fwd_varlen(f64(xbc), f64(w), f64(bias), np.array(cu.cpu()), f64(pool0), np.array(slots),
+    vr, pr = orc.conv1d_fwd_varlen(f64(xbc), f64(w), f64(bias), cu.cpu().numpy(), f64(pool0), np.array(slots),
                                    np.array(has_init))
     if dtype == torch.bfloat16:
         assert_bf16_elementwise(v.cpu(), vr, "conv out")
@@ -146,7 +199,7 @@ def test_conv_varlen_strided_rows_and_no_pool(orc):
     cu, _, _ = tables(lens, None, None)
     v = ssd.ssd_conv1d_fwd_varlen(xbc, w, None, cu)
     torch.cuda.synchronize()
-    vr, _ = orc.conv1d_fwd_varlen(f64(xbc), f64(w), None, np.array(cu.cpu()))
+    vr, _ = orc.conv1d_fwd_varlen(f64(xbc), f64(w), None, cu.cpu().numpy())
     assert_bf16_elementwise(v.cpu(), vr, "conv out")
 
 
@@ -220,9 +273,9 @@ def test_varlen_ultra_serving_mix(orc):
                                   inp["slot_idx"], inp["has_initial_state"], y_dtype=torch.float32)
     torch.cuda.synchronize()
     del tab
-    cu = np.array(inp["cu_seqlens"].cpu())
-    slots = np.array(inp["slot_idx"].cpu())
-    hinit = np.array(inp["has_initial_state"].cpu())
+    cu = inp["cu_seqlens"].cpu().numpy()
+    slots = inp["slot_idx"].cpu().numpy()
+    hinit = inp["has_initial_state"].cpu().numpy()
     hpg = d.nheads // d.ngroups
     I, GN, N, P = d.d_inner, d.ngroups * d.d_state, d.d_state, d.head_dim
     for g in range(d.ngroups):

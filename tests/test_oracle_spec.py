@@ -84,6 +84,42 @@ def test_single_candidate_is_the_plain_update(orc):
     assert np.array_equal(y[:, 0], yr) and np.array_equal(inter[:, 0], sr)
 
 
+def test_scan_varlen_snapshots_are_the_prefix_states(orc):
+    """Packed sequences with snapshots into a pool: the slot that the table names for (sequence s,
+    interval k) holds the brute-force final state of that sequence's first (k + 1) * interval
+    tokens, from its initial state when it has one; table entries past a sequence's snapshot
+    count, negative ones and ones outside the pool store nothing; y and the state pool are the
+    plain packed scan's."""
+    r = np.random.default_rng(16)
+    lens, H, P, G, N, iv = [11, 0, 4, 16, 5], 4, 3, 2, 5, 5
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = r.standard_normal((T, H, P))
+    Bm = r.standard_normal((T, G, N))
+    Cm = r.standard_normal((T, G, N))
+    dt = softplus(r.normal(-2.0, 1.0, (T, H)))
+    A = -np.exp(r.uniform(0, 1, H))
+    D = r.standard_normal(H)
+    pool = r.standard_normal((6, H, P, N))
+    slot, has_init = np.array([3, 0, -1, 5, 1]), np.array([1, 0, 0, 1, 0])
+    snap0 = r.standard_normal((9, H, P, N))
+    table = np.array([[2, 7, 8], [4, -1, 0], [0, 1, 2], [6, 3, 9], [5, -2, 1]])
+    y, newp, snaps = orc.scan_varlen_snapshots(x, Bm, Cm, dt, A, D, cu, pool, slot, has_init, snap0, table, iv)
+    yr, pr = orc.scan_varlen(x, Bm, Cm, dt, A, D, cu, pool, slot, has_init)
+    assert rel_err(y, yr) == 0 and rel_err(newp, pr) == 0
+    want = snap0.copy()
+    for s, L in enumerate(lens):
+        S0 = pool[slot[s]][None] if slot[s] >= 0 and has_init[s] else np.zeros((1, H, P, N))
+        for k in range(min(L // iv, table.shape[1])):
+            if 0 <= table[s, k] < 9:
+                a, e = cu[s], cu[s] + (k + 1) * iv
+                _, fr = semiseparable_scan(x[None, a:e], Bm[None, a:e], Cm[None, a:e], dt[None, a:e], A, D, S0)
+                want[table[s, k]] = fr[0]
+    assert rel_err(snaps, want) < 1e-12
+    # slot 8 is named only by sequence 0's third interval, which its 11 tokens do not reach
+    assert np.array_equal(snaps[8], snap0[8]), "an entry past a sequence's snapshot count stores nothing"
+
+
 def test_scan_snapshots_are_the_prefix_states(orc):
     """State snapshots every `interval` tokens ("modeling_nemotron_h.py" walk-through page,
     部署时如何调这些缓存: a state snapshot every N tokens): snapshot k equals the brute-force final
