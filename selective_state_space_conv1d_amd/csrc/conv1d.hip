@@ -18,7 +18,9 @@
 namespace ssd {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvTokens = 32;  // tokens per thread in the prefill conv
+// tokens per thread in the prefill conv: 24 measured fastest (prefill 1 x 8192 x 18432: 16 or 12 within
+// 2 %, 32 and 20 7-10 % slower: fewer workgroups per CU round)
+constexpr int kConvTokens = 24;
 
 // Rows [ta, tb) of one thread's channel vector: out[t] = silu(bias + sum_k w[k] * in[t-3+k]), with
 // win holding the inputs at ta-3..ta-1 on entry.  Four rows are loaded before any is used, so each
