@@ -45,8 +45,9 @@
  *   update: the scan with one token, state updated in place.
  *
  * Ownership: the caller allocates and frees every buffer (device memory);
- * the library allocates nothing and holds no state between calls, so calls
- * on different streams are independent.  Nothing synchronises.
+ * the library allocates nothing and holds no state between calls beyond a
+ * per-device cache of the compute-unit count (thread-safe), so calls on
+ * different streams are independent.  Nothing synchronises.
  * Errors: every argument is checked on the host before anything is launched;
  * a call that returns an error has launched nothing and written nothing.
  * A launch failure returns SSD_ERR_HIP.  No call throws.
