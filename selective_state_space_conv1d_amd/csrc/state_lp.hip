@@ -25,8 +25,10 @@ constexpr int kLpPerThread = 2;   // octets per thread
 // Philox4x32-R: per round, words 0 and 2 are multiplied by the two multipliers; the high halves
 // of the products are mixed with words 1 and 3 and the key, the low halves become words 1 and 3.
 // The key advances by the Weyl increments before each round after the first.
-__device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int rounds) {
-    for (int r = 0; r < rounds; ++r) {
+template <int R>   // R > 0: that many rounds, unrolled; R = 0: `rounds` rounds
+__device__ __forceinline__ void philox4x32_r(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int rounds) {
+#pragma unroll
+    for (int r = 0; r < (R > 0 ? R : rounds); ++r) {
         if (r) {
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
@@ -40,6 +42,13 @@ __device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32
         c[2] = n2;
         c[3] = static_cast<uint32_t>(p0);
     }
+}
+
+// 5 rounds (the engine setting on the modeling_nemotron_h.py walk-through page, 部署时如何调这些缓存)
+// run unrolled; other round counts loop.
+__device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int rounds) {
+    if (rounds == 5) philox4x32_r<5>(c, k0, k1, rounds);
+    else philox4x32_r<0>(c, k0, k1, rounds);
 }
 
 // 16-bit storage formats: decode to fp32, round-to-nearest-even, stochastic rounding.
