@@ -6,8 +6,8 @@
 //
 // All three kernels are HBM streams with no reuse across threads:
 //  * the SSM update reads each fp32 state element once and writes it k times (one intermediate
-//    state per candidate), with the single-token update's walk of the state as flat float4 and
-//    its arithmetic, in the same order, so k = 1 reproduces it bitwise;
+//    state per candidate), with the single-token update's arithmetic and y summation order, so
+//    k = 1 reproduces it bitwise (a replay mode re-applies accepted tokens in place instead);
 //  * the conv update keeps one 16-byte channel vector's 4-column window in registers across
 //    the k tokens and writes the window after each;
 //  * accept copies one intermediate state per request in 16-byte units.
