@@ -13,7 +13,11 @@
 //
 // Mapping.  One persistent workgroup of 8 waves (two per SIMD) per (batch,
 // head) walks the chunks in order; the fp32 state stays in registers and never
-// goes to HBM between chunks.  The waves have fixed roles:
+// goes to HBM between chunks.  When sequences x heads overfill the chip and the
+// sequences are short, a workgroup instead walks the chunks of a token-balanced
+// range of sequences as one flat (sequence, chunk) stream, handing the state over
+// at each sequence end (the WALK kernel).  Token rows past a chunk's end are
+// skipped.  The waves have fixed roles:
 //   * y waves 0..3: wave t owns the 32 tokens of token tile t and both 32-wide
 //     p tiles.  It keeps its tokens' C rows in registers (the B operand of both
 //     C.H and C.B^T) and loads the next chunk's rows itself, straight into
