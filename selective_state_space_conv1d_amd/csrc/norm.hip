@@ -2,15 +2,17 @@
 // fused kernel, gate applied before the norm, fp32 arithmetic and an fp32 weight):
 //   v = y * silu(z);  out = v / sqrt(mean over the group of v^2 + eps) * weight.
 // One workgroup per (row, group).  Each thread takes 8-channel vectors of the group (16-byte loads
-// of bf16); the first pass sums v^2 (wave reduction, then across the waves in LDS), the second
-// recomputes v from y and z, which the first pass left in the cache, and writes the result.  The
-// kernel moves y and z in and out back once: an HBM stream.
+// of bf16); the first pass forms v and sums v^2 (wave reduction, then across the waves in LDS),
+// the second scales v, held in registers (or, for groups of more than 4096 channels, recomputed
+// from y and z, which the first pass left in the cache), and writes the result.  The kernel reads
+// y and z and writes the output once: an HBM stream.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
 
 constexpr int kNormThreads = 256;
+constexpr int kNormHold = 2;   // 8-channel vectors per thread held in registers between the two passes
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&o)[8]) {
@@ -35,8 +37,26 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const TY* _
     const int64_t c0 = static_cast<int64_t>(g) * gs;
     const TY* yr = y + row * ys + c0;
     const T* zr = z + row * zs + c0;
+    constexpr int kSpan = 8 * kNormThreads;   // channels per pass of the workgroup
+    // the first kNormHold vectors of each thread keep v = y * silu(z) in registers for the second
+    // pass (groups up to 8 * 256 * kNormHold channels); later ones are re-read there
+    float vh[kNormHold][8];
     float ss = 0.f;
-    for (int c = 8 * threadIdx.x; c < gs; c += 8 * kNormThreads) {
+#pragma unroll
+    for (int k = 0; k < kNormHold; ++k) {
+        const int c = 8 * threadIdx.x + k * kSpan;
+        if (c < gs) {
+            float yv[8], zv[8];
+            load8(yr + c, yv);
+            load8(zr + c, zv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vh[k][e] = yv[e] * silu_f(zv[e]);
+                ss = fmaf(vh[k][e], vh[k][e], ss);
+            }
+        }
+    }
+    for (int c = 8 * threadIdx.x + kNormHold * kSpan; c < gs; c += kSpan) {
         float yv[8], zv[8];
         load8(yr + c, yv);
         load8(zr + c, zv);
@@ -55,7 +75,18 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const TY* _
     for (int k = 0; k < kNormThreads / 64; ++k) tot += part[k];
     const float r = rsqrtf(tot / static_cast<float>(gs) + eps);
     T* orow = out + row * I + c0;
-    for (int c = 8 * threadIdx.x; c < gs; c += 8 * kNormThreads) {
+#pragma unroll
+    for (int k = 0; k < kNormHold; ++k) {
+        const int c = 8 * threadIdx.x + k * kSpan;
+        if (c < gs) {
+            float wv[8], o[8];
+            load8(w + c0 + c, wv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = vh[k][e] * r * wv[e];
+            store8(orow + c, o);
+        }
+    }
+    for (int c = 8 * threadIdx.x + kNormHold * kSpan; c < gs; c += kSpan) {
         float yv[8], zv[8], wv[8], o[8];
         load8(yr + c, yv);
         load8(zr + c, zv);

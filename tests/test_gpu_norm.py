@@ -22,7 +22,7 @@ def norm_inputs(rows, I, ydt, zdt, seed, zpad=0):
 
 @pytest.mark.parametrize("ydt,zdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
                                      (torch.float32, torch.float32)])
-@pytest.mark.parametrize("I,G", [(256, 2), (2048, 8), (96, 4)])
+@pytest.mark.parametrize("I,G", [(256, 2), (2048, 8), (96, 4), (12288, 1)])   # the last: a group past the registers
 def test_gated_rmsnorm(orc, ydt, zdt, I, G):
     y, z, w = norm_inputs(37, I, ydt, zdt, 600, zpad=64)     # z is a strided view (row stride I + 64)
     out = ssd.ssd_gated_rmsnorm(y, z, w, G, eps=1e-5)
