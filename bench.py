@@ -88,7 +88,7 @@ def conv_bytes(d, L):
 def update_bytes(d):
     """State read + write (fp32) + x, B, C, dt in and y out (bf16) for one token."""
     st = d.batch * d.nheads * d.head_dim * d.d_state * 4 * 2
-    io = d.batch * (d.nheads * d.head_dim * 2 + 2 * d.ngroups * d.d_state + d.nheads + d.nheads * d.head_dim) * 2
+    io = d.batch * (2 * d.nheads * d.head_dim + 2 * d.ngroups * d.d_state + d.nheads) * 2
     return st + io
 
 
@@ -268,7 +268,7 @@ def lowprec_leg(ssd, torch, dev, steps, warmup):
     s = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(dd, 1030, seqlen=1).items()}
     args = (s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], s["dt"][:, 0].contiguous(), s["A"], s["D"])
     y = torch.empty(B, H, P, dtype=dd.dtype, device=dev)
-    io = B * (H * P * 2 + 2 * dd.ngroups * N + H + H * P) * 2
+    io = B * (2 * H * P + 2 * dd.ngroups * N + H) * 2   # x in and y out, B and C, dt (bf16)
     alg = B * H * P * N * 2 * 2 + io
     out = {"batch": B, "state_bytes_per_request": H * P * N * 2, "algorithmic_bytes": alg}
     for name, sdt, rounds in (("f16_sr5", torch.float16, 5), ("f16_rne", torch.float16, 0),
