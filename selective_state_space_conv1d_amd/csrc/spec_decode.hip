@@ -19,7 +19,9 @@
 namespace ssd {
 
 constexpr int kMultiThreads = 128;
-constexpr int kMultiPerThread = 2;   // measured best at batch 64, k = 4 (4 per thread: 30 % slower)
+// float4 of one state row per thread: 2 (with rows split one float4 per thread, 2 measured best at
+// batch 64, k = 4, and 4 ran 30 % slower; 4 of one row would also leave rows of N = 16 one lane)
+constexpr int kMultiPerThread = 2;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyPerThread = 4;
 
