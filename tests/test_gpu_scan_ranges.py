@@ -99,8 +99,9 @@ def test_varlen_range_of_empty_sequences_only():
 
 
 @pytest.mark.parametrize("snap", [False, True])
-def test_batched_ranges_match_one_call_per_entry(orc, snap):
-    H, B, L = 16, 40, 256
+@pytest.mark.parametrize("L", [256, 300])     # exact chunks; a ragged last chunk in every entry
+def test_batched_ranges_match_one_call_per_entry(orc, snap, L):
+    H, B = 16, 40
     d = LayerDims(B, L, H, 64, 2, 128)
     s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 720).items()}
     kw = dict(y_dtype=torch.float32)
@@ -127,3 +128,26 @@ def test_batched_ranges_match_one_call_per_entry(orc, snap):
                             f64(s["A"][h:h + 1]), f64(s["D"][h:h + 1]), f64(s["init_state"][b:b + 1, h:h + 1]))
     assert_close(y[b:b + 1, :, h:h + 1], yr, BF16_BAR, "y")
     assert_close(fin[b:b + 1, h:h + 1], fr, BF16_BAR, "final state")
+
+
+def test_varlen_ranges_without_tables():
+    """No slot table (sequence s uses slot s) and no initial-state flags (every sequence starts from
+    zeros): the walk equals one call per sequence, and every slot receives its final state."""
+    H, S = 256, 30
+    lens = mixed_lengths(S, 730)
+    d, s = packed(H, lens, 731)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pool0 = torch.randn(S, H, 64, 128, device=DEV)
+    pool = pool0.clone()
+    y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], i32(cu), pool,
+                                  y_dtype=torch.float32)
+    pool1 = pool0.clone()
+    y1 = torch.empty_like(y)
+    for q in range(S):
+        a, b = int(cu[q]), int(cu[q + 1])
+        y1[a:b] = ssd.ssd_chunk_scan_varlen(s["x"][a:b], s["Bm"][a:b], s["Cm"][a:b], s["dt"][a:b], s["A"], s["D"],
+                                            i32([0, b - a]), pool1[q:q + 1], y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1) and torch.equal(pool, pool1)
+    empty = [q for q in range(S) if lens[q] == 0]
+    assert all(not pool[q].any() for q in empty), "an empty sequence without an initial state ends at zero"
