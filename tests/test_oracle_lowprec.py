@@ -149,3 +149,84 @@ def test_lp_update_a0_codes_round_the_fp64_update(orc):
                 assert np.array_equal(new[s], codes[s])
     y, st = orc.state_update_lp(codes, "bf16", None, x, Bm, Cm, dt, np.zeros(H))
     assert rel_err(st[0], orc.state_update(lp.decode(codes[:3], "bf16"), x, Bm, Cm, dt, np.zeros(H))[1][0]) == 0
+
+
+# ----------------------------------------------------------------------------- element -> counter
+# The Philox number that rounds a state element is selected by the element's flat index in the
+# pool, so it follows the element's pool slot, not the request's position in the batch.  The three
+# pins below fix that mapping without re-deriving it from the oracle's own formula: a batch
+# permutation, a reshaping of the pool that keeps every element's flat index, and an absolute
+# count on a tiny pool whose halfway values expose the top bit of each 16-bit number.
+
+def _a0_inputs(r, Bt, H, P, G, N):
+    x = r.standard_normal((Bt, H, P)).astype(np.float32)
+    Bm = r.standard_normal((Bt, G, N)).astype(np.float32)
+    Cm = r.standard_normal((Bt, G, N)).astype(np.float32)
+    dt = softplus(r.normal(-2, 1, (Bt, H))).astype(np.float32)
+    return x, Bm, Cm, dt
+
+
+def test_lp_codes_follow_the_slot_not_the_batch_position(orc):
+    r = np.random.default_rng(21)
+    Bt, H, P, G, N, nslots = 4, 2, 8, 1, 16, 6
+    x, Bm, Cm, dt = _a0_inputs(r, Bt, H, P, G, N)
+    slot = np.array([5, 0, 3, 2])
+    for fmt in ("f16", "bf16"):
+        codes = lp.round_state((r.standard_normal((nslots, H, P, N)) * 0.1).astype(np.float32), fmt)
+        want = orc.state_update_lp_codes_a0(codes, fmt, slot, x, Bm, Cm, dt, (77, 3, 5))
+        for perm in ([3, 2, 1, 0], [1, 3, 0, 2]):
+            got = orc.state_update_lp_codes_a0(codes, fmt, slot[perm], x[perm], Bm[perm], Cm[perm], dt[perm],
+                                               (77, 3, 5))
+            assert np.array_equal(got, want), (fmt, perm)
+        # the same request and starting values in another slot draw other numbers: with slots 1 and 5
+        # holding equal codes, moving request 0 from slot 5 to slot 1 changes some of its codes
+        twin = codes.copy()
+        twin[1] = twin[5]
+        at5 = orc.state_update_lp_codes_a0(twin, fmt, slot, x, Bm, Cm, dt, (77, 3, 5))
+        at1 = orc.state_update_lp_codes_a0(twin, fmt, np.array([1, 0, 3, 2]), x, Bm, Cm, dt, (77, 3, 5))
+        assert not np.array_equal(at1[1], at5[5]), fmt
+        assert np.array_equal(orc.state_update_lp_codes_a0(twin, fmt, slot, x, Bm, Cm, dt, None)[5],
+                              orc.state_update_lp_codes_a0(twin, fmt, np.array([1, 0, 3, 2]), x, Bm, Cm, dt,
+                                                           None)[1]), fmt
+
+
+def test_lp_codes_depend_on_the_flat_pool_index(orc):
+    """Slot s of a pool [S, H, P, N] holds the flat elements [s*H*P*N, (s+1)*H*P*N): a request in slot 1
+    of a 2-slot pool of H heads is rounded exactly like heads H..2H-1 of a 1-slot pool of 2H heads
+    holding the same values (A = 0, each head's B from a group of its own)."""
+    r = np.random.default_rng(22)
+    H, P, N = 2, 4, 16
+    x, Bm, Cm, dt = _a0_inputs(r, 1, H, P, H, N)
+    for fmt in ("f16", "bf16"):
+        st = lp.round_state((r.standard_normal((2, H, P, N)) * 0.1).astype(np.float32), fmt)
+        two = orc.state_update_lp_codes_a0(st, fmt, np.array([1]), x, Bm, Cm, dt, (5, 9, 5))
+        wide = st.reshape(1, 2 * H, P, N)
+        z = np.zeros_like(x)
+        one = orc.state_update_lp_codes_a0(wide, fmt, None, np.concatenate([z, x], 1),
+                                           np.concatenate([Bm, Bm], 1), np.concatenate([Cm, Cm], 1),
+                                           np.concatenate([dt, dt], 1), (5, 9, 5))
+        assert np.array_equal(one[0, H:], two[1]), fmt
+        assert np.array_equal(two[0], st[0]), fmt                        # slot 0 is not in the batch
+
+
+def test_lp_codes_absolute_index_on_a_tiny_pool(orc):
+    """Every element of the request sits exactly halfway between two codes, so it rounds up iff its
+    16-bit number is below 2^15.  Slot 2 of a pool of 16-element slots covers flat elements 32..47,
+    i.e. Philox blocks 4 and 5 (8 elements per block, two 16-bit halves per word, low half first);
+    using the batch position, or starting one block off, changes the pattern."""
+    H, P, N = 1, 2, 8
+    seed, offset, rounds = 0x1234ABCD, 11, 5
+    for fmt, half in (("f16", 2.0 ** -11), ("bf16", 2.0 ** -8)):
+        ones = lp.round_state(np.ones((3, H, P, N), np.float32), fmt)
+        x = np.ones((1, H, P), np.float32)
+        Bm = np.full((1, 1, N), half, np.float32)
+        dt = np.ones((1, H), np.float32)
+        got = orc.state_update_lp_codes_a0(ones, fmt, np.array([2]), x, Bm, Bm, dt, (seed, offset, rounds))
+        up = lp.decode(got[2], fmt).ravel() > 1.0
+        want = []
+        for block in (4, 5):
+            words = lp.philox4((block, 0, offset, 0), (seed, 0), rounds)
+            for k in range(8):
+                want.append(((words[k // 2] >> (16 * (k % 2))) & 0xFFFF) < 0x8000)
+        assert up.tolist() == want, fmt
+        assert np.array_equal(got[:2], ones[:2])
