@@ -64,12 +64,12 @@ def traffic_rate(kernel, seconds):
     return None if b is None else b / seconds / 1e9
 
 
-def scan_bytes(d):
+def scan_bytes(d, init=False):
     """Algorithmic HBM bytes of one chunk-scan launch: read x, B, C, dt once, write y and
-    the final fp32 state once (no initial state in this workload)."""
+    the final fp32 state once, and read the initial fp32 state when there is one."""
     per_token = 2 * (d.nheads * d.head_dim) * 2 + 2 * d.ngroups * d.d_state * 2 + d.nheads * 2
     state = d.batch * d.nheads * d.head_dim * d.d_state * 4
-    return d.batch * d.seqlen * per_token + state
+    return d.batch * d.seqlen * per_token + state * (2 if init else 1)
 
 
 def scan_flops(d):
@@ -351,6 +351,148 @@ def decode_step_leg(ssd, torch, dev, steps, warmup):
             "frac": alg / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": alg}
 
 
+def timed_launches(torch, fns, steps, warmup):
+    """Average seconds of each callable in fns, run in order once per step; each launch bracketed
+    by HIP events on the current stream."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        for j, f in enumerate(fns):
+            evs[i][j].record()
+            f()
+        evs[i][-1].record()
+    torch.cuda.synchronize()
+    return [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1e-3 for j in range(len(fns))]
+
+
+def continuation_leg(ssd, torch, dev, steps, warmup):
+    """Chunked-prefill continuation, 128 heads: batch 8 x 4096 tokens continuing a prior 4096-token
+    prefill of the same rows (its fp32 final states and conv windows are the initial states):
+    ssd_conv1d_fwd with the conv state, then ssd_chunk_scan from the initial state."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, mixer_inputs
+    d = WORKLOADS["continuation_h128_b8"]
+    full = mixer_inputs(d, 1003, device=dev, seqlen=2 * d.seqlen)
+    L = d.seqlen
+    first = {k: (full[k][:, :L].contiguous() if k in ("xbc", "dt") else full[k]) for k in full}
+    second = {k: (full[k][:, L:].contiguous() if k in ("xbc", "dt") else full[k]) for k in full}
+    del full
+    v = torch.empty(d.batch, L, d.conv_dim, dtype=d.dtype, device=dev)
+    x, Bm, Cm = ssd.split_xbc(v, d.nheads, d.head_dim, d.ngroups, d.d_state)
+    cs1 = torch.empty(d.batch, d.conv_dim, 4, dtype=d.dtype, device=dev)
+    st1 = torch.empty(d.batch, d.nheads, d.head_dim, d.d_state, device=dev)
+    y = torch.empty(d.batch, L, d.nheads, d.head_dim, dtype=d.dtype, device=dev)
+    ssd.ssd_conv1d_fwd(first["xbc"], first["w"], first["bias"], None, cs1, out=v)
+    ssd.ssd_chunk_scan(x, Bm, Cm, first["dt"], first["A"], first["D"], None, st1, y=y, chunk=d.chunk)
+    cs2 = torch.empty_like(cs1)
+    st2 = torch.empty_like(st1)
+    conv_s, scan_s = timed_launches(torch, [
+        lambda: ssd.ssd_conv1d_fwd(second["xbc"], second["w"], second["bias"], cs1, cs2, out=v),
+        lambda: ssd.ssd_chunk_scan(x, Bm, Cm, second["dt"], second["A"], second["D"], st1, st2, y=y, chunk=d.chunk),
+    ], steps, warmup)
+    sb = scan_bytes(d, init=True)
+    cb = conv_bytes(d, L) + d.batch * d.conv_dim * 4 * 2
+    T = d.batch * L
+    return {"workload": "continuation_h128_b8", "batch": d.batch, "seqlen": L, "nheads": d.nheads,
+            "tokens_per_s": T / (conv_s + scan_s), "conv_us": conv_s * 1e6, "scan_us": scan_s * 1e6,
+            "scan_tokens_per_s": T / scan_s, "scan_algorithmic_bytes": sb, "scan_GBps": sb / scan_s / 1e9,
+            "scan_frac": sb / scan_s / 1e9 / HBM_PEAK_GBS, "scan_TFLOPs": scan_flops(d) / scan_s / 1e12,
+            "conv_algorithmic_bytes": cb, "conv_GBps": cb / conv_s / 1e9, "conv_frac": cb / conv_s / 1e9 / HBM_PEAK_GBS}
+
+
+def long_leg(ssd, torch, dev, steps, warmup, decode_steps=64):
+    """Long context on the Ultra layer: a 262144-token prefill (conv + scan) timed on its own, then
+    decode_steps single-token decode steps (conv update + state update, batch 1) from the prefill's
+    final state.  Returns the figures and the tensors the oracle check needs (sampled heads)."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, decode_tokens, mixer_inputs
+    d = WORKLOADS["long_ultra_256k"]
+    inp = mixer_inputs(d, 1004, device=dev)
+    v = torch.empty(d.batch, d.seqlen, d.conv_dim, dtype=d.dtype, device=dev)
+    x, Bm, Cm = ssd.split_xbc(v, d.nheads, d.head_dim, d.ngroups, d.d_state)
+    cs = torch.empty(d.batch, d.conv_dim, 4, dtype=d.dtype, device=dev)
+    st = torch.empty(d.batch, d.nheads, d.head_dim, d.d_state, device=dev)
+    y = torch.empty(d.batch, d.seqlen, d.nheads, d.head_dim, dtype=d.dtype, device=dev)
+    conv_s, scan_s = timed_launches(torch, [
+        lambda: ssd.ssd_conv1d_fwd(inp["xbc"], inp["w"], inp["bias"], None, cs, out=v),
+        lambda: ssd.ssd_chunk_scan(x, Bm, Cm, inp["dt"], inp["A"], inp["D"], None, st, y=y, chunk=d.chunk),
+    ], steps, warmup)
+    del y, x, Bm, Cm, v
+    tok = decode_tokens(d.with_(batch=1), 1014, decode_steps, device=dev)
+    u = torch.empty(1, d.conv_dim, dtype=d.dtype, device=dev)
+    xu, Bu, Cu = ssd.split_xbc(u, d.nheads, d.head_dim, d.ngroups, d.d_state)
+    yd = torch.empty(1, d.nheads, d.head_dim, dtype=torch.float32, device=dev)
+    ydec = torch.empty(decode_steps, d.nheads, d.head_dim, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for k in range(decode_steps):
+        ssd.ssd_conv1d_update(tok["xbc"][k], inp["w"], inp["bias"], cs, out=u)
+        ssd.ssd_state_update(st, xu, Bu, Cu, tok["dt"][k], inp["A"], inp["D"], y=yd)
+        ydec[k].copy_(yd[0])
+    ev[1].record()
+    torch.cuda.synchronize()
+    dec_s = ev[0].elapsed_time(ev[1]) * 1e-3 / decode_steps
+    sb = scan_bytes(d)
+    cb = conv_bytes(d, d.seqlen)
+    T = d.batch * d.seqlen
+    res = {"workload": "long_ultra_256k", "seqlen": d.seqlen, "tokens_per_s": T / (conv_s + scan_s),
+           "conv_us": conv_s * 1e6, "scan_us": scan_s * 1e6, "scan_tokens_per_s": T / scan_s,
+           "scan_algorithmic_bytes": sb, "scan_GBps": sb / scan_s / 1e9, "scan_frac": sb / scan_s / 1e9 / HBM_PEAK_GBS,
+           "conv_GBps": cb / conv_s / 1e9, "conv_frac": cb / conv_s / 1e9 / HBM_PEAK_GBS,
+           "decode": {"steps": decode_steps, "batch": 1, "us_per_step": dec_s * 1e6, "tokens_per_s": 1.0 / dec_s,
+                      "note": "batch-1 state (8 MiB) stays in the last-level cache: report only"}}
+    keep = {"inp": {k: inp[k] for k in ("w", "bias", "dt", "A", "D")}, "xbc": inp["xbc"], "tok": tok,
+            "state": st, "ydec": ydec, "dims": d}
+    return res, keep
+
+
+def long_oracle_check(orc, keep):
+    """The oracle on the 8 sampled heads (one per group, h = 33 g) of the long-context workload:
+    conv of their channels and the scan over the 262144 prefill tokens and the decode tokens after
+    them, timed on the host's cores (the CPU baseline of this workload), and the drift of the GPU's
+    fp32 state after prefill + decode, and of its decode y, from the oracle's."""
+    import numpy as np
+    import torch
+    d = keep["dims"]
+    hpg = d.nheads // d.ngroups
+    heads = [g * hpg + g % hpg for g in range(d.ngroups)]
+    I, GN, P, N = d.d_inner, d.ngroups * d.d_state, d.head_dim, d.d_state
+    tok = keep["tok"]
+    nd = tok["xbc"].shape[0]
+    L = d.seqlen + nd
+    out_y, out_s = 0.0, 0.0
+    t_cpu = 0.0
+    for h in heads:
+        g = h // hpg
+        ch = list(range(h * P, (h + 1) * P)) + list(range(I + g * N, I + (g + 1) * N)) + \
+            list(range(I + GN + g * N, I + GN + (g + 1) * N))
+        chd = torch.tensor(ch, device=keep["xbc"].device)
+        u = torch.cat([keep["xbc"][0].index_select(1, chd), tok["xbc"][:, 0].index_select(1, chd)], 0)
+        u = u.double().cpu().numpy()[None]
+        w = keep["inp"]["w"].index_select(0, chd).double().cpu().numpy()
+        bias = keep["inp"]["bias"].index_select(0, chd).double().cpu().numpy()
+        dt = torch.cat([keep["inp"]["dt"][0, :, h], tok["dt"][:, 0, h]]).double().cpu().numpy().reshape(1, L, 1)
+        A = keep["inp"]["A"][h:h + 1].double().cpu().numpy()
+        D = keep["inp"]["D"][h:h + 1].double().cpu().numpy()
+        t0 = time.perf_counter()
+        v, _ = orc.conv1d_fwd(u, w, bias, None)
+        v = torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+        yr, fr = orc.scan(v[..., :P].reshape(1, L, 1, P), v[..., P:P + N].reshape(1, L, 1, N),
+                          v[..., P + N:].reshape(1, L, 1, N), dt, A, D, None)
+        t_cpu += time.perf_counter() - t0
+        sg = keep["state"][0, h].double().cpu().numpy()
+        yg = keep["ydec"][:, h].double().cpu().numpy()
+        out_s = max(out_s, float(np.max(np.abs(sg - fr[0, 0])) / np.max(np.abs(fr[0, 0]))))
+        out_y = max(out_y, float(np.max(np.abs(yg - yr[0, d.seqlen:, 0])) / np.max(np.abs(yr[0, d.seqlen:, 0]))))
+    return {"heads": heads, "tokens": L,
+            "state_drift": out_s, "decode_y_drift": out_y,
+            "metric": "max|state_gpu - state_oracle| / max|state_oracle| over the sampled heads after prefill + decode",
+            "cpu_baseline": {"value": L * len(heads) / d.nheads / t_cpu, "unit": "tokens/s (scaled to 256 heads)",
+                             "cores": orc.num_threads(), "kind": "oracle",
+                             "sample": f"fp64 oracle: conv + scan of {len(heads)}/{d.nheads} heads x {L} tokens "
+                                       f"({t_cpu:.2f} s), not extrapolated beyond scaling by heads"}}
+
+
 def cpu_baseline(orc, inp, d, n_heads=256):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the full conv
     over all channels, and the scan of n_heads heads over all tokens; the scan time is scaled
@@ -540,6 +682,17 @@ def main():
     out["decode_step_fused"] = decode_step_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
     print("[bench] 16-bit state decode (stochastic rounding)", file=sys.stderr, flush=True)
     out["lowprec_decode"] = lowprec_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
+    print("[bench] chunked-prefill continuation (8 x 4096, 128 heads)", file=sys.stderr, flush=True)
+    out["continuation"] = continuation_leg(ssd, torch, dev, max(5, args.steps // 2), max(2, args.warmup // 2))
+    torch.cuda.empty_cache()
+    print("[bench] long context (262144-token prefill + 64 decode steps)", file=sys.stderr, flush=True)
+    out["long_context"], long_keep = long_leg(ssd, torch, dev, max(3, args.steps // 8), max(1, args.warmup // 10))
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] long context: oracle on 8 sampled heads (state drift)", file=sys.stderr, flush=True)
+        out["long_context"]["oracle_check"] = long_oracle_check(oracle.load(), long_keep)
+    del long_keep
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -54,3 +54,17 @@ def oracle_mixer(orc, inp, dims, conv_state=None, init=None):
     Cm = v[..., I + GN:].reshape(Bt, L, dims.ngroups, dims.d_state)
     y, fin = orc.scan(x, Bm, Cm, f64(inp["dt"]), f64(inp["A"]), f64(inp["D"]), f64(init))
     return v, s_out, y, fin
+
+
+def oracle_scan_of_conv(orc, v, dims, dt, A, D, init=None):
+    """Oracle scan fed a conv output v [B, L, CD] (e.g. the GPU's own bf16 conv output): split into
+    x, B, C as the layer's channels are laid out, then scan.  This isolates the scan from the
+    rounding of the stored conv output, which is checked elementwise on its own."""
+    v = f64(v) if isinstance(v, torch.Tensor) else np.asarray(v, np.float64)
+    I = dims.nheads * dims.head_dim
+    GN = dims.ngroups * dims.d_state
+    Bt, L = v.shape[:2]
+    x = v[..., :I].reshape(Bt, L, dims.nheads, dims.head_dim)
+    Bm = v[..., I:I + GN].reshape(Bt, L, dims.ngroups, dims.d_state)
+    Cm = v[..., I + GN:].reshape(Bt, L, dims.ngroups, dims.d_state)
+    return orc.scan(x, Bm, Cm, f64(dt), f64(A), f64(D), f64(init))

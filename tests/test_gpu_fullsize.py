@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import BF16_BAR, assert_bf16_elementwise, assert_close, f64, oracle_mixer, to_act
+from gpu_util import (BF16_BAR, assert_bf16_elementwise, assert_close, f64, oracle_mixer, oracle_scan_of_conv,
+                      rel_max, to_act)
 from selective_state_space_conv1d_amd import ssd
 from selective_state_space_conv1d_amd.synth import WORKLOADS, decode_state, decode_tokens, mixer_inputs
 
@@ -80,13 +81,18 @@ def test_prefill_ultra_8k(orc):
     _, _, y32, fin32 = gpu_prefill(d, inp, ydt=torch.float32)
     assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 y must be RNE of the fp32 y"
     assert torch.equal(fin, fin32)
-    vr, sr, yr, fr = oracle_row_prefill(orc, d, inp, 0)
+    # stage 1: the conv of every channel against the oracle's, within one bf16 ulp
+    vr, sr, yr_e2e, _ = oracle_row_prefill(orc, d, inp, 0)
     assert_bf16_elementwise(v[0].cpu(), vr, "conv, all 18432 channels")
     assert np.array_equal(f64(so[0]), sr), "conv state"
     del vr
-    e_y = assert_close(y32[0], yr, BF16_BAR, "y (fp32 output), all 256 heads")
-    e_s = assert_close(fin[0], fr, BF16_BAR, "final state, all 256 heads")
-    print(f"prefill_ultra_8k vs oracle: y {e_y:.3e}, state {e_s:.3e}", flush=True)
+    # stage 2: the scan of every head, the oracle fed the GPU's bf16 conv output
+    yr, fr = oracle_scan_of_conv(orc, v, d, inp["dt"], inp["A"], inp["D"])
+    e_y = assert_close(y32, yr, BF16_BAR, "y (fp32 output), all 256 heads")
+    e_s = assert_close(fin, fr, BF16_BAR, "final state, all 256 heads")
+    # end to end (the oracle's own bf16 conv output in front of its scan): reported, and held to the same bar
+    e_e2e = assert_close(y32[0], yr_e2e, BF16_BAR, "y end to end")
+    print(f"prefill_ultra_8k vs oracle: y {e_y:.3e}, state {e_s:.3e}, y end to end {e_e2e:.3e}", flush=True)
     # conv state: the last 4 inputs of every channel, bitwise
     assert torch.equal(so[0], inp["xbc"][0, -4:].transpose(0, 1))
 
@@ -142,7 +148,7 @@ def test_continuation_h128_b8(orc):
     full = {k: v.to(DEV) for k, v in mixer_inputs(d, 1003, device=DEV, seqlen=2 * d.seqlen).items()}
     first = dict(full, xbc=full["xbc"][:, :d.seqlen].contiguous(), dt=full["dt"][:, :d.seqlen].contiguous())
     second = dict(full, xbc=full["xbc"][:, d.seqlen:].contiguous(), dt=full["dt"][:, d.seqlen:].contiguous())
-    _, cs1, _, st1 = gpu_prefill(d, first)
+    v1, cs1, _, st1 = gpu_prefill(d, first)
     v2, cs2, y2, st2 = gpu_prefill(d, second, conv_state=cs1, init=st1, ydt=torch.float32)
     dl = d.with_(seqlen=2 * d.seqlen)
     _, csf, yf, stf = gpu_prefill(dl, full, ydt=torch.float32)
@@ -152,13 +158,23 @@ def test_continuation_h128_b8(orc):
     del yf
     L = d.seqlen
     ey = es = 0.0
+    e2e = 0.0
     for b in range(d.batch):
-        vr, sr, yr, fr = oracle_row_prefill(orc, dl, full, b)
+        # conv of both halves against the oracle's conv of the whole row; the scan of every head of
+        # the row, the oracle fed the GPU's bf16 conv outputs of both halves from a zero state
+        vr, sr, yr_e2e, _ = oracle_row_prefill(orc, dl, full, b)
+        assert_bf16_elementwise(v1[b].cpu(), vr[:L], f"first-half conv, row {b}")
         assert_bf16_elementwise(v2[b].cpu(), vr[L:], f"continuation conv, row {b}")
         assert np.array_equal(f64(cs2[b]), sr), f"conv state, row {b}"
-        ey = max(ey, assert_close(y2[b], yr[L:], BF16_BAR, f"continuation y, row {b}, all heads"))
-        es = max(es, assert_close(st2[b], fr, BF16_BAR, f"continuation state, row {b}, all heads"))
-    print(f"continuation_h128_b8 vs oracle (all 8 x 128 pairs): y {ey:.3e}, state {es:.3e}", flush=True)
+        e2e = max(e2e, rel_max(y2[b], yr_e2e[L:]))
+        del vr, yr_e2e
+        vb = torch.cat([v1[b:b + 1], v2[b:b + 1]], 1)
+        yr, fr = oracle_scan_of_conv(orc, vb, dl.with_(batch=1), full["dt"][b:b + 1], full["A"], full["D"])
+        ey = max(ey, assert_close(y2[b], yr[0, L:], BF16_BAR, f"continuation y, row {b}, all heads"))
+        es = max(es, assert_close(st2[b], fr[0], BF16_BAR, f"continuation state, row {b}, all heads"))
+    assert e2e <= BF16_BAR, f"continuation y end to end: {e2e:.3e}"
+    print(f"continuation_h128_b8 vs oracle (all 8 x 128 pairs): y {ey:.3e}, state {es:.3e}, "
+          f"y end to end {e2e:.3e}", flush=True)
 
 
 @pytest.mark.timeout(600)
