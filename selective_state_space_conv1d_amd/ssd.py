@@ -149,7 +149,52 @@ def _dt_params(dt_bias, dt_softplus, dt_limit):
 
 
 def _dims(batch, seqlen, H, P, G, N, act, ydt):
+    if act not in _DT or ydt not in _DT:
+        raise ValueError(f"activation and y dtypes must be float32 or bfloat16 (got {act}, {ydt})")
     return SsdDims(batch, seqlen, H, P, G, N, 4, _DT[act], _DT[ydt])
+
+
+# device types a call accepts (tensors must be GPU memory; the CPU tests of the argument checks widen it)
+_DEVICE_TYPES = ("cuda",)
+
+
+def _need(t, name, dev, shape=None, dtype=None, contiguous=True, optional=False):
+    """Check one tensor argument before anything is launched: it lives on the call's GPU device,
+    has the given dtype and shape, and is contiguous where the kernel assumes a dense layout.  The
+    C ABI sees only pointers, so a wrong buffer would otherwise be read or written out of bounds."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != dev or t.device.type not in _DEVICE_TYPES:
+        raise ValueError(f"{name} must be on {dev} (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _device(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type not in _DEVICE_TYPES:
+        raise ValueError(f"{name} must be a tensor on a GPU device")
+    return t.device
+
+
+def _head_params(dev, H, A, D, name_a="A", name_d="D"):
+    """A [H] fp32 (required) and D [H] fp32 (optional)."""
+    _need(A, name_a, dev, (H,), torch.float32)
+    _need(D, name_d, dev, (H,), torch.float32, optional=True)
+
+
+def _conv_params(dev, CD, act, w, bias):
+    """Conv taps w [CD, 4] and bias [CD] (optional) in the activation dtype."""
+    _need(w, "w", dev, (CD, 4), act)
+    _need(bias, "bias", dev, (CD,), act, optional=True)
 
 
 def ssd_status_string(code):
@@ -162,12 +207,17 @@ def ssd_conv1d_fwd(xbc, w, bias=None, conv_state_in=None, conv_state_out=None, o
     w [CD, 4], bias [CD]|None, conv states [B, CD, 4]|None (out may alias in).
     Returns out [B, L, CD].  The conv only needs CD; (H, P, G, N) may be given
     to describe the layer (CD = H*P + 2*G*N), otherwise any consistent split is used."""
+    dev = _device(xbc, "xbc")
     Bt, L, CD = xbc.shape
     if (xbc.stride(2) != 1 and CD > 1) or not _uniform_rows(xbc, L):
         raise ValueError("xbc must be [B, L, CD] with packed channels and uniform token stride")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(conv_state_in, "conv_state_in", dev, (Bt, CD, 4), xbc.dtype, optional=True)
+    _need(conv_state_out, "conv_state_out", dev, (Bt, CD, 4), xbc.dtype, optional=True)
     if out is None:
         out = torch.empty((Bt, L, CD), dtype=xbc.dtype, device=xbc.device)
+    _need(out, "out", dev, (Bt, L, CD), xbc.dtype)
     d = _dims(Bt, L, H, P, G, N, xbc.dtype, xbc.dtype)
     xs = CD if L == 0 else xbc.stride(1)
     if L == 0:
@@ -192,12 +242,16 @@ def ssd_conv1d_update(xbc, w, bias, conv_state, out=None, nheads=None, head_dim=
                       d_state=None, stream=None):
     """One-token conv.  xbc [B, CD] (rows may be strided), conv_state [B, CD, 4] updated in place.
     Returns out [B, CD]."""
+    dev = _device(xbc, "xbc")
     Bt, CD = xbc.shape
     if xbc.stride(1) != 1:
         raise ValueError("xbc channels must be packed")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(conv_state, "conv_state", dev, (Bt, CD, 4), xbc.dtype)
     if out is None:
         out = torch.empty((Bt, CD), dtype=xbc.dtype, device=xbc.device)
+    _need(out, "out", dev, (Bt, CD), xbc.dtype)
     d = _dims(Bt, 1, H, P, G, N, xbc.dtype, xbc.dtype)
     _check(_lib().ssd_conv1d_update(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias),
                                     _ptr(conv_state), _ptr(out), _stream(stream)), "ssd_conv1d_update")
@@ -217,7 +271,10 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     views into the conv output), dt [B, L, H], A [H] fp32, D [H] fp32|None,
     init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).  Optional dt prologue:
     dt <- clamp(softplus(dt + dt_bias), *dt_limit).  Returns y [B, L, H, P] in y_dtype (default x's)."""
+    dev = _device(x, "x")
     Bt, L, H, P = x.shape
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
     G, N = B.shape[2], B.shape[3]
     if L > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, L)):
         raise ValueError("x must be [B, L, H, P] with packed (H, P) and uniform token stride")
@@ -227,12 +284,17 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
             raise ValueError(f"{nm} must be [B, L, G, N] with packed (G, N) and uniform token stride")
     if B.stride(1) != C.stride(1):
         raise ValueError("B and C must share a token stride")
-    if dt.shape != (Bt, L, H) or not dt.is_contiguous():
-        raise ValueError("dt must be contiguous [B, L, H]")
+    _need(dt, "dt", dev, (Bt, L, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(init_state, "init_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(final_state, "final_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, L, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (Bt, L, H, P))
     d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
+    _need(workspace, "workspace", dev, optional=True)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))
     if L == 0:
@@ -244,9 +306,12 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
                                      _ptr(workspace), ws, _stream(stream)), "ssd_chunk_scan")
         return y
     # state every snapshot_interval tokens into snapshots [B, L // interval, H, P, N] fp32
+    if snapshot_interval <= 0:
+        raise ValueError("snapshot_interval must be positive")
     if snapshots is None or snapshots.shape != (Bt, L // snapshot_interval, H, P, N) or \
             snapshots.dtype != torch.float32 or not snapshots.is_contiguous():
         raise ValueError("snapshots must be contiguous fp32 [B, L // snapshot_interval, H, P, N]")
+    _need(snapshots, "snapshots", dev)
     _check(_lib().ssd_chunk_scan_snapshots(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
                                            _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
                                            _ptr(init_state), _ptr(final_state), _ptr(snapshots),
@@ -260,7 +325,13 @@ def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream
     """One decode token, in place on state [B, H, P, N] fp32.  x [B, H, P], B/C [B, G, N]
     (batch rows may be strided, e.g. views into the conv-update output), dt [B, H].
     Returns y [B, H, P]."""
+    dev = _device(x, "x")
+    _need(state, "state", dev, dtype=torch.float32)
+    if state.dim() != 4:
+        raise ValueError("state must be [B, H, P, N]")
     Bt, H, P, N = state.shape
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
     G = B.shape[1]
     if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
         raise ValueError("x must be [B, H, P] with packed (H, P)")
@@ -269,11 +340,13 @@ def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream
             raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
     if B.stride(0) != C.stride(0):
         raise ValueError("B and C must share a batch stride")
-    if dt.shape != (Bt, H) or not dt.is_contiguous() or not state.is_contiguous():
-        raise ValueError("dt [B, H] and state must be contiguous")
+    _need(dt, "dt", dev, (Bt, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (Bt, H, P))
     d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
     _check(_lib().ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), x.stride(0), _ptr(B), _ptr(C),
                                    B.stride(0), _ptr(dt), _ptr(A), _ptr(D),
@@ -298,13 +371,19 @@ def ssd_conv1d_fwd_varlen(xbc, w, bias, cu_seqlens, conv_state_pool=None, slot_i
     """Prefill conv of a packed batch.  xbc [T, CD] (token rows may be strided, channels packed),
     cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, conv_state_pool
     [nslots, CD, 4]|None, updated in place.  Returns out [T, CD]."""
+    dev = _device(xbc, "xbc")
     T, CD = xbc.shape
+    _need(cu_seqlens, "cu_seqlens", dev, dtype=torch.int32)
     S = cu_seqlens.numel() - 1
     if S < 0:
         raise ValueError("cu_seqlens needs at least one entry")
     if xbc.stride(1) != 1 and CD > 1:
         raise ValueError("xbc channels must be packed")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(conv_state_pool, "conv_state_pool", dev, dtype=xbc.dtype, optional=True)
+    _need(slot_idx, "slot_idx", dev, optional=True)
+    _need(has_initial_state, "has_initial_state", dev, optional=True)
     nslots = 0
     if conv_state_pool is not None:
         if conv_state_pool.dim() != 3 or conv_state_pool.shape[1:] != (CD, 4) or not conv_state_pool.is_contiguous():
@@ -312,6 +391,7 @@ def ssd_conv1d_fwd_varlen(xbc, w, bias, cu_seqlens, conv_state_pool=None, slot_i
         nslots = conv_state_pool.shape[0]
     if out is None:
         out = torch.empty((T, CD), dtype=xbc.dtype, device=xbc.device)
+    _need(out, "out", dev, (T, CD), xbc.dtype)
     d = _dims(S, T, H, P, G, N, xbc.dtype, xbc.dtype)
     xs = CD if T == 0 else xbc.stride(0)
     _check(_lib().ssd_conv1d_fwd_varlen(ctypes.byref(d), _ptr(xbc if T else None), xs, _ptr(w), _ptr(bias),
@@ -327,14 +407,19 @@ def ssd_conv1d_update_slots(xbc, w, bias, conv_state_pool, slot_idx, out=None, n
                             ngroups=None, d_state=None, stream=None):
     """One-token conv for B requests whose windows live in conv_state_pool [nslots, CD, 4]
     (updated in place) at slot_idx [B] int32.  xbc [B, CD] (rows may be strided).  Returns out [B, CD]."""
+    dev = _device(xbc, "xbc")
     Bt, CD = xbc.shape
     if xbc.stride(1) != 1:
         raise ValueError("xbc channels must be packed")
+    _need(conv_state_pool, "conv_state_pool", dev, dtype=xbc.dtype)
     if conv_state_pool.dim() != 3 or conv_state_pool.shape[1:] != (CD, 4) or not conv_state_pool.is_contiguous():
         raise ValueError("conv_state_pool must be contiguous [nslots, CD, 4]")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(slot_idx, "slot_idx", dev)
     if out is None:
         out = torch.empty((Bt, CD), dtype=xbc.dtype, device=xbc.device)
+    _need(out, "out", dev, (Bt, CD), xbc.dtype)
     d = _dims(Bt, 1, H, P, G, N, xbc.dtype, xbc.dtype)
     _check(_lib().ssd_conv1d_update_slots(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias),
                                           _ptr(_table(slot_idx, Bt, "slot_idx")), _ptr(conv_state_pool),
@@ -354,7 +439,11 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     state after every snapshot_interval tokens of sequence s goes to snapshot_pool
     [nsnap_slots, H, P, N] fp32 slot snapshot_table[s, k] (ssd_chunk_scan_varlen_snapshots).
     Returns y [T, H, P] in y_dtype (default x's)."""
+    dev = _device(x, "x")
     T, H, P = x.shape
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
+    _need(cu_seqlens, "cu_seqlens", dev, dtype=torch.int32)
     G, N = B.shape[1], B.shape[2]
     S = cu_seqlens.numel() - 1
     if S < 0:
@@ -366,8 +455,12 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
             raise ValueError(f"{nm} must be [T, G, N] with packed (G, N)")
     if B.stride(0) != C.stride(0):
         raise ValueError("B and C must share a token stride")
-    if dt.shape != (T, H) or not dt.is_contiguous():
-        raise ValueError("dt must be contiguous [T, H]")
+    _need(dt, "dt", dev, (T, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    _need(state_pool, "state_pool", dev, dtype=torch.float32, optional=True)
+    _need(slot_idx, "slot_idx", dev, optional=True)
+    _need(has_initial_state, "has_initial_state", dev, optional=True)
     nslots = 0
     if state_pool is not None:
         if state_pool.shape[1:] != (H, P, N) or state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
@@ -376,6 +469,8 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((T, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (T, H, P))
+    _need(workspace, "workspace", dev, optional=True)
     d = _dims(S, T, H, P, G, N, x.dtype, y.dtype)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     xs, bcs = (P * H, G * N) if T == 0 else (x.stride(0), B.stride(0))
@@ -394,7 +489,10 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     if (snapshot_table.dim() != 2 or snapshot_table.shape[0] != S or snapshot_table.dtype != torch.int32
             or not snapshot_table.is_contiguous() or snapshot_table.device != x.device):
         raise ValueError("snapshot_table must be contiguous int32 [S, max_snaps] on the scan's device")
+    if snapshot_interval <= 0:
+        raise ValueError("snapshot_interval must be positive")
     nsnap = 0
+    _need(snapshot_pool, "snapshot_pool", dev, optional=True)
     if snapshot_pool is not None:
         if (snapshot_pool.dim() != 4 or snapshot_pool.shape[1:] != (H, P, N) or snapshot_pool.dtype != torch.float32
                 or not snapshot_pool.is_contiguous()):
@@ -415,8 +513,15 @@ def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None,
     """One decode token for B requests whose states live in state_pool [nslots, H, P, N] fp32
     (updated in place) at slot_idx [B] int32.  x [B, H, P], B/C [B, G, N], dt [B, H].
     Returns y [B, H, P]."""
+    dev = _device(x, "x")
+    _need(state_pool, "state_pool", dev, dtype=torch.float32)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [nslots, H, P, N]")
     nslots, H, P, N = state_pool.shape
     Bt = x.shape[0]
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
+    _need(slot_idx, "slot_idx", dev)
     G = B.shape[1]
     if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
         raise ValueError("x must be [B, H, P] with packed (H, P)")
@@ -425,11 +530,13 @@ def ssd_state_update_slots(state_pool, slot_idx, x, B, C, dt, A, D=None, y=None,
             raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
     if B.stride(0) != C.stride(0):
         raise ValueError("B and C must share a batch stride")
-    if dt.shape != (Bt, H) or not dt.is_contiguous() or not state_pool.is_contiguous():
-        raise ValueError("dt [B, H] and state_pool must be contiguous")
+    _need(dt, "dt", dev, (Bt, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (Bt, H, P))
     d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
     _check(_lib().ssd_state_update_slots(ctypes.byref(d), _ptr(state_pool), nslots,
                                          _ptr(_table(slot_idx, Bt, "slot_idx")), _ptr(x), x.stride(0),
@@ -456,7 +563,11 @@ def ssd_state_update_multi(state, x, B, C, dt, A, D=None, slot_idx=None, inter_s
     strided, e.g. views into the multi-token conv output), dt [B, k, H].  inter_states: True
     allocates [B, k, H, P, N] fp32, a tensor is written, None/False skips it.
     Returns (y [B, k, H, P], inter_states or None)."""
+    dev = _device(x, "x")
     Bt, k, H, P = x.shape
+    _need(state, "state", dev, dtype=torch.float32)
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
     N = state.shape[3]
     G = B.shape[2]
     if state.dim() != 4 or state.shape[1:] != (H, P, N) or not state.is_contiguous():
@@ -469,8 +580,10 @@ def ssd_state_update_multi(state, x, B, C, dt, A, D=None, slot_idx=None, inter_s
             raise ValueError(f"{nm} must be [B, k, G, N] with packed (G, N) and uniform token stride")
     if B.stride(1) != C.stride(1):
         raise ValueError("B and C must share a token stride")
-    if dt.shape != (Bt, k, H) or not dt.is_contiguous():
-        raise ValueError("dt must be contiguous [B, k, H]")
+    _need(dt, "dt", dev, (Bt, k, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    _need(slot_idx, "slot_idx", dev, optional=True)
     st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
     if inter_states is True:
         inter_states = torch.empty((Bt, k, H, P, N), dtype=torch.float32, device=x.device)
@@ -479,9 +592,11 @@ def ssd_state_update_multi(state, x, B, C, dt, A, D=None, slot_idx=None, inter_s
     if inter_states is not None and (inter_states.shape != (Bt, k, H, P, N) or not inter_states.is_contiguous()
                                      or inter_states.dtype != torch.float32):
         raise ValueError("inter_states must be contiguous fp32 [B, k, H, P, N]")
+    _need(inter_states, "inter_states", dev, optional=True)
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, k, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (Bt, k, H, P))
     d = _dims(Bt, k, H, P, G, N, x.dtype, y.dtype)
     xs, bcs = (P * H, G * N) if k == 0 else (x.stride(1), B.stride(1))
     _check(_lib().ssd_state_update_multi(ctypes.byref(d), _ptr(st), _ptr(tab), nslots, _ptr(x), xs, _ptr(B),
@@ -497,12 +612,16 @@ def ssd_conv1d_update_multi(xbc, w, bias, conv_state, slot_idx=None, inter_conv_
     (read only).  xbc [B, k, CD] (token rows may be strided, uniform).  inter_conv_states: True
     allocates [B, k, CD, 4], a tensor is written, None/False skips it.
     Returns (out [B, k, CD], inter_conv_states or None)."""
+    dev = _device(xbc, "xbc")
     Bt, k, CD = xbc.shape
     if k > 0 and (xbc.stride(2) != 1 or not _uniform_rows(xbc, k)):
         raise ValueError("xbc must be [B, k, CD] with packed channels and uniform token stride")
+    _need(conv_state, "conv_state", dev, dtype=xbc.dtype)
     if conv_state.dim() != 3 or conv_state.shape[1:] != (CD, 4) or not conv_state.is_contiguous():
         raise ValueError("conv_state must be contiguous [B or nslots, CD, 4]")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(slot_idx, "slot_idx", dev, optional=True)
     st, nslots, tab = _state_pool_args(conv_state, slot_idx, Bt)
     if inter_conv_states is True:
         inter_conv_states = torch.empty((Bt, k, CD, 4), dtype=xbc.dtype, device=xbc.device)
@@ -512,8 +631,10 @@ def ssd_conv1d_update_multi(xbc, w, bias, conv_state, slot_idx=None, inter_conv_
                                           or not inter_conv_states.is_contiguous()
                                           or inter_conv_states.dtype != xbc.dtype):
         raise ValueError("inter_conv_states must be contiguous [B, k, CD, 4] in xbc's dtype")
+    _need(inter_conv_states, "inter_conv_states", dev, optional=True)
     if out is None:
         out = torch.empty((Bt, k, CD), dtype=xbc.dtype, device=xbc.device)
+    _need(out, "out", dev, (Bt, k, CD), xbc.dtype)
     d = _dims(Bt, k, H, P, G, N, xbc.dtype, xbc.dtype)
     xs = CD if k == 0 else xbc.stride(1)
     _check(_lib().ssd_conv1d_update_multi(ctypes.byref(d), _ptr(xbc), xs, _ptr(w), _ptr(bias), _ptr(st),
@@ -531,6 +652,13 @@ def ssd_accept_states(accept_len, state=None, inter_states=None, conv_state=None
     if inter_states is None and inter_conv_states is None:
         raise ValueError("nothing to accept")
     ref = inter_states if inter_states is not None else inter_conv_states
+    dev = _device(ref, "intermediate states")
+    for t, nm in ((state, "state"), (inter_states, "inter_states"), (conv_state, "conv_state"),
+                  (inter_conv_states, "inter_conv_states"), (slot_idx, "slot_idx")):
+        _need(t, nm, dev, optional=True)
+    _need(accept_len, "accept_len", dev)
+    if inter_states is not None and inter_states.dtype != torch.float32:
+        raise ValueError("SSM states are fp32")
     Bt, k = ref.shape[:2]
     # the call's dims: (H, P, N) from the SSM states, CD = H*P + 2*G*N from the conv states
     G, N, dtype = 1, 16, torch.float32
@@ -577,10 +705,14 @@ def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y
     place; with slot_idx [B] int32 it is a pool).  The update runs in fp32 and is rounded back to
     nearest even, or stochastically with sr = (seed, offset, rounds) (Philox4x32; use a new offset
     per call).  x [B, H, P], B/C [B, G, N] (16-byte aligned rows), dt [B, H].  Returns y [B, H, P]."""
+    dev = _device(x, "x")
+    _need(state, "state", dev)
     if state.dtype not in _STATE_DT or state.dim() != 4 or not state.is_contiguous():
         raise ValueError("state must be a contiguous float16 or bfloat16 [B or nslots, H, P, N] tensor")
     _, H, P, N = state.shape
     Bt = x.shape[0]
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
     G = B.shape[1]
     if x.shape != (Bt, H, P) or x.stride(2) != 1 or x.stride(1) != P:
         raise ValueError("x must be [B, H, P] with packed (H, P)")
@@ -589,12 +721,15 @@ def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y
             raise ValueError(f"{nm} must be [B, G, N] with packed (G, N)")
     if B.stride(0) != C.stride(0):
         raise ValueError("B and C must share a batch stride")
-    if dt.shape != (Bt, H) or not dt.is_contiguous():
-        raise ValueError("dt [B, H] must be contiguous")
+    _need(dt, "dt", dev, (Bt, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    _need(slot_idx, "slot_idx", dev, optional=True)
     st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
     ydt = y_dtype or x.dtype
     if y is None:
         y = torch.empty((Bt, H, P), dtype=ydt, device=x.device)
+    _need(y, "y", dev, (Bt, H, P))
     d = _dims(Bt, 1, H, P, G, N, x.dtype, y.dtype)
     srp = None if sr is None else ctypes.byref(SsdSrParams(int(sr[0]), int(sr[1]), int(sr[2])))
     _check(_lib().ssd_state_update_lp(ctypes.byref(d), _ptr(st), _STATE_DT[state.dtype], _ptr(tab), nslots,
@@ -610,6 +745,10 @@ def ssd_decode_step(xbc, w, bias, conv_state_in, conv_state_out, state, dt, A, D
     """Conv update + state update in one launch.  xbc [B, CD] (rows may be strided); conv_state_in
     [B, CD, 4] is read, conv_state_out [B, CD, 4] (a different buffer) receives the rolled windows;
     state [B, H, P, N] fp32 is updated in place; dt [B, H].  Returns y [B, H, P]."""
+    dev = _device(xbc, "xbc")
+    _need(state, "state", dev, dtype=torch.float32)
+    if state.dim() != 4:
+        raise ValueError("state must be [B, H, P, N]")
     Bt, CD = xbc.shape
     _, H, P, N = state.shape
     G = ngroups if ngroups is not None else (CD - H * P) // (2 * N)
@@ -622,9 +761,16 @@ def ssd_decode_step(xbc, w, bias, conv_state_in, conv_state_out, state, dt, A, D
             raise ValueError(f"{nm} must be contiguous [B, CD, 4] in xbc's dtype")
     if state.shape[0] != Bt or not state.is_contiguous() or dt.shape != (Bt, H) or not dt.is_contiguous():
         raise ValueError("state [B, H, P, N] and dt [B, H] must be contiguous")
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(conv_state_in, "conv_state_in", dev)
+    _need(conv_state_out, "conv_state_out", dev)
+    _need(dt, "dt", dev, (Bt, H), xbc.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     ydt = y_dtype or xbc.dtype
     if y is None:
         y = torch.empty((Bt, H, P), dtype=ydt, device=xbc.device)
+    _need(y, "y", dev, (Bt, H, P))
     d = _dims(Bt, 1, H, P, G, N, xbc.dtype, y.dtype)
     _check(_lib().ssd_decode_step(ctypes.byref(d), _ptr(xbc), xbc.stride(0), _ptr(w), _ptr(bias), _ptr(conv_state_in),
                                   _ptr(conv_state_out), _ptr(state), _ptr(dt), _ptr(A), _ptr(D),
@@ -639,6 +785,9 @@ def ssd_gated_rmsnorm(y, z, weight, ngroups, eps=1e-5, out=None, stream=None):
     arithmetic).  y [..., I] (e.g. the scan output viewed as [B, L, H*P]; rows may be strided),
     z [..., I] in the activation dtype (rows may be strided), weight [I] fp32.  Returns out
     [..., I] in z's dtype."""
+    dev = _device(y, "y")
+    _need(z, "z", dev, contiguous=False)
+    _need(weight, "weight", dev)
     I = y.shape[-1]
     if z.shape != y.shape or y.stride(-1) != 1 or z.stride(-1) != 1 or y.dim() < 2:
         raise ValueError("y and z must have the same shape [..., I] with packed channels")
@@ -650,6 +799,7 @@ def ssd_gated_rmsnorm(y, z, weight, ngroups, eps=1e-5, out=None, stream=None):
         raise ValueError("ngroups must divide the channel count")
     if out is None:
         out = torch.empty(y.shape, dtype=z.dtype, device=y.device)
+    _need(out, "out", dev, y.shape, z.dtype)
     rows = y2.shape[0]
     d = _dims(rows, 1, ngroups, I // ngroups, ngroups, 16, z.dtype, y.dtype)   # one "head" per group
     _check(_lib().ssd_gated_rmsnorm(ctypes.byref(d), _ptr(y2), y2.stride(0) if rows else I, _ptr(z2),
@@ -663,7 +813,11 @@ def ssd_state_update_accept(state, x, B, C, dt, A, D, accept_len, slot_idx=None,
     """Accept step by recomputation: apply each request's first accept_len[b] (clamped to [0, k])
     candidate tokens to state [B or nslots, H, P, N] fp32 in place.  x, B, C, dt as given to
     ssd_state_update_multi ([B, k, ...])."""
+    dev = _device(x, "x")
     Bt, k, H, P = x.shape
+    _need(state, "state", dev, dtype=torch.float32)
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
     N = state.shape[3]
     G = B.shape[2]
     if state.dim() != 4 or state.shape[1:] != (H, P, N) or not state.is_contiguous():
@@ -674,8 +828,13 @@ def ssd_state_update_accept(state, x, B, C, dt, A, D, accept_len, slot_idx=None,
         if t.shape != (Bt, k, G, N) or (k > 0 and (t.stride(3) != 1 or t.stride(2) != N
                                                     or not _uniform_rows(t, k))):
             raise ValueError(f"{nm} must be [B, k, G, N] with packed (G, N) and uniform token stride")
-    if dt.shape != (Bt, k, H) or not dt.is_contiguous():
-        raise ValueError("dt must be contiguous [B, k, H]")
+    if B.stride(1) != C.stride(1):
+        raise ValueError("B and C must share a token stride")
+    _need(dt, "dt", dev, (Bt, k, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    _need(accept_len, "accept_len", dev)
+    _need(slot_idx, "slot_idx", dev, optional=True)
     st, nslots, tab = _state_pool_args(state, slot_idx, Bt)
     d = _dims(Bt, k, H, P, G, N, x.dtype, x.dtype)
     xs, bcs = (P * H, G * N) if k == 0 else (x.stride(1), B.stride(1))
@@ -690,12 +849,16 @@ def ssd_conv1d_update_accept(xbc, conv_state, accept_len, slot_idx=None, nheads=
     """Accept step by recomputation for the conv windows: request b's window in conv_state
     [B or nslots, CD, 4] becomes the last 4 of (its old window, rows 0 .. n-1 of xbc [B, k, CD]),
     n = accept_len[b] clamped to [0, k]."""
+    dev = _device(xbc, "xbc")
     Bt, k, CD = xbc.shape
     if k > 0 and (xbc.stride(2) != 1 or not _uniform_rows(xbc, k)):
         raise ValueError("xbc must be [B, k, CD] with packed channels and uniform token stride")
+    _need(conv_state, "conv_state", dev, dtype=xbc.dtype)
     if conv_state.dim() != 3 or conv_state.shape[1:] != (CD, 4) or not conv_state.is_contiguous():
         raise ValueError("conv_state must be contiguous [B or nslots, CD, 4]")
     H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _need(accept_len, "accept_len", dev)
+    _need(slot_idx, "slot_idx", dev, optional=True)
     st, nslots, tab = _state_pool_args(conv_state, slot_idx, Bt)
     d = _dims(Bt, k, H, P, G, N, xbc.dtype, xbc.dtype)
     _check(_lib().ssd_conv1d_update_accept(ctypes.byref(d), _ptr(xbc), CD if k == 0 else xbc.stride(1), _ptr(st),
