@@ -139,7 +139,12 @@ ssd_status_t ssd_conv1d_update(const ssd_dims_t* d, const void* xbc, int64_t xbc
                                const void* w, const void* bias, void* conv_state, void* out,
                                hipStream_t stream);
 
-/* Workspace bytes ssd_chunk_scan needs for these sizes (currently always 0). */
+/*
+ * Workspace bytes with which ssd_chunk_scan runs its fp16 path for these sizes: for bf16 inputs
+ * with head_dim 64, d_state 128 and chunk 128, per (batch entry, group, 128-token chunk) 104 KiB
+ * + 8 bytes (the chunk's fp16 B^T and C tiles, the causal tiles of C.B^T in fp32, and two
+ * power-of-two scale exponents); 0 for other sizes, dtypes or chunks, and for a NULL d.
+ */
 size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
 
 /*
@@ -157,7 +162,12 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
  *  init_state   [B, H, P, N] fp32, or NULL (zeros).
  *  final_state  [B, H, P, N] fp32, or NULL (not written).  May alias init_state.
  *  y            [B, L, H, P] contiguous, y dtype.
- *  workspace    may be NULL when ssd_chunk_scan_workspace_size() is 0.
+ *  workspace    NULL (or workspace_bytes 0) runs the bf16 split-operand MFMA scan.  Otherwise a
+ *               caller-owned device buffer, 16-byte aligned, overwritten by the call: when
+ *               ssd_chunk_scan_workspace_size() is non-zero it must hold at least that many bytes
+ *               (else SSD_ERR_WORKSPACE; misaligned: SSD_ERR_ALIGN) and selects the fp16 scan; when
+ *               that size is 0 it is ignored.  Both scans meet the same error bound and differ only
+ *               in rounding.
  * Row strides are in elements: >= the row's extent, multiples of 8 (bf16) or 4 (fp32).
  * B and L above 2^31 - 1 are rejected (SSD_ERR_SHAPE).
  */
@@ -176,7 +186,7 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
  *             (k + 1) * interval - 1 of each batch entry (the same values the final state would
  *             have if the sequence ended there).  May be NULL when L < interval.
  *  interval   a positive multiple of 128.
- * The rest is as for ssd_chunk_scan.
+ * The rest is as for ssd_chunk_scan, except that the workspace is unused (may be NULL).
  */
 ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk,
                                       const void* x, int64_t x_row_stride,
@@ -271,7 +281,7 @@ ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t
  *  state_pool    [nslots, H, P, N] fp32, updated in place: the initial state is read as
  *                has_initial_state says, and the final state is written to every sequence's slot.
  *  y             [T, H, P] contiguous y dtype.
- * chunk, A, D, dt_params and workspace as for ssd_chunk_scan; S and T above 2^31 - 1 are
+ * chunk, A, D and dt_params as for ssd_chunk_scan; workspace is unused (may be NULL); S and T above 2^31 - 1 are
  * rejected (SSD_ERR_SHAPE).  When sequences x heads exceed what the device holds at once,
  * one workgroup scans a range of consecutive sequences (balanced by tokens): sequence
  * states must then sit in distinct slots, as for any in-place pool update.

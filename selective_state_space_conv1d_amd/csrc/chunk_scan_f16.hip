@@ -1,0 +1,1038 @@
+// SSD chunked scan for prefill on fp16 MFMA (gfx950): head_dim 64, d_state 128, chunk 128,
+// bf16 inputs -- the Ultra-family Mamba layer.
+//
+// Method (the structured-semiseparable / chunked form of the Mamba-2 scan: "Mamba 与 Nemotron
+// 系列模型深度调研", Mamba 架构; the 128-token chunked scan that returns the final state in the
+// modeling_nemotron_h.py walk-through, "Prefill 阶段").  Per chunk of Q = 128 tokens, with cs the
+// inclusive prefix sum of dt*A in base-2 units:
+//   M[i][j] = (C_i . B_j) * exp2(cs_i - cs_j) * dt_j   (j <= i), + D on the diagonal
+//   y_i     = sum_j M[i][j] x_j  +  exp2(cs_i) * (C_i . H)
+//   H       = exp2(cs_last) * H + sum_j (exp2(cs_last - cs_j) dt_j x_j) (x) B_j
+// which is the token recurrence re-associated exactly.
+//
+// Precision.  Every product runs as ONE v_mfma_f32_32x32x16_f16 with fp32 accumulation.  fp16 has
+// an 11-bit significand (8x finer than bf16), so one rounding of each fp32-derived operand (M,
+// the decay-weighted x, H) stays well inside the bar, and the bf16 inputs x, B and C convert to
+// fp16 exactly.  fp16's range is narrow, so every operand carries an exact power-of-two scale:
+//   * B and C: a pre-pass converts each (batch, group, chunk) tile with the scale that puts its
+//     largest magnitude in [2^14, 2^15) (exponents eB, eC), and stores what the scan reads: B'^T
+//     as the LDS image of its swizzled tile, C' in the y waves' register order, and the causal
+//     tiles of C'.B'^T in fp32 (shared by every head of the group, so computed once);
+//   * x: the loader wave scales a chunk only when its largest magnitude leaves [2^-8, 2^15)
+//     (exponent ex, usually 0);
+//   * M, the weighted x and H: scales from bounds computed in scalar arithmetic per chunk
+//     (|C.B| <= N max|C| max|B|; decays <= 1; |H| follows bound' = dec bound + sum(w) max|B| max|x|);
+// all of which fold into per-token or per-lane factors the kernel computes anyway.  The state
+// stays fp32 in registers across chunks; only its copy for C.H is rounded.
+//
+// Mapping.  One workgroup of 8 waves (two per SIMD: wave w runs on SIMD w % 4) per (batch, head)
+// walks the chunks in order, one barrier per chunk.  Everything one chunk reads from LDS was
+// written in the chunk before (double buffers), so no wave waits on another inside a chunk:
+//   * y waves 0..3: token tile t (tokens 32t .. 32t+31).  C.H for both 32-wide p tiles from the
+//     state copy H'; then per causal key tile jt <= t: the pre-pass's C.B^T tile (accumulator
+//     rows = key tokens) times the masked decay in registers, converted straight into the next
+//     MFMA's operand, and y^T += X^T M^T.  C rows and C.B^T tiles stay in registers, each set
+//     reloaded with the next chunk's values right after its last use.
+//   * waves 4, 5: the fp32 state H^T of p tile 0 / 1 (4 n tiles each), + B^T (w x) per chunk,
+//     and the fp16 copy H' for the next chunk's C.H.
+//   * waves 6, 7: x rows 0..63 / 64..127, loaded three chunks ahead into registers, converted to fp16
+//     into LDS one chunk ahead (the two halves share their largest |x| through LDS across a barrier);
+//     wave 6 builds each chunk's per-token vectors and scale exponents, wave 7 copies each next
+//     chunk's B tile from the pre-pass into LDS (direct global->LDS).
+// MFMAs per SIMD and chunk: 20 + 32, 24 + 32, 28 + 0, 32 + 0.
+// Operands that contract over tokens are LDS transpose reads (ds_read_b64_tr_b16) of row-major
+// tiles; 16-byte chunks of each row are XOR-permuted so that row and transpose reads are free of
+// bank conflicts.  Workgroups are numbered so that the heads sharing a B/C group sit on one XCD.
+#include <utility>
+
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+namespace scan16 {
+
+constexpr int Q = 128;    // tokens per chunk
+constexpr int P = 64;     // head_dim
+constexpr int NS = 128;   // d_state
+constexpr int kThreads = 512;
+constexpr int kRowB = NS * 2;   // bytes per row of the B and H' tiles
+constexpr int kRowX = P * 2;    // bytes per row of the x tile
+constexpr int kTile = Q * kRowB;   // bytes of one B (or C) tile: 32 KiB
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// floor(log2 v) for finite v > 0 (an upper bound -127 for subnormals); kNoExp for v == 0
+constexpr int kNoExp = -400;
+__device__ __forceinline__ int ilog2f(float v) {
+    const unsigned u = __float_as_uint(v) & 0x7FFFFFFFu;
+    return u == 0 ? kNoExp : static_cast<int>(u >> 23) - 127;
+}
+__device__ __forceinline__ float ldexp_f(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
+__device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Per-chunk quantities, built by the loader wave.  Scale exponents (integers):
+//   eB, eC  pre-pass scales of the chunk's B and C tiles (B = B' 2^eB)
+//   ex      the chunk's x scale (x = x' 2^ex)
+//   sM      lane-factor exponent of M' = M 2^(ex - eM): M' = (C'.B'^T) 2^sM exp2(cs_i - cs_j) dt_j
+//   eM      y accumulates in units of 2^eM
+//   ew      weighted-x scale: w x = (w' x') 2^ew, wS holding w' = w 2^(ex - ew)
+//   sH      the state waves' accumulator units after this chunk (eB + ew)
+//   eHc     units of the fp16 state copy H' this chunk reads; eHn: of the copy it writes
+struct Vec {
+    float cs[Q];        // inclusive prefix sum of dt*A*log2(e)
+    float fM[Q];        // off-diagonal column factor exp2(cs_e - cs_j) dt_j, e = last token of j's tile
+    float vD[Q];        // diagonal column factor exp2(cs_m - cs_j) dt_j, m = token 15 of j's tile
+    float dt[Q];        // dt_j (0 past the chunk's end)
+    float wS[Q];        // exp2(cs_last - cs_j) dt_j 2^(ex - ew) for real tokens, 0 for padding
+    float csE[4];       // cs at the end of each 32-token tile
+    float csM[4];       // cs at token 15 of each tile
+    int diagOK[4];      // the tile's decay range allows the factored diagonal
+    float dec;          // exp2(cs at the last real token): the chunk's decay of H
+    float dx;           // D 2^(ex - eM)
+    int eB, eC, ex, sM, eM, ew, sH, sHp, eHc, eHn;
+    int pad[2];
+};
+
+struct Smem {
+    unsigned char B[2][kTile];           // B'^T[n][j] fp16, double-buffered (the pre-pass's LDS image)
+    unsigned char X[2][Q * kRowX];       // x'[j][p] fp16, double-buffered
+    unsigned char H[2][P * kRowB];       // H'[p][n] fp16, double-buffered
+    Vec vec[2];
+    float hmax[2];                       // |initial state| maxima of the two state waves
+    unsigned xmax[2][2];                 // largest |x| (bf16 bits) of each half of a chunk, by chunk parity
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+
+// LDS swizzle: 256-byte rows XOR their 16-byte chunk index with a 4-bit key of the row, 128-byte
+// rows with a 3-bit key (conflict-free row reads of 16 lanes and transpose reads of 32 lanes).
+__device__ __forceinline__ int key16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int key8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int RB> __device__ __forceinline__ int rkey(int r) { return RB == 256 ? key16(r) : key8(r); }
+template <int RB> __device__ __forceinline__ int soff(int r, int c) { return r * RB + ((c ^ rkey<RB>(r)) << 4); }
+
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+// 8 fp32 values -> fp16x8 (round to nearest even)
+__device__ __forceinline__ f16x8 to_f16x8(const float* v) {
+    f16x8 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f16x2 h = __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, f16x2);
+        r[2 * k] = h[0];
+        r[2 * k + 1] = h[1];
+    }
+    return r;
+}
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Lane-dependent LDS offsets (see the bf16 MFMA scan for the derivation):
+//  * row reads: lane (c32, hf) reads row base + c32, 16-byte chunk 2ks + hf;
+//  * transpose reads: within each 16-lane group lane m supplies row first + 4hf + m/4, columns
+//    col0 + 16g + 4(m%4) .. +3; the receiving lane (c32, hf) then holds column col0 + c32 at
+//    tokens first + 4hf + {0..3}; reads at first and first + 8 give an operand's 8 slots in the
+//    row order of a 32x32 accumulator.
+struct LaneOff {
+    int row[8];
+    int rl, cl, hb;
+    __device__ __forceinline__ LaneOff(int lane) {
+        const int c32 = lane & 31, hf = lane >> 5, rk = key16(c32);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) row[ks] = c32 * 256 + (((2 * ks + hf) ^ rk) << 4);
+        const int m = lane & 15;
+        rl = 4 * hf + (m >> 2);
+        cl = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+        hb = (m & 1) << 3;
+    }
+    template <int RB> __device__ __forceinline__ int tr(int col0, int h) const {
+        return rl * RB + ((((col0 >> 3) + cl) ^ rkey<RB>(rl + 8 * h)) << 4) + hb;
+    }
+};
+
+__device__ __forceinline__ f16x8 ld16(const unsigned char* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+template <int RB>
+__device__ __forceinline__ f16x8 tr_frag(const unsigned char* t, int b0, int b8, int j0) {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(t + b0 + j0 * RB));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_bf16*)(t + b8 + (j0 + 8) * RB));
+    const f16x4 l = __builtin_bit_cast(f16x4, lo), h = __builtin_bit_cast(f16x4, hi);
+    return f16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+}
+
+// Row broadcast (DPP row_newbcast): every lane of each 16-lane row receives lane K of that row.
+template <int K> __device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+}
+// m[k] = (m[k] * f_k) a, f_k = lane k of this lane's row of f: the column factors of an accumulator
+// whose slot k sits on the key token that lane k of the row holds the factor of
+template <int... K>
+__device__ __forceinline__ void scale_cols(f32x16& m, float f, float a, std::integer_sequence<int, K...>) {
+    ((m[K] = (m[K] * row_bcast<K>(f)) * a), ...);
+}
+
+// Workspace of one call, per (batch, group, chunk) tile index:
+//   BT  32 KiB  B'^T as the LDS image the state waves read: row n, 16-byte chunk q at q ^ key16(n); chunk q
+//               holds tokens 16(q/2) + {4(q%2) + 0..3, 8 + 4(q%2) + 0..3}, the slot order of an MFMA
+//               operand whose k runs over tokens;
+//   C   32 KiB  C' in the y waves' register order: token tile t, k step ks, lane l: 16 bytes
+//               C'[32t + l%32][16ks + 8(l/32) + 0..7];
+//   CB  40 KiB  the ten causal 32x32 tiles of (C'.B'^T)^T (rows: key tokens j; columns: tokens i), tile
+//               (it, jt) at index it(it+1)/2 + jt, each lane's 16 accumulator values contiguous;
+// then the (eB, eC) pairs.  C.B^T is the same for every head of a group, so it is computed here once.
+constexpr int kCBBytes = 10 * 4096;
+constexpr int64_t kWsTile = 2 * kTile + kCBBytes;
+struct WsView {
+    unsigned char* tiles;
+    int2* scales;
+    int64_t ntile;   // batch * groups * chunks
+    __device__ __host__ unsigned char* btile(int64_t i) const { return tiles + i * kWsTile; }
+    __device__ __host__ unsigned char* ctile(int64_t i) const { return tiles + i * kWsTile + kTile; }
+    __device__ __host__ unsigned char* cbtile(int64_t i) const { return tiles + i * kWsTile + 2 * kTile; }
+};
+__host__ __device__ inline int64_t ws_bytes(int64_t ntile) { return ntile * (kWsTile + static_cast<int64_t>(sizeof(int2))); }
+
+// ---------------------------------------------------------------------------
+// Pre-pass: one workgroup of 256 threads per (batch, group, chunk).  Thread t holds 16-byte pieces
+// t + 256k (k < 8) of the B tile and of the C tile (piece i: row i / 16, chunk i % 16); rows past the
+// sequence end are zeros.  The scaled fp16 tiles are staged in LDS, from which the four waves write B'^T
+// (transpose reads) and compute the causal C'.B'^T tiles (wave w: tiles w, w + 4, w + 8).
+__global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16* Cg, int64_t bcs, int64_t seqlen,
+                                                      int ngroups, int64_t nchunks, WsView ws) {
+    __shared__ __align__(16) unsigned char lb[kTile];
+    __shared__ __align__(16) unsigned char lc[kTile];
+    __shared__ unsigned wmax[2][4];
+    const int64_t id = blockIdx.x;
+    const int64_t c = id % nchunks;
+    const int64_t bg = id / nchunks;
+    const int g = static_cast<int>(bg % ngroups);
+    const int64_t b = bg / ngroups;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t row0 = b * seqlen + c * Q;
+    const int valid = static_cast<int>(seqlen - c * Q < Q ? seqlen - c * Q : Q);
+    u32x4 vb[8], vc[8];
+    u16x2 mb2 = {0, 0}, mc2 = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int i = t + 256 * k, r = i >> 4, cc = i & 15;
+        vb[k] = u32x4{0, 0, 0, 0};
+        vc[k] = u32x4{0, 0, 0, 0};
+        if (r < valid) {
+            const int64_t off = (row0 + r) * bcs + static_cast<int64_t>(g) * NS + 8 * cc;
+            vb[k] = *reinterpret_cast<const u32x4*>(Bg + off);
+            vc[k] = *reinterpret_cast<const u32x4*>(Cg + off);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            mb2 = __builtin_elementwise_max(mb2, __builtin_bit_cast(u16x2, vb[k][e] & 0x7FFF7FFFu));
+            mc2 = __builtin_elementwise_max(mc2, __builtin_bit_cast(u16x2, vc[k][e] & 0x7FFF7FFFu));
+        }
+    }
+    unsigned mb = max(static_cast<unsigned>(mb2[0]), static_cast<unsigned>(mb2[1]));
+    unsigned mc = max(static_cast<unsigned>(mc2[0]), static_cast<unsigned>(mc2[1]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mb = max(mb, static_cast<unsigned>(__shfl_xor(static_cast<int>(mb), off, 64)));
+        mc = max(mc, static_cast<unsigned>(__shfl_xor(static_cast<int>(mc), off, 64)));
+    }
+    if (lane == 0) {
+        wmax[0][wave] = mb;
+        wmax[1][wave] = mc;
+    }
+    __syncthreads();
+    mb = max(max(wmax[0][0], wmax[0][1]), max(wmax[0][2], wmax[0][3]));
+    mc = max(max(wmax[1][0], wmax[1][1]), max(wmax[1][2], wmax[1][3]));
+    // exponent of the largest magnitude (bf16 bits): scale it into [2^14, 2^15)
+    auto scale_of = [](unsigned m) {
+        if (m == 0 || m >= 0x7F80u) return 0;                 // zeros, or inf/nan (left to propagate)
+        return static_cast<int>(m >> 7) - 127 - 14;
+    };
+    const int eB = scale_of(mb), eC = scale_of(mc);
+    const int64_t tix = id;   // tile index (b, g, c) in the same order
+    unsigned char* bt = ws.btile(tix);
+    unsigned char* ct = ws.ctile(tix);
+    auto conv = [](const u32x4& v, int e) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = ldexp_f(__uint_as_float(v[q] << 16), -e);
+            const float hi = ldexp_f(__uint_as_float(v[q] & 0xFFFF0000u), -e);
+            o[q] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+        }
+        return o;
+    };
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int i = t + 256 * k, r = i >> 4, cc = i & 15;
+        *reinterpret_cast<u32x4*>(lb + soff<kRowB>(r, cc)) = conv(vb[k], eB);
+        const u32x4 cv = conv(vc[k], eC);
+        *reinterpret_cast<u32x4*>(lc + soff<kRowB>(r, cc)) = cv;
+        const int tt = r >> 5, c32 = r & 31, ks = cc >> 1, hf = cc & 1;
+        *reinterpret_cast<u32x4*>(ct + (((tt * 8 + ks) * 64) + hf * 32 + c32) * 16) = cv;
+    }
+    __syncthreads();
+    const LaneOff lo(lane);
+    const int c32 = lane & 31, hf = lane >> 5;
+    {   // B'^T: wave w writes the rows of n tile w
+        const int n = 32 * wave + c32;
+        const int b0 = lo.tr<kRowB>(32 * wave, 0), b8 = lo.tr<kRowB>(32 * wave, 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<f16x8*>(bt + n * kRowB + (((2 * k + hf) ^ key16(n)) << 4)) = tr_frag<kRowB>(lb, b0, b8, 16 * k);
+    }
+    unsigned char* cb = ws.cbtile(tix);
+#pragma unroll
+    for (int T = wave; T < 10; T += 4) {
+        const int it = T >= 6 ? 3 : (T >= 3 ? 2 : (T >= 1 ? 1 : 0));
+        const int jt = T - it * (it + 1) / 2;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            acc = mfma(ld16(lb + 32 * jt * kRowB + lo.row[ks]), ld16(lc + 32 * it * kRowB + lo.row[ks]), acc);
+        f32x4* dst = reinterpret_cast<f32x4*>(cb + T * 4096 + lane * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+    if (t == 0) ws.scales[tix] = int2{eB, eC};
+}
+
+// ---------------------------------------------------------------------------
+struct Ctx {
+    const bf16* xg; const bf16* dtg;
+    int64_t xs, seqlen, b;
+    int H, h, grp, nchunks;
+    int64_t tile0;      // workspace tile index of this (batch, group)'s chunk 0
+    WsView ws;
+    __device__ __forceinline__ int valid(int c) const {
+        const int64_t r = seqlen - static_cast<int64_t>(c) * Q;
+        return r < Q ? static_cast<int>(r) : Q;
+    }
+    __device__ __forceinline__ int64_t row0(int c) const { return b * seqlen + static_cast<int64_t>(c) * Q; }
+};
+
+// ---------------------------------------------------------------------------
+// y wave: token tile IT, both p tiles.
+template <typename TY, int IT>
+__device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    const int c32 = lane & 31, hf = lane >> 5;
+    const int i = 32 * IT + c32;                     // this lane's token within the chunk
+    TY* yg = static_cast<TY*>(a.y);
+    const LaneOff lo(lane);
+    const int trX0 = lo.tr<kRowX>(0, 0), trX1 = lo.tr<kRowX>(32, 0);
+    // the key token whose column factor this lane holds for the row broadcasts: slot k = lane % 16 of
+    // an accumulator of this half-wave
+    const int rb = 8 * ((lane & 15) >> 2) + 4 * hf + (lane & 3);
+
+    // this lane's C' operand of chunk c, k step ks: C'[i][16ks + 8hf .. +7]
+    auto c_load = [&](f16x8 (&cr)[8], int c) {
+        const unsigned char* src = cx.ws.ctile(cx.tile0 + c) + ((IT * 8) * 64 + lane) * 16;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) cr[ks] = *reinterpret_cast<const f16x8*>(src + ks * 64 * 16);
+    };
+    // this lane's 16 values of the pre-pass C'.B'^T tile (IT, jt) of chunk c
+    auto cb_load = [&](int c, int jt) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(cx.ws.cbtile(cx.tile0 + c) + (IT * (IT + 1) / 2 + jt) * 4096 +
+                                                          lane * 64);
+        const f32x4 q0 = src[0], q1 = src[1], q2 = src[2], q3 = src[3];
+        return f32x16{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3],
+                      q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
+    };
+    // bf16 y of the previous chunk, not yet stored (yq_dst null: nothing pending or a token past the end).
+    // Loads and stores share one vector-memory counter, and a wait on it that follows a store also waits
+    // for that store; each chunk's y is therefore stored after the next chunk's first wait for its loads,
+    // which leaves the stores the whole chunk to complete.
+    u32x4 yq[4];
+    TY* yq_dst = nullptr;
+    auto flush_y = [&]() {
+        if constexpr (sizeof(TY) == 2) {
+            if (yq_dst != nullptr) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(yq_dst + 16 * k) = yq[k];
+            }
+        }
+    };
+    // rolling prefetch: each register set is reloaded with the next chunk's data right after its last use
+    f16x8 cf[8];
+    f32x16 cb[IT + 1];
+    if (cx.nchunks > 0) {
+        c_load(cf, 0);
+#pragma unroll
+        for (int jt = 0; jt <= IT; ++jt) cb[jt] = cb_load(0, jt);
+    }
+    __syncthreads();                                 // prologue 1
+    __syncthreads();                                 // chunk 0
+
+    for (int c = 0; c < cx.nchunks; ++c) {
+        const int valid = cx.valid(c);
+        const int buf = c & 1;
+        // the chunk whose values the reloads fetch: the last chunk reloads itself (in bounds, unused), which
+        // keeps the loads unconditional and in place
+        const int cnext = c + 1 < cx.nchunks ? c + 1 : c;
+        // (tokens past a ragged chunk's end are computed like the others, from zero B and C rows and
+        // zero dt, and never stored)
+        const Vec& v = sm.vec[buf];
+        const unsigned char* Xt = sm.X[buf];
+        const unsigned char* Ht = sm.H[buf];
+        // per-chunk factors, issued with the C.H operands: cs_i, the tiles' end values, and this lane's
+        // column factor of each key tile (off-diagonal fM, diagonal vD) for the row broadcasts
+        const float csi = v.cs[i];
+        const f32x4 csE = *reinterpret_cast<const f32x4*>(v.csE);
+        float fcol[IT + 1];
+#pragma unroll
+        for (int jt = 0; jt < IT; ++jt) fcol[jt] = v.fM[32 * jt + rb];
+        fcol[IT] = v.vD[32 * IT + rb];
+
+        // carried state: y^T[p][i] = sum_n H'[p][n] C'[i][n], p tiles 0 and 1; the fragments are
+        // read in batches of 4, two batches ahead of the MFMAs that use them
+        f32x16 y0 = zero16(), y1 = zero16();
+        {
+            auto hfrag = [&](int k) { return ld16(Ht + (k & 1) * 32 * kRowB + lo.row[k >> 1]); };   // k = 2ks + pt
+            f16x8 hv[12];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) hv[k] = hfrag(k);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (g < 2) {
+#pragma unroll
+                    for (int k = 4 * g + 8; k < 4 * g + 12; ++k) hv[k % 12] = hfrag(k);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 4 * g; k < 4 * (g + 1); ++k) {
+                    if (k & 1) y1 = mfma(hv[k % 12], cf[k >> 1], y1);
+                    else y0 = mfma(hv[k % 12], cf[k >> 1], y0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        flush_y();                                   // the previous chunk's y (C.H waited for every load)
+        // the next chunk's C rows: issued after C.H, so that they do not hold up its LDS reads behind
+        // the memory traffic every wave starts at the chunk boundary
+        c_load(cf, cnext);
+        // into the units of y: exp2(cs_i) 2^(eHc + eC - eM)
+        const float ey = ldexp_f(fexp2(csi), v.eHc + v.eC - v.eM);
+        y0 *= ey;
+        y1 *= ey;
+
+        // causal key tiles: the C'.B'^T tile (acc rows = key tokens j, cols = tokens i), M' in
+        // registers, y^T[p][i] += sum_j X'^T[p][j] M'^T[j][i]; the X^T operands of the next tile are
+        // read while this one is scaled
+        const int sM = v.sM;
+        auto x_frags = [&](f16x8 (&xr)[4], int jt) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                xr[2 * q] = tr_frag<kRowX>(Xt, trX0, trX0, 32 * jt + 16 * q);
+                xr[2 * q + 1] = tr_frag<kRowX>(Xt, trX1, trX1, 32 * jt + 16 * q);
+            }
+        };
+        f16x8 xc[4];
+        x_frags(xc, 0);
+#pragma unroll
+        for (int jt = 0; jt <= IT; ++jt) {
+            f32x16 m = cb[jt];       // m[4q + r] = C'_i . B'_jj,  jj = 32jt + 8q + 4hf + r
+            __builtin_amdgcn_sched_barrier(0);
+            cb[jt] = cb_load(cnext, jt);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 xn[4];
+            if (jt < IT) x_frags(xn, jt + 1);
+            if (jt < IT) {
+                scale_cols(m, fcol[jt], fexp2(csi - csE[jt] + static_cast<float>(sM)),
+                           std::make_integer_sequence<int, 16>{});
+            } else if (v.diagOK[jt]) {
+                const float dx = v.dx;
+                scale_cols(m, fcol[jt], fexp2(csi - v.csM[jt] + static_cast<float>(sM)),
+                           std::make_integer_sequence<int, 16>{});
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int jj = 32 * jt + 8 * (k >> 2) + 4 * hf + (k & 3);
+                    const float e = jj == i ? m[k] + dx : m[k];
+                    m[k] = jj <= i ? e : 0.f;
+                }
+            } else {                 // steep decay inside the tile: per-element exp2
+                const float dx = v.dx;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 cj = *reinterpret_cast<const f32x4*>(&v.cs[32 * jt + 8 * q + 4 * hf]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(&v.dt[32 * jt + 8 * q + 4 * hf]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int jj = 32 * jt + 8 * q + 4 * hf + r;
+                        float e = m[4 * q + r] * fexp2(csi - cj[r] + static_cast<float>(sM)) * dj[r];
+                        if (jj == i) e += dx;
+                        m[4 * q + r] = jj <= i ? e : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float mv[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) mv[s] = m[8 * q + s];
+                const f16x8 mh = to_f16x8(mv);
+                y0 = mfma(xc[2 * q], mh, y0);
+                y1 = mfma(xc[2 * q + 1], mh, y1);
+            }
+            if (jt < IT) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) xc[k] = xn[k];
+            }
+        }
+
+        // y[token i][p] = acc 2^eM.  Lane (c32, hf) holds p = 32pt + 8j + 4hf + r in y_pt[4j + r];
+        // swapping j = 1 of the low half-wave with j = 0 of the high one (and 3 with 2) leaves each
+        // lane with p = 32pt + 16g + 8hf + {0..7}: two 16-byte pieces per p tile.
+        const int eM = v.eM;
+        TY* yrow = yg + (cx.row0(c) * cx.H + cx.h) * static_cast<int64_t>(P);
+        const int64_t ystr = static_cast<int64_t>(cx.H) * P;
+        if constexpr (sizeof(TY) == 4) {
+            if (i < valid) {
+                TY* dst = yrow + i * ystr + 8 * hf;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const f32x16& yv = pt ? y1 : y0;
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        u32x4 lo4, hi4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float a0 = ldexp_f(yv[8 * g + r], eM), b0 = ldexp_f(yv[8 * g + 4 + r], eM);
+                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(b0),
+                                                                             false, false);
+                            lo4[r] = sw[0];
+                            hi4[r] = sw[1];
+                        }
+                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g) = lo4;
+                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g + 4) = hi4;
+                    }
+                }
+            }
+        } else {
+            // held until the next chunk's C.H: lane (c32, hf) stores y[i][32pt + 16g + 8hf .. +7] from yq[2pt + g]
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const f32x16& yv = pt ? y1 : y0;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const unsigned pa = pack_bf16(ldexp_f(yv[8 * g + 2 * h2], eM), ldexp_f(yv[8 * g + 2 * h2 + 1], eM));
+                        const unsigned pb = pack_bf16(ldexp_f(yv[8 * g + 4 + 2 * h2], eM),
+                                                      ldexp_f(yv[8 * g + 4 + 2 * h2 + 1], eM));
+                        const auto sw = __builtin_amdgcn_permlane32_swap(pa, pb, false, false);
+                        yq[2 * pt + g][h2] = sw[0];
+                        yq[2 * pt + g][2 + h2] = sw[1];
+                    }
+                }
+            }
+            yq_dst = i < valid ? yrow + i * ystr + 8 * hf : nullptr;
+        }
+        __syncthreads();                             // chunk c + 1
+    }
+    flush_y();
+}
+
+// ---------------------------------------------------------------------------
+// state wave: the 4 n tiles of p tile SP.  Tile t holds Hs[t][4q + r] = H[p = 32SP + c32][n = 32t + 8q + 4hf + r]
+// in units of 2^sH (sH of the last chunk processed; 0 for the initial state).
+template <int SP>
+__device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    const int c32 = lane & 31, hf = lane >> 5;
+    const int hp = 32 * SP + c32;
+    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    const LaneOff lo(lane);
+    const int trW = lo.tr<kRowX>(32 * SP, 0);
+    f32x16 Hs[4];
+    float mx = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 32 * t + 8 * q + 4 * hf;
+            f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+            if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Hs[t][4 * q + r] = v4[r];
+                mx = fmaxf(mx, fabsf(v4[r]));
+            }
+        }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if (lane == 0) sm.hmax[SP] = mx;
+    // fp16 copy of the state in units of 2^e (e.g. H' for the next chunk's C.H), into buffer hb
+    auto write_h = [&](int buf, int sh, int e) {
+        unsigned char* hb = sm.H[buf];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f16x4 h4;
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const f16x2 p2 = __builtin_convertvector(
+                        f32x2{ldexp_f(Hs[t][4 * q + r], sh - e), ldexp_f(Hs[t][4 * q + r + 1], sh - e)}, f16x2);
+                    h4[r] = p2[0];
+                    h4[r + 1] = p2[1];
+                }
+                *reinterpret_cast<f16x4*>(hb + soff<kRowB>(hp, 4 * t + q) + 8 * hf) = h4;
+            }
+    };
+    __syncthreads();                                 // prologue 1
+    {
+        const float bound0 = fmaxf(sm.hmax[0], sm.hmax[1]);
+        write_h(0, 0, max(ilog2f(bound0), -126) + 1 - 15);
+    }
+    __syncthreads();                                 // chunk 0
+
+    int sh = 0;                                      // units of Hs
+    for (int c = 0; c < cx.nchunks; ++c) {
+        const int buf = c & 1;
+        const Vec& v = sm.vec[buf];
+        const unsigned char* Bt = sm.B[buf];
+        const unsigned char* Xt = sm.X[buf];
+        // H <- dec H, re-expressed in this chunk's units 2^sH (a power-of-two change of units)
+        const int du = sh - v.sH;
+        if (du <= 100) {
+            const float dec = ldexp_f(v.dec, du);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Hs[t] *= dec;
+        } else {                                     // the units shrink by more than 2^100
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Hs[t][e] = ldexp_f(Hs[t][e] * v.dec, du);
+        }
+        sh = v.sH;
+        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B'^T[n][j] (w'_j x'_j)[p]; steps past the
+        // chunk's last token would only add zero weights.  Each step's LDS fragments are read one step
+        // ahead of its MFMAs.
+        const int valid = cx.valid(c);
+        struct Frag {
+            f16x8 x, b[4];
+            f32x4 w0, w1;
+        };
+        auto load = [&](Frag& f, int j0) {
+            f.x = tr_frag<kRowX>(Xt, trW, trW, j0);
+            f.w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
+            f.w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) f.b[t] = ld16(Bt + 32 * t * kRowB + lo.row[j0 >> 4]);
+        };
+        auto use = [&](const Frag& f) {
+            float e[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) e[s] = static_cast<float>(f.x[s]) * (s < 4 ? f.w0[s] : f.w1[s - 4]);
+            const f16x8 wx = to_f16x8(e);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Hs[t] = mfma(f.b[t], wx, Hs[t]);
+        };
+        if (valid == Q) {
+            // a full chunk, two steps in flight: step k + 2's fragments are read while step k computes
+            // (scheduling barriers keep each step's reads where they are issued: the compiler would
+            // otherwise sink them next to their MFMAs)
+            Frag f0, f1;
+            load(f0, 0);
+            load(f1, 16);
+#pragma unroll
+            for (int k = 0; k < 8; k += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                use(f0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k + 2 < 8) load(f0, 16 * (k + 2));
+                __builtin_amdgcn_sched_barrier(0);
+                use(f1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k + 3 < 8) load(f1, 16 * (k + 3));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            for (int k = 0; 16 * k < valid; ++k) {
+                Frag f;
+                load(f, 16 * k);
+                use(f);
+            }
+        }
+        if (c + 1 < cx.nchunks) {
+            write_h(buf ^ 1, sh, v.eHn);
+        } else if (a.final_state) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = 32 * t + 8 * q + 4 * hf;
+                    *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
+                        f32x4{ldexp_f(Hs[t][4 * q], sh), ldexp_f(Hs[t][4 * q + 1], sh), ldexp_f(Hs[t][4 * q + 2], sh),
+                              ldexp_f(Hs[t][4 * q + 3], sh)};
+                }
+        }
+        __syncthreads();                             // chunk c + 1
+    }
+    if (cx.nchunks == 0 && a.final_state) {          // no tokens: the final state is the initial one
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 32 * t + 8 * q + 4 * hf;
+                *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
+                    f32x4{Hs[t][4 * q], Hs[t][4 * q + 1], Hs[t][4 * q + 2], Hs[t][4 * q + 3]};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Loader waves 6 and 7: rows 0..63 / 64..127 of each chunk's x tile.  A chunk's rows are loaded into
+// registers three chunks ahead; two chunks ahead each wave takes the largest |x| of its half and leaves
+// it in LDS; one chunk ahead (after the barrier) both read the chunk's maximum, convert their halves to
+// fp16 into the chunk's x tile, and wave 4 builds the chunk's per-token vectors.  Three register sets
+// rotate (the chunk loop is unrolled by three so that they stay registers).
+struct XHalf {
+    u32x4 v[8];      // instruction k: lane l holds row 64 half + 8k + l/8, 16-byte piece l%8
+};
+
+__device__ __forceinline__ void x_load(XHalf& xr, const Ctx& cx, int c, int half, int lane) {
+    const int valid = cx.valid(c);
+    const bf16* base = cx.xg + cx.row0(c) * cx.xs + static_cast<int64_t>(cx.h) * P + 8 * (lane & 7);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        int r = 64 * half + 8 * k + (lane >> 3);
+        r = r < valid ? r : valid - 1;               // past the end: a real row (zero weights)
+        xr.v[k] = *reinterpret_cast<const u32x4*>(base + r * cx.xs);
+    }
+}
+
+struct DtRegs {
+    bf16 d0, d1;     // tokens 2 lane, 2 lane + 1
+    int2 sc;         // (eB, eC) of the chunk
+};
+
+__device__ __forceinline__ void dt_load(DtRegs& dr, const Ctx& cx, int c, int lane) {
+    const int valid = cx.valid(c);
+    const int q0 = 2 * lane < valid ? 2 * lane : valid - 1;
+    const int q1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
+    const int64_t r0 = cx.row0(c);
+    dr.d0 = cx.dtg[(r0 + q0) * cx.H + cx.h];
+    dr.d1 = cx.dtg[(r0 + q1) * cx.H + cx.h];
+    dr.sc = cx.ws.scales[cx.tile0 + c];
+}
+
+// Wave-wide inclusive scans with DPP lane moves (VALU, no LDS round trips): shifts by 1, 2, 4 and 8
+// inside each 16-lane row (lanes shifted in from outside the row read 0), then the last lane of rows
+// 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.  Valid for operations with identity 0
+// on the values involved (sums; maxima of non-negative values).
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ unsigned dpp_u(unsigned x) {
+    return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, RMASK, 0xF, BC));
+}
+template <class OP>
+__device__ __forceinline__ unsigned wave_scan_bits(unsigned v, OP op) {
+    v = op(v, dpp_u<0x111, 0xF, true>(v));
+    v = op(v, dpp_u<0x112, 0xF, true>(v));
+    v = op(v, dpp_u<0x114, 0xF, true>(v));
+    v = op(v, dpp_u<0x118, 0xF, true>(v));
+    v = op(v, dpp_u<0x142, 0xA, false>(v));
+    v = op(v, dpp_u<0x143, 0xC, false>(v));
+    return v;
+}
+__device__ __forceinline__ float wave_incl_sum(float v) {
+    return __uint_as_float(wave_scan_bits(__float_as_uint(v), [](unsigned a, unsigned b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+__device__ __forceinline__ unsigned wave_max_u(unsigned m) {
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(
+        static_cast<int>(wave_scan_bits(m, [](unsigned a, unsigned b) { return a > b ? a : b; })), 63));
+}
+__device__ __forceinline__ float wave_max_f(float m) {      // m >= 0
+    return __int_as_float(__builtin_amdgcn_readlane(static_cast<int>(wave_scan_bits(__float_as_uint(m),
+        [](unsigned a, unsigned b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); })), 63));
+}
+__device__ __forceinline__ float wave_sum_f(float m) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_sum(m)), 63));
+}
+__device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+// value of lane 16 (l / 16) + k, for each lane l (k wave-uniform)
+__device__ __forceinline__ float row_lane_f(float v, int k, int lane) {
+    const float r0 = lane_f(v, k), r1 = lane_f(v, 16 + k), r2 = lane_f(v, 32 + k), r3 = lane_f(v, 48 + k);
+    const int row = lane >> 4;
+    return row == 0 ? r0 : (row == 1 ? r1 : (row == 2 ? r2 : r3));
+}
+
+// largest |x| of a half tile, as bf16 bits
+__device__ __forceinline__ unsigned half_max(const XHalf& xr) {
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, xr.v[k][e] & 0x7FFF7FFFu));
+    return wave_max_u(max(static_cast<unsigned>(m2[0]), static_cast<unsigned>(m2[1])));
+}
+
+// the chunk's x scale from the largest |x| (bf16 bits): 0 while it lies in [2^-8, 2^15)
+__device__ __forceinline__ int x_scale(unsigned mb) {
+    const int e = static_cast<int>(mb >> 7) - 127;
+    return (mb == 0 || mb >= 0x7F80u) ? 0 : ((e >= 15 || e < -8) ? e - 14 : 0);
+}
+
+// a half tile -> fp16 x' = x 2^-ex into x tile xt
+__device__ __forceinline__ void x_convert(const XHalf& xr, unsigned char* xt, int half, int ex, int lane) {
+    const int rp = lane >> 3, pc = lane & 7;
+    auto convert = [&](auto scale) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = scale(__uint_as_float(xr.v[k][q] << 16));
+                const float hi = scale(__uint_as_float(xr.v[k][q] & 0xFFFF0000u));
+                o[q] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+            }
+            *reinterpret_cast<u32x4*>(xt + soff<kRowX>(64 * half + 8 * k + rp, pc)) = o;
+        }
+    };
+    if (ex == 0) convert([](float f) { return f; });
+    else convert([ex](float f) { return ldexp_f(f, -ex); });
+}
+
+// Chunk c's per-token vectors and scale exponents into v.  mb: the chunk's largest |x| (bf16 bits);
+// bound: the bound on |H| at the chunk's start (updated to the bound at its end); eH, sHp: units of the
+// state copy the chunk reads and of the state accumulator before it (updated for the next chunk).
+__device__ __forceinline__ void build_vec(const DtRegs& dr, unsigned mb, Vec& v, const Ctx& cx, const ScanArgs& a,
+                                          int c, int lane, float A2, float Dh, float& bound, int& eH, int& sHp) {
+    const int ex = x_scale(mb);
+    const float maxx = __uint_as_float(mb << 16);
+    // per-token vectors (two tokens per lane)
+    const int valid = cx.valid(c);
+    const int h = cx.h;
+    const float d0 = 2 * lane < valid ? dt_prologue(static_cast<float>(dr.d0), a.dtp, h) : 0.f;
+    const float d1 = 2 * lane + 1 < valid ? dt_prologue(static_cast<float>(dr.d1), a.dtp, h) : 0.f;
+    const float a0 = d0 * A2, a1 = d1 * A2;
+    const float s = wave_incl_sum(a0 + a1);
+    const float c1 = s, c0 = s - a1;                  // inclusive sums at tokens 2 lane + 1 and 2 lane
+    const int last = valid - 1;
+    const float csl = (last & 1) ? lane_f(c1, last >> 1) : lane_f(c0, last >> 1);
+    const float ce = row_lane_f(c1, 15, lane);                 // end of this lane's 32-token tile
+    const float cm = row_lane_f(c1, 7, lane);                  // token 15 of the tile
+    const float cf = row_lane_f(c0, 0, lane);                  // first token of the tile
+    const float maxdt = wave_max_f(fmaxf(d0, d1));
+    const int eB = dr.sc.x, eC = dr.sc.y;
+    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    const float w0 = j0 < valid ? fexp2(csl - c0) * d0 : 0.f;
+    const float w1 = j1 < valid ? fexp2(csl - c1) * d1 : 0.f;
+    const float sumw = wave_sum_f(w0 + w1);
+    // scale exponents (integer arithmetic on bounds)
+    const int ldt = max(ilog2f(maxdt), -100);
+    const int ebM = max(max(37 + eB + eC + ldt + 1, ilog2f(Dh) + 1) + 1, eB + eC - 45);
+    const int eM = ex + ebM - 15;
+    const int sM = eB + eC + ex - eM;
+    const float sbound = sumw * maxx * ldexp_f(1.f, eB + 15);
+    const float dec = fexp2(csl);
+    const float bnext = dec * bound + sbound;
+    const int lbn = max(ilog2f(bnext), -126);
+    const int ew = max(ex + ldt + 1, lbn + 1 - eB - 120);
+    v.cs[j0] = c0;
+    v.cs[j1] = c1;
+    v.dt[j0] = d0;
+    v.dt[j1] = d1;
+    v.fM[j0] = fexp2(ce - c0) * d0;
+    v.fM[j1] = fexp2(ce - c1) * d1;
+    const float range = cf - ce;                              // the tile's decay range (>= 0)
+    const bool dok = range < 48.f;
+    v.vD[j0] = dok ? fexp2(cm - c0) * d0 : 0.f;
+    v.vD[j1] = dok ? fexp2(cm - c1) * d1 : 0.f;
+    v.wS[j0] = ldexp_f(w0, ex - ew);
+    v.wS[j1] = ldexp_f(w1, ex - ew);
+    if ((lane & 15) == 15) {
+        v.csE[lane >> 4] = c1;
+        v.diagOK[lane >> 4] = dok ? 1 : 0;
+    }
+    if ((lane & 15) == 7) v.csM[lane >> 4] = c1;
+    if (lane == 0) {
+        v.dec = dec;
+        v.dx = ldexp_f(Dh, ex - eM);
+        v.eB = eB;
+        v.eC = eC;
+        v.ex = ex;
+        v.sM = sM;
+        v.eM = eM;
+        v.ew = ew;
+        v.sH = eB + ew;
+        v.sHp = sHp;
+        v.eHc = eH;
+        v.eHn = lbn + 1 - 15;
+    }
+    bound = bnext;
+    eH = lbn + 1 - 15;
+    sHp = eB + ew;
+}
+
+// Loader wave for rows 64 half .. 64 half + 63 (half 0: wave 6, which also builds the vectors; half 1:
+// wave 7, which also copies each next chunk's B tile from the pre-pass into LDS).
+template <int HALF>
+__device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    const float A2 = a.A[cx.h] * kLog2e;
+    const float Dh = a.D ? a.D[cx.h] : 0.f;
+    const int nc = cx.nchunks;
+    XHalf r0, r1, r2;           // register set m % 3 holds chunk m
+    DtRegs d0, d1, d2;
+    auto bcopy = [&](int c) {                        // chunk c's B tile into B[c % 2]
+        const unsigned char* src = cx.ws.btile(cx.tile0 + c) + 16 * lane;
+        unsigned char* dst = sm.B[c & 1];
+#pragma unroll
+        for (int k = 0; k < kTile / 1024; ++k)
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 1024 * k),
+                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+    };
+    if (nc > 0) x_load(r0, cx, 0, HALF, lane);
+    if (nc > 1) x_load(r1, cx, 1, HALF, lane);
+    if (nc > 2) x_load(r2, cx, 2, HALF, lane);
+    if constexpr (HALF == 0) {
+        if (nc > 0) dt_load(d0, cx, 0, lane);
+        if (nc > 1) dt_load(d1, cx, 1, lane);
+        if (nc > 2) dt_load(d2, cx, 2, lane);
+    } else {
+        if (nc > 0) bcopy(0);
+    }
+    if (nc > 0) {
+        const unsigned m = half_max(r0);
+        if (lane == 0) sm.xmax[0][HALF] = m;
+    }
+    __syncthreads();                                 // prologue 1
+    float bound = fmaxf(sm.hmax[0], sm.hmax[1]);
+    int eH = max(ilog2f(bound), -126) + 1 - 15;      // units of the initial state copy
+    int sHp = 0;
+    if (nc > 0) {
+        const unsigned mb = max(sm.xmax[0][0], sm.xmax[0][1]);
+        x_convert(r0, sm.X[0], HALF, x_scale(mb), lane);
+        if constexpr (HALF == 0) build_vec(d0, mb, sm.vec[0], cx, a, 0, lane, A2, Dh, bound, eH, sHp);
+        if (nc > 1) {
+            const unsigned m = half_max(r1);
+            if (lane == 0) sm.xmax[1][HALF] = m;
+        }
+        if constexpr (HALF == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B copy
+    }
+    __syncthreads();                                 // chunk 0
+    // chunk c: convert chunk c + 1 (rc, dt in dc), take the maximum of chunk c + 2 (rm), load chunk c + 3
+    // into the sets chunk c used (rl, dl)
+    auto phase = [&](int c, XHalf& rc, DtRegs& dc, XHalf& rm, XHalf& rl, DtRegs& dl) {
+        if (c + 1 < nc) {
+            const unsigned mb = max(sm.xmax[(c + 1) & 1][0], sm.xmax[(c + 1) & 1][1]);
+            x_convert(rc, sm.X[(c + 1) & 1], HALF, x_scale(mb), lane);
+            if constexpr (HALF == 0) build_vec(dc, mb, sm.vec[(c + 1) & 1], cx, a, c + 1, lane, A2, Dh, bound, eH, sHp);
+        }
+        if (c + 2 < nc) {
+            const unsigned m = half_max(rm);
+            if (lane == 0) sm.xmax[c & 1][HALF] = m;
+        }
+        if constexpr (HALF == 1) {
+            if (c + 1 < nc) bcopy(c + 1);
+        }
+        if (c + 3 < nc) x_load(rl, cx, c + 3, HALF, lane);
+        if constexpr (HALF == 0) {
+            if (c + 3 < nc) dt_load(dl, cx, c + 3, lane);
+        } else {
+            // the B copy has landed: vmcnt(8) counts the x loads issued after it
+            if (c + 3 < nc) __builtin_amdgcn_s_waitcnt(0x0F78);
+            else __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        __syncthreads();                             // chunk c + 1
+    };
+    for (int c = 0; c < nc; c += 3) {
+        phase(c, r1, d1, r2, r0, d0);
+        if (c + 1 >= nc) break;
+        phase(c + 1, r2, d2, r0, r1, d1);
+        if (c + 2 >= nc) break;
+        phase(c + 2, r0, d0, r1, r2, d2);
+    }
+}
+
+template <typename TY>
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsView ws) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+    // XCD-aware numbering: workgroup id % 8 picks the XCD; XCD k takes heads [k H/8, (k+1) H/8) of
+    // every batch entry, so a B/C group's heads share that XCD's L2.
+    int64_t id = blockIdx.x;
+    if (a.nheads % 8 == 0) {
+        const int64_t hpx = a.nheads / 8, j = id / 8;
+        id = (j / hpx) * a.nheads + (id % 8) * hpx + j % hpx;
+    }
+    Ctx cx;
+    cx.xg = static_cast<const bf16*>(a.x);
+    cx.dtg = static_cast<const bf16*>(a.dt);
+    cx.xs = a.x_row_stride;
+    cx.seqlen = a.seqlen;
+    cx.b = id / a.nheads;
+    cx.h = static_cast<int>(id % a.nheads);
+    cx.H = a.nheads;
+    cx.grp = cx.h / (a.nheads / a.ngroups);
+    cx.nchunks = static_cast<int>((a.seqlen + Q - 1) / Q);
+    cx.tile0 = (cx.b * a.ngroups + cx.grp) * static_cast<int64_t>(cx.nchunks);
+    cx.ws = ws;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wave == 0) run_y<TY, 0>(sm, a, cx, lane);
+    else if (wave == 1) run_y<TY, 1>(sm, a, cx, lane);
+    else if (wave == 2) run_y<TY, 2>(sm, a, cx, lane);
+    else if (wave == 3) run_y<TY, 3>(sm, a, cx, lane);
+    else if (wave == 4) run_s<0>(sm, a, cx, lane);
+    else if (wave == 5) run_s<1>(sm, a, cx, lane);
+    else if (wave == 6) run_x<0>(sm, a, cx, lane);
+    else run_x<1>(sm, a, cx, lane);
+}
+
+template <typename TY>
+static hipError_t launch_t(const ScanArgs& a, void* workspace, hipStream_t s) {
+    if (a.batch * a.nheads == 0) return hipSuccess;
+    const int64_t nc = (a.seqlen + Q - 1) / Q;
+    const int64_t ntile = a.batch * a.ngroups * nc;
+    WsView ws{static_cast<unsigned char*>(workspace),
+              reinterpret_cast<int2*>(static_cast<unsigned char*>(workspace) + ntile * kWsTile), ntile};
+    if (ntile > 0) {
+        hipLaunchKernelGGL(bc_prep_kernel, dim3(static_cast<uint32_t>(ntile)), dim3(256), 0, s,
+                           static_cast<const bf16*>(a.B), static_cast<const bf16*>(a.C), a.bc_row_stride, a.seqlen,
+                           a.ngroups, nc, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    auto kern = chunk_scan_kernel<TY>;
+    const size_t smem = sizeof(Smem);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(a.batch * a.nheads)), dim3(kThreads), smem, s, a, ws);
+    return hipGetLastError();
+}
+
+}  // namespace scan16
+
+bool f16_scan_supports(int head_dim, int d_state, int chunk) {
+    return head_dim == scan16::P && d_state == scan16::NS && chunk == scan16::Q;
+}
+
+size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int ngroups) {
+    const int64_t nc = (seqlen + scan16::Q - 1) / scan16::Q;
+    return static_cast<size_t>(scan16::ws_bytes(batch * ngroups * nc));
+}
+
+hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s) {
+    return ydt == Dt::BF16 ? scan16::launch_t<bf16>(a, workspace, s) : scan16::launch_t<float>(a, workspace, s);
+}
+
+}  // namespace ssd

@@ -142,10 +142,15 @@ ssd_status_t ssd_conv1d_update_slots(const ssd_dims_t* d, const void* xbc, int64
     return hip_status(ssd::launch_conv1d_update(a, static_cast<Dt>(d->act_dtype), stream));
 }
 
+// The fp16 scan applies to bf16 inputs at (head_dim, d_state, chunk) = (64, 128, 128); its workspace
+// holds the pre-pass's fp16 B and C tiles and their scales.
+static bool f16_scan_applies(const ssd_dims_t* d, int32_t chunk) {
+    return d && d->act_dtype == SSD_BF16 && ssd::f16_scan_supports(d->head_dim, d->d_state, chunk);
+}
+
 size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
-    (void)d;
-    (void)chunk;
-    return 0;
+    if (!f16_scan_applies(d, chunk) || d->batch <= 0 || d->seqlen <= 0 || d->ngroups <= 0) return 0;
+    return ssd::f16_scan_workspace_bytes(d->batch, d->seqlen, d->ngroups);
 }
 
 // the batched scan, with optional state snapshots (internal linkage)
@@ -168,13 +173,18 @@ static ssd_status_t chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x
     for (const void* p : {x, B, C, static_cast<const void*>(y), static_cast<const void*>(init_state), static_cast<const void*>(final_state)})
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
-    if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
-    (void)workspace;
+    // A workspace selects the fp16 scan: it must then be large enough and 16-byte aligned.  Without
+    // one (NULL or 0 bytes) the scan runs on the bf16 split-operand kernel.
+    const size_t ws_need = snapshots ? 0 : ssd_chunk_scan_workspace_size(d, chunk);
+    const bool use_f16 = ws_need > 0 && workspace && workspace_bytes > 0;
+    if (use_f16 && workspace_bytes < ws_need) return SSD_ERR_WORKSPACE;
+    if (use_f16 && !aligned16(workspace)) return SSD_ERR_ALIGN;
     if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, init_state, final_state, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
                     {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params), snapshots, interval};
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
+    if (use_f16) return hip_status(ssd::launch_chunk_scan_f16(a, ydt, workspace, stream));
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
     return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));
@@ -229,8 +239,8 @@ static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const 
     for (const void* p : {x, B, C, static_cast<const void*>(y)})
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
-    if (workspace_bytes < ssd_chunk_scan_workspace_size(d, chunk)) return SSD_ERR_WORKSPACE;
-    (void)workspace;
+    (void)workspace;          // the packed scan needs none
+    (void)workspace_bytes;
     if (d->batch > 0 && !tokens && nslots == 0) return SSD_OK;   // nothing to compute or store
     if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,

@@ -138,6 +138,11 @@ hipError_t launch_conv1d_update_accept(const ConvUpdateArgs& a, const int32_t* a
 // MFMA chunk scan: bf16 inputs with (head_dim, d_state, chunk) = (64, 128, 128).
 bool mfma_scan_supports(int head_dim, int d_state, int chunk);
 hipError_t launch_chunk_scan_mfma(const ScanArgs& a, Dt ydt, hipStream_t s);
+// fp16 MFMA chunk scan (pre-pass of B and C into the workspace, then the scan): bf16 inputs with
+// (head_dim, d_state, chunk) = (64, 128, 128); workspace of f16_scan_workspace_bytes, 16-byte aligned.
+bool f16_scan_supports(int head_dim, int d_state, int chunk);
+size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int ngroups);
+hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s);
 // Generic chunk scan on fp32 FMA (any act dtype, head_dim and d_state <= 128).
 hipError_t launch_chunk_scan_fma(const ScanArgs& a, Dt act, Dt ydt, hipStream_t s);
 

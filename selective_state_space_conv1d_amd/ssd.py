@@ -270,7 +270,10 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     """SSD chunked scan.  x [B, L, H, P], B/C [B, L, G, N] (token rows may be strided, e.g.
     views into the conv output), dt [B, L, H], A [H] fp32, D [H] fp32|None,
     init_state/final_state [B, H, P, N] fp32|None (may be the same tensor).  Optional dt prologue:
-    dt <- clamp(softplus(dt + dt_bias), *dt_limit).  Returns y [B, L, H, P] in y_dtype (default x's)."""
+    dt <- clamp(softplus(dt + dt_bias), *dt_limit).  workspace: None allocates the one the fp16 scan needs
+    (ssd_chunk_scan_workspace_size bytes; bf16 inputs with head_dim 64, d_state 128, chunk 128), a uint8
+    tensor of at least that size is used as given, False runs without one (the bf16 split-operand
+    kernel).  Returns y [B, L, H, P] in y_dtype (default x's)."""
     dev = _device(x, "x")
     Bt, L, H, P = x.shape
     _need(B, "B", dev, dtype=x.dtype, contiguous=False)
@@ -294,6 +297,12 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
         y = torch.empty((Bt, L, H, P), dtype=ydt, device=x.device)
     _need(y, "y", dev, (Bt, L, H, P))
     d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
+    if workspace is None and snapshot_interval is None:
+        # the fp16 scan's workspace (pre-pass tiles of B and C), from torch's caching allocator
+        n = int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+    elif workspace is False:
+        workspace = None         # no workspace: the bf16 split-operand kernel
     _need(workspace, "workspace", dev, optional=True)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))

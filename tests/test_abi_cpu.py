@@ -100,8 +100,24 @@ def test_scan_validation(ssd, lib):
     assert scan(lib, dims(ssd), init=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
 
 
-def test_workspace_size_is_zero(ssd, lib):
-    assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(dims(ssd)), 128) == 0
+def test_workspace_size(ssd, lib):
+    """The fp16 scan's workspace: per (batch, group, 128-token chunk) the fp16 B and C tiles (2 x 32 KiB),
+    the ten causal 32 x 32 fp32 tiles of C.B^T (40 KiB) and two int32 scale exponents; no workspace for
+    other sizes, dtypes or chunks."""
+    ws = lib.ssd_chunk_scan_workspace_size
+    assert ws(ctypes.byref(dims(ssd)), 128) == 2 * 2 * 3 * (65536 + 40960 + 8)          # B 2, G 2, ceil(300/128) = 3
+    assert ws(ctypes.byref(dims(ssd, seqlen=8192, batch=1, ngroups=8, nheads=256)), 128) == 8 * 64 * 106504
+    assert ws(ctypes.byref(dims(ssd)), 64) == 0
+    assert ws(ctypes.byref(dims(ssd, act_dtype=0)), 128) == 0
+    assert ws(ctypes.byref(dims(ssd, head_dim=32)), 128) == 0
+    assert ws(ctypes.byref(dims(ssd, seqlen=0)), 128) == 0
+    assert ws(None, 128) == 0
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    # a workspace that is given must be large enough and aligned; NULL selects the split-operand kernel
+    need = ws(ctypes.byref(dims(ssd)), 128)
+    assert scan(lib, dims(ssd), ws=fp(7), wsb=need - 1, x=None) == E["SSD_ERR_NULL"]     # validation order
+    assert scan(lib, dims(ssd), ws=fp(7), wsb=need - 1) == E["SSD_ERR_WORKSPACE"]
+    assert scan(lib, dims(ssd), ws=ctypes.c_void_p(P0 + 8), wsb=need) == E["SSD_ERR_ALIGN"]
 
 
 def test_conv_validation(ssd, lib):

@@ -19,7 +19,8 @@ class Recorder:
 
     def __getattr__(self, name):
         def f(*args):
-            self.calls.append(name)
+            if not name.endswith("_size"):       # size queries launch nothing
+                self.calls.append(name)
             return 0
         return f
 

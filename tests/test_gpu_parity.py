@@ -121,10 +121,12 @@ def test_state_update_strided_views_no_D(orc):
 
 
 # --------------------------------------------------------------------------- chunk scan
-def run_scan(s, chunk=128, ydt=torch.float32, init="given", final=True):
+def run_scan(s, chunk=128, ydt=torch.float32, init="given", final=True, ws=None):
+    """ws None: the default scan (the fp16 one where it applies); False: the bf16 split-operand kernel."""
     init_t = s["init_state"] if init == "given" else None
     fin = torch.full_like(s["init_state"], 3.0) if final else None
-    y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], init_t, fin, chunk=chunk, y_dtype=ydt)
+    y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], init_t, fin, chunk=chunk, y_dtype=ydt,
+                           workspace=ws)
     torch.cuda.synchronize()
     return y, fin
 
@@ -145,12 +147,13 @@ def test_scan_fp32(orc, L, init):
     assert_close(y, yr, F32_BAR, "y")
 
 
+@pytest.mark.parametrize("ws", [pytest.param(None, id="f16"), pytest.param(False, id="split")])
 @pytest.mark.parametrize("L", [1, 2, 127, 128, 129, 300, 515])
 @pytest.mark.parametrize("slow", [False, True])
-def test_scan_bf16_mfma(orc, L, slow):
+def test_scan_bf16_mfma(orc, L, slow, ws):
     d = LayerDims(2, L, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 40 + L, slow=slow))
-    y, fin = run_scan(s)
+    y, fin = run_scan(s, ws=ws)
     yr, fr = oracle_scan(orc, s)
     assert_close(y, yr, BF16_BAR, "y")
     assert_close(fin, fr, BF16_BAR, "final state")
@@ -168,11 +171,12 @@ def test_scan_bf16_other_shapes(orc, shape, chunk):
     assert_close(fin, fr, BF16_BAR, "final state")
 
 
-def test_scan_bf16_output_is_rounded_fp32_output():
+@pytest.mark.parametrize("ws", [pytest.param(None, id="f16"), pytest.param(False, id="split")])
+def test_scan_bf16_output_is_rounded_fp32_output(ws):
     d = LayerDims(2, 300, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 60))
-    y32, f32_ = run_scan(s, ydt=torch.float32)
-    y16, f16_ = run_scan(s, ydt=torch.bfloat16)
+    y32, f32_ = run_scan(s, ydt=torch.float32, ws=ws)
+    y16, f16_ = run_scan(s, ydt=torch.bfloat16, ws=ws)
     assert torch.equal(y16, y32.to(torch.bfloat16))
     assert torch.equal(f16_, f32_)
 
@@ -190,6 +194,49 @@ def test_scan_views_into_conv_output_and_aliased_state(orc):
     assert_close(st, fr, BF16_BAR, "state")
 
 
+@pytest.mark.parametrize("scale", [(0.0, 0, 0), (-30, 0, 0), (24, 0, 0), (0, -40, 0), (0, 40, 0), (0, 0, -40),
+                                   (0, 0, 40), (-20, 20, -20)])
+def test_scan_f16_operand_scales(orc, scale):
+    """The fp16 scan scales its operands by powers of two chosen from the data (x per chunk, B and C per
+    (batch, group, chunk) tile, the weighted x, M and the state copy from scalar bounds): inputs far from
+    O(1) -- x, B or C scaled by 2^ex, 2^eb, 2^ec, tiny and huge -- stay at the bf16 bar vs the oracle, and
+    a tile that is entirely zero (scale (0, 0, 0) variant: B zero in the second chunk) is exact zeros."""
+    ex, eb, ec = scale
+    d = LayerDims(2, 300, 4, 64, 2, 128)
+    s = cuda(scan_inputs(d, 63))
+    s["x"] = (s["x"].float() * 2.0 ** ex).to(torch.bfloat16)
+    s["Bm"] = (s["Bm"].float() * 2.0 ** eb).to(torch.bfloat16)
+    s["Cm"] = (s["Cm"].float() * 2.0 ** ec).to(torch.bfloat16)
+    s["init_state"] = s["init_state"] * 2.0 ** (ex + eb)
+    if scale == (0.0, 0, 0):
+        s["Bm"][:, 128:256] = 0
+    y, fin = run_scan(s)
+    yr, fr = oracle_scan(orc, s)
+    assert_close(y, yr, BF16_BAR, "y")
+    assert_close(fin, fr, BF16_BAR, "final state")
+
+
+def test_scan_f16_workspace_given_or_allocated():
+    """A caller-provided workspace (reused across calls of different sizes) gives the same bits as the
+    one the binding allocates; a smaller one is rejected."""
+    d = LayerDims(2, 300, 4, 64, 2, 128)
+    s = cuda(scan_inputs(d, 64))
+    y0, f0 = run_scan(s)
+    n = ssd.ssd_chunk_scan_workspace_size(2, 300, 4, 64, 2, 128)
+    assert n > 0
+    ws = torch.empty(n + 4096, dtype=torch.uint8, device=DEV)
+    y1, f1 = run_scan(s, ws=ws)
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    small = {k: (v[:1, :130] if k in ("x", "Bm", "Cm", "dt") else (v[:1] if k == "init_state" else v))
+             for k, v in s.items()}
+    small = {k: (v.contiguous() if isinstance(v, torch.Tensor) else v) for k, v in small.items()}
+    y2, f2 = run_scan(small, ws=ws)
+    y3, f3 = run_scan(small)
+    assert torch.equal(y2, y3) and torch.equal(f2, f3)
+    with pytest.raises(RuntimeError, match="WORKSPACE"):
+        run_scan(s, ws=ws[:n - 16])
+
+
 def test_scan_L0_copies_state():
     d = LayerDims(2, 0, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 62))
@@ -202,67 +249,88 @@ def test_scan_L0_copies_state():
 
 
 # --------------------------------------------------------------------------- invariants on the GPU
+# The bf16 scans at (P, N) = (64, 128) run on two kernels: the fp16 single-pass one (the default, with a
+# workspace) and the bf16 split-operand one (workspace=False).  Each invariant runs on both.
+KERNELS = [pytest.param(None, id="f16"), pytest.param(False, id="split")]
+
+
+@pytest.mark.parametrize("ws", KERNELS)
 @pytest.mark.parametrize("P,N", [(64, 128), (16, 16)])
-def test_invariant_null_init_equals_zero_init_and_determinism(P, N):
+def test_invariant_null_init_equals_zero_init_and_determinism(P, N, ws):
     d = LayerDims(2, 333, 4, P, 2, N)
     s = cuda(scan_inputs(d, 70))
-    y0, f0 = run_scan(s, init=None)
+    y0, f0 = run_scan(s, init=None, ws=ws)
     s0 = dict(s)
     s0["init_state"] = torch.zeros_like(s["init_state"])
-    yz, fz = run_scan(s0)
+    yz, fz = run_scan(s0, ws=ws)
     assert torch.equal(y0, yz) and torch.equal(f0, fz)
-    y1, f1 = run_scan(s)
-    y2, f2 = run_scan(s)
+    y1, f1 = run_scan(s, ws=ws)
+    y2, f2 = run_scan(s, ws=ws)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
-def test_invariant_dt_zero_keeps_state():
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_dt_zero_keeps_state(ws):
     d = LayerDims(2, 300, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 71))
     s["dt"] = torch.zeros_like(s["dt"])
-    _, fin = run_scan(s)
+    _, fin = run_scan(s, ws=ws)
     assert torch.equal(fin, s["init_state"])
 
 
-def test_invariant_reset_under_huge_decay(orc):
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_reset_under_huge_decay(orc, ws):
     d = LayerDims(2, 200, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 72))
     s["A"] = torch.full_like(s["A"], -1e6)
-    y, fin = run_scan(s)
+    y, fin = run_scan(s, ws=ws)
     assert torch.isfinite(y).all() and torch.isfinite(fin).all()
     yr, fr = oracle_scan(orc, s)
     assert_close(y, yr, BF16_BAR, "y")
     assert_close(fin, fr, BF16_BAR, "state")
 
 
-def test_invariant_linearity_and_batch_permutation():
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_linearity_and_batch_permutation(ws):
+    """Batch entries are independent: permuting them permutes the results bit for bit.  Doubling x and the
+    initial state doubles y and the state: exactly on the split kernel (every product scales by an exact
+    factor 2); within fp16 rounding on the fp16 one, whose operand scales follow the data and whose
+    smallest weighted-x values round as fp16 subnormals."""
     d = LayerDims(3, 260, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 73))
-    y, f = run_scan(s)
+    y, f = run_scan(s, ws=ws)
     s2 = dict(s)
     s2["x"] = s["x"] * 2
     s2["init_state"] = s["init_state"] * 2
-    y2, f2 = run_scan(s2)
-    assert torch.equal(y2, 2 * y) and torch.equal(f2, 2 * f)
+    y2, f2 = run_scan(s2, ws=ws)
+    if ws is False:
+        assert torch.equal(y2, 2 * y) and torch.equal(f2, 2 * f)
+    else:
+        assert_close(y2, f64(2 * y), 2e-4, "2x y")
+        assert_close(f2, f64(2 * f), 2e-4, "2x state")
     perm = torch.tensor([2, 0, 1], device=DEV)
     sp = {k: (v[perm] if k in ("x", "Bm", "Cm", "dt", "init_state") else v) for k, v in s.items()}
-    yp, fp_ = run_scan(sp)
+    yp, fp_ = run_scan(sp, ws=ws)
     assert torch.equal(yp, y[perm]) and torch.equal(fp_, f[perm])
 
 
-def test_invariant_split_prefill_and_decode_continuation(orc):
-    """prefill(L1) -> prefill(L2 from its state) == prefill(L1+L2); then decode steps continue it."""
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_split_prefill_and_decode_continuation(orc, ws):
+    """prefill(L1) -> prefill(L2 from its state) == prefill(L1+L2); then decode steps continue it.  The two
+    ways agree to 1e-5 on the split kernel (fp32 products of bf16 halves) and to fp16 rounding (2e-4 of
+    the largest value, well inside the bf16 bar) on the fp16 one, where chunk boundaries move."""
     d = LayerDims(2, 384, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 74))
-    y_all, f_all = run_scan(s)
+    y_all, f_all = run_scan(s, ws=ws)
     L1 = 200
     a = {k: (v[:, :L1].contiguous() if k in ("x", "Bm", "Cm", "dt") else v) for k, v in s.items()}
     bpart = {k: (v[:, L1:].contiguous() if k in ("x", "Bm", "Cm", "dt") else v) for k, v in s.items()}
-    y1, f1 = run_scan(a)
+    y1, f1 = run_scan(a, ws=ws)
     bpart["init_state"] = f1
-    y2, f2 = run_scan(bpart)
-    assert_close(torch.cat([y1, y2], 1), f64(y_all), 1e-5, "split y")
-    assert_close(f2, f64(f_all), 1e-5, "split state")
+    y2, f2 = run_scan(bpart, ws=ws)
+    tol = 1e-5 if ws is False else 1e-3
+    assert_close(torch.cat([y1, y2], 1), f64(y_all), tol, "split y")
+    assert_close(f2, f64(f_all), tol, "split state")
     # decode: continue from f_all with the state update, compare with the oracle over the longer sequence
     st = f_all.clone()
     dec = cuda(scan_inputs(d.with_(seqlen=4), 75))
@@ -276,26 +344,31 @@ def test_invariant_split_prefill_and_decode_continuation(orc):
     assert_close(st, fr, BF16_BAR, "decode state")
 
 
-def test_invariant_scan_L1_equals_state_update():
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_scan_L1_equals_state_update(ws):
+    """A one-token scan is one state update: to 1e-5 on the split kernel, to fp16 rounding of the state
+    copy and operands (1e-3) on the fp16 one."""
     d = LayerDims(2, 1, 4, 64, 2, 128)
     s = cuda(scan_inputs(d, 76))
-    y, fin = run_scan(s)
+    y, fin = run_scan(s, ws=ws)
     st = s["init_state"].clone()
     yu = ssd.ssd_state_update(st, s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], s["dt"][:, 0], s["A"], s["D"],
                               y_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_close(fin, f64(st), 1e-5, "state")
-    assert_close(y[:, 0], f64(yu), 1e-5, "y")
+    tol = 1e-5 if ws is False else 1e-3
+    assert_close(fin, f64(st), tol, "state")
+    assert_close(y[:, 0], f64(yu), tol, "y")
 
 
-def test_invariant_identical_groups_equal_one_group():
+@pytest.mark.parametrize("ws", KERNELS)
+def test_invariant_identical_groups_equal_one_group(ws):
     d = LayerDims(2, 200, 4, 64, 1, 128)
     s = cuda(scan_inputs(d, 77))
-    y1, f1 = run_scan(s)
+    y1, f1 = run_scan(s, ws=ws)
     s2 = dict(s)
     s2["Bm"] = s["Bm"].repeat(1, 1, 2, 1)
     s2["Cm"] = s["Cm"].repeat(1, 1, 2, 1)
-    y2, f2 = run_scan(s2)
+    y2, f2 = run_scan(s2, ws=ws)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 

@@ -85,8 +85,9 @@ def test_scan_varlen_equal_lengths_is_the_batched_scan(P, N):
     d = LayerDims(3, 300, 4, P, 2, N)
     s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 220).items()}
     fin = torch.empty_like(s["init_state"])
+    # the packed scan runs the split-operand kernel of the batched scan: compare with that one
     yb = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], s["init_state"], fin,
-                            y_dtype=torch.float32)
+                            y_dtype=torch.float32, workspace=False)
     pool = s["init_state"][[2, 0, 1]].clone()          # sequence b lives in slot perm[b]
     perm = torch.tensor([1, 2, 0], dtype=torch.int32, device=DEV)
     cu = torch.arange(4, dtype=torch.int32, device=DEV) * 300
@@ -358,7 +359,7 @@ def test_scan_varlen_dt_prologue_matches_batched():
     kw = dict(dt_bias=bias, dt_softplus=True, dt_limit=(0.0, 1.0))
     fin = torch.empty_like(s["init_state"])
     yb = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], raw, s["A"], s["D"], s["init_state"], fin,
-                            y_dtype=torch.float32, **kw)
+                            y_dtype=torch.float32, workspace=False, **kw)
     pool = s["init_state"].clone()
     flat = lambda t: t.reshape((t.shape[0] * t.shape[1],) + tuple(t.shape[2:]))
     cu = torch.tensor([0, 200, 400], dtype=torch.int32, device=DEV)
