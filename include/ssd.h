@@ -180,6 +180,26 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ssd_chunk_scan for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call): where ssd_chunk_scan would take a workspace (bf16 inputs,
+ * head_dim 64, d_state 128, chunk 128) it uses a static 64 MiB device array instead, one per
+ * device, held until the process ends -- enough for batch x ngroups x ceil(L / 128) <= 630
+ * (e.g. one 8192-token sequence with 8 groups); larger sizes return SSD_ERR_WORKSPACE.  Other
+ * sizes run the kernels ssd_chunk_scan runs without a workspace.  Results are those of
+ * ssd_chunk_scan with a workspace, bit for bit.  Every call on a device shares that device's
+ * array (each call overwrites all of it that it reads): calls that overlap on one device, e.g.
+ * on two streams, race.  Arguments, layouts and errors are otherwise those of ssd_chunk_scan.
+ */
+ssd_status_t ssd_chunk_scan_noalloc(const ssd_dims_t* d, int32_t chunk,
+                                    const void* x, int64_t x_row_stride,
+                                    const void* B, const void* C, int64_t bc_row_stride,
+                                    const void* dt, const float* A, const float* D,
+                                    const ssd_dt_params_t* dt_params,
+                                    const float* init_state, float* final_state, void* y,
+                                    hipStream_t stream);
+
+/*
  * ssd_chunk_scan that also stores the state every `interval` tokens ([P2] 部署时如何调这些缓存:
  * one engine's setting writes an SSM state snapshot every N tokens, for prefix caching).
  *  snapshots  [B, L / interval, H, P, N] fp32, 16-byte aligned: entry k is the state after token

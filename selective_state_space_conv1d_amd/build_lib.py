@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 SOURCES = ["ssd_api.cpp", "conv1d.hip", "state_update.hip", "spec_decode.hip", "state_lp.hip", "norm.hip", "decode_step.hip",
-           "chunk_scan_fma.hip", "chunk_scan_mfma.hip", "chunk_scan_f16.hip"]
+           "chunk_scan_fma.hip", "chunk_scan_mfma.hip", "chunk_scan_f16.hip", "scan_scratch.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 vector ops are kept off (hipcc would otherwise emit them from float2 code)

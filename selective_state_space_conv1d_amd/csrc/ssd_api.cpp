@@ -200,6 +200,22 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
                       nullptr, 0, y, workspace, workspace_bytes, stream);
 }
 
+ssd_status_t ssd_chunk_scan_noalloc(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                    const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                    const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                    const float* init_state, float* final_state, void* y, hipStream_t stream) {
+    // the fp16 scan's workspace is the static per-device array; the other scans need none
+    const size_t need = ssd_chunk_scan_workspace_size(d, chunk);
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        if (ssd::f16_scan_scratch(&ws, &ws_bytes) != hipSuccess) return SSD_ERR_HIP;
+        if (need > ws_bytes) return SSD_ERR_WORKSPACE;
+    }
+    return chunk_scan(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, init_state, final_state,
+                      nullptr, 0, y, ws, ws_bytes, stream);
+}
+
 ssd_status_t ssd_chunk_scan_snapshots(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                       const void* B, const void* C, int64_t bc_row_stride, const void* dt,
                                       const float* A, const float* D, const ssd_dt_params_t* dt_params,

@@ -24,7 +24,7 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
            "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
-           "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots"]
+           "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc"]
 
 
 class SsdDims(ctypes.Structure):
@@ -73,6 +73,8 @@ def _lib():
         _PDT = ctypes.POINTER(SsdDtParams)
         lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP, _VP,
                                        _VP, ctypes.c_size_t, _VP]
+        lib.ssd_chunk_scan_noalloc.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
+                                               _VP, _VP, _VP]
         lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP]
         lib.ssd_conv1d_fwd_varlen.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
         lib.ssd_conv1d_update_slots.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
@@ -101,7 +103,7 @@ def _lib():
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
                   "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
                   "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept",
-                  "ssd_chunk_scan_varlen_snapshots"):
+                  "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -274,29 +276,12 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
     (ssd_chunk_scan_workspace_size bytes; bf16 inputs with head_dim 64, d_state 128, chunk 128), a uint8
     tensor of at least that size is used as given, False runs without one (the bf16 split-operand
     kernel).  Returns y [B, L, H, P] in y_dtype (default x's)."""
-    dev = _device(x, "x")
-    Bt, L, H, P = x.shape
-    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
-    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
-    G, N = B.shape[2], B.shape[3]
-    if L > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, L)):
-        raise ValueError("x must be [B, L, H, P] with packed (H, P) and uniform token stride")
-    for t, nm in ((B, "B"), (C, "C")):
-        if t.shape != (Bt, L, G, N) or (L > 0 and (t.stride(3) != 1 or t.stride(2) != N
-                                                    or not _uniform_rows(t, L))):
-            raise ValueError(f"{nm} must be [B, L, G, N] with packed (G, N) and uniform token stride")
-    if B.stride(1) != C.stride(1):
-        raise ValueError("B and C must share a token stride")
-    _need(dt, "dt", dev, (Bt, L, H), x.dtype)
-    _head_params(dev, H, A, D)
-    _need(init_state, "init_state", dev, (Bt, H, P, N), torch.float32, optional=True)
-    _need(final_state, "final_state", dev, (Bt, H, P, N), torch.float32, optional=True)
-    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     ydt = y_dtype or x.dtype
     if y is None:
-        y = torch.empty((Bt, L, H, P), dtype=ydt, device=x.device)
-    _need(y, "y", dev, (Bt, L, H, P))
-    d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
+        y = torch.empty(x.shape, dtype=ydt, device=x.device)
+    dev, d, xs, bcs = _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias)
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
     if workspace is None and snapshot_interval is None:
         # the fp16 scan's workspace (pre-pass tiles of B and C), from torch's caching allocator
         n = int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
@@ -305,7 +290,6 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
         workspace = None         # no workspace: the bf16 split-operand kernel
     _need(workspace, "workspace", dev, optional=True)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))
     if L == 0:
         x = B = C = dt = None
     if snapshot_interval is None:
@@ -327,6 +311,50 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
                                            int(snapshot_interval), _ptr(y), _ptr(workspace), ws, _stream(stream)),
            "ssd_chunk_scan_snapshots")
     return y
+
+
+def ssd_chunk_scan_noalloc(x, B, C, dt, A, D, init_state, final_state, y, chunk=128, stream=None, dt_bias=None,
+                           dt_softplus=False, dt_limit=None):
+    """ssd_chunk_scan that allocates nothing (for graph capture and serving loops): the caller passes y
+    [B, L, H, P] (bf16 or fp32) and the states; the fp16 scan's workspace is the library's static
+    per-device array (up to batch x groups x ceil(L / 128) = 630 tiles, else SSD_ERR_WORKSPACE).
+    Calls that overlap on one device race on that array.  Returns y."""
+    if y is None:
+        raise ValueError("ssd_chunk_scan_noalloc needs y from the caller")
+    dev, d, xs, bcs = _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias)
+    if x.shape[1] == 0:
+        x = B = C = dt = None
+    _check(_lib().ssd_chunk_scan_noalloc(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs,
+                                         _ptr(dt), _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit),
+                                         _ptr(init_state), _ptr(final_state), _ptr(y), _stream(stream)),
+           "ssd_chunk_scan_noalloc")
+    return y
+
+
+def _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias):
+    """Checks the batched scan's tensors; returns (device, dims, x row stride, B/C row stride)."""
+    dev = _device(x, "x")
+    Bt, L, H, P = x.shape
+    _need(B, "B", dev, dtype=x.dtype, contiguous=False)
+    _need(C, "C", dev, dtype=x.dtype, contiguous=False)
+    G, N = B.shape[2], B.shape[3]
+    if L > 0 and (x.stride(3) != 1 or x.stride(2) != P or not _uniform_rows(x, L)):
+        raise ValueError("x must be [B, L, H, P] with packed (H, P) and uniform token stride")
+    for t, nm in ((B, "B"), (C, "C")):
+        if t.shape != (Bt, L, G, N) or (L > 0 and (t.stride(3) != 1 or t.stride(2) != N
+                                                    or not _uniform_rows(t, L))):
+            raise ValueError(f"{nm} must be [B, L, G, N] with packed (G, N) and uniform token stride")
+    if B.stride(1) != C.stride(1):
+        raise ValueError("B and C must share a token stride")
+    _need(dt, "dt", dev, (Bt, L, H), x.dtype)
+    _head_params(dev, H, A, D)
+    _need(init_state, "init_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(final_state, "final_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    _need(y, "y", dev, (Bt, L, H, P))
+    d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
+    xs, bcs = (P * H, G * N) if L == 0 else (x.stride(1), B.stride(1))
+    return dev, d, xs, bcs
 
 
 def ssd_state_update(state, x, B, C, dt, A, D=None, y=None, y_dtype=None, stream=None, dt_bias=None,
