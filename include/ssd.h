@@ -141,9 +141,10 @@ ssd_status_t ssd_conv1d_update(const ssd_dims_t* d, const void* xbc, int64_t xbc
 
 /*
  * Workspace bytes with which ssd_chunk_scan runs its fp16 path for these sizes: for bf16 inputs
- * with head_dim 64, d_state 128 and chunk 128, per (batch entry, group, 128-token chunk) 104 KiB
- * + 8 bytes (the chunk's fp16 B^T and C tiles, the causal tiles of C.B^T in fp32, and two
- * power-of-two scale exponents); 0 for other sizes, dtypes or chunks, and for a NULL d.
+ * with head_dim 64, d_state 128 and chunk 128, per (batch entry, group, 128-token chunk) 84 KiB
+ * + 8 bytes (the chunk's fp16 B^T and C tiles, the causal tiles of C.B^T in fp16, and two
+ * power-of-two scale exponents) plus 512 bytes per (batch entry, head, chunk) (dt after the dt
+ * prologue); 0 for other sizes, dtypes or chunks, and for a NULL d.
  */
 size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk);
 
@@ -184,8 +185,9 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
  * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
  * hipFree or allocating library call): where ssd_chunk_scan would take a workspace (bf16 inputs,
  * head_dim 64, d_state 128, chunk 128) it uses a static 64 MiB device array instead, one per
- * device, held until the process ends -- enough for batch x ngroups x ceil(L / 128) <= 630
- * (e.g. one 8192-token sequence with 8 groups); larger sizes return SSD_ERR_WORKSPACE.  Other
+ * device, held until the process ends -- enough while ssd_chunk_scan_workspace_size() <= 64 MiB
+ * (one 8192-token sequence with 8 groups and 256 heads needs 50 MiB); larger sizes return
+ * SSD_ERR_WORKSPACE.  Other
  * sizes run the kernels ssd_chunk_scan runs without a workspace.  Results are those of
  * ssd_chunk_scan with a workspace, bit for bit.  Every call on a device shares that device's
  * array (each call overwrites all of it that it reads): calls that overlap on one device, e.g.

@@ -33,12 +33,15 @@
 //     rows = key tokens) times the masked decay in registers, converted straight into the next
 //     MFMA's operand, and y^T += X^T M^T.  C rows and C.B^T tiles stay in registers, each set
 //     reloaded with the next chunk's values right after its last use.
-//   * waves 4, 5: the fp32 state H^T of p tile 0 / 1 (4 n tiles each), + B^T (w x) per chunk,
-//     and the fp16 copy H' for the next chunk's C.H.
-//   * waves 6, 7: x rows 0..63 / 64..127, loaded three chunks ahead into registers, converted to fp16
-//     into LDS one chunk ahead (the two halves share their largest |x| through LDS across a barrier);
-//     wave 6 builds each chunk's per-token vectors and scale exponents, wave 7 copies each next
-//     chunk's B tile from the pre-pass into LDS (direct global->LDS).
+//   * waves 4, 5: the fp32 state H^T of n tiles 0, 1 / 2, 3 (both p tiles), + B^T (w x) per chunk with
+//     B^T operands loaded from the pre-pass into registers a chunk ahead, and the fp16 copy H' for the
+//     next chunk's C.H.
+//   * waves 6, 7: x rows 0..31 / 32..127, loaded three chunks ahead into registers, converted to fp16
+//     into LDS one chunk ahead (the two parts share their largest |x| through LDS across a barrier);
+//     wave 6 also builds each chunk's per-token vectors and scale exponents.
+// The kernel is bound by the vector-memory path of each CU (every head's workgroup reads its group's
+// B, C and C.B^T tiles, ~84 KiB per chunk, besides its own x and dt): loads are laid out so that each
+// instruction reads whole 1 KiB runs, and are spread over the waves instead of issued in bursts.
 // MFMAs per SIMD and chunk: 20 + 32, 24 + 32, 28 + 0, 32 + 0.
 // Operands that contract over tokens are LDS transpose reads (ds_read_b64_tr_b16) of row-major
 // tiles; 16-byte chunks of each row are XOR-permuted so that row and transpose reads are free of
@@ -104,9 +107,9 @@ struct Vec {
 };
 
 struct Smem {
-    unsigned char B[2][kTile];           // B'^T[n][j] fp16, double-buffered (the pre-pass's LDS image)
     unsigned char X[2][Q * kRowX];       // x'[j][p] fp16, double-buffered
     unsigned char H[2][P * kRowB];       // H'[p][n] fp16, double-buffered
+    unsigned char stage[4][32 * kRowX];  // private to y wave t: its chunk's bf16 y rows, stored one chunk later
     Vec vec[2];
     float hmax[2];                       // |initial state| maxima of the two state waves
     unsigned xmax[2][2];                 // largest |x| (bf16 bits) of each half of a chunk, by chunk parity
@@ -189,33 +192,43 @@ __device__ __forceinline__ void scale_cols(f32x16& m, float f, float a, std::int
 }
 
 // Workspace of one call, per (batch, group, chunk) tile index:
-//   BT  32 KiB  B'^T as the LDS image the state waves read: row n, 16-byte chunk q at q ^ key16(n); chunk q
-//               holds tokens 16(q/2) + {4(q%2) + 0..3, 8 + 4(q%2) + 0..3}, the slot order of an MFMA
-//               operand whose k runs over tokens;
+//   BT  32 KiB  B'^T in the state waves' register order: n tile t, token step ks, lane l: 16 bytes
+//               B'[16ks + 4(l/32) + {0..3, 8..11}][32t + l%32] (the slot order of an MFMA operand whose k
+//               runs over tokens);
 //   C   32 KiB  C' in the y waves' register order: token tile t, k step ks, lane l: 16 bytes
 //               C'[32t + l%32][16ks + 8(l/32) + 0..7];
-//   CB  40 KiB  the ten causal 32x32 tiles of (C'.B'^T)^T (rows: key tokens j; columns: tokens i), tile
-//               (it, jt) at index it(it+1)/2 + jt, each lane's 16 accumulator values contiguous;
-// then the (eB, eC) pairs.  C.B^T is the same for every head of a group, so it is computed here once.
-constexpr int kCBBytes = 10 * 4096;
+//   CB  20 KiB  the ten causal 32x32 tiles of (C'.B'^T)^T 2^-kCBShift in fp16 (rows: key tokens j; columns:
+//               tokens i), tile (it, jt) at index it(it+1)/2 + jt; within a tile, accumulator values
+//               8h .. 8h+7 of lane l at 16 (64h + l), so that each 16-byte load of a wave reads 1 KiB in one run;
+// then per (batch, head, chunk) the 128 dt values after the dt prologue (fp32, 0 past the sequence end),
+// then the (eB, eC) pairs.  C.B^T is the same for every head of a group, so it is computed here once; the
+// per-head dt rows replace 128 scattered 2-byte reads (one cache line each) by one 512-byte read.
+// |C'.B'^T| < N 2^15 2^15 = 2^37, so the fp16 copy with the shift below stays under 2^14.
+constexpr int kCBShift = 23;
+constexpr int kCBBytes = 10 * 2048;
 constexpr int64_t kWsTile = 2 * kTile + kCBBytes;
 struct WsView {
     unsigned char* tiles;
+    float* dts;      // [batch * heads * chunks][Q]
     int2* scales;
     int64_t ntile;   // batch * groups * chunks
     __device__ __host__ unsigned char* btile(int64_t i) const { return tiles + i * kWsTile; }
     __device__ __host__ unsigned char* ctile(int64_t i) const { return tiles + i * kWsTile + kTile; }
     __device__ __host__ unsigned char* cbtile(int64_t i) const { return tiles + i * kWsTile + 2 * kTile; }
 };
-__host__ __device__ inline int64_t ws_bytes(int64_t ntile) { return ntile * (kWsTile + static_cast<int64_t>(sizeof(int2))); }
+// workspace bytes for ntile (batch, group, chunk) tiles and nhc (batch, head, chunk) dt rows
+__host__ __device__ inline int64_t ws_bytes(int64_t ntile, int64_t nhc) {
+    return ntile * kWsTile + nhc * Q * static_cast<int64_t>(sizeof(float)) + ntile * static_cast<int64_t>(sizeof(int2));
+}
 
 // ---------------------------------------------------------------------------
 // Pre-pass: one workgroup of 256 threads per (batch, group, chunk).  Thread t holds 16-byte pieces
 // t + 256k (k < 8) of the B tile and of the C tile (piece i: row i / 16, chunk i % 16); rows past the
 // sequence end are zeros.  The scaled fp16 tiles are staged in LDS, from which the four waves write B'^T
 // (transpose reads) and compute the causal C'.B'^T tiles (wave w: tiles w, w + 4, w + 8).
-__global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16* Cg, int64_t bcs, int64_t seqlen,
-                                                      int ngroups, int64_t nchunks, WsView ws) {
+__global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16* Cg, int64_t bcs, const bf16* dtg,
+                                                      DtParams dtp, int64_t seqlen, int nheads, int ngroups,
+                                                      int64_t nchunks, WsView ws) {
     __shared__ __align__(16) unsigned char lb[kTile];
     __shared__ __align__(16) unsigned char lc[kTile];
     __shared__ unsigned wmax[2][4];
@@ -290,12 +303,11 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
     __syncthreads();
     const LaneOff lo(lane);
     const int c32 = lane & 31, hf = lane >> 5;
-    {   // B'^T: wave w writes the rows of n tile w
-        const int n = 32 * wave + c32;
+    {   // B'^T: wave w writes the fragments of n tile w
         const int b0 = lo.tr<kRowB>(32 * wave, 0), b8 = lo.tr<kRowB>(32 * wave, 1);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<f16x8*>(bt + n * kRowB + (((2 * k + hf) ^ key16(n)) << 4)) = tr_frag<kRowB>(lb, b0, b8, 16 * k);
+            *reinterpret_cast<f16x8*>(bt + ((wave * 8 + k) * 64 + lane) * 16) = tr_frag<kRowB>(lb, b0, b8, 16 * k);
     }
     unsigned char* cb = ws.cbtile(tix);
 #pragma unroll
@@ -306,9 +318,28 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             acc = mfma(ld16(lb + 32 * jt * kRowB + lo.row[ks]), ld16(lc + 32 * it * kRowB + lo.row[ks]), acc);
-        f32x4* dst = reinterpret_cast<f32x4*>(cb + T * 4096 + lane * 64);
+        f16x8* dst = reinterpret_cast<f16x8*>(cb + T * 2048) + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        for (int h = 0; h < 2; ++h) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = ldexp_f(acc[8 * h + k], -kCBShift);
+            dst[64 * h] = to_f16x8(v);
+        }
+    }
+    // the dt rows of the group's heads: item (head hh, 16-token segment sg)
+    const int hpg = nheads / ngroups;
+    for (int item = t; item < hpg * 8; item += 256) {
+        const int hh = item >> 3, sg = item & 7, h = g * hpg + hh;
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int j = 16 * sg + k;
+            v[k] = j < valid ? dt_prologue(static_cast<float>(dtg[(row0 + j) * nheads + h]), dtp, h) : 0.f;
+        }
+        f32x4* dst = reinterpret_cast<f32x4*>(ws.dts + ((b * nheads + h) * nchunks + c) * Q + 16 * sg);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
     }
     if (t == 0) ws.scales[tix] = int2{eB, eC};
 }
@@ -319,6 +350,7 @@ struct Ctx {
     int64_t xs, seqlen, b;
     int H, h, grp, nchunks;
     int64_t tile0;      // workspace tile index of this (batch, group)'s chunk 0
+    int64_t hrow0;      // workspace dt row of this (batch, head)'s chunk 0
     WsView ws;
     __device__ __forceinline__ int valid(int c) const {
         const int64_t r = seqlen - static_cast<int64_t>(c) * Q;
@@ -346,31 +378,53 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) cr[ks] = *reinterpret_cast<const f16x8*>(src + ks * 64 * 16);
     };
-    // this lane's 16 values of the pre-pass C'.B'^T tile (IT, jt) of chunk c
+    // this lane's 16 values of the pre-pass C'.B'^T tile (IT, jt) of chunk c (fp16, in units of 2^kCBShift)
+    struct CbReg { f16x8 h0, h1; };
     auto cb_load = [&](int c, int jt) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(cx.ws.cbtile(cx.tile0 + c) + (IT * (IT + 1) / 2 + jt) * 4096 +
-                                                          lane * 64);
-        const f32x4 q0 = src[0], q1 = src[1], q2 = src[2], q3 = src[3];
-        return f32x16{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3],
-                      q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
+        const f16x8* src = reinterpret_cast<const f16x8*>(cx.ws.cbtile(cx.tile0 + c) + (IT * (IT + 1) / 2 + jt) * 2048) +
+                           lane;
+        return CbReg{src[0], src[64]};
     };
-    // bf16 y of the previous chunk, not yet stored (yq_dst null: nothing pending or a token past the end).
-    // Loads and stores share one vector-memory counter, and a wait on it that follows a store also waits
-    // for that store; each chunk's y is therefore stored after the next chunk's first wait for its loads,
-    // which leaves the stores the whole chunk to complete.
-    u32x4 yq[4];
-    TY* yq_dst = nullptr;
+    auto cb_f32 = [](const CbReg& r) {
+        f32x16 m;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            m[k] = static_cast<float>(r.h0[k]);
+            m[8 + k] = static_cast<float>(r.h1[k]);
+        }
+        return m;
+    };
+    // bf16 y: each chunk's 32 x 64 block goes to this wave's LDS stage (rows of 128 bytes, 16-byte chunks
+    // XOR-permuted), is read back at the next chunk's start as whole rows and stored after that chunk's
+    // C.H: 8 rows per store instead of 32 partial ones, and -- since loads and stores share one vector-
+    // memory counter, so that a wait for a load also waits for earlier stores -- after the first wait for
+    // that chunk's loads, which leaves the stores a whole chunk to complete.
+    u32x4 yq[4];                                     // lane l: row 8k + l/8, 16-byte piece l%8
+    unsigned char* st = sm.stage[IT];
+    int yq_valid = 0;                                // valid tokens of the staged chunk
+    TY* yq_row = nullptr;                            // its first y row (null: nothing staged)
+    auto stage_read = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + (lane >> 3), ch = lane & 7;
+            yq[k] = *reinterpret_cast<const u32x4*>(st + r * kRowX + ((ch ^ ((r >> 1) & 7)) << 4));
+        }
+    };
     auto flush_y = [&]() {
         if constexpr (sizeof(TY) == 2) {
-            if (yq_dst != nullptr) {
+            if (yq_row != nullptr) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(yq_dst + 16 * k) = yq[k];
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 8 * k + (lane >> 3);
+                    if (32 * IT + r < yq_valid)
+                        *reinterpret_cast<u32x4*>(yq_row + (32 * IT + r) * static_cast<int64_t>(cx.H) * P + 8 * (lane & 7)) = yq[k];
+                }
             }
         }
     };
     // rolling prefetch: each register set is reloaded with the next chunk's data right after its last use
     f16x8 cf[8];
-    f32x16 cb[IT + 1];
+    CbReg cb[IT + 1];
     if (cx.nchunks > 0) {
         c_load(cf, 0);
 #pragma unroll
@@ -390,6 +444,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         const Vec& v = sm.vec[buf];
         const unsigned char* Xt = sm.X[buf];
         const unsigned char* Ht = sm.H[buf];
+        if constexpr (sizeof(TY) == 2) stage_read();
         // per-chunk factors, issued with the C.H operands: cs_i, the tiles' end values, and this lane's
         // column factor of each key tile (off-diagonal fM, diagonal vD) for the row broadcasts
         const float csi = v.cs[i];
@@ -434,7 +489,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         // causal key tiles: the C'.B'^T tile (acc rows = key tokens j, cols = tokens i), M' in
         // registers, y^T[p][i] += sum_j X'^T[p][j] M'^T[j][i]; the X^T operands of the next tile are
         // read while this one is scaled
-        const int sM = v.sM;
+        const int sM = v.sM + kCBShift;             // m holds C'.B'^T 2^-kCBShift
         auto x_frags = [&](f16x8 (&xr)[4], int jt) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -446,7 +501,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         x_frags(xc, 0);
 #pragma unroll
         for (int jt = 0; jt <= IT; ++jt) {
-            f32x16 m = cb[jt];       // m[4q + r] = C'_i . B'_jj,  jj = 32jt + 8q + 4hf + r
+            f32x16 m = cb_f32(cb[jt]);   // m[4q + r] = C'_i . B'_jj 2^-kCBShift,  jj = 32jt + 8q + 4hf + r
             __builtin_amdgcn_sched_barrier(0);
             cb[jt] = cb_load(cnext, jt);
             __builtin_amdgcn_sched_barrier(0);
@@ -524,75 +579,103 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 }
             }
         } else {
-            // held until the next chunk's C.H: lane (c32, hf) stores y[i][32pt + 16g + 8hf .. +7] from yq[2pt + g]
+            // into the stage: lane (c32, hf) holds y[i][32pt + 16g + 8hf .. +7] after the swap
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 const f32x16& yv = pt ? y1 : y0;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
+                    u32x4 o;
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const unsigned pa = pack_bf16(ldexp_f(yv[8 * g + 2 * h2], eM), ldexp_f(yv[8 * g + 2 * h2 + 1], eM));
                         const unsigned pb = pack_bf16(ldexp_f(yv[8 * g + 4 + 2 * h2], eM),
                                                       ldexp_f(yv[8 * g + 4 + 2 * h2 + 1], eM));
                         const auto sw = __builtin_amdgcn_permlane32_swap(pa, pb, false, false);
-                        yq[2 * pt + g][h2] = sw[0];
-                        yq[2 * pt + g][2 + h2] = sw[1];
+                        o[h2] = sw[0];
+                        o[2 + h2] = sw[1];
                     }
+                    const int ch = 4 * pt + 2 * g + hf;
+                    *reinterpret_cast<u32x4*>(st + c32 * kRowX + ((ch ^ ((c32 >> 1) & 7)) << 4)) = o;
                 }
             }
-            yq_dst = i < valid ? yrow + i * ystr + 8 * hf : nullptr;
+            yq_row = yrow;
+            yq_valid = valid;
         }
         __syncthreads();                             // chunk c + 1
     }
+    if constexpr (sizeof(TY) == 2) stage_read();
     flush_y();
 }
 
 // ---------------------------------------------------------------------------
-// state wave: the 4 n tiles of p tile SP.  Tile t holds Hs[t][4q + r] = H[p = 32SP + c32][n = 32t + 8q + 4hf + r]
-// in units of 2^sH (sH of the last chunk processed; 0 for the initial state).
-template <int SP>
+// state wave SN: n tiles 2SN, 2SN + 1 of both p tiles.  Accumulator u = 2 tt + pt holds
+// Hs[u][4q + r] = H[p = 32pt + c32][n = 32(2SN + tt) + 8q + 4hf + r] in units of 2^sH (sH of the last chunk
+// processed; 0 for the initial state).  Its B'^T operands come straight from the pre-pass in registers,
+// one chunk ahead: each token step's pair is reloaded with the next chunk's right after its MFMAs.
+template <int SN>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
-    const int hp = 32 * SP + c32;
     const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
     const LaneOff lo(lane);
-    const int trW = lo.tr<kRowX>(32 * SP, 0);
+    const int trW0 = lo.tr<kRowX>(0, 0), trW1 = lo.tr<kRowX>(32, 0);
+    // element (u, q) of the state: row p, columns n .. n + 3
+    auto p_of = [&](int u) { return 32 * (u & 1) + c32; };
+    auto n_of = [&](int u, int q) { return 32 * (2 * SN + (u >> 1)) + 8 * q + 4 * hf; };
     f32x16 Hs[4];
     float mx = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int n = 32 * t + 8 * q + 4 * hf;
             f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
-            if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + hp * NS + n);
+            if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Hs[t][4 * q + r] = v4[r];
+                Hs[u][4 * q + r] = v4[r];
                 mx = fmaxf(mx, fabsf(v4[r]));
             }
         }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) sm.hmax[SP] = mx;
+    if (lane == 0) sm.hmax[SN] = mx;
+    // B'^T operands of chunk c: bq[tt][ks] for n tile 2SN + tt, token step ks
+    f16x8 bq[2][8];
+    auto b_load = [&](int c, int tt, int ks) {
+        return *reinterpret_cast<const f16x8*>(cx.ws.btile(cx.tile0 + c) + (((2 * SN + tt) * 8 + ks) * 64 + lane) * 16);
+    };
+    if (cx.nchunks > 0) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) bq[tt][ks] = b_load(0, tt, ks);
+    }
     // fp16 copy of the state in units of 2^e (e.g. H' for the next chunk's C.H), into buffer hb
     auto write_h = [&](int buf, int sh, int e) {
         unsigned char* hb = sm.H[buf];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 f16x4 h4;
 #pragma unroll
                 for (int r = 0; r < 4; r += 2) {
                     const f16x2 p2 = __builtin_convertvector(
-                        f32x2{ldexp_f(Hs[t][4 * q + r], sh - e), ldexp_f(Hs[t][4 * q + r + 1], sh - e)}, f16x2);
+                        f32x2{ldexp_f(Hs[u][4 * q + r], sh - e), ldexp_f(Hs[u][4 * q + r + 1], sh - e)}, f16x2);
                     h4[r] = p2[0];
                     h4[r + 1] = p2[1];
                 }
-                *reinterpret_cast<f16x4*>(hb + soff<kRowB>(hp, 4 * t + q) + 8 * hf) = h4;
+                *reinterpret_cast<f16x4*>(hb + soff<kRowB>(p_of(u), 4 * (2 * SN + (u >> 1)) + q) + 8 * hf) = h4;
             }
+    };
+    auto store_state = [&](int sh) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(a.final_state + sbase + p_of(u) * NS + n_of(u, q)) =
+                    f32x4{ldexp_f(Hs[u][4 * q], sh), ldexp_f(Hs[u][4 * q + 1], sh), ldexp_f(Hs[u][4 * q + 2], sh),
+                          ldexp_f(Hs[u][4 * q + 3], sh)};
     };
     __syncthreads();                                 // prologue 1
     {
@@ -604,131 +687,103 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     int sh = 0;                                      // units of Hs
     for (int c = 0; c < cx.nchunks; ++c) {
         const int buf = c & 1;
+        const int cnext = c + 1 < cx.nchunks ? c + 1 : c;   // the last chunk reloads itself (unused)
         const Vec& v = sm.vec[buf];
-        const unsigned char* Bt = sm.B[buf];
         const unsigned char* Xt = sm.X[buf];
         // H <- dec H, re-expressed in this chunk's units 2^sH (a power-of-two change of units)
         const int du = sh - v.sH;
         if (du <= 100) {
             const float dec = ldexp_f(v.dec, du);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) Hs[t] *= dec;
+            for (int u = 0; u < 4; ++u) Hs[u] *= dec;
         } else {                                     // the units shrink by more than 2^100
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Hs[t][e] = ldexp_f(Hs[t][e] * v.dec, du);
+                for (int e = 0; e < 16; ++e) Hs[u][e] = ldexp_f(Hs[u][e] * v.dec, du);
         }
         sh = v.sH;
-        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B'^T[n][j] (w'_j x'_j)[p]; steps past the
-        // chunk's last token would only add zero weights.  Each step's LDS fragments are read one step
-        // ahead of its MFMAs.
-        const int valid = cx.valid(c);
+        // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B'^T[n][j] (w'_j x'_j)[p].  Steps past a
+        // ragged chunk's end add zero weights (w' = 0 there).  The x operands and weights of step k + 2
+        // are read from LDS while step k computes (scheduling barriers keep the reads where they are
+        // issued: the compiler would otherwise sink them next to their use).
         struct Frag {
-            f16x8 x, b[4];
+            f16x8 x0, x1;
             f32x4 w0, w1;
         };
         auto load = [&](Frag& f, int j0) {
-            f.x = tr_frag<kRowX>(Xt, trW, trW, j0);
+            f.x0 = tr_frag<kRowX>(Xt, trW0, trW0, j0);
+            f.x1 = tr_frag<kRowX>(Xt, trW1, trW1, j0);
             f.w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
             f.w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) f.b[t] = ld16(Bt + 32 * t * kRowB + lo.row[j0 >> 4]);
         };
-        auto use = [&](const Frag& f) {
+        auto wx = [](const f16x8& x, const f32x4& w0, const f32x4& w1) {
             float e[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) e[s] = static_cast<float>(f.x[s]) * (s < 4 ? f.w0[s] : f.w1[s - 4]);
-            const f16x8 wx = to_f16x8(e);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) Hs[t] = mfma(f.b[t], wx, Hs[t]);
+            for (int s = 0; s < 8; ++s) e[s] = static_cast<float>(x[s]) * (s < 4 ? w0[s] : w1[s - 4]);
+            return to_f16x8(e);
         };
-        if (valid == Q) {
-            // a full chunk, two steps in flight: step k + 2's fragments are read while step k computes
-            // (scheduling barriers keep each step's reads where they are issued: the compiler would
-            // otherwise sink them next to their MFMAs)
-            Frag f0, f1;
-            load(f0, 0);
-            load(f1, 16);
+        Frag f[3];
+        load(f[0], 0);
+        load(f[1], 16);
 #pragma unroll
-            for (int k = 0; k < 8; k += 2) {
-                __builtin_amdgcn_sched_barrier(0);
-                use(f0);
-                __builtin_amdgcn_sched_barrier(0);
-                if (k + 2 < 8) load(f0, 16 * (k + 2));
-                __builtin_amdgcn_sched_barrier(0);
-                use(f1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (k + 3 < 8) load(f1, 16 * (k + 3));
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (k + 2 < 8) load(f[(k + 2) % 3], 16 * (k + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            const Frag& g = f[k % 3];
+            const f16x8 wx0 = wx(g.x0, g.w0, g.w1), wx1 = wx(g.x1, g.w0, g.w1);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                Hs[2 * tt] = mfma(bq[tt][k], wx0, Hs[2 * tt]);
+                Hs[2 * tt + 1] = mfma(bq[tt][k], wx1, Hs[2 * tt + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
-        } else {
-            for (int k = 0; 16 * k < valid; ++k) {
-                Frag f;
-                load(f, 16 * k);
-                use(f);
-            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) bq[tt][k] = b_load(cnext, tt, k);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (c + 1 < cx.nchunks) {
             write_h(buf ^ 1, sh, v.eHn);
         } else if (a.final_state) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = 32 * t + 8 * q + 4 * hf;
-                    *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
-                        f32x4{ldexp_f(Hs[t][4 * q], sh), ldexp_f(Hs[t][4 * q + 1], sh), ldexp_f(Hs[t][4 * q + 2], sh),
-                              ldexp_f(Hs[t][4 * q + 3], sh)};
-                }
+            store_state(sh);
         }
         __syncthreads();                             // chunk c + 1
     }
-    if (cx.nchunks == 0 && a.final_state) {          // no tokens: the final state is the initial one
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = 32 * t + 8 * q + 4 * hf;
-                *reinterpret_cast<f32x4*>(a.final_state + sbase + hp * NS + n) =
-                    f32x4{Hs[t][4 * q], Hs[t][4 * q + 1], Hs[t][4 * q + 2], Hs[t][4 * q + 3]};
-            }
-    }
+    if (cx.nchunks == 0 && a.final_state) store_state(0);   // no tokens: the final state is the initial one
 }
 
 // ---------------------------------------------------------------------------
-// Loader waves 6 and 7: rows 0..63 / 64..127 of each chunk's x tile.  A chunk's rows are loaded into
-// registers three chunks ahead; two chunks ahead each wave takes the largest |x| of its half and leaves
-// it in LDS; one chunk ahead (after the barrier) both read the chunk's maximum, convert their halves to
-// fp16 into the chunk's x tile, and wave 4 builds the chunk's per-token vectors.  Three register sets
-// rotate (the chunk loop is unrolled by three so that they stay registers).
-struct XHalf {
-    u32x4 v[8];      // instruction k: lane l holds row 64 half + 8k + l/8, 16-byte piece l%8
+// Loader waves 6 and 7: rows 0..31 / 32..127 of each chunk's x tile (wave 6 also builds the vectors,
+// so it converts fewer rows).  A chunk's rows are loaded into registers three chunks ahead; two chunks
+// ahead each wave takes the largest |x| of its rows and leaves it in LDS; one chunk ahead (after the
+// barrier) both read the chunk's maximum, convert their rows to fp16 into the chunk's x tile, and wave 6
+// builds the chunk's per-token vectors.  Three register sets rotate (the chunk loop is unrolled by
+// three so that they stay registers).
+template <int NK>
+struct XPart {
+    u32x4 v[NK];     // instruction k: lane l holds row r0 + 8k + l/8 of the wave's rows, 16-byte piece l%8
 };
 
-__device__ __forceinline__ void x_load(XHalf& xr, const Ctx& cx, int c, int half, int lane) {
+template <int NK>
+__device__ __forceinline__ void x_load(XPart<NK>& xr, const Ctx& cx, int c, int r0, int lane) {
     const int valid = cx.valid(c);
     const bf16* base = cx.xg + cx.row0(c) * cx.xs + static_cast<int64_t>(cx.h) * P + 8 * (lane & 7);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        int r = 64 * half + 8 * k + (lane >> 3);
+    for (int k = 0; k < NK; ++k) {
+        int r = r0 + 8 * k + (lane >> 3);
         r = r < valid ? r : valid - 1;               // past the end: a real row (zero weights)
         xr.v[k] = *reinterpret_cast<const u32x4*>(base + r * cx.xs);
     }
 }
 
 struct DtRegs {
-    bf16 d0, d1;     // tokens 2 lane, 2 lane + 1
+    f32x2 d;         // dt of tokens 2 lane, 2 lane + 1 (after the prologue; 0 past the end)
     int2 sc;         // (eB, eC) of the chunk
 };
 
 __device__ __forceinline__ void dt_load(DtRegs& dr, const Ctx& cx, int c, int lane) {
-    const int valid = cx.valid(c);
-    const int q0 = 2 * lane < valid ? 2 * lane : valid - 1;
-    const int q1 = 2 * lane + 1 < valid ? 2 * lane + 1 : valid - 1;
-    const int64_t r0 = cx.row0(c);
-    dr.d0 = cx.dtg[(r0 + q0) * cx.H + cx.h];
-    dr.d1 = cx.dtg[(r0 + q1) * cx.H + cx.h];
+    dr.d = reinterpret_cast<const f32x2*>(cx.ws.dts + (cx.hrow0 + c) * Q)[lane];
     dr.sc = cx.ws.scales[cx.tile0 + c];
 }
 
@@ -774,11 +829,12 @@ __device__ __forceinline__ float row_lane_f(float v, int k, int lane) {
     return row == 0 ? r0 : (row == 1 ? r1 : (row == 2 ? r2 : r3));
 }
 
-// largest |x| of a half tile, as bf16 bits
-__device__ __forceinline__ unsigned half_max(const XHalf& xr) {
+// largest |x| of a wave's rows, as bf16 bits
+template <int NK>
+__device__ __forceinline__ unsigned half_max(const XPart<NK>& xr) {
     u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < NK; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, xr.v[k][e] & 0x7FFF7FFFu));
     return wave_max_u(max(static_cast<unsigned>(m2[0]), static_cast<unsigned>(m2[1])));
@@ -790,12 +846,13 @@ __device__ __forceinline__ int x_scale(unsigned mb) {
     return (mb == 0 || mb >= 0x7F80u) ? 0 : ((e >= 15 || e < -8) ? e - 14 : 0);
 }
 
-// a half tile -> fp16 x' = x 2^-ex into x tile xt
-__device__ __forceinline__ void x_convert(const XHalf& xr, unsigned char* xt, int half, int ex, int lane) {
+// a wave's rows -> fp16 x' = x 2^-ex into x tile xt
+template <int NK>
+__device__ __forceinline__ void x_convert(const XPart<NK>& xr, unsigned char* xt, int r0, int ex, int lane) {
     const int rp = lane >> 3, pc = lane & 7;
     auto convert = [&](auto scale) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < NK; ++k) {
             u32x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -803,7 +860,7 @@ __device__ __forceinline__ void x_convert(const XHalf& xr, unsigned char* xt, in
                 const float hi = scale(__uint_as_float(xr.v[k][q] & 0xFFFF0000u));
                 o[q] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, f16x2));
             }
-            *reinterpret_cast<u32x4*>(xt + soff<kRowX>(64 * half + 8 * k + rp, pc)) = o;
+            *reinterpret_cast<u32x4*>(xt + soff<kRowX>(r0 + 8 * k + rp, pc)) = o;
         }
     };
     if (ex == 0) convert([](float f) { return f; });
@@ -820,8 +877,7 @@ __device__ __forceinline__ void build_vec(const DtRegs& dr, unsigned mb, Vec& v,
     // per-token vectors (two tokens per lane)
     const int valid = cx.valid(c);
     const int h = cx.h;
-    const float d0 = 2 * lane < valid ? dt_prologue(static_cast<float>(dr.d0), a.dtp, h) : 0.f;
-    const float d1 = 2 * lane + 1 < valid ? dt_prologue(static_cast<float>(dr.d1), a.dtp, h) : 0.f;
+    const float d0 = dr.d[0], d1 = dr.d[1];
     const float a0 = d0 * A2, a1 = d1 * A2;
     const float s = wave_incl_sum(a0 + a1);
     const float c1 = s, c0 = s - a1;                  // inclusive sums at tokens 2 lane + 1 and 2 lane
@@ -886,28 +942,21 @@ __device__ __forceinline__ void build_vec(const DtRegs& dr, unsigned mb, Vec& v,
 // wave 7, which also copies each next chunk's B tile from the pre-pass into LDS).
 template <int HALF>
 __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+    constexpr int NK = HALF ? 12 : 4;                // wave 6: rows 0..31 (it also builds the vectors); 7: 32..127
+    constexpr int R0 = HALF ? 32 : 0;
+    using XHalf = XPart<NK>;
     const float A2 = a.A[cx.h] * kLog2e;
     const float Dh = a.D ? a.D[cx.h] : 0.f;
     const int nc = cx.nchunks;
     XHalf r0, r1, r2;           // register set m % 3 holds chunk m
     DtRegs d0, d1, d2;
-    auto bcopy = [&](int c) {                        // chunk c's B tile into B[c % 2]
-        const unsigned char* src = cx.ws.btile(cx.tile0 + c) + 16 * lane;
-        unsigned char* dst = sm.B[c & 1];
-#pragma unroll
-        for (int k = 0; k < kTile / 1024; ++k)
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 1024 * k),
-                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
-    };
-    if (nc > 0) x_load(r0, cx, 0, HALF, lane);
-    if (nc > 1) x_load(r1, cx, 1, HALF, lane);
-    if (nc > 2) x_load(r2, cx, 2, HALF, lane);
+    if (nc > 0) x_load(r0, cx, 0, R0, lane);
+    if (nc > 1) x_load(r1, cx, 1, R0, lane);
+    if (nc > 2) x_load(r2, cx, 2, R0, lane);
     if constexpr (HALF == 0) {
         if (nc > 0) dt_load(d0, cx, 0, lane);
         if (nc > 1) dt_load(d1, cx, 1, lane);
         if (nc > 2) dt_load(d2, cx, 2, lane);
-    } else {
-        if (nc > 0) bcopy(0);
     }
     if (nc > 0) {
         const unsigned m = half_max(r0);
@@ -919,13 +968,12 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     int sHp = 0;
     if (nc > 0) {
         const unsigned mb = max(sm.xmax[0][0], sm.xmax[0][1]);
-        x_convert(r0, sm.X[0], HALF, x_scale(mb), lane);
+        x_convert(r0, sm.X[0], R0, x_scale(mb), lane);
         if constexpr (HALF == 0) build_vec(d0, mb, sm.vec[0], cx, a, 0, lane, A2, Dh, bound, eH, sHp);
         if (nc > 1) {
             const unsigned m = half_max(r1);
             if (lane == 0) sm.xmax[1][HALF] = m;
         }
-        if constexpr (HALF == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the B copy
     }
     __syncthreads();                                 // chunk 0
     // chunk c: convert chunk c + 1 (rc, dt in dc), take the maximum of chunk c + 2 (rm), load chunk c + 3
@@ -933,23 +981,16 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     auto phase = [&](int c, XHalf& rc, DtRegs& dc, XHalf& rm, XHalf& rl, DtRegs& dl) {
         if (c + 1 < nc) {
             const unsigned mb = max(sm.xmax[(c + 1) & 1][0], sm.xmax[(c + 1) & 1][1]);
-            x_convert(rc, sm.X[(c + 1) & 1], HALF, x_scale(mb), lane);
+            x_convert(rc, sm.X[(c + 1) & 1], R0, x_scale(mb), lane);
             if constexpr (HALF == 0) build_vec(dc, mb, sm.vec[(c + 1) & 1], cx, a, c + 1, lane, A2, Dh, bound, eH, sHp);
         }
         if (c + 2 < nc) {
             const unsigned m = half_max(rm);
             if (lane == 0) sm.xmax[c & 1][HALF] = m;
         }
-        if constexpr (HALF == 1) {
-            if (c + 1 < nc) bcopy(c + 1);
-        }
-        if (c + 3 < nc) x_load(rl, cx, c + 3, HALF, lane);
+        if (c + 3 < nc) x_load(rl, cx, c + 3, R0, lane);
         if constexpr (HALF == 0) {
             if (c + 3 < nc) dt_load(dl, cx, c + 3, lane);
-        } else {
-            // the B copy has landed: vmcnt(8) counts the x loads issued after it
-            if (c + 3 < nc) __builtin_amdgcn_s_waitcnt(0x0F78);
-            else __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         __syncthreads();                             // chunk c + 1
     };
@@ -984,6 +1025,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
     cx.grp = cx.h / (a.nheads / a.ngroups);
     cx.nchunks = static_cast<int>((a.seqlen + Q - 1) / Q);
     cx.tile0 = (cx.b * a.ngroups + cx.grp) * static_cast<int64_t>(cx.nchunks);
+    cx.hrow0 = (cx.b * a.nheads + cx.h) * static_cast<int64_t>(cx.nchunks);
     cx.ws = ws;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1002,12 +1044,14 @@ static hipError_t launch_t(const ScanArgs& a, void* workspace, hipStream_t s) {
     if (a.batch * a.nheads == 0) return hipSuccess;
     const int64_t nc = (a.seqlen + Q - 1) / Q;
     const int64_t ntile = a.batch * a.ngroups * nc;
-    WsView ws{static_cast<unsigned char*>(workspace),
-              reinterpret_cast<int2*>(static_cast<unsigned char*>(workspace) + ntile * kWsTile), ntile};
+    const int64_t nhc = a.batch * a.nheads * nc;
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    WsView ws{w, reinterpret_cast<float*>(w + ntile * kWsTile),
+              reinterpret_cast<int2*>(w + ntile * kWsTile + nhc * Q * static_cast<int64_t>(sizeof(float))), ntile};
     if (ntile > 0) {
         hipLaunchKernelGGL(bc_prep_kernel, dim3(static_cast<uint32_t>(ntile)), dim3(256), 0, s,
-                           static_cast<const bf16*>(a.B), static_cast<const bf16*>(a.C), a.bc_row_stride, a.seqlen,
-                           a.ngroups, nc, ws);
+                           static_cast<const bf16*>(a.B), static_cast<const bf16*>(a.C), a.bc_row_stride,
+                           static_cast<const bf16*>(a.dt), a.dtp, a.seqlen, a.nheads, a.ngroups, nc, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1026,9 +1070,9 @@ bool f16_scan_supports(int head_dim, int d_state, int chunk) {
     return head_dim == scan16::P && d_state == scan16::NS && chunk == scan16::Q;
 }
 
-size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int ngroups) {
+size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int ngroups) {
     const int64_t nc = (seqlen + scan16::Q - 1) / scan16::Q;
-    return static_cast<size_t>(scan16::ws_bytes(batch * ngroups * nc));
+    return static_cast<size_t>(scan16::ws_bytes(batch * ngroups * nc, batch * nheads * nc));
 }
 
 hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s) {

@@ -149,8 +149,8 @@ static bool f16_scan_applies(const ssd_dims_t* d, int32_t chunk) {
 }
 
 size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
-    if (!f16_scan_applies(d, chunk) || d->batch <= 0 || d->seqlen <= 0 || d->ngroups <= 0) return 0;
-    return ssd::f16_scan_workspace_bytes(d->batch, d->seqlen, d->ngroups);
+    if (!f16_scan_applies(d, chunk) || d->batch <= 0 || d->seqlen <= 0 || d->ngroups <= 0 || d->nheads <= 0) return 0;
+    return ssd::f16_scan_workspace_bytes(d->batch, d->seqlen, d->nheads, d->ngroups);
 }
 
 // the batched scan, with optional state snapshots (internal linkage)

@@ -317,7 +317,7 @@ def ssd_chunk_scan_noalloc(x, B, C, dt, A, D, init_state, final_state, y, chunk=
                            dt_softplus=False, dt_limit=None):
     """ssd_chunk_scan that allocates nothing (for graph capture and serving loops): the caller passes y
     [B, L, H, P] (bf16 or fp32) and the states; the fp16 scan's workspace is the library's static
-    per-device array (up to batch x groups x ceil(L / 128) = 630 tiles, else SSD_ERR_WORKSPACE).
+    per-device array (workspaces up to 64 MiB, else SSD_ERR_WORKSPACE).
     Calls that overlap on one device race on that array.  Returns y."""
     if y is None:
         raise ValueError("ssd_chunk_scan_noalloc needs y from the caller")

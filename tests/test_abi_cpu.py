@@ -102,11 +102,11 @@ def test_scan_validation(ssd, lib):
 
 def test_workspace_size(ssd, lib):
     """The fp16 scan's workspace: per (batch, group, 128-token chunk) the fp16 B and C tiles (2 x 32 KiB),
-    the ten causal 32 x 32 fp32 tiles of C.B^T (40 KiB) and two int32 scale exponents; no workspace for
-    other sizes, dtypes or chunks."""
+    the ten causal 32 x 32 fp16 tiles of C.B^T (20 KiB) and two int32 scale exponents, and per (batch, head,
+    chunk) the 128 fp32 dt values; no workspace for other sizes, dtypes or chunks."""
     ws = lib.ssd_chunk_scan_workspace_size
-    assert ws(ctypes.byref(dims(ssd)), 128) == 2 * 2 * 3 * (65536 + 40960 + 8)          # B 2, G 2, ceil(300/128) = 3
-    assert ws(ctypes.byref(dims(ssd, seqlen=8192, batch=1, ngroups=8, nheads=256)), 128) == 8 * 64 * 106504
+    assert ws(ctypes.byref(dims(ssd)), 128) == 2 * 2 * 3 * (65536 + 20480 + 8) + 2 * 4 * 3 * 512          # B 2, G 2, ceil(300/128) = 3
+    assert ws(ctypes.byref(dims(ssd, seqlen=8192, batch=1, ngroups=8, nheads=256)), 128) == 8 * 64 * 86024 + 256 * 64 * 512
     assert ws(ctypes.byref(dims(ssd)), 64) == 0
     assert ws(ctypes.byref(dims(ssd, act_dtype=0)), 128) == 0
     assert ws(ctypes.byref(dims(ssd, head_dim=32)), 128) == 0

@@ -3,7 +3,7 @@
 It runs the same kernels as ssd_chunk_scan with a caller workspace, on the library's static
 per-device array instead, so its results must equal that entry point's bit for bit -- on two calls
 in a row, the second smaller (the array keeps the first call's contents, which the second must not
-read).  Sizes past the array's 630 tiles are refused before anything runs.
+read).  Sizes whose workspace exceeds the 64 MiB array are refused before anything runs.
 """
 import pytest
 import torch
@@ -47,7 +47,7 @@ def test_noalloc_equals_workspace_scan_two_calls(ydt):
 
 
 def test_noalloc_at_the_prefill_size_then_other_kernels():
-    """The 8192-token, 8-group layer (512 tiles) fits; sizes with no workspace run the other scans."""
+    """The 8192-token, 8-group layer fits; sizes with no workspace run the other scans."""
     s = cuda(scan_inputs(LayerDims(1, 8192, 16, 64, 8, 128), 803))
     (yr, fr), (y, f) = both(s, torch.bfloat16)
     assert torch.equal(y, yr) and torch.equal(f, fr)
@@ -57,7 +57,7 @@ def test_noalloc_at_the_prefill_size_then_other_kernels():
 
 
 def test_noalloc_refuses_sizes_past_the_static_array():
-    s = cuda(scan_inputs(LayerDims(1, 128 * 80, 8, 64, 8, 128), 805))  # 8 groups x 80 chunks = 640 tiles
+    s = cuda(scan_inputs(LayerDims(1, 128 * 100, 8, 64, 8, 128), 805))  # 800 tiles of 84 KiB: 69 MB
     fin = torch.empty_like(s["init_state"])
     y = torch.full(s["x"].shape, 3.0, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(RuntimeError, match="SSD_ERR_WORKSPACE"):
