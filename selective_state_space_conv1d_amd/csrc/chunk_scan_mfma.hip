@@ -43,7 +43,9 @@
 // state are in LDS).  The state is single-buffered in LDS: each y wave bumps an
 // LDS counter once it has read it, and the state waves wait for all four before
 // writing the new one (a bounded wait; the y waves never wait on the state waves
-// inside a chunk, so the counter always fills).
+// inside a chunk, so the counter always fills).  Should the wait ever run out, the
+// state waves poison their state with NaN before writing it, so that y from then on
+// and the final state are NaN instead of silently wrong.
 //
 // Precision.  x, B and C arrive in bf16 and are exact operands.  Operands
 // computed in fp32 (M, H and the decay-weighted x) are split into bf16 hi + lo
@@ -62,6 +64,7 @@
 #include "ssd_kernels.h"
 
 #include <atomic>
+#include <cstdlib>
 
 namespace ssd {
 namespace scan32 {
@@ -555,7 +558,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
 // ---------------------------------------------------------------------------
 // state wave: NT tiles of H^T, n tiles SN0 .. SN0+NT-1 of p tile SP.  Tile t holds
 // Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].
-constexpr int kSpinMax = 1 << 20;
+constexpr int kSpinMax = 1 << 20;   // iterations of the bounded wait (each ~64 cycles of sleep)
 
 template <int NT, int SP, int SN0, class CX>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane) {
@@ -698,9 +701,19 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
         }
         // the y waves must have read the previous state before it is overwritten
         const int target = 4 * static_cast<int>(gc + 1);
-        for (int n = 0; n < kSpinMax; ++n) {
-            if (__hip_atomic_load(&sm.hread, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        bool seen = false;
+        for (int n = 0; n < a.spin_max; ++n) {
+            if (__hip_atomic_load(&sm.hread, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+                seen = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
+        }
+        if (!seen) {                                // the wait ran out: make it visible in every later output
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Hs[t][e] = __builtin_nanf("");
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the state writes stay after the wait
         write_h();
@@ -866,6 +879,12 @@ static hipError_t mfma_t(const ScanArgs& args, hipStream_t s) {
     const int64_t rows = a.seq.cu_seqlens ? a.seqlen : a.batch * a.seqlen;   // all sequences' rows
     const bool walk = a.batch > want && rows <= kWalkChunks * scan32::Q * a.batch;
     a.nranges = walk ? want : a.batch;
+    // SSD_SCAN_SPIN_MAX (a test hook) shortens the bounded wait, e.g. to 0 to check that running out is seen
+    static const int spin_env = [] {
+        const char* v = std::getenv("SSD_SCAN_SPIN_MAX");
+        return v ? std::atoi(v) : -1;
+    }();
+    a.spin_max = spin_env >= 0 ? spin_env : scan32::kSpinMax;
     const int64_t blocks = a.nranges * a.nheads;
     auto kern = a.nranges < a.batch ? scan32::chunk_scan_kernel<TY, true> : scan32::chunk_scan_kernel<TY, false>;
     const size_t smem = sizeof(scan32::Smem);

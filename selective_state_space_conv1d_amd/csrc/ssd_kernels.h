@@ -63,6 +63,7 @@ struct ScanArgs {
     const int32_t* snap_table;   // packed sequences: [S, snap_max] pool slot per (sequence, interval), or NULL
     int64_t snap_max, snap_slots;
     int64_t nranges;         // set by the launcher: sequence ranges per head (workgroups = nranges * nheads)
+    int spin_max;            // set by the launcher: iterations of the split scan's bounded LDS-counter wait
 };
 
 struct UpdateArgs {

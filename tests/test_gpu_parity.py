@@ -416,3 +416,30 @@ def test_ultra_geometry_mini_smoke(orc):
     # the scan consumed the GPU's bf16 conv output; the oracle its own bf16-rounded conv output
     assert_close(y, yr, BF16_BAR, "y")
     assert_close(st, fr, BF16_BAR, "state")
+
+
+def test_split_scan_bounded_wait_running_out_is_visible():
+    """The split kernel's state waves wait (boundedly) for the y waves to have read the carried state
+    before overwriting it.  Forced to run out at once (SSD_SCAN_SPIN_MAX=0, read when the library
+    launches its first split scan, so in a child process), they poison the state: every y after the
+    first chunk and the final state are NaN, where a silent race could otherwise pass unnoticed.  The
+    kernel still ends normally."""
+    import os
+    import subprocess
+    import sys
+    code = r'''
+import torch
+from selective_state_space_conv1d_amd import ssd
+from selective_state_space_conv1d_amd.synth import LayerDims, scan_inputs
+s = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(LayerDims(1, 300, 4, 64, 2, 128), 78).items()}
+fin = torch.empty_like(s["init_state"])
+y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], s["init_state"], fin, y_dtype=torch.float32,
+                       workspace=False)
+torch.cuda.synchronize()
+print(int(torch.isfinite(y[:, :128]).all()), int(torch.isnan(y[:, 128:]).all()), int(torch.isnan(fin).all()))
+'''
+    env = dict(os.environ, SSD_SCAN_SPIN_MAX="0")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split()[-3:] == ["1", "1", "1"], r.stdout
