@@ -91,6 +91,16 @@ def conv_bytes(d, L):
     return d.batch * L * d.conv_dim * 2 * 2 + d.conv_dim * 5 * 2 + d.batch * d.conv_dim * 4 * 2
 
 
+def fused_bytes(d, init=False):
+    """Algorithmic HBM bytes of the fused conv + scan (ssd_conv_chunk_scan): read xBC, the taps and bias and
+    dt once, write y, the final fp32 state and the conv state (read the initial states when given)."""
+    per_token = d.conv_dim * 2 + d.nheads * 2 + d.nheads * d.head_dim * 2
+    state = d.batch * d.nheads * d.head_dim * d.d_state * 4
+    cstate = d.batch * d.conv_dim * 4 * 2
+    return (d.batch * d.seqlen * per_token + d.conv_dim * 5 * 2 + state * (2 if init else 1)
+            + cstate * (2 if init else 1))
+
+
 def update_bytes(d):
     """State read + write (fp32) + x, B, C, dt in and y out (bf16) for one token."""
     st = d.batch * d.nheads * d.head_dim * d.d_state * 4 * 2
@@ -409,6 +419,38 @@ def continuation_leg(ssd, torch, dev, steps, warmup):
             "conv_algorithmic_bytes": cb, "conv_GBps": cb / conv_s / 1e9, "conv_frac": cb / conv_s / 1e9 / HBM_PEAK_GBS}
 
 
+def fused_leg(ssd, torch, dev, steps, warmup, name):
+    """The prefill conv fused into the scan (ssd_conv_chunk_scan: xBC in, y and the states out, no conv
+    output in HBM) against the two launches (ssd_conv1d_fwd, then ssd_chunk_scan on its output), on the
+    same inputs and the same fp16 scan -- their results are equal bit for bit."""
+    from selective_state_space_conv1d_amd.synth import WORKLOADS, mixer_inputs
+    d = WORKLOADS[name]
+    init = name != "prefill_ultra_8k"
+    inp = mixer_inputs(d, 1005, device=dev, conv_state=init, init_state=init)
+    cs_in, st_in = inp.get("conv_state"), inp.get("init_state")
+    v = torch.empty(d.batch, d.seqlen, d.conv_dim, dtype=d.dtype, device=dev)
+    x, Bm, Cm = ssd.split_xbc(v, d.nheads, d.head_dim, d.ngroups, d.d_state)
+    cs = torch.empty(d.batch, d.conv_dim, 4, dtype=d.dtype, device=dev)
+    st = torch.empty(d.batch, d.nheads, d.head_dim, d.d_state, device=dev)
+    y = torch.empty(d.batch, d.seqlen, d.nheads, d.head_dim, dtype=d.dtype, device=dev)
+    ws = scan_workspace(ssd, torch, d, dev)
+    conv_s, scan_s, fused_s = timed_launches(torch, [
+        lambda: ssd.ssd_conv1d_fwd(inp["xbc"], inp["w"], inp["bias"], cs_in, cs, out=v),
+        lambda: ssd.ssd_chunk_scan(x, Bm, Cm, inp["dt"], inp["A"], inp["D"], st_in, st, y=y, chunk=d.chunk,
+                                   workspace=ws),
+        lambda: ssd.ssd_conv_chunk_scan(inp["xbc"], inp["w"], inp["bias"], inp["dt"], inp["A"], inp["D"], d.nheads,
+                                        d.head_dim, d.ngroups, d.d_state, conv_state_in=cs_in, conv_state_out=cs,
+                                        init_state=st_in, final_state=st, y=y, chunk=d.chunk, workspace=ws),
+    ], steps, warmup)
+    T = d.batch * d.seqlen
+    fb = fused_bytes(d, init)
+    return {"workload": name, "batch": d.batch, "seqlen": d.seqlen, "nheads": d.nheads,
+            "two_launch_us": (conv_s + scan_s) * 1e6, "two_launch_tokens_per_s": T / (conv_s + scan_s),
+            "fused_us": fused_s * 1e6, "fused_tokens_per_s": T / fused_s, "speedup": (conv_s + scan_s) / fused_s,
+            "fused_algorithmic_bytes": fb, "fused_GBps": fb / fused_s / 1e9,
+            "fused_frac": fb / fused_s / 1e9 / HBM_PEAK_GBS}
+
+
 def long_leg(ssd, torch, dev, steps, warmup, decode_steps=64):
     """Long context on the Ultra layer: a 262144-token prefill (conv + scan) timed on its own, then
     decode_steps single-token decode steps (conv update + state update, batch 1) from the prefill's
@@ -695,6 +737,12 @@ def main():
     out["lowprec_decode"] = lowprec_leg(ssd, torch, dev, max(5, args.steps), max(2, args.warmup))
     print("[bench] chunked-prefill continuation (8 x 4096, 128 heads)", file=sys.stderr, flush=True)
     out["continuation"] = continuation_leg(ssd, torch, dev, max(5, args.steps // 2), max(2, args.warmup // 2))
+    print("[bench] conv fused into the scan (1 x 8192 layer; 8 x 4096 continuation)", file=sys.stderr, flush=True)
+    out["prefill_fused"] = fused_leg(ssd, torch, dev, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                     "prefill_ultra_8k")
+    out["continuation_fused"] = fused_leg(ssd, torch, dev, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                          "continuation_h128_b8")
+    torch.cuda.empty_cache()
     torch.cuda.empty_cache()
     print("[bench] long context (262144-token prefill + 64 decode steps)", file=sys.stderr, flush=True)
     out["long_context"], long_keep = long_leg(ssd, torch, dev, max(3, args.steps // 8), max(1, args.warmup // 10))

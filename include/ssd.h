@@ -181,6 +181,29 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The prefill conv fused into the chunked scan ([P3] 5.4, item 2: the conv folded into the
+ * scan's launches; [P2] "Prefill 阶段" for what each step computes): the result of
+ * ssd_conv1d_fwd(xbc, conv_w, conv_bias, conv_state_in, conv_state_out) followed by
+ * ssd_chunk_scan over the x, B and C views of its output with a workspace -- y, final_state and
+ * conv_state_out equal that pair's bit for bit -- without writing or re-reading the conv output:
+ * x, B and C are convolved from xbc inside the scan.  bf16 activations with head_dim 64,
+ * d_state 128 and chunk 128 only (else SSD_ERR_UNSUPPORTED); workspace as for ssd_chunk_scan
+ * (ssd_chunk_scan_workspace_size() bytes, required when L > 0).  The rest of the arguments are
+ * those of the two calls (conv_state_out may alias conv_state_in, final_state init_state).
+ * One difference in rounding: x's power-of-two scale per chunk comes from a bound on the conv's
+ * result (|bias| + sum |w| max|input|) rather than from its maximum; both choose 1 while the
+ * values lie in [2^-8, 2^15), which is where the bit-for-bit equality holds.
+ */
+ssd_status_t ssd_conv_chunk_scan(const ssd_dims_t* d, int32_t chunk,
+                                 const void* xbc, int64_t xbc_row_stride,
+                                 const void* conv_w, const void* conv_bias,
+                                 const void* conv_state_in, void* conv_state_out,
+                                 const void* dt, const float* A, const float* D,
+                                 const ssd_dt_params_t* dt_params,
+                                 const float* init_state, float* final_state, void* y,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * ssd_chunk_scan for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
  * hipFree or allocating library call): where ssd_chunk_scan would take a workspace (bf16 inputs,

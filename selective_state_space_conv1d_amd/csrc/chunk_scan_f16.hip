@@ -113,6 +113,12 @@ struct Smem {
     Vec vec[2];
     float hmax[2];                       // |initial state| maxima of the two state waves
     unsigned xmax[2][2];                 // largest |x| (bf16 bits) of each half of a chunk, by chunk parity
+    // fused conv only (the unfused kernel allocates up to Xr): a chunk's raw xBC x rows (3 rows before it,
+    // then its 128 rows; bf16, swizzled like X), double-buffered; the head's taps cw[k][ch] (k = 4: bias)
+    // and the bounds |bias| <= cbound[0], sum_k |w_k| <= cbound[1] over its channels
+    unsigned char Xr[2][(Q + 3) * kRowX];
+    float cw[5][P];
+    float cbound[2];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
@@ -222,13 +228,115 @@ __host__ __device__ inline int64_t ws_bytes(int64_t ntile, int64_t nhc) {
 }
 
 // ---------------------------------------------------------------------------
+// The fused conv (ssd_conv_chunk_scan): the scan reads the conv's input xBC instead of its output and
+// computes the causal depthwise conv (width 4) + SiLU itself, in the order and rounding of the conv
+// kernel -- bias, then taps 0..3 by fused multiply-adds in fp32, SiLU, nearest-even bf16 -- so that its
+// results equal conv-then-scan bit for bit.
+struct ConvIn {
+    const bf16* w;       // [CD, 4] taps (tap 3 multiplies the current token)
+    const bf16* bias;    // [CD], or null
+    const bf16* s_in;    // [B, CD, 4] conv state: inputs at tokens -4..-1, or null (zeros)
+    bf16* s_out;         // [B, CD, 4] new conv state (inputs at tokens L-4..L-1), or null
+    const bf16* xbc;     // [B, L, CD] the conv input, row stride xs
+    int64_t xs, cd, hp;  // hp = H P: the first B channel
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float conv_silu_bf16(float bias, const float* w, float u0, float u1, float u2, float u3) {
+    float acc = bias;
+    acc = fmaf(w[0], u0, acc);
+    acc = fmaf(w[1], u1, acc);
+    acc = fmaf(w[2], u2, acc);
+    acc = fmaf(w[3], u3, acc);
+    return static_cast<float>(static_cast<bf16>(silu_f(acc)));
+}
+
+// Pre-pass conv: rows rb .. rb + 7 of the chunk starting at token tok0 of batch entry b, channels ch .. ch + 7;
+// inputs before token 0 come from the conv state; rows at or past `valid` are zeros.
+__device__ __forceinline__ void conv8_rows(u32x4 (&o)[8], const ConvIn& cv, int64_t b, int64_t seqlen, int64_t tok0,
+                                           int rb, int valid, int64_t ch) {
+    float w[8][4], bs[8];
+    {
+        const u32x4* wp = reinterpret_cast<const u32x4*>(cv.w + ch * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 v = wp[q];                   // channels ch + 2q, ch + 2q + 1
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                w[2 * q + e][0] = bf16_lo(v[2 * e]);
+                w[2 * q + e][1] = bf16_hi(v[2 * e]);
+                w[2 * q + e][2] = bf16_lo(v[2 * e + 1]);
+                w[2 * q + e][3] = bf16_hi(v[2 * e + 1]);
+            }
+        }
+        u32x4 bv = {0, 0, 0, 0};
+        if (cv.bias) bv = *reinterpret_cast<const u32x4*>(cv.bias + ch);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bs[2 * q] = bf16_lo(bv[q]);
+            bs[2 * q + 1] = bf16_hi(bv[q]);
+        }
+    }
+    float u[11][8];                                  // inputs at rows rb - 3 .. rb + 7
+#pragma unroll
+    for (int j = 0; j < 11; ++j) {
+        const int row = rb - 3 + j;
+        const int64_t tok = tok0 + row;
+        u32x4 v = {0, 0, 0, 0};
+        if (row < valid && tok >= 0) {
+            v = *reinterpret_cast<const u32x4*>(cv.xbc + (b * seqlen + tok) * cv.xs + ch);
+        } else if (row < valid && cv.s_in) {         // tokens -3 .. -1: the conv state
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const unsigned short lo = reinterpret_cast<const unsigned short*>(cv.s_in)[(b * cv.cd + ch + 2 * q) * 4 + 4 + tok];
+                const unsigned short hi = reinterpret_cast<const unsigned short*>(cv.s_in)[(b * cv.cd + ch + 2 * q + 1) * 4 + 4 + tok];
+                v[q] = static_cast<unsigned>(lo) | (static_cast<unsigned>(hi) << 16);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u[j][2 * q] = bf16_lo(v[q]);
+            u[j][2 * q + 1] = bf16_hi(v[q]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        bf16x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            r[e] = static_cast<bf16>(rb + j < valid ? conv_silu_bf16(bs[e], w[e], u[j][e], u[j + 1][e], u[j + 2][e], u[j + 3][e])
+                                                  : 0.f);
+        o[j] = __builtin_bit_cast(u32x4, r);
+    }
+}
+
+// The new conv state of channel ch: the inputs at tokens L-4 .. L-1 (from the old state where negative)
+__device__ __forceinline__ void conv_state_out(const ConvIn& cv, int64_t b, int64_t seqlen, int64_t ch) {
+    unsigned short v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t tau = seqlen - 4 + k;
+        if (tau >= 0)
+            v[k] = reinterpret_cast<const unsigned short*>(cv.xbc)[(b * seqlen + tau) * cv.xs + ch];
+        else
+            v[k] = cv.s_in ? reinterpret_cast<const unsigned short*>(cv.s_in)[(b * cv.cd + ch) * 4 + 4 + tau] : 0;
+    }
+    *reinterpret_cast<uint2*>(cv.s_out + (b * cv.cd + ch) * 4) =
+        uint2{v[0] | (static_cast<unsigned>(v[1]) << 16), v[2] | (static_cast<unsigned>(v[3]) << 16)};
+}
+
+// ---------------------------------------------------------------------------
 // Pre-pass: one workgroup of 256 threads per (batch, group, chunk).  Thread t holds 16-byte pieces
 // t + 256k (k < 8) of the B tile and of the C tile (piece i: row i / 16, chunk i % 16); rows past the
 // sequence end are zeros.  The scaled fp16 tiles are staged in LDS, from which the four waves write B'^T
 // (transpose reads) and compute the causal C'.B'^T tiles (wave w: tiles w, w + 4, w + 8).
+// Fused conv: thread t computes channel piece t % 16 of B and of C over rows 8 (t / 16) .. + 7 from
+// xBC instead (same pieces, another row order), and the chunk-0 workgroup writes the group's new conv state.
+template <bool CONV>
 __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16* Cg, int64_t bcs, const bf16* dtg,
                                                       DtParams dtp, int64_t seqlen, int nheads, int ngroups,
-                                                      int64_t nchunks, WsView ws) {
+                                                      int64_t nchunks, WsView ws, ConvIn cv) {
     __shared__ __align__(16) unsigned char lb[kTile];
     __shared__ __align__(16) unsigned char lc[kTile];
     __shared__ unsigned wmax[2][4];
@@ -241,16 +349,26 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
     const int64_t row0 = b * seqlen + c * Q;
     const int valid = static_cast<int>(seqlen - c * Q < Q ? seqlen - c * Q : Q);
     u32x4 vb[8], vc[8];
+    // piece k of this thread: row, 16-byte chunk
+    auto piece_r = [&](int k) { return CONV ? 8 * (t >> 4) + k : (t + 256 * k) >> 4; };
+    auto piece_c = [&](int k) { return CONV ? (t & 15) : ((t + 256 * k) & 15); };
+    if constexpr (CONV) {
+        const int64_t gn = static_cast<int64_t>(g) * NS + 8 * (t & 15);
+        conv8_rows(vb, cv, b, seqlen, c * Q, 8 * (t >> 4), valid, cv.hp + gn);
+        conv8_rows(vc, cv, b, seqlen, c * Q, 8 * (t >> 4), valid, cv.hp + static_cast<int64_t>(ngroups) * NS + gn);
+    }
     u16x2 mb2 = {0, 0}, mc2 = {0, 0};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int i = t + 256 * k, r = i >> 4, cc = i & 15;
-        vb[k] = u32x4{0, 0, 0, 0};
-        vc[k] = u32x4{0, 0, 0, 0};
-        if (r < valid) {
-            const int64_t off = (row0 + r) * bcs + static_cast<int64_t>(g) * NS + 8 * cc;
-            vb[k] = *reinterpret_cast<const u32x4*>(Bg + off);
-            vc[k] = *reinterpret_cast<const u32x4*>(Cg + off);
+        if constexpr (!CONV) {
+            const int r = piece_r(k), cc = piece_c(k);
+            vb[k] = u32x4{0, 0, 0, 0};
+            vc[k] = u32x4{0, 0, 0, 0};
+            if (r < valid) {
+                const int64_t off = (row0 + r) * bcs + static_cast<int64_t>(g) * NS + 8 * cc;
+                vb[k] = *reinterpret_cast<const u32x4*>(Bg + off);
+                vc[k] = *reinterpret_cast<const u32x4*>(Cg + off);
+            }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -293,7 +411,7 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
     };
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int i = t + 256 * k, r = i >> 4, cc = i & 15;
+        const int r = piece_r(k), cc = piece_c(k);
         *reinterpret_cast<u32x4*>(lb + soff<kRowB>(r, cc)) = conv(vb[k], eB);
         const u32x4 cv = conv(vc[k], eC);
         *reinterpret_cast<u32x4*>(lc + soff<kRowB>(r, cc)) = cv;
@@ -342,6 +460,15 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
         for (int k = 0; k < 4; ++k) dst[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
     }
     if (t == 0) ws.scales[tix] = int2{eB, eC};
+    if constexpr (CONV) {
+        // the group's new conv state, written by the workgroup that read the old one (the state may be
+        // updated in place): 128 B channels, then 128 C channels
+        if (c == 0 && cv.s_out) {
+            __syncthreads();
+            const int64_t gch = static_cast<int64_t>(g) * NS + (t & 127);
+            conv_state_out(cv, b, seqlen, cv.hp + (t < 128 ? 0 : static_cast<int64_t>(ngroups) * NS) + gch);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -352,6 +479,7 @@ struct Ctx {
     int64_t tile0;      // workspace tile index of this (batch, group)'s chunk 0
     int64_t hrow0;      // workspace dt row of this (batch, head)'s chunk 0
     WsView ws;
+    ConvIn cv;          // fused conv only
     __device__ __forceinline__ int valid(int c) const {
         const int64_t r = seqlen - static_cast<int64_t>(c) * Q;
         return r < Q ? static_cast<int>(r) : Q;
@@ -360,8 +488,77 @@ struct Ctx {
 };
 
 // ---------------------------------------------------------------------------
+// Fused conv: the scale of chunk x tile from its raw inputs' largest magnitude (bf16 bits, over the chunk's
+// rows and the 3 before them) -- the conv's result is bounded by |bias| + sum_k |w_k| max|u| (fp32 rounding
+// and the bf16 rounding of SiLU's result add under 2^-7), and |silu(z)| <= |z| -- with the rule of the
+// unfused path applied to that bound.  Returns ex; maxx receives the bound.
+__device__ __forceinline__ int conv_scale(const Smem& sm, int slot, float& maxx) {
+    const unsigned m = max(sm.xmax[slot][0], sm.xmax[slot][1]);
+    const float mu = __uint_as_float(m << 16);
+    maxx = (sm.cbound[0] + sm.cbound[1] * mu) * (1.f + 0x1p-7f);
+    const int e = ilog2f(maxx);
+    return (maxx == 0.f || !(maxx < 3.0e38f)) ? 0 : ((e >= 15 || e < -8) ? e - 14 : 0);
+}
+
+// Fused conv: slice w turns rows 16w .. 16w+15 of chunk c1's raw tile into its fp16 x tile
+// (x' = bf16(silu(conv)) 2^-ex); lane l takes channels 8 (l % 8) .. + 7 of rows 16w + 2 (l / 8) + {0, 1}.
+// The slices each wave takes (-1: none): y waves 0..3, state waves 4, 5 (no registers to spare), loaders
+// 6, 7 (they convert nothing in this mode).  The lighter waves take more: timed at 1 x 8192, 256 heads,
+// this split runs the fused call in 323 us; one slice per y wave and two per loader, 344 us.
+#ifndef SSD_CONV_SLICES
+#define SSD_CONV_SLICES {{0, 1, -1}, {2, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}, {3, 4, -1}, {5, 6, 7}}
+#endif
+constexpr int kConvSlices[8][3] = SSD_CONV_SLICES;
+__device__ __forceinline__ void conv_slice(Smem& sm, int wave, int lane, int c1);
+template <int W>
+__device__ __forceinline__ void conv_slices(Smem& sm, int lane, int c1) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (kConvSlices[W][k] >= 0) conv_slice(sm, kConvSlices[W][k], lane, c1);
+}
+__device__ __forceinline__ void conv_slice(Smem& sm, int wave, int lane, int c1) {
+    float maxx;
+    const int ex = conv_scale(sm, c1 & 1, maxx);
+    const unsigned char* xr = sm.Xr[c1 & 1];
+    unsigned char* xt = sm.X[c1 & 1];
+    const int pc = lane & 7, r0 = 16 * wave + 2 * (lane >> 3);
+    u32x4 raw[5];                                    // inputs at rows r0 - 3 .. r0 + 1
+#pragma unroll
+    for (int j = 0; j < 5; ++j) raw[j] = *reinterpret_cast<const u32x4*>(xr + soff<kRowX>(r0 + j, pc));
+    float acc[2][8];
+    {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sm.cw[4][8 * pc]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sm.cw[4][8 * pc + 4]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[0][e] = acc[1][e] = e < 4 ? b0[e] : b1[e - 4];
+    }
+    auto u = [&](int j, int e) { return (e & 1) ? bf16_hi(raw[j][e >> 1]) : bf16_lo(raw[j][e >> 1]); };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.cw[k][8 * pc]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.cw[k][8 * pc + 4]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = e < 4 ? w0[e] : w1[e - 4];
+            acc[0][e] = fmaf(w, u(k, e), acc[0][e]);
+            acc[1][e] = fmaf(w, u(k + 1, e), acc[1][e]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = static_cast<float>(static_cast<bf16>(silu_f(acc[j][e])));
+            v[e] = ex == 0 ? o : ldexp_f(o, -ex);
+        }
+        *reinterpret_cast<f16x8*>(xt + soff<kRowX>(r0 + j, pc)) = to_f16x8(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // y wave: token tile IT, both p tiles.
-template <typename TY, int IT>
+template <typename TY, int IT, bool CONV>
 __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int i = 32 * IT + c32;                     // this lane's token within the chunk
@@ -431,6 +628,9 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         for (int jt = 0; jt <= IT; ++jt) cb[jt] = cb_load(0, jt);
     }
     __syncthreads();                                 // prologue 1
+    if constexpr (CONV) {
+        if (cx.nchunks > 0) conv_slices<IT>(sm, lane, 0);
+    }
     __syncthreads();                                 // chunk 0
 
     for (int c = 0; c < cx.nchunks; ++c) {
@@ -602,6 +802,9 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
             yq_row = yrow;
             yq_valid = valid;
         }
+        if constexpr (CONV) {
+            if (c + 1 < cx.nchunks) conv_slices<IT>(sm, lane, c + 1);
+        }
         __syncthreads();                             // chunk c + 1
     }
     if constexpr (sizeof(TY) == 2) stage_read();
@@ -613,7 +816,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 // Hs[u][4q + r] = H[p = 32pt + c32][n = 32(2SN + tt) + 8q + 4hf + r] in units of 2^sH (sH of the last chunk
 // processed; 0 for the initial state).  Its B'^T operands come straight from the pre-pass in registers,
 // one chunk ahead: each token step's pair is reloaded with the next chunk's right after its MFMAs.
-template <int SN>
+template <int SN, bool CONV>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
@@ -867,13 +1070,12 @@ __device__ __forceinline__ void x_convert(const XPart<NK>& xr, unsigned char* xt
     else convert([ex](float f) { return ldexp_f(f, -ex); });
 }
 
-// Chunk c's per-token vectors and scale exponents into v.  mb: the chunk's largest |x| (bf16 bits);
+// Chunk c's per-token vectors and scale exponents into v.  ex: the chunk's x scale; maxx: its largest |x|
+// (or a bound on it);
 // bound: the bound on |H| at the chunk's start (updated to the bound at its end); eH, sHp: units of the
 // state copy the chunk reads and of the state accumulator before it (updated for the next chunk).
-__device__ __forceinline__ void build_vec(const DtRegs& dr, unsigned mb, Vec& v, const Ctx& cx, const ScanArgs& a,
+__device__ __forceinline__ void build_vec(const DtRegs& dr, int ex, float maxx, Vec& v, const Ctx& cx, const ScanArgs& a,
                                           int c, int lane, float A2, float Dh, float& bound, int& eH, int& sHp) {
-    const int ex = x_scale(mb);
-    const float maxx = __uint_as_float(mb << 16);
     // per-token vectors (two tokens per lane)
     const int valid = cx.valid(c);
     const int h = cx.h;
@@ -940,10 +1142,12 @@ __device__ __forceinline__ void build_vec(const DtRegs& dr, unsigned mb, Vec& v,
 
 // Loader wave for rows 64 half .. 64 half + 63 (half 0: wave 6, which also builds the vectors; half 1:
 // wave 7, which also copies each next chunk's B tile from the pre-pass into LDS).
-template <int HALF>
+template <int HALF, bool CONV>
 __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
-    constexpr int NK = HALF ? 12 : 4;                // wave 6: rows 0..31 (it also builds the vectors); 7: 32..127
-    constexpr int R0 = HALF ? 32 : 0;
+    // wave 6: rows 0..31 (it also builds the vectors), wave 7: 32..127; fused conv (no conversion here,
+    // two conv slices each): 0..63 / 64..127
+    constexpr int NK = CONV ? 8 : (HALF ? 12 : 4);
+    constexpr int R0 = CONV ? 64 * HALF : (HALF ? 32 : 0);
     using XHalf = XPart<NK>;
     const float A2 = a.A[cx.h] * kLog2e;
     const float Dh = a.D ? a.D[cx.h] : 0.f;
@@ -958,7 +1162,73 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         if (nc > 1) dt_load(d1, cx, 1, lane);
         if (nc > 2) dt_load(d2, cx, 2, lane);
     }
-    if (nc > 0) {
+    // fused conv: a chunk's raw rows into Xr (after the 3 rows before the chunk), and wave 7's share of the
+    // next chunk's first rows: rows 125..127 of chunk rp (lanes 40..63 of its last instruction)
+    auto raw_write = [&](const XHalf& xr, int slot) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+            *reinterpret_cast<u32x4*>(sm.Xr[slot] + soff<kRowX>(3 + R0 + 8 * k + (lane >> 3), lane & 7)) = xr.v[k];
+    };
+    auto halo_write = [&](const XHalf& rp, int slot) {
+        if constexpr (HALF == 1) {
+            if (lane >= 40) *reinterpret_cast<u32x4*>(sm.Xr[slot] + soff<kRowX>((lane >> 3) - 5, lane & 7)) = rp.v[NK - 1];
+        }
+    };
+    // largest |raw| of this wave's rows of a chunk, with (wave 7) the 3 rows before it from the previous chunk
+    auto raw_max = [&](const XHalf& xr, const XHalf& rp) {
+        unsigned m = half_max(xr);
+        if constexpr (HALF == 1) {
+            unsigned mh = 0;
+            if (lane >= 40) {
+                u16x2 m2 = {0, 0};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, rp.v[NK - 1][e] & 0x7FFF7FFFu));
+                mh = max(static_cast<unsigned>(m2[0]), static_cast<unsigned>(m2[1]));
+            }
+            m = max(m, wave_max_u(mh));
+        }
+        return m;
+    };
+    if constexpr (CONV) {
+        if constexpr (HALF == 0) {
+            // the head's taps and bias (lane = channel), their bounds, and chunk 0's 3 earlier rows from the
+            // conv state (zeros without one)
+            const int64_t ch = static_cast<int64_t>(cx.h) * P + lane;
+            const uint2 wv = *reinterpret_cast<const uint2*>(cx.cv.w + ch * 4);
+            const float w4[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+            const float bv = cx.cv.bias ? static_cast<float>(cx.cv.bias[ch]) : 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sm.cw[k][lane] = w4[k];
+            sm.cw[4][lane] = bv;
+            const float sw = fabsf(w4[0]) + fabsf(w4[1]) + fabsf(w4[2]) + fabsf(w4[3]);
+            const float mbias = wave_max_f(fabsf(bv)), msw = wave_max_f(sw);
+            if (lane == 0) {
+                sm.cbound[0] = mbias;
+                sm.cbound[1] = msw * (1.f + 0x1p-20f);
+            }
+            unsigned short sv[3] = {0, 0, 0};
+            if (cx.cv.s_in) {
+                const uint2 s4 = *reinterpret_cast<const uint2*>(cx.cv.s_in + (cx.b * cx.cv.cd + ch) * 4);
+                sv[0] = static_cast<unsigned short>(s4.x >> 16);
+                sv[1] = static_cast<unsigned short>(s4.y & 0xFFFFu);
+                sv[2] = static_cast<unsigned short>(s4.y >> 16);
+            }
+            unsigned mh = 0;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                *reinterpret_cast<unsigned short*>(sm.Xr[0] + soff<kRowX>(j, lane >> 3) + 2 * (lane & 7)) = sv[j];
+                mh = max(mh, static_cast<unsigned>(sv[j] & 0x7FFFu));
+            }
+            if (nc > 0) {
+                const unsigned m = max(half_max(r0), wave_max_u(mh));
+                if (lane == 0) sm.xmax[0][0] = m;
+            }
+        } else if (nc > 0) {
+            const unsigned m = half_max(r0);
+            if (lane == 0) sm.xmax[0][1] = m;
+        }
+        if (nc > 0) raw_write(r0, 0);
+    } else if (nc > 0) {
         const unsigned m = half_max(r0);
         if (lane == 0) sm.xmax[0][HALF] = m;
     }
@@ -966,31 +1236,60 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     float bound = fmaxf(sm.hmax[0], sm.hmax[1]);
     int eH = max(ilog2f(bound), -126) + 1 - 15;      // units of the initial state copy
     int sHp = 0;
+    // the scale of chunk c's x tile and its largest |x| (or a bound on it)
+    auto x_scale_of = [&](int c, float& maxx) {
+        if constexpr (CONV) {
+            return conv_scale(sm, c & 1, maxx);
+        } else {
+            const unsigned mb = max(sm.xmax[c & 1][0], sm.xmax[c & 1][1]);
+            maxx = __uint_as_float(mb << 16);
+            return x_scale(mb);
+        }
+    };
     if (nc > 0) {
-        const unsigned mb = max(sm.xmax[0][0], sm.xmax[0][1]);
-        x_convert(r0, sm.X[0], R0, x_scale(mb), lane);
-        if constexpr (HALF == 0) build_vec(d0, mb, sm.vec[0], cx, a, 0, lane, A2, Dh, bound, eH, sHp);
+        float maxx;
+        const int ex = x_scale_of(0, maxx);
+        if constexpr (!CONV) x_convert(r0, sm.X[0], R0, ex, lane);
+        if constexpr (HALF == 0) build_vec(d0, ex, maxx, sm.vec[0], cx, a, 0, lane, A2, Dh, bound, eH, sHp);
         if (nc > 1) {
-            const unsigned m = half_max(r1);
+            const unsigned m = CONV ? raw_max(r1, r0) : half_max(r1);
             if (lane == 0) sm.xmax[1][HALF] = m;
+            if constexpr (CONV) {
+                raw_write(r1, 1);
+                halo_write(r0, 1);
+            }
+        }
+        if constexpr (CONV) {
+            conv_slices<6 + HALF>(sm, lane, 0);
         }
     }
     __syncthreads();                                 // chunk 0
-    // chunk c: convert chunk c + 1 (rc, dt in dc), take the maximum of chunk c + 2 (rm), load chunk c + 3
+    // chunk c: convert chunk c + 1 (rc, dt in dc) -- fused conv: all waves convolve it from its raw tile --
+    // take the maximum of chunk c + 2 (rm; fused conv: and put its raw rows in LDS), load chunk c + 3
     // into the sets chunk c used (rl, dl)
     auto phase = [&](int c, XHalf& rc, DtRegs& dc, XHalf& rm, XHalf& rl, DtRegs& dl) {
         if (c + 1 < nc) {
-            const unsigned mb = max(sm.xmax[(c + 1) & 1][0], sm.xmax[(c + 1) & 1][1]);
-            x_convert(rc, sm.X[(c + 1) & 1], R0, x_scale(mb), lane);
-            if constexpr (HALF == 0) build_vec(dc, mb, sm.vec[(c + 1) & 1], cx, a, c + 1, lane, A2, Dh, bound, eH, sHp);
+            float maxx;
+            const int ex = x_scale_of(c + 1, maxx);
+            if constexpr (!CONV) x_convert(rc, sm.X[(c + 1) & 1], R0, ex, lane);
+            if constexpr (HALF == 0) build_vec(dc, ex, maxx, sm.vec[(c + 1) & 1], cx, a, c + 1, lane, A2, Dh, bound, eH, sHp);
         }
         if (c + 2 < nc) {
-            const unsigned m = half_max(rm);
+            const unsigned m = CONV ? raw_max(rm, rc) : half_max(rm);
             if (lane == 0) sm.xmax[c & 1][HALF] = m;
+            if constexpr (CONV) {
+                raw_write(rm, c & 1);
+                halo_write(rc, c & 1);
+            }
         }
         if (c + 3 < nc) x_load(rl, cx, c + 3, R0, lane);
         if constexpr (HALF == 0) {
             if (c + 3 < nc) dt_load(dl, cx, c + 3, lane);
+        }
+        if constexpr (CONV) {
+            if (c + 1 < nc) {
+                conv_slices<6 + HALF>(sm, lane, c + 1);
+            }
         }
         __syncthreads();                             // chunk c + 1
     };
@@ -1001,10 +1300,14 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         if (c + 2 >= nc) break;
         phase(c + 2, r0, d0, r1, r2, d2);
     }
+    if constexpr (CONV && HALF == 0) {
+        // the head's new conv state (this workgroup read the old one)
+        if (cx.cv.s_out) conv_state_out(cx.cv, cx.b, cx.seqlen, static_cast<int64_t>(cx.h) * P + lane);
+    }
 }
 
-template <typename TY>
-__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsView ws) {
+template <typename TY, bool CONV>
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsView ws, ConvIn cv) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     // XCD-aware numbering: workgroup id % 8 picks the XCD; XCD k takes heads [k H/8, (k+1) H/8) of
@@ -1027,20 +1330,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
     cx.tile0 = (cx.b * a.ngroups + cx.grp) * static_cast<int64_t>(cx.nchunks);
     cx.hrow0 = (cx.b * a.nheads + cx.h) * static_cast<int64_t>(cx.nchunks);
     cx.ws = ws;
+    cx.cv = cv;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (wave == 0) run_y<TY, 0>(sm, a, cx, lane);
-    else if (wave == 1) run_y<TY, 1>(sm, a, cx, lane);
-    else if (wave == 2) run_y<TY, 2>(sm, a, cx, lane);
-    else if (wave == 3) run_y<TY, 3>(sm, a, cx, lane);
-    else if (wave == 4) run_s<0>(sm, a, cx, lane);
-    else if (wave == 5) run_s<1>(sm, a, cx, lane);
-    else if (wave == 6) run_x<0>(sm, a, cx, lane);
-    else run_x<1>(sm, a, cx, lane);
+    if (wave == 0) run_y<TY, 0, CONV>(sm, a, cx, lane);
+    else if (wave == 1) run_y<TY, 1, CONV>(sm, a, cx, lane);
+    else if (wave == 2) run_y<TY, 2, CONV>(sm, a, cx, lane);
+    else if (wave == 3) run_y<TY, 3, CONV>(sm, a, cx, lane);
+    else if (wave == 4) run_s<0, CONV>(sm, a, cx, lane);
+    else if (wave == 5) run_s<1, CONV>(sm, a, cx, lane);
+    else if (wave == 6) run_x<0, CONV>(sm, a, cx, lane);
+    else run_x<1, CONV>(sm, a, cx, lane);
 }
 
-template <typename TY>
-static hipError_t launch_t(const ScanArgs& a, void* workspace, hipStream_t s) {
+template <typename TY, bool CONV>
+static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv, hipStream_t s) {
     if (a.batch * a.nheads == 0) return hipSuccess;
     const int64_t nc = (a.seqlen + Q - 1) / Q;
     const int64_t ntile = a.batch * a.ngroups * nc;
@@ -1049,18 +1353,18 @@ static hipError_t launch_t(const ScanArgs& a, void* workspace, hipStream_t s) {
     WsView ws{w, reinterpret_cast<float*>(w + ntile * kWsTile),
               reinterpret_cast<int2*>(w + ntile * kWsTile + nhc * Q * static_cast<int64_t>(sizeof(float))), ntile};
     if (ntile > 0) {
-        hipLaunchKernelGGL(bc_prep_kernel, dim3(static_cast<uint32_t>(ntile)), dim3(256), 0, s,
+        hipLaunchKernelGGL(bc_prep_kernel<CONV>, dim3(static_cast<uint32_t>(ntile)), dim3(256), 0, s,
                            static_cast<const bf16*>(a.B), static_cast<const bf16*>(a.C), a.bc_row_stride,
-                           static_cast<const bf16*>(a.dt), a.dtp, a.seqlen, a.nheads, a.ngroups, nc, ws);
+                           static_cast<const bf16*>(a.dt), a.dtp, a.seqlen, a.nheads, a.ngroups, nc, ws, cv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    auto kern = chunk_scan_kernel<TY>;
-    const size_t smem = sizeof(Smem);
+    auto kern = chunk_scan_kernel<TY, CONV>;
+    const size_t smem = CONV ? sizeof(Smem) : offsetof(Smem, Xr);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(smem));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(a.batch * a.nheads)), dim3(kThreads), smem, s, a, ws);
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(a.batch * a.nheads)), dim3(kThreads), smem, s, a, ws, cv);
     return hipGetLastError();
 }
 
@@ -1076,7 +1380,19 @@ size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int n
 }
 
 hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s) {
-    return ydt == Dt::BF16 ? scan16::launch_t<bf16>(a, workspace, s) : scan16::launch_t<float>(a, workspace, s);
+    const scan16::ConvIn none{};
+    return ydt == Dt::BF16 ? scan16::launch_t<bf16, false>(a, workspace, none, s)
+                           : scan16::launch_t<float, false>(a, workspace, none, s);
+}
+
+hipError_t launch_conv_chunk_scan_f16(const ScanArgs& a, Dt ydt, const ConvScanArgs& c, void* workspace,
+                                      hipStream_t s) {
+    const scan16::ConvIn cv{static_cast<const bf16*>(c.w), static_cast<const bf16*>(c.bias),
+                            static_cast<const bf16*>(c.state_in), static_cast<bf16*>(c.state_out),
+                            static_cast<const bf16*>(c.xbc), c.xbc_row_stride, c.conv_dim,
+                            static_cast<int64_t>(a.nheads) * a.head_dim};
+    return ydt == Dt::BF16 ? scan16::launch_t<bf16, true>(a, workspace, cv, s)
+                           : scan16::launch_t<float, true>(a, workspace, cv, s);
 }
 
 }  // namespace ssd

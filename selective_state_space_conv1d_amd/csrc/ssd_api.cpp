@@ -200,6 +200,49 @@ ssd_status_t ssd_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, i
                       nullptr, 0, y, workspace, workspace_bytes, stream);
 }
 
+ssd_status_t ssd_conv_chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* xbc, int64_t xbc_row_stride,
+                                 const void* conv_w, const void* conv_bias, const void* conv_state_in,
+                                 void* conv_state_out, const void* dt, const float* A, const float* D,
+                                 const ssd_dt_params_t* dt_params, const float* init_state, float* final_state,
+                                 void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    if (!f16_scan_applies(d, chunk)) return SSD_ERR_UNSUPPORTED;
+    if (d->batch > INT32_MAX || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    const int64_t CD = ssd_conv_dim(d);
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!xbc || !conv_w || !dt || !A || !y)) return SSD_ERR_NULL;
+    if (tokens && xbc_row_stride < CD) return SSD_ERR_SHAPE;
+    if (!stride_ok(xbc_row_stride, d->act_dtype)) return SSD_ERR_ALIGN;
+    for (const void* p : {xbc, conv_w, conv_bias, conv_state_in, static_cast<const void*>(conv_state_out),
+                          static_cast<const void*>(y), static_cast<const void*>(init_state),
+                          static_cast<const void*>(final_state)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
+    if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
+    const int64_t I = static_cast<int64_t>(d->nheads) * d->head_dim;
+    const int64_t GN = static_cast<int64_t>(d->ngroups) * d->d_state;
+    if (!tokens) {
+        // no tokens: the conv state and the SSM state are carried through (as conv-then-scan does)
+        ssd::ConvFwdArgs ca{xbc, xbc_row_stride, conv_w, conv_bias, conv_state_in, conv_state_out, nullptr,
+                            d->batch, d->seqlen, CD};
+        st = hip_status(ssd::launch_conv1d_fwd(ca, static_cast<Dt>(d->act_dtype), stream));
+        if (st != SSD_OK) return st;
+        return chunk_scan(d, chunk, nullptr, I, nullptr, nullptr, GN, nullptr, A, D, dt_params, init_state,
+                          final_state, nullptr, 0, y, nullptr, 0, stream);
+    }
+    const size_t need = ssd_chunk_scan_workspace_size(d, chunk);
+    if (!workspace || workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SSD_ERR_ALIGN;
+    const char* xb = static_cast<const char*>(xbc);
+    const size_t es = elem_size(d->act_dtype);
+    ssd::ScanArgs a{xbc, xbc_row_stride, xb + I * es, xb + (I + GN) * es, xbc_row_stride, dt, A, D,
+                    init_state, final_state, y, d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups,
+                    d->d_state, chunk, {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params), nullptr, 0};
+    const ssd::ConvScanArgs c{xbc, xbc_row_stride, conv_w, conv_bias, conv_state_in, conv_state_out, CD};
+    return hip_status(ssd::launch_conv_chunk_scan_f16(a, static_cast<Dt>(d->y_dtype), c, workspace, stream));
+}
+
 ssd_status_t ssd_chunk_scan_noalloc(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                     const void* B, const void* C, int64_t bc_row_stride, const void* dt,
                                     const float* A, const float* D, const ssd_dt_params_t* dt_params,

@@ -146,6 +146,15 @@ size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int n
 // the device address and size of the current device's static fp16-scan workspace (looked up once per device)
 hipError_t f16_scan_scratch(void** ptr, size_t* bytes);
 hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s);
+// the fp16 scan with the prefill conv fused in: x, B and C are convolved from xBC inside the scan's launches
+struct ConvScanArgs {
+    const void* xbc; int64_t xbc_row_stride;
+    const void* w; const void* bias;
+    const void* state_in; void* state_out;
+    int64_t conv_dim;
+};
+hipError_t launch_conv_chunk_scan_f16(const ScanArgs& a, Dt ydt, const ConvScanArgs& c, void* workspace,
+                                      hipStream_t s);
 // Generic chunk scan on fp32 FMA (any act dtype, head_dim and d_state <= 128).
 hipError_t launch_chunk_scan_fma(const ScanArgs& a, Dt act, Dt ydt, hipStream_t s);
 

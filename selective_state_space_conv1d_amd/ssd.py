@@ -24,7 +24,8 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_chunk_scan_varlen", "ssd_conv1d_update_slots", "ssd_state_update_slots",
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
            "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
-           "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc"]
+           "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc",
+           "ssd_conv_chunk_scan"]
 
 
 class SsdDims(ctypes.Structure):
@@ -73,6 +74,8 @@ def _lib():
         _PDT = ctypes.POINTER(SsdDtParams)
         lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP, _VP,
                                        _VP, ctypes.c_size_t, _VP]
+        lib.ssd_conv_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _PDT, _VP,
+                                            _VP, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_chunk_scan_noalloc.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
                                                _VP, _VP, _VP]
         lib.ssd_state_update.argtypes = [_PD, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP]
@@ -103,7 +106,7 @@ def _lib():
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
                   "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
                   "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept",
-                  "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc"):
+                  "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc", "ssd_conv_chunk_scan"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -310,6 +313,47 @@ def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=
                                            _ptr(init_state), _ptr(final_state), _ptr(snapshots),
                                            int(snapshot_interval), _ptr(y), _ptr(workspace), ws, _stream(stream)),
            "ssd_chunk_scan_snapshots")
+    return y
+
+
+def ssd_conv_chunk_scan(xbc, w, bias, dt, A, D, nheads, head_dim, ngroups, d_state, conv_state_in=None,
+                        conv_state_out=None, init_state=None, final_state=None, y=None, chunk=128, y_dtype=None,
+                        workspace=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
+    """The prefill conv fused into the chunked scan: xbc [B, L, CD] (token rows may be strided, channels
+    packed; CD = H*P + 2*G*N), taps w [CD, 4], bias [CD]|None, conv states [B, CD, 4]|None (out may alias
+    in), dt [B, L, H], A/D [H], SSM states [B, H, P, N] fp32|None.  Equals ssd_conv1d_fwd followed by
+    ssd_chunk_scan on the x, B, C views of its output, without materialising that output.  bf16, P 64,
+    N 128, chunk 128.  workspace: None allocates one (ssd_chunk_scan_workspace_size bytes).  Returns y."""
+    dev = _device(xbc, "xbc")
+    Bt, L, CD = xbc.shape
+    if (xbc.stride(2) != 1 and CD > 1) or not _uniform_rows(xbc, L):
+        raise ValueError("xbc must be [B, L, CD] with packed channels and uniform token stride")
+    H, P, G, N = _split_cd(CD, nheads, head_dim, ngroups, d_state)
+    _conv_params(dev, CD, xbc.dtype, w, bias)
+    _need(conv_state_in, "conv_state_in", dev, (Bt, CD, 4), xbc.dtype, optional=True)
+    _need(conv_state_out, "conv_state_out", dev, (Bt, CD, 4), xbc.dtype, optional=True)
+    _need(dt, "dt", dev, (Bt, L, H), xbc.dtype)
+    _head_params(dev, H, A, D)
+    _need(init_state, "init_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(final_state, "final_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
+    if y is None:
+        y = torch.empty((Bt, L, H, P), dtype=y_dtype or xbc.dtype, device=xbc.device)
+    _need(y, "y", dev, (Bt, L, H, P))
+    d = _dims(Bt, L, H, P, G, N, xbc.dtype, y.dtype)
+    if workspace is None:
+        n = int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+    _need(workspace, "workspace", dev, optional=True)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    xs = CD if L == 0 else xbc.stride(1)
+    if L == 0:
+        xbc = dt = None
+    _check(_lib().ssd_conv_chunk_scan(ctypes.byref(d), chunk, _ptr(xbc), xs, _ptr(w), _ptr(bias),
+                                      _ptr(conv_state_in), _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D),
+                                      _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(init_state),
+                                      _ptr(final_state), _ptr(y), _ptr(workspace), ws, _stream(stream)),
+           "ssd_conv_chunk_scan")
     return y
 
 
