@@ -4,8 +4,9 @@
 // "MAX 平台 Nemotron-H 混合架构解析", 5.4: a narrower stored state, fp32 accumulation).
 //
 // The state moves 2 + 2 bytes per element instead of 4 + 4.  Each thread owns octets of 8
-// consecutive state elements (16 bytes, one wave-wide access of 1 KB); one Philox4x32 call per
-// octet gives the 8 16-bit random numbers its stochastic rounding uses.  Stochastic rounding
+// consecutive state elements (16 bytes) of one n position in several rows of a head, so the B and C
+// octet it needs is loaded once; one Philox4x32 call per octet gives the 8 16-bit random numbers its
+// stochastic rounding uses.  Stochastic rounding
 // (Philox stream and rule as in include/ssd.h):
 //   element e (flat index in the state array or pool) draws r16 = 16-bit half (e mod 2), low
 //   first, of word (e mod 8) div 2 of Philox4x32-R(counter (e/8 low, e/8 high, offset low,
@@ -20,7 +21,6 @@
 namespace ssd {
 
 constexpr int kLpThreads = 128;
-constexpr int kLpPerThread = 2;   // octets per thread
 
 // Philox4x32-R: per round, words 0 and 2 are multiplied by the two multipliers; the high halves
 // of the products are mixed with words 1 and 3 and the key, the low halves become words 1 and 3.
@@ -52,7 +52,18 @@ __device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32
 }
 
 // 16-bit storage formats: decode to fp32, round-to-nearest-even, stochastic rounding.
+// Stochastic rounding "up (away from zero) iff r16 < 65536 * dropped fraction" equals "add the noise
+// 2^d - 1 - floor(r16 / 2^(16-d)) to the d dropped bits and truncate" (d = 16 for bf16, 13 for fp16's
+// normal range): both carry exactly when floor(r16 / 2^(16-d)) < the dropped bits.  The fast forms
+// below use it; they hold for finite values (bf16) and for 2^-14 <= |v| < 65536 (fp16), which the
+// kernel checks for the whole wave before taking them.
 struct Bf16Fmt {
+    static __device__ __forceinline__ bool special(float v) {
+        return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
+    }
+    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
+        return (__float_as_uint(v) + (0xFFFFu - r16)) >> 16;
+    }
     static __device__ __forceinline__ float dec(uint32_t code) { return __uint_as_float(code << 16); }
     static __device__ __forceinline__ uint32_t rne(float v) {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
@@ -69,6 +80,14 @@ struct Bf16Fmt {
 };
 
 struct F16Fmt {
+    static __device__ __forceinline__ bool special(float v) {
+        return ((__float_as_uint(v) & 0x7FFFFFFFu) - 0x38800000u) >= (0x47800000u - 0x38800000u);
+    }
+    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
+        const uint32_t u = __float_as_uint(v);
+        const uint32_t c = ((u & 0x7FFFFFFFu) + (0x1FFFu - (r16 >> 3)) - 0x38000000u) >> 13;
+        return ((u >> 16) & 0x8000u) | c;
+    }
     static __device__ __forceinline__ float dec(uint32_t code) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(code)));
     }
@@ -106,137 +125,115 @@ __device__ __forceinline__ void load8_f32(const T* p, float (&out)[8]) {
     if constexpr (Vec16<T>::n == 4) load16_f32(p + 4, out + 4);
 }
 
-// Grid: one thread per kLpPerThread octets of the [B, H, P, N] walk, 128-thread strides.
-template <typename T, typename TY, class F, int N, bool SR, bool DTP>
+// Grid: one block per (batch entry, head).  Thread t owns octet q = t % (N/8) of rows t / (N/8) + R k
+// (R = 128 / (N/8) rows per pass): the group's B and C octet and the head's dt, A, D are loaded once and
+// reused for every row, so the loads per state byte stay close to the state's own (the state is read and
+// written once; the x value of a row is a broadcast load).  All of the thread's state octets are loaded
+// before any is used.
+template <typename T, typename TY, class F, int N, int PMAX, bool SR, bool DTP>   // head_dim <= PMAX
 __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     uint16_t* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
     const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, TY* __restrict__ y, int64_t total8, int H, int P, int hpg,
+    const float* __restrict__ D, TY* __restrict__ y, int H, int P, int hpg,
     const int32_t* __restrict__ slot_idx, int64_t nslots, DtParams dtp, uint64_t seed, uint64_t offset,
     int rounds) {
-    constexpr int OPR = N / 8;  // octets per state row
-    constexpr int kSpan = kLpThreads * kLpPerThread;
+    constexpr int OPR = N / 8;                 // octets per state row
+    constexpr int R = kLpThreads / OPR;        // rows per pass
+    constexpr int K = PMAX / R > 0 ? PMAX / R : 1;   // passes for head_dim PMAX
     const int64_t per_b = static_cast<int64_t>(H) * P * OPR;
-    const int lp = __builtin_ctz(static_cast<unsigned>(P));   // head_dim is a power of two
     u32x4* st = reinterpret_cast<u32x4*>(state);
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kSpan;
-    const int64_t base = f0 + threadIdx.x;
-    // The block's octets almost always lie in one batch entry (UNI): its index and slot are then
-    // block constants (one slot lookup for the block) and each octet's offset in the entry is the
-    // block's plus the thread's; otherwise each octet divides its flat index.
-    const int64_t ub = f0 / per_b;
-    const int64_t r0 = f0 - ub * per_b;
-    const int64_t span = total8 - f0 < kSpan ? total8 - f0 : kSpan;
-    auto body = [&](auto uni_tag) {
-        constexpr bool UNI = decltype(uni_tag)::value;
-        const int64_t uslot = UNI ? (slot_idx ? seq_slot(slot_idx, ub, nslots) : ub) : 0;
-
-        // per octet: batch entry, offset inside its state (< 2^31: the ABI bounds H*P*N), octet index
-        // in the state array (-1: padding)
-        u32x4 raw[kLpPerThread];
-        int64_t bb[kLpPerThread], so[kLpPerThread];
-        uint32_t rem[kLpPerThread];
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = static_cast<int>(bh - b * H);
+    const int g = h / hpg;
+    const int q = static_cast<int>(threadIdx.x) % OPR, rr = static_cast<int>(threadIdx.x) / OPR;
+    const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    // this thread's octets: rows rr + R k (< P); octet index in the state array or pool (-1: padding)
+    const int64_t so0 = slot >= 0 ? slot * per_b + (static_cast<int64_t>(h) * P + rr) * OPR + q : -1;
+    auto so_of = [&](int k) { return (so0 >= 0 && rr + R * k < P) ? so0 + static_cast<int64_t>(k) * R * OPR : -1; };
+    u32x4 raw[K];
+    float xv[K];
 #pragma unroll
-        for (int i = 0; i < kLpPerThread; ++i) {
-            const int64_t f = base + i * kLpThreads;
-            const int64_t ff = f < total8 ? f : 0;
-            int64_t slot;
-            if constexpr (UNI) {
-                bb[i] = ub;
-                rem[i] = f < total8 ? static_cast<uint32_t>(r0) + threadIdx.x + i * kLpThreads : 0u;
-                slot = uslot;
-            } else {
-                bb[i] = ff / per_b;
-                rem[i] = static_cast<uint32_t>(ff - bb[i] * per_b);
-                slot = slot_idx ? seq_slot(slot_idx, bb[i], nslots) : bb[i];
-            }
-            so[i] = (f < total8 && slot >= 0) ? slot * per_b + rem[i] : -1;
-            raw[i] = so[i] >= 0 ? __builtin_nontemporal_load(st + so[i]) : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < K; ++k) {
+        const int p = rr + R * k;
+        const int64_t so = so_of(k);
+        raw[k] = so >= 0 ? __builtin_nontemporal_load(st + so) : u32x4{0u, 0u, 0u, 0u};
+        xv[k] = p < P ? static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]) : 0.f;
+    }
+    const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
+    const float a = __expf(dtv * A[h]);
+    const float Dh = D ? D[h] : 0.f;
+    const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 8 * q;
+    float bv[8], cv[8];
+    load8_f32(Bm + bo, bv);
+    load8_f32(Cm + bo, cv);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int p = rr + R * k;
+        if (R * k >= P) break;                 // no row of this pass exists (uniform)
+        const bool ok = p < P;
+        const float dx = dtv * xv[k];
+        float part = 0.f, v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t word = raw[k][e >> 1];
+            v[e] = fmaf(a, F::dec((e & 1) ? word >> 16 : word & 0xFFFFu), dx * bv[e]);
+            part = fmaf(v[e], cv[e], part);
         }
+        if (!ok) part = 0.f;
+        part = group_sum_last<OPR>(part);
+        if (ok && q == OPR - 1) y[bh * P + p] = static_cast<TY>(part + (D ? Dh * xv[k] : 0.f));
+        const int64_t so = so_of(k);
+        if (so >= 0) {
+            uint32_t rw[4];
+            if constexpr (SR) {
+                const uint64_t o = static_cast<uint64_t>(so);
+                uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
+                                 static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
+                philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
+                // the fast form for every value; the few outside its range (fp16 subnormals, overflow,
+                // inf and NaN) are redone by the full form, in a branch only their lanes take
+                uint32_t hw[8];
 #pragma unroll
-        for (int i = 0; i < kLpPerThread; ++i) {
-            const bool ok = base + i * kLpThreads < total8;
-            const int64_t b = bb[i];
-            const uint32_t rin = rem[i] / OPR;  // h*P + p inside the batch entry
-            const int q = static_cast<int>(rem[i] % OPR);
-            const int h = static_cast<int>(rin >> lp);
-            const int p = static_cast<int>(rin & static_cast<uint32_t>(P - 1));
-            const int g = h / hpg;
-            const int64_t bh = b * H + h;
-            const int64_t row = bh * P + p;
-            const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
-            const float a = __expf(dtv * A[h]);
-            const float xv = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]);
-            const int64_t bo = b * bcs + static_cast<int64_t>(g) * N + 8 * q;
-            float bv[8], cv[8], v[8];
-            load8_f32(Bm + bo, bv);
-            load8_f32(Cm + bo, cv);
-            const float dx = dtv * xv;
-            float part = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t word = raw[i][e >> 1];
-                v[e] = fmaf(a, F::dec((e & 1) ? word >> 16 : word & 0xFFFFu), dx * bv[e]);
-                part = fmaf(v[e], cv[e], part);
-            }
-            if (!ok) part = 0.f;
-            part = group_sum_last<OPR>(part);
-            if (ok && q == OPR - 1) y[row] = static_cast<TY>(part + (D ? D[h] * xv : 0.f));
-            if (so[i] >= 0) {
-                uint32_t rw[4];
-                if constexpr (SR) {
-                    const uint64_t o = static_cast<uint64_t>(so[i]);
-                    uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
-                                     static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
-                    philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
-                    // values below 2^-14 (fp16's subnormal range) anywhere in the wave?
-                    bool sub = false;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sub |= (__float_as_uint(v[e]) & 0x7FFFFFFFu) < 0x38800000u;
-                    if (__builtin_amdgcn_ballot_w64(sub)) {
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            rw[w] = F::template sr<true>(v[2 * w], c[w] & 0xFFFFu) |
-                                    (F::template sr<true>(v[2 * w + 1], c[w] >> 16) << 16);
-                    } else {
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            rw[w] = F::template sr<false>(v[2 * w], c[w] & 0xFFFFu) |
-                                    (F::template sr<false>(v[2 * w + 1], c[w] >> 16) << 16);
-                    }
-                } else {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t r16 = (e & 1) ? c[e >> 1] >> 16 : c[e >> 1] & 0xFFFFu;
+                    hw[e] = F::sr_fast(v[e], r16);
+                    if (__builtin_expect(F::special(v[e]), 0)) hw[e] = F::template sr<true>(v[e], r16);
                 }
-                __builtin_nontemporal_store(u32x4{rw[0], rw[1], rw[2], rw[3]}, st + so[i]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) rw[w] = hw[2 * w] | (hw[2 * w + 1] << 16);
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
             }
+            __builtin_nontemporal_store(u32x4{rw[0], rw[1], rw[2], rw[3]}, st + so);
         }
-    };
-    if (r0 + span <= per_b) body(std::true_type{});
-    else body(std::false_type{});
+    }
 }
 
 template <typename T, typename TY, class F, int N>
 static hipError_t lp_launch(const LpUpdateArgs& a, hipStream_t s) {
     const UpdateArgs& u = a.u;
-    const int64_t total8 = u.batch * u.nheads * static_cast<int64_t>(u.head_dim) * (N / 8);
-    if (total8 == 0) return hipSuccess;
-    const int64_t per_block = kLpThreads * kLpPerThread;
-    const dim3 grid(static_cast<uint32_t>((total8 + per_block - 1) / per_block));
+    const int64_t blocks = u.batch * u.nheads;
+    if (blocks == 0) return hipSuccess;
     const bool dtp = u.dtp.bias || u.dtp.softplus || u.dtp.lo < u.dtp.hi;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(kLpThreads), 0, s, static_cast<uint16_t*>(a.state),
-                           static_cast<const T*>(u.x), u.x_row_stride, static_cast<const T*>(u.B),
-                           static_cast<const T*>(u.C), u.bc_row_stride, static_cast<const T*>(u.dt), u.A, u.D,
-                           static_cast<TY*>(u.y), total8, u.nheads, u.head_dim, u.nheads / u.ngroups, u.slot_idx,
-                           u.nslots, u.dtp, a.seed, a.offset, a.rounds);
+        hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kLpThreads), 0, s,
+                           static_cast<uint16_t*>(a.state), static_cast<const T*>(u.x), u.x_row_stride,
+                           static_cast<const T*>(u.B), static_cast<const T*>(u.C), u.bc_row_stride,
+                           static_cast<const T*>(u.dt), u.A, u.D, static_cast<TY*>(u.y), u.nheads, u.head_dim,
+                           u.nheads / u.ngroups, u.slot_idx, u.nslots, u.dtp, a.seed, a.offset, a.rounds);
         return hipGetLastError();
     };
-    if (a.rounds > 0)
-        return dtp ? go(state_update_lp_kernel<T, TY, F, N, true, true>)
-                   : go(state_update_lp_kernel<T, TY, F, N, true, false>);
-    return dtp ? go(state_update_lp_kernel<T, TY, F, N, false, true>)
-               : go(state_update_lp_kernel<T, TY, F, N, false, false>);
+    auto pick = [&](auto pmax) {
+        constexpr int PM = decltype(pmax)::value;
+        if (a.rounds > 0)
+            return dtp ? go(state_update_lp_kernel<T, TY, F, N, PM, true, true>)
+                       : go(state_update_lp_kernel<T, TY, F, N, PM, true, false>);
+        return dtp ? go(state_update_lp_kernel<T, TY, F, N, PM, false, true>)
+                   : go(state_update_lp_kernel<T, TY, F, N, PM, false, false>);
+    };
+    return u.head_dim <= 64 ? pick(std::integral_constant<int, 64>{}) : pick(std::integral_constant<int, 128>{});
 }
 
 template <typename T, typename TY, class F>
