@@ -72,11 +72,34 @@ def test_state_update_multi_is_k_single_updates_bitwise(shape):
         torch.cuda.synchronize()
         assert torch.equal(y[:, j], yj), j
         assert torch.equal(inter[:, j], st), j
-    # no intermediate output: y alone, identical
-    y2, none = ssd.ssd_state_update_multi(s["init_state"], s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"],
-                                          inter_states=None)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("shape", [None] + STRADDLE)
+def test_multi_y_only_form(orc, k, shape):
+    """y without intermediate states: for 2 <= k <= 4 the chunk (dual) form, which sums the same value
+    in another order -- within the fp32 bar of the oracle and of the sequential form; k = 1 and k > 4
+    run the sequential form, bitwise the y of the call with intermediate states (k = 1: the
+    single-token update)."""
+    d = WORKLOADS["decode_ultra_b64"].with_(batch=5) if shape is None else LayerDims(shape[0], 1, *shape[1:])
+    s = ssm_inputs(d, k, 415)
+    args = (s["init_state"], s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"])
+    y_seq, _ = ssd.ssd_state_update_multi(*args, y_dtype=torch.float32)
+    y_only, none = ssd.ssd_state_update_multi(*args, inter_states=None, y_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert none is None and torch.equal(y2, y)
+    assert none is None
+    if k == 1 or k > 4:
+        assert torch.equal(y_only, y_seq)
+    if k == 1:
+        st = s["init_state"].clone()
+        y1 = ssd.ssd_state_update(st, s["x"][:, 0], s["Bm"][:, 0], s["Cm"][:, 0], s["dt"][:, 0].contiguous(),
+                                  s["A"], s["D"], y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y_only[:, 0], y1)
+    assert_close(y_only, f64(y_seq), F32_BAR, "y against the sequential form")
+    yr, _ = orc.state_update_multi(f64(s["init_state"]), None, f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]),
+                                   f64(s["dt"]), f64(s["A"]), f64(s["D"]))
+    assert_close(y_only, yr, F32_BAR, "y against the oracle")
 
 
 def test_state_update_multi_dt_prologue(orc):
@@ -93,6 +116,11 @@ def test_state_update_multi_dt_prologue(orc):
                                     f64(s["A"]), f64(s["D"]))
     assert_close(y, yr, F32_BAR, "y")
     assert_close(inter, ir, F32_BAR, "intermediate states")
+    y2, _ = ssd.ssd_state_update_multi(s["init_state"], s["x"], s["Bm"], s["Cm"], raw, s["A"], s["D"],
+                                       inter_states=None, y_dtype=torch.float32, dt_bias=bias, dt_softplus=True,
+                                       dt_limit=(0.0, 2.0))
+    torch.cuda.synchronize()
+    assert_close(y2, yr, F32_BAR, "y without intermediate states")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -251,7 +279,7 @@ def test_accept_by_recomputation_is_the_stored_intermediate(use_slots, k, H, P, 
     else:
         spool0, slots, slot = s["init_state"], list(range(6)), None
     acc = torch.tensor([2, 0, 3, k, 9, 1], dtype=torch.int32, device=DEV)    # 9 > k clamps to k
-    # y with and without intermediate states: identical (the y reductions run in token blocks)
+    # y with and without intermediate states: the same values (summed in another order for k <= 4)
     y1, inter = ssd.ssd_state_update_multi(spool0, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], slot_idx=slot)
     y2, none = ssd.ssd_state_update_multi(spool0, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], slot_idx=slot,
                                           inter_states=None)
@@ -262,6 +290,30 @@ def test_accept_by_recomputation_is_the_stored_intermediate(use_slots, k, H, P, 
     ssd.ssd_state_update_accept(sp_re, s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], acc, slot_idx=slot)
     ssd.ssd_conv1d_update_accept(xbc, cp_re, acc, slot_idx=slot)
     torch.cuda.synchronize()
-    assert none is None and torch.equal(y1, y2)
+    assert none is None
+    assert_close(y2, f64(y1), BF16_BAR, "y without intermediate states")
     assert torch.equal(sp_re, sp_copy), "recomputed states must equal the stored intermediate ones"
     assert torch.equal(cp_re, cp_copy), "recomputed conv windows must equal the stored ones"
+
+
+@pytest.mark.parametrize("H,P,N", [(8, 64, 128), (3, 16, 16)])
+def test_multi_y_with_x_rows_not_a_multiple_of_four_apart(H, P, N):
+    """x token rows H*P + 2 elements apart (the four x values of a row group are then loaded one by
+    one): y, and the recomputed accept, bitwise as with packed x."""
+    d = LayerDims(5, 1, H, P, 1, N)
+    k = 3
+    s = ssm_inputs(d, k, 490)
+    wide = torch.zeros(d.batch, k, H * P + 2, dtype=s["x"].dtype, device=DEV)
+    wide[..., :H * P] = s["x"].reshape(d.batch, k, H * P)
+    xo = wide[..., :H * P].view(d.batch, k, H, P)
+    assert xo.stride(1) == H * P + 2
+    args = (s["Bm"], s["Cm"], s["dt"], s["A"], s["D"])
+    y1, _ = ssd.ssd_state_update_multi(s["init_state"], s["x"], *args, inter_states=None)
+    y2, _ = ssd.ssd_state_update_multi(s["init_state"], xo, *args, inter_states=None)
+    acc = torch.tensor([1, 3, 0, 2, 3], dtype=torch.int32, device=DEV)
+    st1, st2 = s["init_state"].clone(), s["init_state"].clone()
+    ssd.ssd_state_update_accept(st1, s["x"], *args[:2], s["dt"], s["A"], s["D"], acc)
+    ssd.ssd_state_update_accept(st2, xo, *args[:2], s["dt"], s["A"], s["D"], acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(st1, st2)
