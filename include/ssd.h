@@ -463,6 +463,34 @@ ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state
                                  hipStream_t stream);
 
 /*
+ * The chunked scans with 16-bit state arrays (the modeling_nemotron_h.py walk-through,
+ * 部署时如何调这些缓存: an fp16 Mamba state cache with Philox stochastic rounding; [P3] 5.4: the
+ * stored state narrower than the fp32 the scan accumulates in).  The initial states are fp16 or
+ * bf16 codes (state_dtype SSD_F16 or SSD_BF16, else SSD_ERR_DTYPE), read exactly; the scan runs as
+ * in fp32; each final state element is rounded into a code as ssd_state_update_lp rounds
+ * (sr NULL: nearest even; else stochastically, element e being its flat index in the array or pool,
+ * rounds 1..16 else SSD_ERR_UNSUPPORTED).  The code arrays are 16-byte aligned.
+ *  ssd_chunk_scan_lp          init_state / final_state [B, H, P, N] codes, or NULL (zeros / not
+ *                             stored); they may alias.  Everything else as ssd_chunk_scan (a
+ *                             workspace selects the fp16 scan there too).
+ *  ssd_chunk_scan_varlen_lp   state_pool [nslots, H, P, N] codes, read and written in place as
+ *                             ssd_chunk_scan_varlen's fp32 pool.
+ */
+ssd_status_t ssd_chunk_scan_lp(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                               const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                               const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                               const void* init_state, void* final_state, int32_t state_dtype,
+                               const ssd_sr_params_t* sr, void* y, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+ssd_status_t ssd_chunk_scan_varlen_lp(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                      const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                      const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                      const int32_t* cu_seqlens, const int32_t* slot_idx,
+                                      const int32_t* has_initial_state, void* state_pool, int32_t state_dtype,
+                                      int64_t nslots, const ssd_sr_params_t* sr, void* y, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Gated group RMSNorm of the mixer output ([P3] 5.4, item 4: one fused kernel; the gate is applied
  * before the norm, in fp32, with an fp32 weight).  Per row and group g of gs = H*P/G channels:
  *   v = y * silu(z);  out = v / sqrt(mean over the group of v^2 + eps) * weight.

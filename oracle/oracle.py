@@ -337,6 +337,44 @@ class Oracle:
         return codes
 
 
+    # ------------------------------------------------------------------ 16-bit state arrays
+    # The scans on a state held as fp16 / bf16 codes (the modeling_nemotron_h.py walk-through,
+    # 部署时如何调这些缓存: the Mamba state cache in fp16 with Philox stochastic rounding; "MAX
+    # 平台 Nemotron-H 混合架构解析" 5.4: the state stored narrower than the fp32 the scan
+    # accumulates in): the initial codes decode exactly, the scan runs on their values, and each
+    # final state is rounded to fp32 and then to a code, element e (its flat index in the array or
+    # pool) drawing its random number as in state_update_lp_codes_a0.  The kernels round their own
+    # fp32 final state, so the codes returned here are theirs exactly when the fp64 final state is
+    # representable in fp32 (A = 0 with inputs on a coarse dyadic grid); otherwise they are one of
+    # the two codes around it.
+
+    @staticmethod
+    def round_states(vals, fmt, sr=None, first=0):
+        """fp64 states [n, H, P, N], entries first .. first + n - 1 of their array -> uint16 codes."""
+        v32 = np.asarray(vals, dtype=np.float64).astype(np.float32)
+        r16 = None
+        if sr is not None:
+            e = first * int(np.prod(v32.shape[1:])) + np.arange(v32.size, dtype=np.int64).reshape(v32.shape)
+            r16 = lowprec.random16(e, sr[0], sr[1], sr[2])
+        return lowprec.round_state(v32, fmt, r16)
+
+    # codes [B,H,P,N] uint16|None (zeros) -> y, final state (fp64), final codes
+    def scan_lp(self, x, Bm, Cm, dt, A, D, codes, fmt, sr=None):
+        init = None if codes is None else lowprec.decode(codes, fmt)
+        y, fin = self.scan(x, Bm, Cm, dt, A, D, init)
+        return y, fin, self.round_states(fin, fmt, sr)
+
+    # pool codes [nslots,H,P,N] -> y [T,H,P], new pool codes (slots no sequence names keep theirs)
+    def scan_varlen_lp(self, x, Bm, Cm, dt, A, D, cu, codes, fmt, slot=None, has_init=None, sr=None):
+        codes = np.array(codes, dtype=np.uint16, copy=True)
+        y, new = self.scan_varlen(x, Bm, Cm, dt, A, D, cu, lowprec.decode(codes, fmt), slot, has_init)
+        for s in range(len(cu) - 1):
+            k = self._slot(slot, s, codes.shape[0])
+            if k >= 0:
+                codes[k] = self.round_states(new[k][None], fmt, sr, first=k)[0]
+        return y, codes
+
+
 _DEFAULT = None
 
 

@@ -50,6 +50,7 @@
 
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include "state_codes.h"
 
 namespace ssd {
 namespace scan16 {
@@ -833,6 +834,7 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         for (int q = 0; q < 4; ++q) {
             f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
             if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
+            else if (a.init16) v4 = codes_load4(a.init16, a.codes.f16, sbase + p_of(u) * NS + n_of(u, q));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 Hs[u][4 * q + r] = v4[r];
@@ -875,10 +877,13 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4*>(a.final_state + sbase + p_of(u) * NS + n_of(u, q)) =
-                    f32x4{ldexp_f(Hs[u][4 * q], sh), ldexp_f(Hs[u][4 * q + 1], sh), ldexp_f(Hs[u][4 * q + 2], sh),
-                          ldexp_f(Hs[u][4 * q + 3], sh)};
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = {ldexp_f(Hs[u][4 * q], sh), ldexp_f(Hs[u][4 * q + 1], sh),
+                                 ldexp_f(Hs[u][4 * q + 2], sh), ldexp_f(Hs[u][4 * q + 3], sh)};
+                const int64_t e = sbase + p_of(u) * NS + n_of(u, q);
+                if (a.final16) codes_store4(a.final16, a.codes, e, v);
+                else *reinterpret_cast<f32x4*>(a.final_state + e) = v;
+            }
     };
     __syncthreads();                                 // prologue 1
     {
@@ -948,12 +953,12 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         }
         if (c + 1 < cx.nchunks) {
             write_h(buf ^ 1, sh, v.eHn);
-        } else if (a.final_state) {
+        } else if (a.final_state || a.final16) {
             store_state(sh);
         }
         __syncthreads();                             // chunk c + 1
     }
-    if (cx.nchunks == 0 && a.final_state) store_state(0);   // no tokens: the final state is the initial one
+    if (cx.nchunks == 0 && (a.final_state || a.final16)) store_state(0);   // no tokens: the final state is the initial one
 }
 
 // ---------------------------------------------------------------------------

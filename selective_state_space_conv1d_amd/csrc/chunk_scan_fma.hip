@@ -13,6 +13,7 @@
 // rounding); the caller's chunk size only selects the MFMA kernel's tiling.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include "state_codes.h"
 
 namespace ssd {
 
@@ -60,7 +61,10 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
 
     for (int e = tid; e < P * N; e += kFmaThreads) {
         const int p = e / N, n = e - p * N;
-        sm.H[p][n] = (a.init_state && use_init) ? a.init_state[sbase + e] : 0.f;
+        float v = 0.f;
+        if (use_init && a.init_state) v = a.init_state[sbase + e];
+        else if (use_init && a.init16) v = code_dec(a.init16[sbase + e], a.codes.f16);
+        sm.H[p][n] = v;
     }
 
     for (int64_t t0 = 0; t0 < L; t0 += kT) {
@@ -136,10 +140,11 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
         }
     }
     __syncthreads();
-    if (a.final_state && write_final)
+    if ((a.final_state || a.final16) && write_final)
         for (int e = tid; e < P * N; e += kFmaThreads) {
             const int p = e / N, n = e - p * N;
-            a.final_state[sbase + e] = sm.H[p][n];
+            if (a.final16) codes_store1(a.final16, a.codes, sbase + e, sm.H[p][n]);
+            else a.final_state[sbase + e] = sm.H[p][n];
         }
 }
 

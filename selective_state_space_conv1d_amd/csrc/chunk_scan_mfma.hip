@@ -62,6 +62,7 @@
 // sit on one XCD.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include "state_codes.h"
 
 #include <atomic>
 #include <cstdlib>
@@ -579,28 +580,30 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
     // dst = the initial state of sequence s (zeros without one)
     auto load_init = [&](int64_t s, f32x16 (&dst)[NT]) {
         const int64_t sl = cx.slot(s);
-        const bool from = a.init_state && sl >= 0 && cx.use_init(s);
+        const bool from = (a.init_state || a.init16) && sl >= 0 && cx.use_init(s);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (from) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
+                if (from && a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
+                else if (from) v = codes_load4(a.init16, a.codes.f16, sbase(sl) + hp * NS + n);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[t][4 * j + r] = v[r];
             }
     };
     auto store_final = [&](int64_t s, const f32x16 (&src)[NT]) {   // src as the final state of sequence s
         const int64_t sl = cx.slot(s);
-        if (!a.final_state || sl < 0) return;
+        if ((!a.final_state && !a.final16) || sl < 0) return;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
-                *reinterpret_cast<f32x4*>(a.final_state + sbase(sl) + hp * NS + n) =
-                    f32x4{src[t][4 * j], src[t][4 * j + 1], src[t][4 * j + 2], src[t][4 * j + 3]};
+                const f32x4 v = {src[t][4 * j], src[t][4 * j + 1], src[t][4 * j + 2], src[t][4 * j + 3]};
+                if (a.final16) codes_store4(a.final16, a.codes, sbase(sl) + hp * NS + n, v);
+                else *reinterpret_cast<f32x4*>(a.final_state + sbase(sl) + hp * NS + n) = v;
             }
     };
     // empty sequences in [s0, s1) end with their initial state (zeros without one)

@@ -153,13 +153,40 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
     return ssd::f16_scan_workspace_bytes(d->batch, d->seqlen, d->nheads, d->ngroups);
 }
 
-// the batched scan, with optional state snapshots (internal linkage)
+// 16-bit initial / final states of a scan, in place of the fp32 ones
+struct States16 {
+    const void* init;
+    void* fin;
+    int32_t dtype;
+    const ssd_sr_params_t* sr;
+};
+
+static ssd_status_t check_states16(const States16* s16) {
+    if (!s16) return SSD_OK;
+    if (s16->dtype != SSD_F16 && s16->dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (s16->sr && (s16->sr->rounds < 1 || s16->sr->rounds > 16)) return SSD_ERR_UNSUPPORTED;
+    for (const void* p : {s16->init, static_cast<const void*>(s16->fin)})
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+static void set_states16(ssd::ScanArgs& a, const States16* s16) {
+    if (!s16) return;
+    a.init16 = static_cast<const uint16_t*>(s16->init);
+    a.final16 = static_cast<uint16_t*>(s16->fin);
+    a.codes = ssd::Codes{s16->dtype == SSD_F16, s16->sr ? s16->sr->seed : 0, s16->sr ? s16->sr->offset : 0,
+                         s16->sr ? s16->sr->rounds : 0};
+}
+
+// the batched scan, with optional state snapshots or 16-bit states (internal linkage)
 static ssd_status_t chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                const void* B, const void* C, int64_t bc_row_stride, const void* dt, const float* A,
                                const float* D, const ssd_dt_params_t* dt_params, const float* init_state,
                                float* final_state, float* snapshots, int64_t interval, void* y, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               size_t workspace_bytes, hipStream_t stream, const States16* s16 = nullptr) {
     ssd_status_t st = check_dims(d, true);
+    if (st != SSD_OK) return st;
+    st = check_states16(s16);
     if (st != SSD_OK) return st;
     if (d->batch > INT32_MAX || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
@@ -183,6 +210,7 @@ static ssd_status_t chunk_scan(const ssd_dims_t* d, int32_t chunk, const void* x
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, init_state, final_state, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
                     {nullptr, nullptr, nullptr, 0}, dt_params_of(dt_params), snapshots, interval};
+    set_states16(a, s16);
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
     if (use_f16) return hip_status(ssd::launch_chunk_scan_f16(a, ydt, workspace, stream));
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
@@ -281,10 +309,12 @@ static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const 
                                       const int32_t* has_initial_state, float* state_pool, int64_t nslots,
                                       float* snap_pool, int64_t nsnap_slots, const int32_t* snap_table,
                                       int32_t max_snaps, int64_t interval, void* y, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+                                      size_t workspace_bytes, hipStream_t stream, const States16* s16 = nullptr) {
     ssd_status_t st = check_dims(d, true);
     if (st != SSD_OK) return st;
-    st = check_seq_tables(d, cu_seqlens, state_pool, nslots);
+    st = check_seq_tables(d, cu_seqlens, s16 ? s16->fin : state_pool, nslots);
+    if (st != SSD_OK) return st;
+    st = check_states16(s16);
     if (st != SSD_OK) return st;
     if (d->batch > INT32_MAX || d->seqlen > INT32_MAX) return SSD_ERR_SHAPE;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
@@ -305,6 +335,7 @@ static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const 
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,
                     d->batch, d->seqlen, d->nheads, d->head_dim, d->ngroups, d->d_state, chunk,
                     {cu_seqlens, slot_idx, has_initial_state, nslots}, dt_params_of(dt_params)};
+    set_states16(a, s16);
     if (snap_table && max_snaps > 0 && nsnap_slots > 0) {   // otherwise no snapshot can be stored
         a.snapshots = snap_pool;
         a.snap_interval = interval;
@@ -506,6 +537,30 @@ ssd_status_t ssd_accept_states(const ssd_dims_t* d, const int32_t* accept_len, c
     ssd::AcceptArgs a{accept_len, slot_idx, nslots, d->batch, static_cast<int>(d->seqlen),
                       state, inter_states, state_bytes, conv_state, inter_conv_states, conv_bytes};
     return hip_status(ssd::launch_accept_states(a, stream));
+}
+
+ssd_status_t ssd_chunk_scan_lp(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                               const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                               const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                               const void* init_state, void* final_state, int32_t state_dtype,
+                               const ssd_sr_params_t* sr, void* y, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    const States16 s16{init_state, final_state, state_dtype, sr};
+    return chunk_scan(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, nullptr, nullptr,
+                      nullptr, 0, y, workspace, workspace_bytes, stream, &s16);
+}
+
+ssd_status_t ssd_chunk_scan_varlen_lp(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
+                                      const void* B, const void* C, int64_t bc_row_stride, const void* dt,
+                                      const float* A, const float* D, const ssd_dt_params_t* dt_params,
+                                      const int32_t* cu_seqlens, const int32_t* slot_idx,
+                                      const int32_t* has_initial_state, void* state_pool, int32_t state_dtype,
+                                      int64_t nslots, const ssd_sr_params_t* sr, void* y, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    const States16 s16{state_pool, state_pool, state_dtype, sr};
+    return chunk_scan_varlen(d, chunk, x, x_row_stride, B, C, bc_row_stride, dt, A, D, dt_params, cu_seqlens,
+                             slot_idx, has_initial_state, nullptr, nslots, nullptr, 0, nullptr, 0, 0, y, workspace,
+                             workspace_bytes, stream, &s16);
 }
 
 ssd_status_t ssd_state_update_lp(const ssd_dims_t* d, void* state, int32_t state_dtype, const int32_t* slot_idx,

@@ -47,6 +47,14 @@ struct ConvUpdateArgs {
     int k;         // multi-token: tokens per request (the state is then read only)
 };
 
+// How a state array of 16-bit codes is read and rounded: fp16 or bf16 codes; rounds = 0 rounds to
+// nearest even, otherwise stochastically with Philox4x32-(rounds) keyed by seed at offset.
+struct Codes {
+    bool f16;
+    uint64_t seed, offset;
+    int rounds;
+};
+
 struct ScanArgs {
     const void* x; int64_t x_row_stride;
     const void* B; const void* C; int64_t bc_row_stride;
@@ -64,6 +72,11 @@ struct ScanArgs {
     int64_t snap_max, snap_slots;
     int64_t nranges;         // set by the launcher: sequence ranges per head (workgroups = nranges * nheads)
     int spin_max;            // set by the launcher: iterations of the split scan's bounded LDS-counter wait
+    // 16-bit state arrays (init_state and final_state NULL): the initial states as codes, or NULL
+    // (zeros), and the final states rounded into codes, or NULL (not stored); may alias
+    const uint16_t* init16;
+    uint16_t* final16;
+    Codes codes;
 };
 
 struct UpdateArgs {

@@ -12,111 +12,16 @@
 //   first, of word (e mod 8) div 2 of Philox4x32-R(counter (e/8 low, e/8 high, offset low,
 //   offset high), key (seed low, seed high)), and moves to the next code away from zero iff
 //   r16 < 65536 * (distance past the code toward zero) / spacing.
-// Philox4x32 is written from its publication (Salmon, Moraes, Dror, Shaw, SC 2011).
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include "state_codes.h"
 
 #include <type_traits>
 
 namespace ssd {
 
 constexpr int kLpThreads = 128;
-
-// Philox4x32-R: per round, words 0 and 2 are multiplied by the two multipliers; the high halves
-// of the products are mixed with words 1 and 3 and the key, the low halves become words 1 and 3.
-// The key advances by the Weyl increments before each round after the first.
-template <int R>   // R > 0: that many rounds, unrolled; R = 0: `rounds` rounds
-__device__ __forceinline__ void philox4x32_r(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int rounds) {
-#pragma unroll
-    for (int r = 0; r < (R > 0 ? R : rounds); ++r) {
-        if (r) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
-        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
-        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c[1] ^ k0;
-        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c[3] ^ k1;
-        c[0] = n0;
-        c[1] = static_cast<uint32_t>(p1);
-        c[2] = n2;
-        c[3] = static_cast<uint32_t>(p0);
-    }
-}
-
-// 5 rounds (the engine setting on the modeling_nemotron_h.py walk-through page, 部署时如何调这些缓存)
-// run unrolled; other round counts loop.
-__device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int rounds) {
-    if (rounds == 5) philox4x32_r<5>(c, k0, k1, rounds);
-    else philox4x32_r<0>(c, k0, k1, rounds);
-}
-
-// 16-bit storage formats: decode to fp32, round-to-nearest-even, stochastic rounding.
-// Stochastic rounding "up (away from zero) iff r16 < 65536 * dropped fraction" equals "add the noise
-// 2^d - 1 - floor(r16 / 2^(16-d)) to the d dropped bits and truncate" (d = 16 for bf16, 13 for fp16's
-// normal range): both carry exactly when floor(r16 / 2^(16-d)) < the dropped bits.  The fast forms
-// below use it; they hold for finite values (bf16) and for 2^-14 <= |v| < 65536 (fp16), which the
-// kernel checks for the whole wave before taking them.
-struct Bf16Fmt {
-    static __device__ __forceinline__ bool special(float v) {
-        return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
-    }
-    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
-        return (__float_as_uint(v) + (0xFFFFu - r16)) >> 16;
-    }
-    static __device__ __forceinline__ float dec(uint32_t code) { return __uint_as_float(code << 16); }
-    static __device__ __forceinline__ uint32_t rne(float v) {
-        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-    }
-    // bf16 keeps fp32's exponent: the 16 dropped bits are the distance past the truncated code
-    // in units of 2^-16 spacing, and the truncated code + 1 is the next code away from zero.
-    // Written with selects only: a branch per element would split the wave.
-    template <bool SUB = true>
-    static __device__ __forceinline__ uint32_t sr(float v, uint32_t r16) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t t = (u >> 16) + (r16 < (u & 0xFFFFu) ? 1u : 0u);
-        return (u & 0x7F800000u) == 0x7F800000u ? rne(v) : t;
-    }
-};
-
-struct F16Fmt {
-    static __device__ __forceinline__ bool special(float v) {
-        return ((__float_as_uint(v) & 0x7FFFFFFFu) - 0x38800000u) >= (0x47800000u - 0x38800000u);
-    }
-    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t c = ((u & 0x7FFFFFFFu) + (0x1FFFu - (r16 >> 3)) - 0x38000000u) >> 13;
-        return ((u >> 16) & 0x8000u) | c;
-    }
-    static __device__ __forceinline__ float dec(uint32_t code) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(code)));
-    }
-    static __device__ __forceinline__ uint32_t rne(float v) {
-        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-    }
-    // Selects only, as for bf16.  SUB: some value of the wave is in fp16's subnormal range (the
-    // caller tests that once per octet for the whole wave; the normal-range path alone is cheaper).
-    template <bool SUB = true>
-    static __device__ __forceinline__ uint32_t sr(float v, uint32_t r16) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t a = u & 0x7FFFFFFFu;
-        // fp16 normal range (|v| >= 2^-14): the code is fp32's top 10 mantissa bits under the
-        // exponent rebiased from 127 to 15; 13 bits are dropped, so frac * 65536 = dropped << 3
-        const uint32_t cn = (a >> 13) - (112u << 10) + (r16 < ((a & 0x1FFFu) << 3) ? 1u : 0u);
-        // fp16 subnormals: q = |v| * 2^24 counts units of 2^-24 and is exact in fp32, as are its
-        // integer part (the code), its fraction and the fraction * 65536
-        uint32_t c = cn;   // +1 carries into the exponent, past 65504 into infinity
-        if constexpr (SUB) {
-            const float q = __uint_as_float(a < 0x38800000u ? a : 0u) * 16777216.0f;   // < 1024 (0 outside)
-            const uint32_t ci = static_cast<uint32_t>(q);
-            const uint32_t cs = ci + (static_cast<float>(r16) < (q - static_cast<float>(ci)) * 65536.0f ? 1u : 0u);
-            c = a < 0x38800000u ? cs : cn;
-        }
-        c = a >= 0x47800000u ? 0x7C00u : c;       // |v| >= 65536: infinity
-        const uint32_t r = ((u >> 16) & 0x8000u) | c;
-        return a >= 0x7F800000u ? rne(v) : r;     // inf, NaN
-    }
-};
+constexpr int kLpRows = 32;   // state rows per block
 
 // Eight consecutive activation values as fp32.
 template <typename T>
@@ -125,12 +30,12 @@ __device__ __forceinline__ void load8_f32(const T* p, float (&out)[8]) {
     if constexpr (Vec16<T>::n == 4) load16_f32(p + 4, out + 4);
 }
 
-// Grid: one block per (batch entry, head).  Thread t owns octet q = t % (N/8) of rows t / (N/8) + R k
-// (R = 128 / (N/8) rows per pass): the group's B and C octet and the head's dt, A, D are loaded once and
-// reused for every row, so the loads per state byte stay close to the state's own (the state is read and
-// written once; the x value of a row is a broadcast load).  All of the thread's state octets are loaded
-// before any is used.
-template <typename T, typename TY, class F, int N, int PMAX, bool SR, bool DTP>   // head_dim <= PMAX
+// Grid: each block takes RPB = max(RB, R) consecutive rows of one (batch entry, head) (R = 128 / (N/8)
+// rows per pass).  Thread t owns octet q = t % (N/8) of rows p0 + t / (N/8) + R k: the group's B and C
+// octet and the head's dt, A, D are loaded once and reused for every row, so the loads per state byte
+// stay close to the state's own (the state is read and written once; the x value of a row is a
+// broadcast load).  All of the thread's state octets are loaded before any is used.
+template <typename T, typename TY, class F, int N, int RB, bool SR, bool DTP, bool HAS_STATE>
 __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     uint16_t* __restrict__ state, const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm,
     const T* __restrict__ Cm, int64_t bcs, const T* __restrict__ dt, const float* __restrict__ A,
@@ -139,26 +44,31 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     int rounds) {
     constexpr int OPR = N / 8;                 // octets per state row
     constexpr int R = kLpThreads / OPR;        // rows per pass
-    constexpr int K = PMAX / R > 0 ? PMAX / R : 1;   // passes for head_dim PMAX
+    constexpr int RPB = RB > R ? RB : R;       // rows per block
+    constexpr int K = RPB / R;                 // passes
+    const int nsplit = (P + RPB - 1) / RPB;    // blocks per head
     const int64_t per_b = static_cast<int64_t>(H) * P * OPR;
     u32x4* st = reinterpret_cast<u32x4*>(state);
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x / nsplit;
+    const int p0 = static_cast<int>(blockIdx.x - bh * nsplit) * RPB;   // the block's first row
     const int64_t b = bh / H;
     const int h = static_cast<int>(bh - b * H);
     const int g = h / hpg;
-    const int q = static_cast<int>(threadIdx.x) % OPR, rr = static_cast<int>(threadIdx.x) / OPR;
+    const int q = static_cast<int>(threadIdx.x) % OPR, rr = p0 + static_cast<int>(threadIdx.x) / OPR;
     const int64_t slot = slot_idx ? seq_slot(slot_idx, b, nslots) : b;
+    const bool pad = slot < 0;
     // this thread's octets: rows rr + R k (< P); octet index in the state array or pool (-1: padding)
     const int64_t so0 = slot >= 0 ? slot * per_b + (static_cast<int64_t>(h) * P + rr) * OPR + q : -1;
     auto so_of = [&](int k) { return (so0 >= 0 && rr + R * k < P) ? so0 + static_cast<int64_t>(k) * R * OPR : -1; };
-    u32x4 raw[K];
+    // x, B and C first, then the state octets in order, all unconditional (rows past P and padding
+    // requests read a valid row and drop it), so that the compiler's wait counts stay exact and the
+    // first octet is computed while the later ones are still in flight
     float xv[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int p = rr + R * k;
-        const int64_t so = so_of(k);
-        raw[k] = so >= 0 ? __builtin_nontemporal_load(st + so) : u32x4{0u, 0u, 0u, 0u};
-        xv[k] = p < P ? static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + p]) : 0.f;
+        const float v = static_cast<float>(x[b * xs + static_cast<int64_t>(h) * P + (p < P ? p : P - 1)]);
+        xv[k] = p < P ? v : 0.f;
     }
     const float dtv = DTP ? dt_prologue(static_cast<float>(dt[bh]), dtp, h) : static_cast<float>(dt[bh]);
     const float a = __expf(dtv * A[h]);
@@ -167,10 +77,22 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
     float bv[8], cv[8];
     load8_f32(Bm + bo, bv);
     load8_f32(Cm + bo, cv);
+    const int64_t sl0 = (pad ? 0 : slot) * per_b + static_cast<int64_t>(h) * P * OPR + q;   // row 0, octet q
+    u32x4 raw[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int p = rr + R * k;
-        if (R * k >= P) break;                 // no row of this pass exists (uniform)
+        if constexpr (HAS_STATE) {
+            raw[k] = __builtin_nontemporal_load(st + sl0 + static_cast<int64_t>(p < P ? p : P - 1) * OPR);
+            if (pad) raw[k] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            raw[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int p = rr + R * k;
+        if (p0 + R * k >= P) break;            // no row of this pass exists (uniform)
         const bool ok = p < P;
         const float dx = dtv * xv[k];
         float part = 0.f, v[8];
@@ -214,7 +136,11 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
 template <typename T, typename TY, class F, int N>
 static hipError_t lp_launch(const LpUpdateArgs& a, hipStream_t s) {
     const UpdateArgs& u = a.u;
-    const int64_t blocks = u.batch * u.nheads;
+    // a block takes kLpRows rows of a head (at least one pass); 32 rows at P = 64, N = 128 measured
+    // faster than a whole head per block
+    constexpr int R = kLpThreads / (N / 8);
+    constexpr int RPB = kLpRows > R ? kLpRows : R;
+    const int64_t blocks = u.batch * u.nheads * ((u.head_dim + RPB - 1) / RPB);
     if (blocks == 0) return hipSuccess;
     const bool dtp = u.dtp.bias || u.dtp.softplus || u.dtp.lo < u.dtp.hi;
     auto go = [&](auto kern) {
@@ -225,15 +151,13 @@ static hipError_t lp_launch(const LpUpdateArgs& a, hipStream_t s) {
                            u.nheads / u.ngroups, u.slot_idx, u.nslots, u.dtp, a.seed, a.offset, a.rounds);
         return hipGetLastError();
     };
-    auto pick = [&](auto pmax) {
-        constexpr int PM = decltype(pmax)::value;
-        if (a.rounds > 0)
-            return dtp ? go(state_update_lp_kernel<T, TY, F, N, PM, true, true>)
-                       : go(state_update_lp_kernel<T, TY, F, N, PM, true, false>);
-        return dtp ? go(state_update_lp_kernel<T, TY, F, N, PM, false, true>)
-                   : go(state_update_lp_kernel<T, TY, F, N, PM, false, false>);
-    };
-    return u.head_dim <= 64 ? pick(std::integral_constant<int, 64>{}) : pick(std::integral_constant<int, 128>{});
+    if (!a.state)   // no pool (every request is padding): y from zero states, nothing stored
+        return go(state_update_lp_kernel<T, TY, F, N, kLpRows, false, true, false>);
+    if (a.rounds > 0)
+        return dtp ? go(state_update_lp_kernel<T, TY, F, N, kLpRows, true, true, true>)
+                   : go(state_update_lp_kernel<T, TY, F, N, kLpRows, true, false, true>);
+    return dtp ? go(state_update_lp_kernel<T, TY, F, N, kLpRows, false, true, true>)
+               : go(state_update_lp_kernel<T, TY, F, N, kLpRows, false, false, true>);
 }
 
 template <typename T, typename TY, class F>

@@ -25,7 +25,7 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
            "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
            "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc",
-           "ssd_conv_chunk_scan"]
+           "ssd_conv_chunk_scan", "ssd_chunk_scan_lp", "ssd_chunk_scan_varlen_lp"]
 
 
 class SsdDims(ctypes.Structure):
@@ -101,12 +101,18 @@ def _lib():
                                                  _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
         lib.ssd_state_update_lp.argtypes = [_PD, _VP, _I32, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
                                             _PDT, ctypes.POINTER(SsdSrParams), _VP, _VP]
+        _PSR = ctypes.POINTER(SsdSrParams)
+        lib.ssd_chunk_scan_lp.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP,
+                                          _I32, _PSR, _VP, _VP, ctypes.c_size_t, _VP]
+        lib.ssd_chunk_scan_varlen_lp.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP,
+                                                 _VP, _VP, _VP, _I32, _I64, _PSR, _VP, _VP, ctypes.c_size_t, _VP]
         for f in ("ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_scan", "ssd_state_update",
                   "ssd_conv1d_fwd_varlen", "ssd_conv1d_update_slots", "ssd_chunk_scan_varlen",
                   "ssd_state_update_slots", "ssd_state_update_multi", "ssd_conv1d_update_multi",
                   "ssd_accept_states", "ssd_state_update_lp", "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm",
                   "ssd_decode_step", "ssd_state_update_accept", "ssd_conv1d_update_accept",
-                  "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc", "ssd_conv_chunk_scan"):
+                  "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc", "ssd_conv_chunk_scan",
+                  "ssd_chunk_scan_lp", "ssd_chunk_scan_varlen_lp"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -375,7 +381,7 @@ def ssd_chunk_scan_noalloc(x, B, C, dt, A, D, init_state, final_state, y, chunk=
     return y
 
 
-def _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias):
+def _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias, state_dtype=torch.float32):
     """Checks the batched scan's tensors; returns (device, dims, x row stride, B/C row stride)."""
     dev = _device(x, "x")
     Bt, L, H, P = x.shape
@@ -392,8 +398,8 @@ def _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias):
         raise ValueError("B and C must share a token stride")
     _need(dt, "dt", dev, (Bt, L, H), x.dtype)
     _head_params(dev, H, A, D)
-    _need(init_state, "init_state", dev, (Bt, H, P, N), torch.float32, optional=True)
-    _need(final_state, "final_state", dev, (Bt, H, P, N), torch.float32, optional=True)
+    _need(init_state, "init_state", dev, (Bt, H, P, N), state_dtype, optional=True)
+    _need(final_state, "final_state", dev, (Bt, H, P, N), state_dtype, optional=True)
     _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
     _need(y, "y", dev, (Bt, L, H, P))
     d = _dims(Bt, L, H, P, G, N, x.dtype, y.dtype)
@@ -509,17 +515,10 @@ def ssd_conv1d_update_slots(xbc, w, bias, conv_state_pool, slot_idx, out=None, n
     return out
 
 
-def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None,
-                          has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None,
-                          dt_bias=None, dt_softplus=False, dt_limit=None, snapshot_pool=None, snapshot_table=None,
-                          snapshot_interval=None):
-    """SSD chunked scan of a packed batch.  x [T, H, P], B/C [T, G, N] (token rows may be strided,
-    e.g. views into the varlen conv output), dt [T, H], A [H] fp32, D [H] fp32|None,
-    cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, state_pool
-    [nslots, H, P, N] fp32|None, updated in place.  With snapshot_table [S, max_snaps] int32 the
-    state after every snapshot_interval tokens of sequence s goes to snapshot_pool
-    [nsnap_slots, H, P, N] fp32 slot snapshot_table[s, k] (ssd_chunk_scan_varlen_snapshots).
-    Returns y [T, H, P] in y_dtype (default x's)."""
+def _varlen_args(x, B, C, dt, A, D, cu_seqlens, state_pool, slot_idx, has_initial_state, y, y_dtype, workspace,
+                 dt_bias, state_dtype):
+    """Checks the packed scan's tensors; returns (device, dims, x row stride, B/C row stride, the
+    three sequence tables, y, workspace bytes, nslots, S)."""
     dev = _device(x, "x")
     T, H, P = x.shape
     _need(B, "B", dev, dtype=x.dtype, contiguous=False)
@@ -539,13 +538,13 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     _need(dt, "dt", dev, (T, H), x.dtype)
     _head_params(dev, H, A, D)
     _need(dt_bias, "dt_bias", dev, (H,), torch.float32, optional=True)
-    _need(state_pool, "state_pool", dev, dtype=torch.float32, optional=True)
+    _need(state_pool, "state_pool", dev, dtype=state_dtype, optional=True)
     _need(slot_idx, "slot_idx", dev, optional=True)
     _need(has_initial_state, "has_initial_state", dev, optional=True)
     nslots = 0
     if state_pool is not None:
-        if state_pool.shape[1:] != (H, P, N) or state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
-            raise ValueError("state_pool must be contiguous fp32 [nslots, H, P, N]")
+        if state_pool.dim() != 4 or state_pool.shape[1:] != (H, P, N) or not state_pool.is_contiguous():
+            raise ValueError("state_pool must be contiguous [nslots, H, P, N]")
         nslots = state_pool.shape[0]
     ydt = y_dtype or x.dtype
     if y is None:
@@ -555,10 +554,29 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     d = _dims(S, T, H, P, G, N, x.dtype, y.dtype)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     xs, bcs = (P * H, G * N) if T == 0 else (x.stride(0), B.stride(0))
-    if T == 0:
-        x = B = C = dt = None
     tabs = (_ptr(_table(cu_seqlens, S + 1, "cu_seqlens")), _ptr(_table(slot_idx, S, "slot_idx")),
             _ptr(_table(has_initial_state, S, "has_initial_state")))
+    return dev, d, xs, bcs, tabs, y, ws, nslots, S
+
+
+def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None,
+                          has_initial_state=None, y=None, chunk=128, y_dtype=None, workspace=None, stream=None,
+                          dt_bias=None, dt_softplus=False, dt_limit=None, snapshot_pool=None, snapshot_table=None,
+                          snapshot_interval=None):
+    """SSD chunked scan of a packed batch.  x [T, H, P], B/C [T, G, N] (token rows may be strided,
+    e.g. views into the varlen conv output), dt [T, H], A [H] fp32, D [H] fp32|None,
+    cu_seqlens [S + 1] int32, slot_idx / has_initial_state [S] int32|None, state_pool
+    [nslots, H, P, N] fp32|None, updated in place.  With snapshot_table [S, max_snaps] int32 the
+    state after every snapshot_interval tokens of sequence s goes to snapshot_pool
+    [nsnap_slots, H, P, N] fp32 slot snapshot_table[s, k] (ssd_chunk_scan_varlen_snapshots).
+    Returns y [T, H, P] in y_dtype (default x's)."""
+    dev, d, xs, bcs, tabs, y, ws, nslots, S = _varlen_args(x, B, C, dt, A, D, cu_seqlens, state_pool, slot_idx,
+                                                           has_initial_state, y, y_dtype, workspace, dt_bias,
+                                                           torch.float32)
+    T, H, P = x.shape
+    N = B.shape[2]
+    if T == 0:
+        x = B = C = dt = None
     if snapshot_table is None:
         _check(_lib().ssd_chunk_scan_varlen(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
                                             _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), *tabs,
@@ -568,7 +586,7 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     if snapshot_interval is None:
         raise ValueError("snapshot_table needs snapshot_interval")
     if (snapshot_table.dim() != 2 or snapshot_table.shape[0] != S or snapshot_table.dtype != torch.int32
-            or not snapshot_table.is_contiguous() or snapshot_table.device != x.device):
+            or not snapshot_table.is_contiguous() or snapshot_table.device != y.device):
         raise ValueError("snapshot_table must be contiguous int32 [S, max_snaps] on the scan's device")
     if snapshot_interval <= 0:
         raise ValueError("snapshot_interval must be positive")
@@ -821,6 +839,62 @@ def ssd_state_update_lp(state, x, B, C, dt, A, D=None, slot_idx=None, sr=None, y
 
 
 # --------------------------------------------------------------------------- one-launch decode step
+def _sr_params(sr):
+    return None if sr is None else ctypes.byref(SsdSrParams(int(sr[0]), int(sr[1]), int(sr[2])))
+
+
+def _states16_dtype(*states):
+    dts = {t.dtype for t in states if t is not None}
+    if len(dts) > 1 or not dts <= set(_STATE_DT):
+        raise ValueError("16-bit states must all be float16 or all bfloat16")
+    return dts.pop() if dts else torch.float16
+
+
+def ssd_chunk_scan_lp(x, B, C, dt, A, D=None, init_state=None, final_state=None, sr=None, y=None, chunk=128,
+                      y_dtype=None, workspace=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
+    """ssd_chunk_scan with 16-bit states: init_state / final_state [B, H, P, N] float16 or bfloat16
+    codes (one dtype; may be the same tensor), read exactly; the final state is rounded to nearest
+    even, or stochastically with sr = (seed, offset, rounds) (Philox4x32, as ssd_state_update_lp).
+    The other arguments as ssd_chunk_scan.  Returns y."""
+    sdt = _states16_dtype(init_state, final_state)
+    ydt = y_dtype or x.dtype
+    if y is None:
+        y = torch.empty(x.shape, dtype=ydt, device=x.device)
+    dev, d, xs, bcs = _scan_args(x, B, C, dt, A, D, init_state, final_state, y, dt_bias, sdt)
+    if workspace is None:
+        n = int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+    elif workspace is False:
+        workspace = None
+    _need(workspace, "workspace", dev, optional=True)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if x.shape[1] == 0:
+        x = B = C = dt = None
+    _check(_lib().ssd_chunk_scan_lp(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt), _ptr(A),
+                                    _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), _ptr(init_state),
+                                    _ptr(final_state), _STATE_DT[sdt], _sr_params(sr), _ptr(y), _ptr(workspace), ws,
+                                    _stream(stream)), "ssd_chunk_scan_lp")
+    return y
+
+
+def ssd_chunk_scan_varlen_lp(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_idx=None, has_initial_state=None,
+                             sr=None, y=None, chunk=128, y_dtype=None, stream=None, dt_bias=None, dt_softplus=False,
+                             dt_limit=None):
+    """ssd_chunk_scan_varlen on a 16-bit state pool [nslots, H, P, N] (float16 or bfloat16 codes,
+    updated in place): initial states read exactly, final states rounded as ssd_chunk_scan_lp.
+    Returns y [T, H, P]."""
+    sdt = _states16_dtype(state_pool)
+    dev, d, xs, bcs, tabs, y, ws, nslots, S = _varlen_args(x, B, C, dt, A, D, cu_seqlens, state_pool, slot_idx,
+                                                           has_initial_state, y, y_dtype, None, dt_bias, sdt)
+    if x.shape[0] == 0:
+        x = B = C = dt = None
+    _check(_lib().ssd_chunk_scan_varlen_lp(ctypes.byref(d), chunk, _ptr(x), xs, _ptr(B), _ptr(C), bcs, _ptr(dt),
+                                           _ptr(A), _ptr(D), _dt_params(dt_bias, dt_softplus, dt_limit), *tabs,
+                                           _ptr(state_pool), _STATE_DT[sdt], nslots, _sr_params(sr), _ptr(y), None, 0,
+                                           _stream(stream)), "ssd_chunk_scan_varlen_lp")
+    return y
+
+
 def ssd_decode_step(xbc, w, bias, conv_state_in, conv_state_out, state, dt, A, D=None, nheads=None, head_dim=None,
                     ngroups=None, y=None, y_dtype=None, stream=None, dt_bias=None, dt_softplus=False, dt_limit=None):
     """Conv update + state update in one launch.  xbc [B, CD] (rows may be strided); conv_state_in

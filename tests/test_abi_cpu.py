@@ -267,6 +267,36 @@ def test_lowprec_state_validation(ssd, lib):
     assert upd(dims(ssd, batch=2, seqlen=1, d_state=24)) == E["SSD_ERR_UNSUPPORTED"]
 
 
+def test_scan_lp_validation(ssd, lib):
+    """The scans on 16-bit states reject a bad state dtype, bad rounding parameters and misaligned
+    code arrays before any launch; the scans' own checks still apply."""
+    E = {n: i for i, n in enumerate(ssd.STATUS)}
+    d = dims(ssd, batch=2, seqlen=300)
+
+    def sc(dd=d, init=fp(8), fin=fp(9), sdt=1, sr=None, x=fp(1)):
+        return lib.ssd_chunk_scan_lp(ctypes.byref(dd), 128, x, 256, fp(2), fp(3), 256, fp(4), fp(5), None, None,
+                                     init, fin, sdt, sr, fp(6), None, 0, None)
+    assert sc(sdt=0) == E["SSD_ERR_DTYPE"]                  # fp32 is not a 16-bit state
+    assert sc(sdt=5) == E["SSD_ERR_DTYPE"]
+    assert sc(sr=ctypes.byref(ssd.SsdSrParams(1, 2, 0))) == E["SSD_ERR_UNSUPPORTED"]
+    assert sc(sr=ctypes.byref(ssd.SsdSrParams(1, 2, 17))) == E["SSD_ERR_UNSUPPORTED"]
+    assert sc(init=ctypes.c_void_p(P0 + 8)) == E["SSD_ERR_ALIGN"]
+    assert sc(fin=ctypes.c_void_p(P0 + 2)) == E["SSD_ERR_ALIGN"]
+    assert sc(x=None) == E["SSD_ERR_NULL"]
+    assert sc(dims(ssd, batch=2, seqlen=300, head_dim=48)) == E["SSD_ERR_UNSUPPORTED"]
+    d3 = dims(ssd, batch=3, seqlen=300)
+
+    def vl(dd=d3, pool=fp(9), nslots=4, sdt=2, sr=None, cu=fp(11)):
+        return lib.ssd_chunk_scan_varlen_lp(ctypes.byref(dd), 128, fp(1), 256, fp(2), fp(3), 256, fp(4), fp(5), None,
+                                            None, cu, None, None, pool, sdt, nslots, sr, fp(6), None, 0, None)
+    assert vl(sdt=3) == E["SSD_ERR_DTYPE"]
+    assert vl(sr=ctypes.byref(ssd.SsdSrParams(1, 2, 0))) == E["SSD_ERR_UNSUPPORTED"]
+    assert vl(pool=ctypes.c_void_p(P0 + 4)) == E["SSD_ERR_ALIGN"]
+    assert vl(pool=None) == E["SSD_ERR_NULL"]
+    assert vl(cu=None) == E["SSD_ERR_NULL"]
+    assert vl(nslots=-1) == E["SSD_ERR_SHAPE"]
+
+
 def test_snapshot_scan_validation(ssd, lib):
     """The snapshot form of the scan rejects a bad interval or a missing buffer before any launch."""
     E = {n: i for i, n in enumerate(ssd.STATUS)}

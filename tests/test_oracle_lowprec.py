@@ -230,3 +230,58 @@ def test_lp_codes_absolute_index_on_a_tiny_pool(orc):
                 want.append(((words[k // 2] >> (16 * (k % 2))) & 0xFFFF) < 0x8000)
         assert up.tolist() == want, fmt
         assert np.array_equal(got[:2], ones[:2])
+
+
+# ----------------------------------------------------------------------------- scans on 16-bit states
+def dyadic_scan_inputs(r, Bt, L, H, P, G, N, fmt, nstate=None):
+    """Inputs on a coarse dyadic grid with A = 0: every product dt*x*B is a multiple of 2^-17 below
+    2^-8 in magnitude and every initial value a code of fmt that is a multiple of 2^-17 below 2, so
+    every partial sum of a scan over a few hundred tokens is exact in fp32 (and in fp64)."""
+    x = r.integers(-16, 17, (Bt, L, H, P)) / 64.0
+    Bm = r.integers(-16, 17, (Bt, L, G, N)) / 64.0
+    Cm = r.integers(-16, 17, (Bt, L, G, N)) / 64.0
+    dt = 2.0 ** -r.integers(3, 6, (Bt, L, H)).astype(np.float64)
+    k = r.integers(-1024, 1025, (nstate or Bt, H, P, N)) / 1024.0
+    codes = lp.round_state(k.astype(np.float32), fmt)
+    return x, Bm, Cm, dt, codes
+
+
+def test_scan_lp_of_one_token_is_the_a0_update(orc):
+    """The 16-bit scan of one token with A = 0 stores the codes of the pinned A = 0 decode update:
+    same values, same flat element indices, same random numbers."""
+    r = np.random.default_rng(31)
+    Bt, H, P, G, N = 3, 4, 8, 2, 16
+    for fmt in ("f16", "bf16"):
+        x, Bm, Cm, dt, codes = dyadic_scan_inputs(r, Bt, 1, H, P, G, N, fmt)
+        A = np.zeros(H)
+        for sr in (None, (0xC0FFEE, 17, 5), (3, 2 ** 33 + 1, 7)):
+            _, fin, got = orc.scan_lp(x, Bm, Cm, dt, A, None, codes, fmt, sr)
+            want = orc.state_update_lp_codes_a0(codes, fmt, None, x[:, 0], Bm[:, 0], Cm[:, 0], dt[:, 0], sr)
+            assert np.array_equal(got, want), (fmt, sr)
+            assert np.array_equal(fin.astype(np.float32).astype(np.float64), fin)   # exact in fp32
+        # no tokens: the final state is the initial one, stored unchanged
+        _, _, same = orc.scan_lp(x[:, :0], Bm[:, :0], Cm[:, :0], dt[:, :0], A, None, codes, fmt, (9, 9, 5))
+        assert np.array_equal(same, codes), fmt
+
+
+def test_scan_varlen_lp_rounds_at_the_slot_index(orc):
+    """Packed one-token sequences into pool slots: the codes of the A = 0 update at the same slots;
+    a sequence without an initial state starts from zeros; padding and unnamed slots keep their
+    codes."""
+    r = np.random.default_rng(32)
+    H, P, G, N, nslots = 2, 8, 1, 16, 7
+    slot = np.array([5, 0, -1, 3, 6])
+    has_init = np.array([1, 1, 1, 0, 1])
+    S = len(slot)
+    for fmt in ("f16", "bf16"):
+        x, Bm, Cm, dt, codes = dyadic_scan_inputs(r, S, 1, H, P, G, N, fmt, nstate=nslots)
+        cu = np.arange(S + 1)
+        sr = (0xABCDEF, 5, 5)
+        _, got = orc.scan_varlen_lp(x[:, 0], Bm[:, 0], Cm[:, 0], dt[:, 0], np.zeros(H), None, cu, codes, fmt, slot,
+                                    has_init, sr)
+        start = codes.copy()
+        start[3] = lp.round_state(np.zeros((H, P, N), np.float32), fmt)      # sequence 3 starts from zeros
+        want = orc.state_update_lp_codes_a0(start, fmt, slot, x[:, 0], Bm[:, 0], Cm[:, 0], dt[:, 0], sr)
+        assert np.array_equal(got, want), fmt
+        for k in (1, 2, 4):                                                  # no sequence names these
+            assert np.array_equal(got[k], codes[k]), (fmt, k)
