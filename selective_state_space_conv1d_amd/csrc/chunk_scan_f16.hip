@@ -817,8 +817,10 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 // Hs[u][4q + r] = H[p = 32pt + c32][n = 32(2SN + tt) + 8q + 4hf + r] in units of 2^sH (sH of the last chunk
 // processed; 0 for the initial state).  Its B'^T operands come straight from the pre-pass in registers,
 // one chunk ahead: each token step's pair is reloaded with the next chunk's right after its MFMAs.
-template <int SN, bool CONV>
-__device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
+// LP: the initial and final states are 16-bit codes (a separate instantiation, so that the fp32
+// kernel carries none of the rounding code)
+template <int SN, bool CONV, bool LP>
+__device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
     const LaneOff lo(lane);
@@ -833,8 +835,11 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
-            if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
-            else if (a.init16) v4 = codes_load4(a.init16, a.codes.f16, sbase + p_of(u) * NS + n_of(u, q));
+            if constexpr (LP) {
+                if (a.init16) v4 = codes_load4(a.init16, a.codes.f16, sbase + p_of(u) * NS + n_of(u, q));
+            } else {
+                if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 Hs[u][4 * q + r] = v4[r];
@@ -881,8 +886,14 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 const f32x4 v = {ldexp_f(Hs[u][4 * q], sh), ldexp_f(Hs[u][4 * q + 1], sh),
                                  ldexp_f(Hs[u][4 * q + 2], sh), ldexp_f(Hs[u][4 * q + 3], sh)};
                 const int64_t e = sbase + p_of(u) * NS + n_of(u, q);
-                if (a.final16) codes_store4(a.final16, a.codes, e, v);
-                else *reinterpret_cast<f32x4*>(a.final_state + e) = v;
+                if constexpr (LP) {
+                    // one quad at a time: interleaving the Philox blocks of all 16 quads spills
+                    __builtin_amdgcn_sched_barrier(0);
+                    codes_store4(a.final16, a.codes, e, v);
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    *reinterpret_cast<f32x4*>(a.final_state + e) = v;
+                }
             }
     };
     __syncthreads();                                 // prologue 1
@@ -953,12 +964,17 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
         }
         if (c + 1 < cx.nchunks) {
             write_h(buf ^ 1, sh, v.eHn);
-        } else if (a.final_state || a.final16) {
+        } else if (!LP && a.final_state) {
             store_state(sh);
         }
         __syncthreads();                             // chunk c + 1
     }
-    if (cx.nchunks == 0 && (a.final_state || a.final16)) store_state(0);   // no tokens: the final state is the initial one
+    if constexpr (LP) {
+        // after the loop, where its prefetch registers are free for the rounding (sh = 0 without chunks)
+        if (a.final16) store_state(sh);
+    } else {
+        if (cx.nchunks == 0 && a.final_state) store_state(0);   // no tokens: the final state is the initial one
+    }   // no tokens: the final state is the initial one
 }
 
 // ---------------------------------------------------------------------------
@@ -1311,7 +1327,7 @@ __device__ void run_x(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     }
 }
 
-template <typename TY, bool CONV>
+template <typename TY, bool CONV, bool LP>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsView ws, ConvIn cv) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -1342,13 +1358,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
     else if (wave == 1) run_y<TY, 1, CONV>(sm, a, cx, lane);
     else if (wave == 2) run_y<TY, 2, CONV>(sm, a, cx, lane);
     else if (wave == 3) run_y<TY, 3, CONV>(sm, a, cx, lane);
-    else if (wave == 4) run_s<0, CONV>(sm, a, cx, lane);
-    else if (wave == 5) run_s<1, CONV>(sm, a, cx, lane);
+    else if (wave == 4) run_s<0, CONV, LP>(sm, a, cx, lane);
+    else if (wave == 5) run_s<1, CONV, LP>(sm, a, cx, lane);
     else if (wave == 6) run_x<0, CONV>(sm, a, cx, lane);
     else run_x<1, CONV>(sm, a, cx, lane);
 }
 
-template <typename TY, bool CONV>
+template <typename TY, bool CONV, bool LP>
 static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv, hipStream_t s) {
     if (a.batch * a.nheads == 0) return hipSuccess;
     const int64_t nc = (a.seqlen + Q - 1) / Q;
@@ -1364,7 +1380,7 @@ static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv,
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    auto kern = chunk_scan_kernel<TY, CONV>;
+    auto kern = chunk_scan_kernel<TY, CONV, LP>;
     const size_t smem = CONV ? sizeof(Smem) : offsetof(Smem, Xr);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(smem));
@@ -1386,8 +1402,11 @@ size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int n
 
 hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s) {
     const scan16::ConvIn none{};
-    return ydt == Dt::BF16 ? scan16::launch_t<bf16, false>(a, workspace, none, s)
-                           : scan16::launch_t<float, false>(a, workspace, none, s);
+    if (a.init16 || a.final16)
+        return ydt == Dt::BF16 ? scan16::launch_t<bf16, false, true>(a, workspace, none, s)
+                               : scan16::launch_t<float, false, true>(a, workspace, none, s);
+    return ydt == Dt::BF16 ? scan16::launch_t<bf16, false, false>(a, workspace, none, s)
+                           : scan16::launch_t<float, false, false>(a, workspace, none, s);
 }
 
 hipError_t launch_conv_chunk_scan_f16(const ScanArgs& a, Dt ydt, const ConvScanArgs& c, void* workspace,
@@ -1396,8 +1415,8 @@ hipError_t launch_conv_chunk_scan_f16(const ScanArgs& a, Dt ydt, const ConvScanA
                             static_cast<const bf16*>(c.state_in), static_cast<bf16*>(c.state_out),
                             static_cast<const bf16*>(c.xbc), c.xbc_row_stride, c.conv_dim,
                             static_cast<int64_t>(a.nheads) * a.head_dim};
-    return ydt == Dt::BF16 ? scan16::launch_t<bf16, true>(a, workspace, cv, s)
-                           : scan16::launch_t<float, true>(a, workspace, cv, s);
+    return ydt == Dt::BF16 ? scan16::launch_t<bf16, true, false>(a, workspace, cv, s)
+                           : scan16::launch_t<float, true, false>(a, workspace, cv, s);
 }
 
 }  // namespace ssd

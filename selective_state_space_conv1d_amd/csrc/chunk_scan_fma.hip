@@ -32,7 +32,8 @@ struct FmaSmem {
     float wl[kT];
 };
 
-template <typename T, typename TY>
+// LP: the initial and final states are 16-bit codes (a separate instantiation)
+template <typename T, typename TY, bool LP>
 __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     FmaSmem& sm = *reinterpret_cast<FmaSmem*>(smem_raw);
@@ -62,8 +63,11 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
     for (int e = tid; e < P * N; e += kFmaThreads) {
         const int p = e / N, n = e - p * N;
         float v = 0.f;
-        if (use_init && a.init_state) v = a.init_state[sbase + e];
-        else if (use_init && a.init16) v = code_dec(a.init16[sbase + e], a.codes.f16);
+        if constexpr (LP) {
+            if (use_init && a.init16) v = code_dec(a.init16[sbase + e], a.codes.f16);
+        } else {
+            if (use_init && a.init_state) v = a.init_state[sbase + e];
+        }
         sm.H[p][n] = v;
     }
 
@@ -140,10 +144,10 @@ __global__ __launch_bounds__(kFmaThreads) void chunk_scan_fma_kernel(ScanArgs a)
         }
     }
     __syncthreads();
-    if ((a.final_state || a.final16) && write_final)
+    if ((LP ? a.final16 != nullptr : a.final_state != nullptr) && write_final)
         for (int e = tid; e < P * N; e += kFmaThreads) {
             const int p = e / N, n = e - p * N;
-            if (a.final16) codes_store1(a.final16, a.codes, sbase + e, sm.H[p][n]);
+            if constexpr (LP) codes_store1(a.final16, a.codes, sbase + e, sm.H[p][n]);
             else a.final_state[sbase + e] = sm.H[p][n];
         }
 }
@@ -152,7 +156,7 @@ template <typename T, typename TY>
 static hipError_t fma_t(const ScanArgs& a, hipStream_t s) {
     const int64_t blocks = a.batch * a.nheads;
     if (blocks == 0) return hipSuccess;
-    auto kern = chunk_scan_fma_kernel<T, TY>;
+    auto kern = (a.init16 || a.final16) ? chunk_scan_fma_kernel<T, TY, true> : chunk_scan_fma_kernel<T, TY, false>;
     const size_t smem = sizeof(FmaSmem);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));

@@ -561,7 +561,9 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
 // Hs[t][4j + r] = H[p = 32SP + c32][n = 32(SN0 + t) + 8j + 4hf + r].
 constexpr int kSpinMax = 1 << 20;   // iterations of the bounded wait (each ~64 cycles of sleep)
 
-template <int NT, int SP, int SN0, class CX>
+// LP: the initial and final states are 16-bit codes (a separate instantiation, so that the fp32
+// kernel carries none of the rounding code)
+template <int NT, int SP, int SN0, bool LP, class CX>
 __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
     const int hp = 32 * SP + c32;
@@ -580,29 +582,32 @@ __device__ void run_s(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
     // dst = the initial state of sequence s (zeros without one)
     auto load_init = [&](int64_t s, f32x16 (&dst)[NT]) {
         const int64_t sl = cx.slot(s);
-        const bool from = (a.init_state || a.init16) && sl >= 0 && cx.use_init(s);
+        const bool from = (LP ? a.init16 != nullptr : a.init_state != nullptr) && sl >= 0 && cx.use_init(s);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (from && a.init_state) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
-                else if (from) v = codes_load4(a.init16, a.codes.f16, sbase(sl) + hp * NS + n);
+                if constexpr (LP) {
+                    if (from) v = codes_load4(a.init16, a.codes.f16, sbase(sl) + hp * NS + n);
+                } else {
+                    if (from) v = *reinterpret_cast<const f32x4*>(a.init_state + sbase(sl) + hp * NS + n);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[t][4 * j + r] = v[r];
             }
     };
     auto store_final = [&](int64_t s, const f32x16 (&src)[NT]) {   // src as the final state of sequence s
         const int64_t sl = cx.slot(s);
-        if ((!a.final_state && !a.final16) || sl < 0) return;
+        if ((LP ? a.final16 == nullptr : a.final_state == nullptr) || sl < 0) return;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = 32 * (SN0 + t) + 8 * j + 4 * hf;
                 const f32x4 v = {src[t][4 * j], src[t][4 * j + 1], src[t][4 * j + 2], src[t][4 * j + 3]};
-                if (a.final16) codes_store4(a.final16, a.codes, sbase(sl) + hp * NS + n, v);
+                if constexpr (LP) codes_store4(a.final16, a.codes, sbase(sl) + hp * NS + n, v);
                 else *reinterpret_cast<f32x4*>(a.final_state + sbase(sl) + hp * NS + n) = v;
             }
     };
@@ -792,7 +797,7 @@ __device__ int64_t range_start(const ScanArgs& a, int64_t r) {
     return lo;
 }
 
-template <typename TY, bool WALK>
+template <typename TY, bool WALK, bool LP>
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -836,9 +841,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a) {
     else if (wave == 1) run_y<TY, 1>(sm, a, cx, lane);
     else if (wave == 2) run_y<TY, 2>(sm, a, cx, lane);
     else if (wave == 3) run_y<TY, 3>(sm, a, cx, lane);
-    else if (wave == 4) run_s<4, 0, 0>(sm, a, cx, lane);
-    else if (wave == 5) run_s<3, 1, 0>(sm, a, cx, lane);
-    else if (wave == 6) run_s<1, 1, 3>(sm, a, cx, lane);
+    else if (wave == 4) run_s<4, 0, 0, LP>(sm, a, cx, lane);
+    else if (wave == 5) run_s<3, 1, 0, LP>(sm, a, cx, lane);
+    else if (wave == 6) run_s<1, 1, 3, LP>(sm, a, cx, lane);
     else run_l(sm, a, cx, lane);
 }
 
@@ -889,7 +894,10 @@ static hipError_t mfma_t(const ScanArgs& args, hipStream_t s) {
     }();
     a.spin_max = spin_env >= 0 ? spin_env : scan32::kSpinMax;
     const int64_t blocks = a.nranges * a.nheads;
-    auto kern = a.nranges < a.batch ? scan32::chunk_scan_kernel<TY, true> : scan32::chunk_scan_kernel<TY, false>;
+    const bool lp = a.init16 || a.final16;
+    const bool wk = a.nranges < a.batch;
+    auto kern = wk ? (lp ? scan32::chunk_scan_kernel<TY, true, true> : scan32::chunk_scan_kernel<TY, true, false>)
+                   : (lp ? scan32::chunk_scan_kernel<TY, false, true> : scan32::chunk_scan_kernel<TY, false, false>);
     const size_t smem = sizeof(scan32::Smem);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
