@@ -75,13 +75,20 @@ def test_state_update_multi_is_k_single_updates_bitwise(shape):
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("shape", [None] + STRADDLE)
+@pytest.mark.parametrize("shape", [None] + STRADDLE + ["fp32", "fp32_straddle"])
 def test_multi_y_only_form(orc, k, shape):
     """y without intermediate states: for 2 <= k <= 4 the chunk (dual) form, which sums the same value
     in another order -- within the fp32 bar of the oracle and of the sequential form; k = 1 and k > 4
     run the sequential form, bitwise the y of the call with intermediate states (k = 1: the
     single-token update)."""
-    d = WORKLOADS["decode_ultra_b64"].with_(batch=5) if shape is None else LayerDims(shape[0], 1, *shape[1:])
+    if shape is None:
+        d = WORKLOADS["decode_ultra_b64"].with_(batch=5)
+    elif shape == "fp32":                      # fp32 activations: the quads are f32x4, C.B by FMAs
+        d = LayerDims(3, 1, 8, 64, 2, 128, dtype=torch.float32)
+    elif shape == "fp32_straddle":
+        d = LayerDims(5, 1, 3, 16, 1, 16, dtype=torch.float32)
+    else:
+        d = LayerDims(shape[0], 1, *shape[1:])
     s = ssm_inputs(d, k, 415)
     args = (s["init_state"], s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"])
     y_seq, _ = ssd.ssd_state_update_multi(*args, y_dtype=torch.float32)
