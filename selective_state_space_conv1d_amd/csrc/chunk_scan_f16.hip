@@ -367,8 +367,10 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
             vc[k] = u32x4{0, 0, 0, 0};
             if (r < valid) {
                 const int64_t off = (row0 + r) * bcs + static_cast<int64_t>(g) * NS + 8 * cc;
-                vb[k] = *reinterpret_cast<const u32x4*>(Bg + off);
-                vc[k] = *reinterpret_cast<const u32x4*>(Cg + off);
+                // read by this workgroup only: non-temporal (measured 1-3 % faster; the workspace tiles the
+                // scan reads, shared by a group's heads through L2, stay cached: non-temporal there cost 10 %)
+                vb[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bg + off));
+                vc[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + off));
             }
         }
 #pragma unroll
@@ -596,7 +598,8 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
     // XOR-permuted), is read back at the next chunk's start as whole rows and stored after that chunk's
     // C.H: 8 rows per store instead of 32 partial ones, and -- since loads and stores share one vector-
     // memory counter, so that a wait for a load also waits for earlier stores -- after the first wait for
-    // that chunk's loads, which leaves the stores a whole chunk to complete.
+    // that chunk's loads, which leaves the stores a whole chunk to complete.  The stores are non-temporal:
+    // y is written once, and dirty y lines left in the caches cost the next launch their write-back.
     u32x4 yq[4];                                     // lane l: row 8k + l/8, 16-byte piece l%8
     unsigned char* st = sm.stage[IT];
     int yq_valid = 0;                                // valid tokens of the staged chunk
@@ -615,7 +618,8 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 for (int k = 0; k < 4; ++k) {
                     const int r = 8 * k + (lane >> 3);
                     if (32 * IT + r < yq_valid)
-                        *reinterpret_cast<u32x4*>(yq_row + (32 * IT + r) * static_cast<int64_t>(cx.H) * P + 8 * (lane & 7)) = yq[k];
+                        __builtin_nontemporal_store(yq[k], reinterpret_cast<u32x4*>(
+                            yq_row + (32 * IT + r) * static_cast<int64_t>(cx.H) * P + 8 * (lane & 7)));
                 }
             }
         }
@@ -997,7 +1001,7 @@ __device__ __forceinline__ void x_load(XPart<NK>& xr, const Ctx& cx, int c, int 
     for (int k = 0; k < NK; ++k) {
         int r = r0 + 8 * k + (lane >> 3);
         r = r < valid ? r : valid - 1;               // past the end: a real row (zero weights)
-        xr.v[k] = *reinterpret_cast<const u32x4*>(base + r * cx.xs);
+        xr.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + r * cx.xs));   // read once
     }
 }
 

@@ -311,7 +311,8 @@ struct Ctx {
 // When every row is real the lane's part of the address is one of a few offsets
 // precomputed per lane (the key of row 4k + lane/16 depends on lane and k % 4 only;
 // that of row 8k + lane/8 on the lane only), added to a wave-uniform row base.
-template <int RB, int K0, int K1>
+// AUX is the copies' cache policy: 2 (non-temporal) for rows that only this workgroup reads.
+template <int RB, int K0, int K1, int AUX = 0>
 __device__ __forceinline__ void dma_rows(unsigned char* dst, const bf16* src0, int64_t row_stride, int64_t row0,
                                          int r_lo, int valid, int lane) {
     constexpr int RPK = 1024 / RB;                 // rows per copy instruction
@@ -328,7 +329,7 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const bf16* src0, i
         for (int k = K0; k < K1; ++k) {
             const unsigned char* src = g0 + k * RPK * sb + off[k & 3];
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, AUX);
         }
     } else {
 #pragma unroll
@@ -338,7 +339,7 @@ __device__ __forceinline__ void dma_rows(unsigned char* dst, const bf16* src0, i
             const int r = r_lo + row < valid ? row : valid - 1 - r_lo;
             const unsigned char* src = g0 + r * sb + 16 * (cp ^ rkey<RB>(r_lo + row));
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, AUX);
         }
     }
 }
@@ -516,8 +517,8 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
                             lo4[r] = sw[0];
                             hi4[r] = sw[1];
                         }
-                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g) = lo4;
-                        *reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g + 4) = hi4;
+                        __builtin_nontemporal_store(lo4, reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g));
+                        __builtin_nontemporal_store(hi4, reinterpret_cast<u32x4*>(dst + 32 * pt + 16 * g + 4));
                     }
                 }
             }
@@ -547,7 +548,8 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
             for (int k = 0; k < 4; ++k) {
                 const int r = 8 * k + (lane >> 3), ch = lane & 7;
                 const u32x4 o = *reinterpret_cast<const u32x4*>(st + r * kRowX + ((ch ^ ((r >> 1) & 7)) << 4));
-                if (32 * IT + r < valid) *reinterpret_cast<u32x4*>(yrow + (32 * IT + r) * ystr + 8 * ch) = o;
+                if (32 * IT + r < valid)
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(yrow + (32 * IT + r) * ystr + 8 * ch));
             }
         }
         if constexpr (IT == 0) wait_vmem();
@@ -751,7 +753,9 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
         const int v0 = cur.valid();
         const int64_t r0 = cur.first_row();
         load_dt(d0, d1, r0, v0);
-        dma_rows<kRowX, 0, 16>(sm.X[0], xsrc, cx.xs, r0, 0, v0, lane);
+        // the head's x rows are read by this workgroup only, and y is written once: both streamed
+        // (non-temporal), which leaves the caches to the B/C tiles the group's heads share
+        dma_rows<kRowX, 0, 16, 2>(sm.X[0], xsrc, cx.xs, r0, 0, v0, lane);
         dma_rows<kRowB, 0, 32>(sm.B[0], bsrc, cx.bcs, r0, 0, v0, lane);
         build_vec(sm.vec[0], d0, d1, A2, v0, lane, a.dtp, cx.h);
     }
@@ -766,7 +770,7 @@ __device__ void run_l(Smem& sm, const ScanArgs& a, const CX& cx, const int lane)
             const int vn = nx.valid();
             bf16 d0, d1;
             load_dt(d0, d1, r0, vn);
-            dma_rows<kRowX, 0, 16>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
+            dma_rows<kRowX, 0, 16, 2>(sm.X[buf ^ 1], xsrc, cx.xs, r0, 0, vn, lane);
             dma_rows<kRowB, 0, kYB>(sm.B[buf ^ 1], bsrc, cx.bcs, r0, 0, vn, lane);
             build_vec(sm.vec[buf ^ 1], d0, d1, A2, vn, lane, a.dtp, cx.h);
         }

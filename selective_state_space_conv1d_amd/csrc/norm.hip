@@ -19,10 +19,17 @@ __device__ __forceinline__ void load8(const T* p, float (&o)[8]) {
     load16_f32(p, o);
     if constexpr (Vec16<T>::n == 4) load16_f32(p + 4, o + 4);
 }
+// y and z rows held in registers between the passes are read once, and the output is written once:
+// non-temporal (143 -> 139 us on 8192 x 16384, and the launch before it runs faster too)
+template <typename T>
+__device__ __forceinline__ void load8_nt(const T* p, float (&o)[8]) {
+    load16_f32_nt(p, o);
+    if constexpr (Vec16<T>::n == 4) load16_f32_nt(p + 4, o + 4);
+}
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&o)[8]) {
-    store16_f32(p, o);
-    if constexpr (Vec16<T>::n == 4) store16_f32(p + 4, o + 4);
+    store16_f32_nt(p, o);
+    if constexpr (Vec16<T>::n == 4) store16_f32_nt(p + 4, o + 4);
 }
 
 template <typename TY, typename T>
@@ -47,8 +54,8 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const TY* _
         const int c = 8 * threadIdx.x + k * kSpan;
         if (c < gs) {
             float yv[8], zv[8];
-            load8(yr + c, yv);
-            load8(zr + c, zv);
+            load8_nt(yr + c, yv);
+            load8_nt(zr + c, zv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 vh[k][e] = yv[e] * silu_f(zv[e]);
