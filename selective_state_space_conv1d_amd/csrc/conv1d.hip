@@ -51,6 +51,9 @@ __device__ __forceinline__ void conv_rows(const T* __restrict__ xr, int64_t xs, 
         float u[4][V];
 #pragma unroll
         for (int r = 0; r < 4; ++r) load16_f32_nt(xr + (t + r) * xs, u[r]);
+        // keeps the four loads ahead of the rows' arithmetic and stores (left to itself the scheduler
+        // interleaves them, and each row's wait then also waits for the previous row's store)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) step(u[r], t + r);
     }
@@ -95,8 +98,8 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
 
     const T* xb = xbc + b * L * xs;
     float win[3][V];   // inputs at t-3, t-2, t-1
-    float st[4][V];    // incoming state (token tile 0 only)
     if (tile == 0) {
+        float st[4][V];    // incoming state
         if (s_in) {
             float tmp[4 * V];
 #pragma unroll
@@ -130,16 +133,15 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
             const int64_t tau = L - 4 + k;
             if (tau >= 0) {
                 load16_f32(xb + tau * xs + c0, ns[k]);
-            } else {
-                const int j = 4 + static_cast<int>(tau);  // 0..3
+            } else if (s_in) {
+                // old column 4 + tau, read by address (a private array indexed by the run-time column
+                // would live in scratch memory); every read precedes the stores below
+                const T* col = s_in + (b * CD + c0) * 4 + (4 + tau);
 #pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    float s = st[0][v];
-                    if (j == 1) s = st[1][v];
-                    if (j == 2) s = st[2][v];
-                    if (j == 3) s = st[3][v];
-                    ns[k][v] = s;
-                }
+                for (int v = 0; v < V; ++v) ns[k][v] = static_cast<float>(col[4 * v]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) ns[k][v] = 0.f;
             }
         }
         float tmp[4 * V];
@@ -261,44 +263,31 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
         const int64_t ta = start > t0 ? start : t0;
         const int64_t tb = end < t1 ? end : t1;
         if (ta >= tb) continue;
-        // window at row ta: inputs ta-3..ta-1, from the slot's state (or zeros) before the sequence
+        // window at row ta: inputs ta-3..ta-1, from the slot's state (or zeros) before the sequence.
+        // Input row ta-3+k precedes the sequence when k < 3 - d; it is then state column d+1+k.  The
+        // column is read from the pool by address: a private array indexed by the (run-time) column
+        // would live in scratch memory, whose writes cost every thread 96 bytes of HBM traffic.
         float win[3][V];
         {
+            const int64_t d = ta - start;   // rows of the sequence before ta
             const int64_t slot = seq_slot(sv.slot, s, sv.nslots);
             const bool from_state = slot >= 0 && sv.init && sv.init[s] != 0;
-            float st[4][V];
-            if (from_state && ta - start < 3) {
-                float tmp[4 * V];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) load16_f32(pool + (slot * CD + c0) * 4 + q * V, tmp + q * V);
-#pragma unroll
-                for (int v = 0; v < V; ++v)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) st[k][v] = tmp[v * 4 + k];
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-#pragma unroll
-                    for (int v = 0; v < V; ++v) st[k][v] = 0.f;
-            }
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const int64_t tau = ta - 3 + k;   // input row of window slot k
-                if (tau >= start) {
-                    load16_f32(xbc + tau * xs + c0, win[k]);
-                } else {
-                    const int j = 4 + static_cast<int>(tau - start);   // state column 1..3
+                if (d >= 3 - k) {
+                    load16_f32(xbc + (ta - 3 + k) * xs + c0, win[k]);
+                } else if (from_state) {
+                    const T* col = pool + (slot * CD + c0) * 4 + (d + 1 + k);
 #pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        float x = st[1][v];
-                        if (j == 2) x = st[2][v];
-                        if (j == 3) x = st[3][v];
-                        win[k][v] = x;
-                    }
+                    for (int v = 0; v < V; ++v) win[k][v] = static_cast<float>(col[4 * v]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) win[k][v] = 0.f;
                 }
             }
         }
         conv_rows<T, V>(xbc + c0, xs, out + c0, CD, ta, tb, wt, bs, win);
+        if (tb == t1) break;   // tile done: no table read for a next sequence
     }
 }
 
@@ -317,38 +306,22 @@ __global__ __launch_bounds__(kConvThreads) void conv_state_varlen_kernel(const T
     int64_t start, end;
     sv.span(s, start, end);
     T* sp = pool + (slot * CD + c0) * 4;
-    float old[4][V];
     const bool from_state = sv.init && sv.init[s] != 0;
-    {
-        float tmp[4 * V];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (from_state) load16_f32(sp + q * V, tmp + q * V);
-            else
-#pragma unroll
-                for (int v = 0; v < V; ++v) tmp[q * V + v] = 0.f;
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) old[k][v] = tmp[v * 4 + k];
-    }
+    // old columns are read by address (a private array indexed by the run-time column would live in
+    // scratch memory), all of them before the new state is stored over them
     float ns[4][V];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int64_t tau = end - 4 + k;
         if (tau >= start) {
             load16_f32(xbc + tau * xs + c0, ns[k]);
-        } else {
-            const int64_t j = 4 + (tau - start);   // old column 0..3 (at least k)
+        } else if (from_state) {
+            const T* col = sp + (4 + (tau - start));   // old column 4 + tau - start (at least k)
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                float x = old[0][v];
-                if (j == 1) x = old[1][v];
-                if (j == 2) x = old[2][v];
-                if (j == 3) x = old[3][v];
-                ns[k][v] = x;
-            }
+            for (int v = 0; v < V; ++v) ns[k][v] = static_cast<float>(col[4 * v]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) ns[k][v] = 0.f;
         }
     }
     float tmp[4 * V];

@@ -165,10 +165,16 @@ def test_scan_varlen_snapshots(orc, case):
 
 
 # --------------------------------------------------------------------------- conv
+# token tiles are 24 rows: in the first layout a tile starts 2 rows into a sequence (row 48), in the
+# second 1 row (row 24) and 0 rows (row 48); the window then takes state columns and input rows
+CONV_LAYOUTS = {"mixed": [3, 0, 1, 2, 40, 31, 33, 65, 4], "tile_offsets": [23, 2, 20, 3, 1, 40, 0, 9, 5]}
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_conv_varlen(orc, dtype):
+@pytest.mark.parametrize("layout", list(CONV_LAYOUTS))
+def test_conv_varlen(orc, dtype, layout):
     d = LayerDims(1, 1, 4, 16, 1, 16, dtype=dtype)      # CD = 96
-    lens = [3, 0, 1, 2, 40, 31, 33, 65, 4]
+    lens = CONV_LAYOUTS[layout]
     T, CD = sum(lens), d.conv_dim
     g = torch.Generator(device="cpu").manual_seed(240)
     xbc = torch.randn(T, CD, generator=g).to(dtype).to(DEV)
