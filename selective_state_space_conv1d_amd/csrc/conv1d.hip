@@ -24,9 +24,9 @@ constexpr int kConvTokens = 24;
 
 // Rows [ta, tb) of one thread's channel vector: out[t] = silu(bias + sum_k w[k] * in[t-3+k]), with
 // win holding the inputs at ta-3..ta-1 on entry.  Four rows are loaded before any is used, so each
-// thread keeps four 16-byte loads in flight.  The input rows are read once (non-temporal loads: 125 -> 113 us
+// thread keeps four 16-byte loads in flight.  STREAM reads the input rows non-temporally (125 -> 113 us
 // on the 1 x 8192 x 18432 prefill); the output, which the scan reads next, stays cacheable.
-template <typename T, int V>
+template <typename T, int V, bool STREAM>
 __device__ __forceinline__ void conv_rows(const T* __restrict__ xr, int64_t xs, T* __restrict__ orow, int64_t os,
                                           int64_t ta, int64_t tb, const float (&wt)[4][V], const float (&bs)[V],
                                           float (&win)[3][V]) {
@@ -50,7 +50,10 @@ __device__ __forceinline__ void conv_rows(const T* __restrict__ xr, int64_t xs, 
     for (; t + 4 <= tb; t += 4) {
         float u[4][V];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) load16_f32_nt(xr + (t + r) * xs, u[r]);
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (STREAM) load16_f32_nt(xr + (t + r) * xs, u[r]);
+            else load16_f32(xr + (t + r) * xs, u[r]);
+        }
         // keeps the four loads ahead of the rows' arithmetic and stores (left to itself the scheduler
         // interleaves them, and each row's wait then also waits for the previous row's store)
         __builtin_amdgcn_sched_barrier(0);
@@ -59,24 +62,43 @@ __device__ __forceinline__ void conv_rows(const T* __restrict__ xr, int64_t xs, 
     }
     for (; t < tb; ++t) {
         float u[V];
-        load16_f32_nt(xr + t * xs, u);
+        if constexpr (STREAM) load16_f32_nt(xr + t * xs, u);
+        else load16_f32(xr + t * xs, u);
         step(u, t);
     }
+}
+
+// Launches of more than kWideGrid workgroups run many rounds on the chip.  There the workgroups are
+// numbered XCD-contiguously (the hardware deals them to the 8 XCDs round-robin; XCD k takes the k-th
+// eighth of the tiles) and the input is read through the caches: a tile's three halo rows are the
+// previous tile's last rows, read on the same XCD shortly before (262144-token prefill: 3905 -> 3541
+// us).  Smaller launches keep the plain numbering and stream the input, which measured faster for them
+// and for the scan that reads their output (1 x 8192: conv 111 -> 110 us, scan after it 221 -> 214 us).
+constexpr int64_t kWideGrid = 16384;
+
+// Workgroup index in [0, n) for the linear dispatch index id: XCD-contiguous when WIDE.
+template <bool WIDE>
+__device__ __forceinline__ int64_t conv_wg_index(int64_t id, int64_t n) {
+    if constexpr (!WIDE) return id;
+    const int64_t per = n / 8, rem = n % 8, xcd = id % 8;
+    return xcd * per + (xcd < rem ? xcd : rem) + id / 8;
 }
 
 // Grid: x = channel blocks * token tiles (channel block fastest), y = batch.
 // The thread of token tile 0 reads the incoming state before it writes the
 // outgoing one, so conv_state_out may alias conv_state_in.
-template <typename T>
+template <typename T, bool WIDE>
 __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
     const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w, const T* __restrict__ bias,
     const T* s_in, T* s_out, T* __restrict__ out, int64_t L, int64_t CD, int64_t cblocks) {
     constexpr int V = Vec16<T>::n;
-    const int64_t cb = blockIdx.x % cblocks;
-    const int64_t tile = blockIdx.x / cblocks;
+    const int64_t nx = gridDim.x;
+    const int64_t wg = conv_wg_index<WIDE>(static_cast<int64_t>(blockIdx.y) * nx + blockIdx.x, nx * gridDim.y);
+    const int64_t cb = wg % nx % cblocks;
+    const int64_t tile = wg % nx / cblocks;
     const int64_t c0 = (cb * kConvThreads + threadIdx.x) * V;
     if (c0 >= CD) return;
-    const int64_t b = blockIdx.y;
+    const int64_t b = wg / nx;
     const int64_t t0 = tile * kConvTokens;
     const int64_t t1 = (t0 + kConvTokens < L) ? t0 + kConvTokens : L;
 
@@ -123,7 +145,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_kernel(
         for (int k = 0; k < 3; ++k) load16_f32(xb + (t0 - 3 + k) * xs + c0, win[k]);
     }
 
-    conv_rows<T, V>(xb + c0, xs, out + b * L * CD + c0, CD, t0, t1, wt, bs, win);
+    conv_rows<T, V, !WIDE>(xb + c0, xs, out + b * L * CD + c0, CD, t0, t1, wt, bs, win);
 
     if (tile == 0 && s_out) {
         // new state column k = input at token L-4+k (from the old state when negative)
@@ -218,13 +240,14 @@ struct SeqView {
     }
 };
 
-template <typename T>
+template <typename T, bool WIDE>
 __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
     const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w, const T* __restrict__ bias,
     const T* pool, T* __restrict__ out, int64_t CD, int64_t cblocks, SeqView sv) {
     constexpr int V = Vec16<T>::n;
-    const int64_t cb = blockIdx.x % cblocks;
-    const int64_t tile = blockIdx.x / cblocks;
+    const int64_t wg = conv_wg_index<WIDE>(blockIdx.x, gridDim.x);
+    const int64_t cb = wg % cblocks;
+    const int64_t tile = wg / cblocks;
     const int64_t c0 = (cb * kConvThreads + threadIdx.x) * V;
     if (c0 >= CD) return;
     const int64_t t0 = tile * kConvTokens;
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_fwd_varlen_kernel(
                 }
             }
         }
-        conv_rows<T, V>(xbc + c0, xs, out + c0, CD, ta, tb, wt, bs, win);
+        conv_rows<T, V, !WIDE>(xbc + c0, xs, out + c0, CD, ta, tb, wt, bs, win);
         if (tb == t1) break;   // tile done: no table read for a next sequence
     }
 }
@@ -342,7 +365,8 @@ static hipError_t conv_fwd_varlen_t(const ConvFwdArgs& a, hipStream_t s) {
     T* pool = static_cast<T*>(a.state_out);
     if (a.seqlen > 0) {
         const int64_t tiles = (a.seqlen + kConvTokens - 1) / kConvTokens;
-        hipLaunchKernelGGL(conv1d_fwd_varlen_kernel<T>, dim3(static_cast<uint32_t>(cblocks * tiles)),
+        auto kern = cblocks * tiles > kWideGrid ? conv1d_fwd_varlen_kernel<T, true> : conv1d_fwd_varlen_kernel<T, false>;
+        hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(cblocks * tiles)),
                            dim3(kConvThreads), 0, s, static_cast<const T*>(a.xbc), a.xbc_row_stride,
                            static_cast<const T*>(a.w), static_cast<const T*>(a.bias), pool,
                            static_cast<T*>(a.out), a.channels, cblocks, sv);
@@ -364,7 +388,8 @@ static hipError_t conv_fwd_t(const ConvFwdArgs& a, hipStream_t s) {
     if (a.batch == 0 || a.channels == 0) return hipSuccess;
     if (a.seqlen == 0 && a.state_out == nullptr) return hipSuccess;
     dim3 grid(static_cast<uint32_t>(cblocks * tiles), static_cast<uint32_t>(a.batch));
-    hipLaunchKernelGGL(conv1d_fwd_kernel<T>, grid, dim3(kConvThreads), 0, s,
+    auto kern = cblocks * tiles * a.batch > kWideGrid ? conv1d_fwd_kernel<T, true> : conv1d_fwd_kernel<T, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(kConvThreads), 0, s,
                        static_cast<const T*>(a.xbc), a.xbc_row_stride, static_cast<const T*>(a.w),
                        static_cast<const T*>(a.bias), static_cast<const T*>(a.state_in),
                        static_cast<T*>(a.state_out), static_cast<T*>(a.out), a.seqlen, a.channels,
