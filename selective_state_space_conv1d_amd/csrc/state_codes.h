@@ -45,15 +45,25 @@ __device__ __forceinline__ void philox4x32(uint32_t (&c)[4], uint32_t k0, uint32
 // 16-bit storage formats: decode to fp32, round-to-nearest-even, stochastic rounding.
 // Stochastic rounding "up (away from zero) iff r16 < 65536 * dropped fraction" equals "add the noise
 // 2^d - 1 - floor(r16 / 2^(16-d)) to the d dropped bits and truncate" (d = 16 for bf16, 13 for fp16's
-// normal range): both carry exactly when floor(r16 / 2^(16-d)) < the dropped bits.  The fast forms
-// (sr_fast) use it; they hold for finite values (bf16) and for 2^-14 <= |v| < 65536 (fp16), and
-// special() flags the values outside that range, which take sr().
+// normal range): both carry exactly when floor(r16 / 2^(16-d)) < the dropped bits.  The noise is the
+// complement's top d bits, (~r16) >> (16 - d).  sr_pair rounds the two values of one Philox word that
+// way (finite values for bf16, 2^-14 <= |v| < 65504 for fp16); special() flags the others, which take
+// sr().
 struct Bf16Fmt {
-    static __device__ __forceinline__ bool special(float v) {
-        return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u;
-    }
-    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
-        return (__float_as_uint(v) + (0xFFFFu - r16)) >> 16;
+    static __device__ __forceinline__ bool special(float v) { return !(fabsf(v) < __builtin_inff()); }
+    // v0 into the low code, v1 into the high one, r16 the low and high halves of word
+    static __device__ __forceinline__ uint32_t sr_pair(float v0, float v1, uint32_t word) {
+        const uint32_t nw = ~word;
+        const uint32_t x0 = __float_as_uint(v0) + (nw & 0xFFFFu);
+        const uint32_t x1 = __float_as_uint(v1) + (nw >> 16);
+        uint32_t r = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        const bool s0 = special(v0), s1 = special(v1);
+        if (__builtin_expect(s0 || s1, 0)) {   // one branch per pair, taken by the lanes that need it
+            const uint32_t c0 = s0 ? sr<true>(v0, word & 0xFFFFu) : (r & 0xFFFFu);
+            const uint32_t c1 = s1 ? sr<true>(v1, word >> 16) : (r >> 16);
+            r = c0 | (c1 << 16);
+        }
+        return r;
     }
     static __device__ __forceinline__ float dec(uint32_t code) { return __uint_as_float(code << 16); }
     static __device__ __forceinline__ uint32_t rne(float v) {
@@ -71,13 +81,26 @@ struct Bf16Fmt {
 };
 
 struct F16Fmt {
-    static __device__ __forceinline__ bool special(float v) {
-        return ((__float_as_uint(v) & 0x7FFFFFFFu) - 0x38800000u) >= (0x47800000u - 0x38800000u);
+    static __device__ __forceinline__ bool special(float v) {   // true for NaN too
+        const float m = fabsf(v);
+        return !(m >= 0x1p-14f && m < 65504.0f);
     }
-    static __device__ __forceinline__ uint32_t sr_fast(float v, uint32_t r16) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t c = ((u & 0x7FFFFFFFu) + (0x1FFFu - (r16 >> 3)) - 0x38000000u) >> 13;
-        return ((u >> 16) & 0x8000u) | c;
+    // The noise goes into the 13 dropped bits of the fp32 pattern (a carry reaches the next code away
+    // from zero, past the top of a binade into the next exponent), and the hardware's pair conversion
+    // with round-toward-zero drops them: one conversion for both values.  Below 65504 the sum stays
+    // under 65536, where that conversion would give the largest finite code instead of infinity.
+    static __device__ __forceinline__ uint32_t sr_pair(float v0, float v1, uint32_t word) {
+        const uint32_t nw = ~word;
+        const float f0 = __uint_as_float(__float_as_uint(v0) + ((nw & 0xFFFFu) >> 3));
+        const float f1 = __uint_as_float(__float_as_uint(v1) + (nw >> 19));
+        uint32_t r = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
+        const bool s0 = special(v0), s1 = special(v1);
+        if (__builtin_expect(s0 || s1, 0)) {   // one branch per pair, taken by the lanes that need it
+            const uint32_t c0 = s0 ? sr<true>(v0, word & 0xFFFFu) : (r & 0xFFFFu);
+            const uint32_t c1 = s1 ? sr<true>(v1, word >> 16) : (r >> 16);
+            r = c0 | (c1 << 16);
+        }
+        return r;
     }
     static __device__ __forceinline__ float dec(uint32_t code) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(code)));

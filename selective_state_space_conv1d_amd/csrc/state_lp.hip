@@ -113,17 +113,10 @@ __global__ __launch_bounds__(kLpThreads) void state_update_lp_kernel(
                 uint32_t c[4] = {static_cast<uint32_t>(o), static_cast<uint32_t>(o >> 32),
                                  static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)};
                 philox4x32(c, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), rounds);
-                // the fast form for every value; the few outside its range (fp16 subnormals, overflow,
-                // inf and NaN) are redone by the full form, in a branch only their lanes take
-                uint32_t hw[8];
+                // the pair form for every value; the few outside its range (fp16 subnormals and values
+                // near overflow, inf and NaN) are redone by the full form, in a branch only their lanes take
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t r16 = (e & 1) ? c[e >> 1] >> 16 : c[e >> 1] & 0xFFFFu;
-                    hw[e] = F::sr_fast(v[e], r16);
-                    if (__builtin_expect(F::special(v[e]), 0)) hw[e] = F::template sr<true>(v[e], r16);
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) rw[w] = hw[2 * w] | (hw[2 * w + 1] << 16);
+                for (int w = 0; w < 4; ++w) rw[w] = F::sr_pair(v[2 * w], v[2 * w + 1], c[w]);
             } else {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) rw[w] = F::rne(v[2 * w]) | (F::rne(v[2 * w + 1]) << 16);
