@@ -89,7 +89,7 @@ __device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(
 //   ex      the chunk's x scale (x = x' 2^ex)
 //   sM      lane-factor exponent of M' = M 2^(ex - eM): M' = (C'.B'^T) 2^sM exp2(cs_i - cs_j) dt_j
 //   eM      y accumulates in units of 2^eM
-//   ew      weighted-x scale: w x = (w' x') 2^ew, wS holding w' = w 2^(ex - ew)
+//   ew      weighted-x scale: w x = (w' x') 2^ew, wS holding w' = w 2^(ex - ew) (in fp16)
 //   sH      the state waves' accumulator units after this chunk (eB + ew)
 //   eHc     units of the fp16 state copy H' this chunk reads; eHn: of the copy it writes
 struct Vec {
@@ -97,7 +97,7 @@ struct Vec {
     float fM[Q];        // off-diagonal column factor exp2(cs_e - cs_j) dt_j, e = last token of j's tile
     float vD[Q];        // diagonal column factor exp2(cs_m - cs_j) dt_j, m = token 15 of j's tile
     float dt[Q];        // dt_j (0 past the chunk's end)
-    float wS[Q];        // exp2(cs_last - cs_j) dt_j 2^(ex - ew) for real tokens, 0 for padding
+    f16 wS[Q];          // exp2(cs_last - cs_j) dt_j 2^(ex - ew) for real tokens, 0 for padding: w' <= 1, in fp16
     float csE[4];       // cs at the end of each 32-token tile
     float csM[4];       // cs at token 15 of each tile
     int diagOK[4];      // the tile's decay range allows the factored diagonal
@@ -122,6 +122,7 @@ struct Smem {
     float cbound[2];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(sizeof(Vec) % 8 == 0, "8-byte reads of the second vector block");
 
 // LDS swizzle: 256-byte rows XOR their 16-byte chunk index with a 4-bit key of the row, 128-byte
 // rows with a 3-bit key (conflict-free row reads of 16 lanes and transpose reads of 32 lanes).
@@ -930,21 +931,21 @@ __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a
         // ragged chunk's end add zero weights (w' = 0 there).  The x operands and weights of step k + 2
         // are read from LDS while step k computes (scheduling barriers keep the reads where they are
         // issued: the compiler would otherwise sink them next to their use).
+        // The weighted x is one packed fp16 product per pair of values, w'_j x'_j rounded once more after
+        // w' itself: both factors are fp16 (|w'| <= 1, |x'| < 2^15), two roundings of 2^-11 each.
         struct Frag {
             f16x8 x0, x1;
-            f32x4 w0, w1;
+            f16x4 w0, w1;
         };
         auto load = [&](Frag& f, int j0) {
             f.x0 = tr_frag<kRowX>(Xt, trW0, trW0, j0);
             f.x1 = tr_frag<kRowX>(Xt, trW1, trW1, j0);
-            f.w0 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 4 * hf]);
-            f.w1 = *reinterpret_cast<const f32x4*>(&v.wS[j0 + 8 + 4 * hf]);
+            f.w0 = *reinterpret_cast<const f16x4*>(&v.wS[j0 + 4 * hf]);
+            f.w1 = *reinterpret_cast<const f16x4*>(&v.wS[j0 + 8 + 4 * hf]);
         };
-        auto wx = [](const f16x8& x, const f32x4& w0, const f32x4& w1) {
-            float e[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) e[s] = static_cast<float>(x[s]) * (s < 4 ? w0[s] : w1[s - 4]);
-            return to_f16x8(e);
+        auto wx = [](const f16x8& x, const f16x4& w0, const f16x4& w1) {
+            const f16x8 w = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+            return x * w;
         };
         Frag f[3];
         load(f[0], 0);
@@ -1139,8 +1140,8 @@ __device__ __forceinline__ void build_vec(const DtRegs& dr, int ex, float maxx, 
     const bool dok = range < 48.f;
     v.vD[j0] = dok ? fexp2(cm - c0) * d0 : 0.f;
     v.vD[j1] = dok ? fexp2(cm - c1) * d1 : 0.f;
-    v.wS[j0] = ldexp_f(w0, ex - ew);
-    v.wS[j1] = ldexp_f(w1, ex - ew);
+    v.wS[j0] = static_cast<f16>(ldexp_f(w0, ex - ew));
+    v.wS[j1] = static_cast<f16>(ldexp_f(w1, ex - ew));
     if ((lane & 15) == 15) {
         v.csE[lane >> 4] = c1;
         v.diagOK[lane >> 4] = dok ? 1 : 0;
