@@ -213,6 +213,8 @@ __device__ __forceinline__ void scale_cols(f32x16& m, float f, float a, std::int
 // per-head dt rows replace 128 scattered 2-byte reads (one cache line each) by one 512-byte read.
 // |C'.B'^T| < N 2^15 2^15 = 2^37, so the fp16 copy with the shift below stays under 2^14.
 constexpr int kCBShift = 23;
+constexpr int kDtHeads = 32;                       // most heads per group whose dt the pre-pass reads as rows
+constexpr int kDtItems = kDtHeads / 8 * Q / 256;   // 16-byte dt loads per thread
 constexpr int kCBBytes = 10 * 2048;
 constexpr int64_t kWsTile = 2 * kTile + kCBBytes;
 struct WsView {
@@ -350,6 +352,23 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t row0 = b * seqlen + c * Q;
     const int valid = static_cast<int>(seqlen - c * Q < Q ? seqlen - c * Q : Q);
+    // dt, read as whole rows with the B and C tiles: item (token j, heads 8q .. 8q + 7 of the group) is one
+    // 16-byte load; tokens past the end read nothing.  Used when the group's heads come in 16-byte pieces (at
+    // most kDtHeads of them), else the per-head loop at the end.
+    const int hpg = nheads / ngroups;
+    const int q8 = hpg >> 3;
+    const bool dt_rows = hpg <= kDtHeads && (hpg & 7) == 0 && (nheads & 7) == 0 &&
+                         (reinterpret_cast<uintptr_t>(dtg) & 15) == 0;
+    u32x4 vdt[kDtItems];
+    if (dt_rows) {
+#pragma unroll
+        for (int k = 0; k < kDtItems; ++k) {
+            const int item = t + 256 * k, j = item / (q8 > 0 ? q8 : 1);
+            vdt[k] = u32x4{0, 0, 0, 0};
+            if (item < Q * q8 && j < valid)
+                vdt[k] = *reinterpret_cast<const u32x4*>(dtg + (row0 + j) * nheads + g * hpg + 8 * (item % q8));
+        }
+    }
     u32x4 vb[8], vc[8];
     // piece k of this thread: row, 16-byte chunk
     auto piece_r = [&](int k) { return CONV ? 8 * (t >> 4) + k : (t + 256 * k) >> 4; };
@@ -449,9 +468,24 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
             dst[64 * h] = to_f16x8(v);
         }
     }
-    // the dt rows of the group's heads: item (head hh, 16-token segment sg)
-    const int hpg = nheads / ngroups;
-    for (int item = t; item < hpg * 8; item += 256) {
+    // the dt rows of the group's heads (each store instruction of a wave writes 64-byte runs of 4 rows); else
+    // item (head hh, 16-token segment sg) read per element
+    if (dt_rows) {
+#pragma unroll
+        for (int k = 0; k < kDtItems; ++k) {
+            const int item = t + 256 * k;
+            if (item < Q * q8) {
+                const int j = item / q8, h0 = 8 * (item % q8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned u = vdt[k][e >> 1];
+                    const float raw = (e & 1) ? bf16_hi(u) : bf16_lo(u);
+                    const int h = g * hpg + h0 + e;
+                    ws.dts[((b * nheads + h) * nchunks + c) * Q + j] = j < valid ? dt_prologue(raw, dtp, h) : 0.f;
+                }
+            }
+        }
+    } else for (int item = t; item < hpg * 8; item += 256) {
         const int hh = item >> 3, sg = item & 7, h = g * hpg + hh;
         float v[16];
 #pragma unroll

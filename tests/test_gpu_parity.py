@@ -171,6 +171,37 @@ def test_scan_bf16_other_shapes(orc, shape, chunk):
     assert_close(fin, fr, BF16_BAR, "final state")
 
 
+@pytest.mark.parametrize("H,G", [(16, 2), (32, 2), (64, 2), (24, 1)])
+@pytest.mark.parametrize("L", [130, 300])
+@pytest.mark.parametrize("prologue", [False, True])
+def test_scan_f16_dt_read_as_rows(orc, H, G, L, prologue):
+    """The fp16 scan's pre-pass reads dt as whole token rows when a group's heads come in 16-byte pieces
+    (8, 16 or 32 heads per group here; 24 per group and a dt view shifted by one element take the
+    per-element path), with a ragged last chunk and, optionally, the dt_bias + softplus + clamp prologue."""
+    d = LayerDims(2, L, H, 64, G, 128)
+    s = cuda(scan_inputs(d, 60 + H + L))
+    kw, dt_eff = {}, f64(s["dt"])
+    if prologue:
+        g = torch.Generator().manual_seed(H + L)
+        bias = (torch.randn(H, generator=g) - 1.0).to("cuda")
+        kw = dict(dt_bias=bias, dt_softplus=True, dt_limit=(0.0, 0.5))
+        dt_eff = orc.dt_prologue(f64(s["dt"]), f64(bias), True, (0.0, 0.5))
+    yr, fr = orc.scan(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), dt_eff, f64(s["A"]), f64(s["D"]),
+                      f64(s["init_state"]))
+    for shift in (False, True):
+        dt = s["dt"]
+        if shift:   # same values, storage offset by one element (2 bytes): not 16-byte aligned
+            buf = torch.empty(dt.numel() + 1, dtype=dt.dtype, device="cuda")
+            dt = buf[1:].view(dt.shape)
+            dt.copy_(s["dt"])
+        fin = torch.empty_like(s["init_state"])
+        y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], dt, s["A"], s["D"], s["init_state"], fin,
+                               y_dtype=torch.float32, **kw)
+        torch.cuda.synchronize()
+        assert_close(y, yr, BF16_BAR, f"y (dt shifted: {shift})")
+        assert_close(fin, fr, BF16_BAR, f"final state (dt shifted: {shift})")
+
+
 @pytest.mark.parametrize("ws", [pytest.param(None, id="f16"), pytest.param(False, id="split")])
 def test_scan_bf16_output_is_rounded_fp32_output(ws):
     d = LayerDims(2, 300, 4, 64, 2, 128)
