@@ -188,9 +188,11 @@ __device__ __forceinline__ f16x8 tr_frag(const unsigned char* t, int b0, int b8,
     return f16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
 }
 
-// Row broadcast (DPP row_newbcast): every lane of each 16-lane row receives lane K of that row.
+// Row broadcast (DPP row_newbcast): every lane of each 16-lane row receives lane K of that row.  Every
+// source lane exists, so bound_ctrl (zero for a missing source) changes nothing; with it and no old value
+// the compiler no longer copies a zero into each slot's register before the broadcast (15 moves per tile).
 template <int K> __device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + K, 0xF, 0xF, true));
 }
 // m[k] = (m[k] * f_k) a, f_k = lane k of this lane's row of f: the column factors of an accumulator
 // whose slot k sits on the key token that lane k of the row holds the factor of
