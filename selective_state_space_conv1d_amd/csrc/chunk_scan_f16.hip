@@ -951,16 +951,18 @@ __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a
         const Vec& v = sm.vec[buf];
         const unsigned char* Xt = sm.X[buf];
         // H <- dec H, re-expressed in this chunk's units 2^sH (a power-of-two change of units)
+        // Units that shrink by more than 2^100 take the change of units per element after the decay, in place.
         const int du = sh - v.sH;
-        if (du <= 100) {
-            const float dec = ldexp_f(v.dec, du);
+        {
+            const float dec = du <= 100 ? ldexp_f(v.dec, du) : v.dec;
 #pragma unroll
             for (int u = 0; u < 4; ++u) Hs[u] *= dec;
-        } else {                                     // the units shrink by more than 2^100
+        }
+        if (du > 100) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Hs[u][e] = ldexp_f(Hs[u][e] * v.dec, du);
+                for (int e = 0; e < 16; ++e) Hs[u][e] = ldexp_f(Hs[u][e], du);
         }
         sh = v.sH;
         // token step k (tokens 16k .. 16k+15): H^T[n][p] += sum_j B'^T[n][j] (w'_j x'_j)[p].  Steps past a
