@@ -208,8 +208,9 @@ __device__ __forceinline__ void scale_cols(f32x16& m, float f, float a, std::int
 //   C   32 KiB  C' in the y waves' register order: token tile t, k step ks, lane l: 16 bytes
 //               C'[32t + l%32][16ks + 8(l/32) + 0..7];
 //   CB  20 KiB  the ten causal 32x32 tiles of (C'.B'^T)^T 2^-kCBShift in fp16 (rows: key tokens j; columns:
-//               tokens i), tile (it, jt) at index it(it+1)/2 + jt; within a tile, accumulator values
-//               8h .. 8h+7 of lane l at 16 (64h + l), so that each 16-byte load of a wave reads 1 KiB in one run;
+//               tokens i), tile (it, jt) at index it(it+1)/2 + jt, the four diagonal tiles zero where j > i;
+//               within a tile, accumulator values 8h .. 8h+7 of lane l at 16 (64h + l), so that each 16-byte
+//               load of a wave reads 1 KiB in one run;
 // then per (batch, head, chunk) the 128 dt values after the dt prologue (fp32, 0 past the sequence end),
 // then the (eB, eC) pairs.  C.B^T is the same for every head of a group, so it is computed here once; the
 // per-head dt rows replace 128 scattered 2-byte reads (one cache line each) by one 512-byte read.
@@ -461,6 +462,11 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             acc = mfma(ld16(lb + 32 * jt * kRowB + lo.row[ks]), ld16(lc + 32 * it * kRowB + lo.row[ks]), acc);
+        if (it == jt) {   // a diagonal tile: zero above the diagonal (key token after the token), the causal mask
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) > (lane & 31)) acc[e] = 0.f;
+        }
         f16x8* dst = reinterpret_cast<f16x8*>(cb + T * 2048) + lane;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -757,10 +763,9 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
                 scale_cols(m, fcol[jt], fexp2(csi - v.csM[jt] + static_cast<float>(sM)),
                            std::make_integer_sequence<int, 16>{});
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const int jj = 32 * jt + 8 * (k >> 2) + 4 * hf + (k & 3);
-                    const float e = jj == i ? m[k] + dx : m[k];
-                    m[k] = jj <= i ? e : 0.f;
+                for (int k = 0; k < 16; ++k) {      // above the diagonal the pre-pass's tile holds zeros, and
+                    const int jj = 32 * jt + 8 * (k >> 2) + 4 * hf + (k & 3);   // both factors are finite there
+                    if (jj == i) m[k] += dx;
                 }
             } else {                 // steep decay inside the tile: per-element exp2
                 const float dx = v.dx;
