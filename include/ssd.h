@@ -326,11 +326,23 @@ ssd_status_t ssd_conv1d_fwd_varlen(const ssd_dims_t* d, const void* xbc, int64_t
  *  state_pool    [nslots, H, P, N] fp32, updated in place: the initial state is read as
  *                has_initial_state says, and the final state is written to every sequence's slot.
  *  y             [T, H, P] contiguous y dtype.
- * chunk, A, D and dt_params as for ssd_chunk_scan; workspace is unused (may be NULL); S and T above 2^31 - 1 are
- * rejected (SSD_ERR_SHAPE).  When sequences x heads exceed what the device holds at once,
- * one workgroup scans a range of consecutive sequences (balanced by tokens): sequence
- * states must then sit in distinct slots, as for any in-place pool update.
+ * chunk, A, D and dt_params as for ssd_chunk_scan; S and T above 2^31 - 1 are rejected (SSD_ERR_SHAPE).
+ *  workspace     optional, 16-byte aligned, at least ssd_chunk_scan_varlen_workspace_size bytes: it selects
+ *                the fp16 scan (bf16 inputs, head_dim 64, d_state 128, chunk 128), one workgroup per
+ *                (sequence, head); a smaller nonzero buffer is SSD_ERR_WORKSPACE.  Without one (NULL or 0
+ *                bytes) the bf16 split-operand kernel runs: when sequences x heads exceed what the device
+ *                holds at once, one of its workgroups scans a range of consecutive sequences (balanced by
+ *                tokens).  Either way sequence states must sit in distinct slots, as for any in-place pool
+ *                update.
  */
+/*
+ * Workspace of the fp16 packed scan (above) for S = d->batch sequences over T = d->seqlen packed rows:
+ * per group and per head, the pre-pass's tiles and dt rows for S + ceil(T / 128) chunk slots (chunk c of
+ * sequence s, whose first row is r, takes slot s + floor(r / 128) + c).  0 where that scan does not apply
+ * (then no workspace is needed).  d may be NULL (returns 0).
+ */
+size_t ssd_chunk_scan_varlen_workspace_size(const ssd_dims_t* d, int32_t chunk);
+
 ssd_status_t ssd_chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const void* x, int64_t x_row_stride,
                                    const void* B, const void* C, int64_t bc_row_stride, const void* dt,
                                    const float* A, const float* D, const ssd_dt_params_t* dt_params,

@@ -333,8 +333,15 @@ __device__ __forceinline__ void conv_state_out(const ConvIn& cv, int64_t b, int6
         uint2{v[0] | (static_cast<unsigned>(v[1]) << 16), v[2] | (static_cast<unsigned>(v[3]) << 16)};
 }
 
+// Packed batches (cu_seqlens): chunk c of sequence s (first row start) takes workspace chunk slot
+// s + floor(start / Q) + c.  floor(a / Q) + ceil(L / Q) <= floor((a + L) / Q) + 1 keeps the slots of distinct
+// (sequence, chunk) pairs distinct, and below S + ceil(T / Q) for any table clamped into [0, T].
+__device__ __forceinline__ int64_t packed_slot0(int64_t s, int64_t start) { return s + start / Q; }
+__host__ __device__ inline int64_t packed_slots(int64_t nseq, int64_t rows) { return nseq + (rows + Q - 1) / Q; }
+
 // ---------------------------------------------------------------------------
-// Pre-pass: one workgroup of 256 threads per (batch, group, chunk).  Thread t holds 16-byte pieces
+// Pre-pass: one workgroup of 256 threads per (batch, group, chunk); packed batches: per (group, chunk slot),
+// the workgroups of unused slots return at once.  Thread t holds 16-byte pieces
 // t + 256k (k < 8) of the B tile and of the C tile (piece i: row i / 16, chunk i % 16); rows past the
 // sequence end are zeros.  The scaled fp16 tiles are staged in LDS, from which the four waves write B'^T
 // (transpose reads) and compute the causal C'.B'^T tiles (wave w: tiles w, w + 4, w + 8).
@@ -343,18 +350,45 @@ __device__ __forceinline__ void conv_state_out(const ConvIn& cv, int64_t b, int6
 template <bool CONV>
 __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16* Cg, int64_t bcs, const bf16* dtg,
                                                       DtParams dtp, int64_t seqlen, int nheads, int ngroups,
-                                                      int64_t nchunks, WsView ws, ConvIn cv) {
+                                                      int64_t nchunks, WsView ws, ConvIn cv, int64_t batch, SeqMap seq) {
     __shared__ __align__(16) unsigned char lb[kTile];
     __shared__ __align__(16) unsigned char lc[kTile];
     __shared__ unsigned wmax[2][4];
     const int64_t id = blockIdx.x;
-    const int64_t c = id % nchunks;
-    const int64_t bg = id / nchunks;
-    const int g = static_cast<int>(bg % ngroups);
-    const int64_t b = bg / ngroups;
+    // batched: id = (b G + g) nchunks + c, rows b seqlen + c Q ..; packed (seqlen = all rows, nchunks = chunk
+    // slots): id = g nchunks + slot, the slot's sequence found by bisection (the slots' first indices
+    // increase with s)
+    int64_t c, b, row0, len;
+    int g;
+    if (seq.cu_seqlens) {
+        g = static_cast<int>(id / nchunks);
+        const int64_t slot = id % nchunks;
+        int64_t lo = 0, hi = batch;                  // the last s with packed_slot0(s) <= slot, in [lo, hi)
+        while (hi - lo > 1) {
+            const int64_t m = (lo + hi) / 2;
+            int64_t st, ln;
+            seq_span(seq.cu_seqlens, m, seqlen, st, ln);
+            if (packed_slot0(m, st) <= slot) lo = m; else hi = m;
+        }
+        b = lo;
+        seq_span(seq.cu_seqlens, b, seqlen, row0, len);
+        c = slot - packed_slot0(b, row0);
+        if (c < 0 || c * Q >= len) return;           // no chunk of any sequence here (uniform: before any barrier)
+        row0 += c * Q;
+    } else {
+        c = id % nchunks;
+        const int64_t bg = id / nchunks;
+        g = static_cast<int>(bg % ngroups);
+        b = bg / ngroups;
+        row0 = b * seqlen + c * Q;
+        len = seqlen;
+    }
+    // the workspace dt row of head h for this chunk
+    auto hrow = [&](int h) {
+        return seq.cu_seqlens ? static_cast<int64_t>(h) * nchunks + id % nchunks : (b * nheads + h) * nchunks + c;
+    };
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int64_t row0 = b * seqlen + c * Q;
-    const int valid = static_cast<int>(seqlen - c * Q < Q ? seqlen - c * Q : Q);
+    const int valid = static_cast<int>(len - c * Q < Q ? len - c * Q : Q);
     // dt, read as whole rows with the B and C tiles: item (token j, heads 8q .. 8q + 7 of the group) is one
     // 16-byte load; tokens past the end read nothing.  Used when the group's heads come in 16-byte pieces (at
     // most kDtHeads of them), else the per-head loop at the end.
@@ -489,7 +523,7 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
                     const unsigned u = vdt[k][e >> 1];
                     const float raw = (e & 1) ? bf16_hi(u) : bf16_lo(u);
                     const int h = g * hpg + h0 + e;
-                    ws.dts[((b * nheads + h) * nchunks + c) * Q + j] = j < valid ? dt_prologue(raw, dtp, h) : 0.f;
+                    ws.dts[hrow(h) * Q + j] = j < valid ? dt_prologue(raw, dtp, h) : 0.f;
                 }
             }
         }
@@ -501,7 +535,7 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
             const int j = 16 * sg + k;
             v[k] = j < valid ? dt_prologue(static_cast<float>(dtg[(row0 + j) * nheads + h]), dtp, h) : 0.f;
         }
-        f32x4* dst = reinterpret_cast<f32x4*>(ws.dts + ((b * nheads + h) * nchunks + c) * Q + 16 * sg);
+        f32x4* dst = reinterpret_cast<f32x4*>(ws.dts + hrow(h) * Q + 16 * sg);
 #pragma unroll
         for (int k = 0; k < 4; ++k) dst[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
     }
@@ -520,7 +554,10 @@ __global__ __launch_bounds__(256) void bc_prep_kernel(const bf16* Bg, const bf16
 // ---------------------------------------------------------------------------
 struct Ctx {
     const bf16* xg; const bf16* dtg;
-    int64_t xs, seqlen, b;
+    int64_t xs, seqlen, b;   // seqlen: this sequence's rows; b: its batch entry (packed: sequence)
+    int64_t rowbase;         // its first token row
+    int64_t sslot;           // its state row in init_state / final_state (packed: pool slot; -1: none)
+    bool use_init;           // it starts from init_state (else from zeros)
     int H, h, grp, nchunks;
     int64_t tile0;      // workspace tile index of this (batch, group)'s chunk 0
     int64_t hrow0;      // workspace dt row of this (batch, head)'s chunk 0
@@ -530,7 +567,7 @@ struct Ctx {
         const int64_t r = seqlen - static_cast<int64_t>(c) * Q;
         return r < Q ? static_cast<int>(r) : Q;
     }
-    __device__ __forceinline__ int64_t row0(int c) const { return b * seqlen + static_cast<int64_t>(c) * Q; }
+    __device__ __forceinline__ int64_t row0(int c) const { return rowbase + static_cast<int64_t>(c) * Q; }
 };
 
 // ---------------------------------------------------------------------------
@@ -868,7 +905,7 @@ __device__ void run_y(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane
 template <int SN, bool CONV, bool LP>
 __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a, const Ctx& cx, const int lane) {
     const int c32 = lane & 31, hf = lane >> 5;
-    const int64_t sbase = (cx.b * cx.H + cx.h) * static_cast<int64_t>(P) * NS;
+    const int64_t sbase = (cx.sslot >= 0 ? cx.sslot * cx.H + cx.h : 0) * static_cast<int64_t>(P) * NS;
     const LaneOff lo(lane);
     const int trW0 = lo.tr<kRowX>(0, 0), trW1 = lo.tr<kRowX>(32, 0);
     // element (u, q) of the state: row p, columns n .. n + 3
@@ -884,7 +921,8 @@ __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a
             if constexpr (LP) {
                 if (a.init16) v4 = codes_load4(a.init16, a.codes.f16, sbase + p_of(u) * NS + n_of(u, q));
             } else {
-                if (a.init_state) v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
+                if (a.init_state && cx.use_init)
+                    v4 = *reinterpret_cast<const f32x4*>(a.init_state + sbase + p_of(u) * NS + n_of(u, q));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1012,7 +1050,7 @@ __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a
         }
         if (c + 1 < cx.nchunks) {
             write_h(buf ^ 1, sh, v.eHn);
-        } else if (!LP && a.final_state) {
+        } else if (!LP && a.final_state && cx.sslot >= 0) {
             store_state(sh);
         }
         __syncthreads();                             // chunk c + 1
@@ -1021,7 +1059,7 @@ __device__ __attribute__((always_inline)) void run_s(Smem& sm, const ScanArgs& a
         // after the loop, where its prefetch registers are free for the rounding (sh = 0 without chunks)
         if (a.final16) store_state(sh);
     } else {
-        if (cx.nchunks == 0 && a.final_state) store_state(0);   // no tokens: the final state is the initial one
+        if (cx.nchunks == 0 && a.final_state && cx.sslot >= 0) store_state(0);   // no tokens: the final state is the initial one
     }   // no tokens: the final state is the initial one
 }
 
@@ -1390,14 +1428,27 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
     cx.xg = static_cast<const bf16*>(a.x);
     cx.dtg = static_cast<const bf16*>(a.dt);
     cx.xs = a.x_row_stride;
-    cx.seqlen = a.seqlen;
     cx.b = id / a.nheads;
     cx.h = static_cast<int>(id % a.nheads);
     cx.H = a.nheads;
     cx.grp = cx.h / (a.nheads / a.ngroups);
-    cx.nchunks = static_cast<int>((a.seqlen + Q - 1) / Q);
-    cx.tile0 = (cx.b * a.ngroups + cx.grp) * static_cast<int64_t>(cx.nchunks);
-    cx.hrow0 = (cx.b * a.nheads + cx.h) * static_cast<int64_t>(cx.nchunks);
+    if (a.seq.cu_seqlens) {      // packed: sequence b's rows, its workspace chunk slots and its pool slot
+        seq_span(a.seq.cu_seqlens, cx.b, a.seqlen, cx.rowbase, cx.seqlen);
+        const int64_t ns = packed_slots(a.batch, a.seqlen), s0 = packed_slot0(cx.b, cx.rowbase);
+        cx.tile0 = cx.grp * ns + s0;
+        cx.hrow0 = cx.h * ns + s0;
+        cx.sslot = seq_slot(a.seq.slot_idx, cx.b, a.seq.nslots);
+        cx.use_init = cx.sslot >= 0 && a.seq.has_init && a.seq.has_init[cx.b] != 0;
+    } else {
+        cx.seqlen = a.seqlen;
+        cx.rowbase = cx.b * a.seqlen;
+        const int64_t nc = (a.seqlen + Q - 1) / Q;
+        cx.tile0 = (cx.b * a.ngroups + cx.grp) * nc;
+        cx.hrow0 = (cx.b * a.nheads + cx.h) * nc;
+        cx.sslot = cx.b;
+        cx.use_init = true;
+    }
+    cx.nchunks = static_cast<int>((cx.seqlen + Q - 1) / Q);
     cx.ws = ws;
     cx.cv = cv;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1415,16 +1466,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
 template <typename TY, bool CONV, bool LP>
 static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv, hipStream_t s) {
     if (a.batch * a.nheads == 0) return hipSuccess;
-    const int64_t nc = (a.seqlen + Q - 1) / Q;
-    const int64_t ntile = a.batch * a.ngroups * nc;
-    const int64_t nhc = a.batch * a.nheads * nc;
+    // chunks per (batch entry, group), or packed: chunk slots per group (one workspace layout, [G][slot])
+    const bool packed = a.seq.cu_seqlens != nullptr;
+    const int64_t nc = packed ? packed_slots(a.batch, a.seqlen) : (a.seqlen + Q - 1) / Q;
+    const int64_t ntile = (packed ? 1 : a.batch) * a.ngroups * nc;
+    const int64_t nhc = (packed ? 1 : a.batch) * a.nheads * nc;
     unsigned char* w = static_cast<unsigned char*>(workspace);
     WsView ws{w, reinterpret_cast<float*>(w + ntile * kWsTile),
               reinterpret_cast<int2*>(w + ntile * kWsTile + nhc * Q * static_cast<int64_t>(sizeof(float))), ntile};
     if (ntile > 0) {
         hipLaunchKernelGGL(bc_prep_kernel<CONV>, dim3(static_cast<uint32_t>(ntile)), dim3(256), 0, s,
                            static_cast<const bf16*>(a.B), static_cast<const bf16*>(a.C), a.bc_row_stride,
-                           static_cast<const bf16*>(a.dt), a.dtp, a.seqlen, a.nheads, a.ngroups, nc, ws, cv);
+                           static_cast<const bf16*>(a.dt), a.dtp, a.seqlen, a.nheads, a.ngroups, nc, ws, cv,
+                           a.batch, a.seq);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1441,6 +1495,11 @@ static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv,
 
 bool f16_scan_supports(int head_dim, int d_state, int chunk) {
     return head_dim == scan16::P && d_state == scan16::NS && chunk == scan16::Q;
+}
+
+size_t f16_scan_varlen_workspace_bytes(int64_t nseq, int64_t rows, int nheads, int ngroups) {
+    const int64_t ns = scan16::packed_slots(nseq, rows);
+    return static_cast<size_t>(scan16::ws_bytes(ngroups * ns, nheads * ns));
 }
 
 size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int ngroups) {

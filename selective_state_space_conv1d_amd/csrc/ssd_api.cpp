@@ -153,6 +153,11 @@ size_t ssd_chunk_scan_workspace_size(const ssd_dims_t* d, int32_t chunk) {
     return ssd::f16_scan_workspace_bytes(d->batch, d->seqlen, d->nheads, d->ngroups);
 }
 
+size_t ssd_chunk_scan_varlen_workspace_size(const ssd_dims_t* d, int32_t chunk) {
+    if (!f16_scan_applies(d, chunk) || d->batch <= 0 || d->seqlen <= 0 || d->ngroups <= 0 || d->nheads <= 0) return 0;
+    return ssd::f16_scan_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads, d->ngroups);
+}
+
 // 16-bit initial / final states of a scan, in place of the fp32 ones
 struct States16 {
     const void* init;
@@ -328,8 +333,12 @@ static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const 
     for (const void* p : {x, B, C, static_cast<const void*>(y)})
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(dt) % elem_size(d->act_dtype)) != 0) return SSD_ERR_ALIGN;
-    (void)workspace;          // the packed scan needs none
-    (void)workspace_bytes;
+    // A workspace selects the fp16 scan (fp32 state pool, no snapshots): it must then be large enough and
+    // 16-byte aligned.  Without one the packed scan runs on the bf16 split-operand kernel.
+    const size_t ws_need = (snap_table || s16) ? 0 : ssd_chunk_scan_varlen_workspace_size(d, chunk);
+    const bool use_f16 = ws_need > 0 && workspace && workspace_bytes > 0;
+    if (use_f16 && workspace_bytes < ws_need) return SSD_ERR_WORKSPACE;
+    if (use_f16 && !aligned16(workspace)) return SSD_ERR_ALIGN;
     if (d->batch > 0 && !tokens && nslots == 0) return SSD_OK;   // nothing to compute or store
     if (!dt_params_ok(dt_params)) return SSD_ERR_ALIGN;
     ssd::ScanArgs a{x, x_row_stride, B, C, bc_row_stride, dt, A, D, state_pool, state_pool, y,
@@ -344,6 +353,7 @@ static ssd_status_t chunk_scan_varlen(const ssd_dims_t* d, int32_t chunk, const 
         a.snap_slots = nsnap_slots;
     }
     const Dt act = static_cast<Dt>(d->act_dtype), ydt = static_cast<Dt>(d->y_dtype);
+    if (use_f16) return hip_status(ssd::launch_chunk_scan_f16(a, ydt, workspace, stream));
     if (act == Dt::BF16 && ssd::mfma_scan_supports(d->head_dim, d->d_state, chunk))
         return hip_status(ssd::launch_chunk_scan_mfma(a, ydt, stream));
     return hip_status(ssd::launch_chunk_scan_fma(a, act, ydt, stream));

@@ -156,6 +156,8 @@ hipError_t launch_chunk_scan_mfma(const ScanArgs& a, Dt ydt, hipStream_t s);
 // (head_dim, d_state, chunk) = (64, 128, 128); workspace of f16_scan_workspace_bytes, 16-byte aligned.
 bool f16_scan_supports(int head_dim, int d_state, int chunk);
 size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int ngroups);
+// packed batches (ScanArgs.seq set): nseq sequences over rows token rows
+size_t f16_scan_varlen_workspace_bytes(int64_t nseq, int64_t rows, int nheads, int ngroups);
 // the device address and size of the current device's static fp16-scan workspace (looked up once per device)
 hipError_t f16_scan_scratch(void** ptr, size_t* bytes);
 hipError_t launch_chunk_scan_f16(const ScanArgs& a, Dt ydt, void* workspace, hipStream_t s);

@@ -25,7 +25,8 @@ EXPORTS = ["ssd_conv_dim", "ssd_conv1d_fwd", "ssd_conv1d_update", "ssd_chunk_sca
            "ssd_state_update_multi", "ssd_conv1d_update_multi", "ssd_accept_states", "ssd_state_update_lp",
            "ssd_chunk_scan_snapshots", "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_state_update_accept",
            "ssd_conv1d_update_accept", "ssd_chunk_scan_varlen_snapshots", "ssd_chunk_scan_noalloc",
-           "ssd_conv_chunk_scan", "ssd_chunk_scan_lp", "ssd_chunk_scan_varlen_lp"]
+           "ssd_conv_chunk_scan", "ssd_chunk_scan_lp", "ssd_chunk_scan_varlen_lp",
+           "ssd_chunk_scan_varlen_workspace_size"]
 
 
 class SsdDims(ctypes.Structure):
@@ -71,6 +72,8 @@ def _lib():
         lib.ssd_conv1d_update.argtypes = [_PD, _VP, _I64, _VP, _VP, _VP, _VP, _VP]
         lib.ssd_chunk_scan_workspace_size.argtypes = [_PD, _I32]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [_PD, _I32]
+        lib.ssd_chunk_scan_varlen_workspace_size.restype = ctypes.c_size_t
         _PDT = ctypes.POINTER(SsdDtParams)
         lib.ssd_chunk_scan.argtypes = [_PD, _I32, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _PDT, _VP, _VP, _VP,
                                        _VP, ctypes.c_size_t, _VP]
@@ -273,6 +276,13 @@ def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, head_dim, ngroups, d_st
                                   act_dtype=torch.bfloat16, y_dtype=torch.bfloat16):
     d = _dims(batch, seqlen, nheads, head_dim, ngroups, d_state, act_dtype, y_dtype)
     return int(_lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), chunk))
+
+
+def ssd_chunk_scan_varlen_workspace_size(nseq, rows, nheads, head_dim, ngroups, d_state, chunk=128,
+                                         act_dtype=torch.bfloat16, y_dtype=torch.bfloat16):
+    """Bytes of the fp16 packed scan's workspace for nseq sequences over rows packed token rows (0: none)."""
+    d = _dims(nseq, rows, nheads, head_dim, ngroups, d_state, act_dtype, y_dtype)
+    return int(_lib().ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), chunk))
 
 
 def ssd_chunk_scan(x, B, C, dt, A, D=None, init_state=None, final_state=None, y=None, chunk=128,
@@ -569,10 +579,20 @@ def ssd_chunk_scan_varlen(x, B, C, dt, A, D, cu_seqlens, state_pool=None, slot_i
     [nslots, H, P, N] fp32|None, updated in place.  With snapshot_table [S, max_snaps] int32 the
     state after every snapshot_interval tokens of sequence s goes to snapshot_pool
     [nsnap_slots, H, P, N] fp32 slot snapshot_table[s, k] (ssd_chunk_scan_varlen_snapshots).
-    Returns y [T, H, P] in y_dtype (default x's)."""
+    workspace: None allocates the one the fp16 scan needs where it applies (ssd_chunk_scan_varlen_workspace_size
+    bytes; no snapshots), a uint8 tensor is used as given, False runs without one (the bf16 split-operand
+    kernel).  Returns y [T, H, P] in y_dtype (default x's)."""
+    allocate = workspace is None and snapshot_table is None
+    if workspace is False:
+        workspace = None
     dev, d, xs, bcs, tabs, y, ws, nslots, S = _varlen_args(x, B, C, dt, A, D, cu_seqlens, state_pool, slot_idx,
                                                            has_initial_state, y, y_dtype, workspace, dt_bias,
                                                            torch.float32)
+    if allocate:
+        n = int(_lib().ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), chunk))
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+            ws = n
     T, H, P = x.shape
     N = B.shape[2]
     if T == 0:

@@ -53,7 +53,7 @@ def test_varlen_ranges_match_one_call_per_sequence(orc, H, S):
     pool0 = torch.randn(nslots, H, 64, 128, device=DEV) * 0.1
     pool = pool0.clone()
     y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], i32(cu), pool, i32(slots),
-                                  i32(has_init), y_dtype=torch.float32)
+                                  i32(has_init), y_dtype=torch.float32, workspace=False)
     # the same sequences, one call each
     pool1 = pool0.clone()
     y1 = torch.empty_like(y)
@@ -61,7 +61,7 @@ def test_varlen_ranges_match_one_call_per_sequence(orc, H, S):
         a, b = int(cu[q]), int(cu[q + 1])
         y1[a:b] = ssd.ssd_chunk_scan_varlen(s["x"][a:b], s["Bm"][a:b], s["Cm"][a:b], s["dt"][a:b], s["A"], s["D"],
                                             i32([0, b - a]), pool1, i32(slots[q:q + 1]), i32(has_init[q:q + 1]),
-                                            y_dtype=torch.float32)
+                                            y_dtype=torch.float32, workspace=False)
     torch.cuda.synchronize()
     assert torch.equal(y, y1), "y differs from the per-sequence calls"
     assert torch.equal(pool, pool1), "state pool differs from the per-sequence calls"
@@ -90,7 +90,7 @@ def test_varlen_range_of_empty_sequences_only():
     pool0 = torch.randn(S, H, 64, 128, device=DEV)
     pool = pool0.clone()
     ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], i32(cu), pool, i32(slots),
-                              i32(has_init))
+                              i32(has_init), workspace=False)
     torch.cuda.synchronize()
     for q in range(S):
         if lens[q] == 0:
@@ -140,13 +140,13 @@ def test_varlen_ranges_without_tables():
     pool0 = torch.randn(S, H, 64, 128, device=DEV)
     pool = pool0.clone()
     y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], i32(cu), pool,
-                                  y_dtype=torch.float32)
+                                  y_dtype=torch.float32, workspace=False)
     pool1 = pool0.clone()
     y1 = torch.empty_like(y)
     for q in range(S):
         a, b = int(cu[q]), int(cu[q + 1])
         y1[a:b] = ssd.ssd_chunk_scan_varlen(s["x"][a:b], s["Bm"][a:b], s["Cm"][a:b], s["dt"][a:b], s["A"], s["D"],
-                                            i32([0, b - a]), pool1[q:q + 1], y_dtype=torch.float32)
+                                            i32([0, b - a]), pool1[q:q + 1], y_dtype=torch.float32, workspace=False)
     torch.cuda.synchronize()
     assert torch.equal(y, y1) and torch.equal(pool, pool1)
     empty = [q for q in range(S) if lens[q] == 0]

@@ -32,16 +32,21 @@ def packed_scan(d, lens, seed, slow=False):
     return {k: v[0].to(DEV) if k in ("x", "Bm", "Cm", "dt") else v.to(DEV) for k, v in s.items() if v is not None}
 
 
-def run_scan_varlen(s, cu, slot, has_init, pool, chunk=128, ydt=torch.float32):
+def run_scan_varlen(s, cu, slot, has_init, pool, chunk=128, ydt=torch.float32, ws=None):
+    """ws None: the default (the fp16 scan where it applies); False: the bf16 split-operand kernel."""
     y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], cu, pool, slot, has_init,
-                                  chunk=chunk, y_dtype=ydt)
+                                  chunk=chunk, y_dtype=ydt, workspace=ws)
     torch.cuda.synchronize()
     return y
 
 
 # --------------------------------------------------------------------------- scan
+WS = [pytest.param(None, id="f16"), pytest.param(False, id="split")]
+
+
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("slow", [False, True])
-def test_scan_varlen_mfma(orc, slow):
+def test_scan_varlen_mfma(orc, slow, ws):
     d = LayerDims(1, 1, 4, 64, 2, 128)
     s = packed_scan(d, LENS, 200 + slow, slow=slow)
     nslots = 12
@@ -50,7 +55,7 @@ def test_scan_varlen_mfma(orc, slow):
     cu, slot, hi = tables(LENS, slots, has_init)
     pool0 = torch.randn(nslots, 4, 64, 128, device=DEV) * 0.1
     pool = pool0.clone()
-    y = run_scan_varlen(s, cu, slot, hi, pool)
+    y = run_scan_varlen(s, cu, slot, hi, pool, ws=ws)
     yr, pr = orc.scan_varlen(f64(s["x"]), f64(s["Bm"]), f64(s["Cm"]), f64(s["dt"]), f64(s["A"]), f64(s["D"]),
                              cu.cpu().numpy(), f64(pool0), np.array(slots), np.array(has_init))
     assert_close(y, yr, BF16_BAR, "y")
@@ -60,7 +65,7 @@ def test_scan_varlen_mfma(orc, slow):
     assert torch.equal(pool[others], pool0[others]), "slots no sequence names must be untouched"
     # bf16 output mode is the RNE of the fp32 output
     pool2 = pool0.clone()
-    y16 = run_scan_varlen(s, cu, slot, hi, pool2, ydt=torch.bfloat16)
+    y16 = run_scan_varlen(s, cu, slot, hi, pool2, ydt=torch.bfloat16, ws=ws)
     assert torch.equal(y16, y.to(torch.bfloat16)) and torch.equal(pool2, pool)
 
 
@@ -80,24 +85,35 @@ def test_scan_varlen_fp32_path(orc):
     assert_close(pool, pr, F32_BAR, "pool")
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("P,N", [(64, 128), (16, 32)])
-def test_scan_varlen_equal_lengths_is_the_batched_scan(P, N):
-    d = LayerDims(3, 300, 4, P, 2, N)
+def test_scan_varlen_equal_lengths_is_the_batched_scan(P, N, ws):
+    d = LayerDims(3, 300, 8, P, 2, N)
     s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 220).items()}
     fin = torch.empty_like(s["init_state"])
-    # the packed scan runs the split-operand kernel of the batched scan: compare with that one
+    # the packed scan runs the batched scan's kernel (fp16 with a workspace, else split-operand): bitwise equal
     yb = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], s["init_state"], fin,
-                            y_dtype=torch.float32, workspace=False)
+                            y_dtype=torch.float32, workspace=ws)
     pool = s["init_state"][[2, 0, 1]].clone()          # sequence b lives in slot perm[b]
     perm = torch.tensor([1, 2, 0], dtype=torch.int32, device=DEV)
     cu = torch.arange(4, dtype=torch.int32, device=DEV) * 300
     flat = lambda t: t.reshape((t.shape[0] * t.shape[1],) + tuple(t.shape[2:]))
     y = ssd.ssd_chunk_scan_varlen(flat(s["x"]), flat(s["Bm"]), flat(s["Cm"]), flat(s["dt"]), s["A"], s["D"],
                                   cu, pool, perm, torch.ones(3, dtype=torch.int32, device=DEV),
-                                  y_dtype=torch.float32)
+                                  y_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(y.reshape(3, 300, 4, P), yb)
+    assert torch.equal(y.reshape(3, 300, 8, P), yb)
     assert torch.equal(pool[perm.long()], fin)
+
+
+def test_scan_varlen_f16_workspace_too_small_is_refused():
+    d = LayerDims(1, 1, 4, 64, 2, 128)
+    s = packed_scan(d, [130, 7], 231)
+    cu, slot, hi = tables([130, 7], [0, 1], [0, 0])
+    pool = torch.zeros(2, 4, 64, 128, device=DEV)
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(Exception, match="WORKSPACE|workspace"):
+        run_scan_varlen(s, cu, slot, hi, pool, ws=small)
 
 
 def test_scan_varlen_no_tokens_copies_or_zeroes_states():
@@ -144,8 +160,8 @@ def test_scan_varlen_snapshots(orc, case):
     y = ssd.ssd_chunk_scan_varlen(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], cu, pool, slot, hi, chunk=chunk,
                                   y_dtype=torch.float32, snapshot_pool=snaps, snapshot_table=tab,
                                   snapshot_interval=iv)
-    pool2 = pool0.clone()
-    y2 = run_scan_varlen(s, cu, slot, hi, pool2, chunk=chunk)
+    pool2 = pool0.clone()     # the snapshot scan runs the split-operand kernel: compare with it without snapshots
+    y2 = run_scan_varlen(s, cu, slot, hi, pool2, chunk=chunk, ws=False)
     assert torch.equal(y, y2) and torch.equal(pool, pool2), "snapshots must not change y or the states"
     hpg = H // G
     heads = list(range(H)) if H <= 4 else [g * hpg + (5 * g) % hpg for g in range(0, G, 3)]
@@ -357,7 +373,8 @@ def test_state_update_and_slots_dt_prologue(orc, opts):
     assert torch.equal(y2, y) and torch.equal(pool[slot.long()], st)
 
 
-def test_scan_varlen_dt_prologue_matches_batched():
+@pytest.mark.parametrize("ws", WS)
+def test_scan_varlen_dt_prologue_matches_batched(ws):
     d = LayerDims(2, 200, 4, 64, 2, 128)
     s = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in scan_inputs(d, 300).items()}
     raw = (torch.randn(2, 200, 4, device=DEV) - 1.0).to(torch.bfloat16)
@@ -365,11 +382,12 @@ def test_scan_varlen_dt_prologue_matches_batched():
     kw = dict(dt_bias=bias, dt_softplus=True, dt_limit=(0.0, 1.0))
     fin = torch.empty_like(s["init_state"])
     yb = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], raw, s["A"], s["D"], s["init_state"], fin,
-                            y_dtype=torch.float32, workspace=False, **kw)
+                            y_dtype=torch.float32, workspace=ws, **kw)
     pool = s["init_state"].clone()
     flat = lambda t: t.reshape((t.shape[0] * t.shape[1],) + tuple(t.shape[2:]))
     cu = torch.tensor([0, 200, 400], dtype=torch.int32, device=DEV)
     y = ssd.ssd_chunk_scan_varlen(flat(s["x"]), flat(s["Bm"]), flat(s["Cm"]), flat(raw), s["A"], s["D"], cu, pool,
-                                  None, torch.ones(2, dtype=torch.int32, device=DEV), y_dtype=torch.float32, **kw)
+                                  None, torch.ones(2, dtype=torch.int32, device=DEV), y_dtype=torch.float32,
+                                  workspace=ws, **kw)
     torch.cuda.synchronize()
     assert torch.equal(y.reshape(2, 200, 4, 64), yb) and torch.equal(pool, fin)
