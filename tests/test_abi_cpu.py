@@ -120,6 +120,22 @@ def test_workspace_size(ssd, lib):
     assert scan(lib, dims(ssd), ws=ctypes.c_void_p(P0 + 8), wsb=need) == E["SSD_ERR_ALIGN"]
 
 
+def test_varlen_workspace_size(ssd, lib):
+    """The fp16 packed scan's workspace: S + ceil(T / 128) chunk slots per group (tiles and scales) and per head
+    (dt rows), S = d->batch sequences over T = d->seqlen packed rows; none where the fp16 scan does not apply."""
+    ws = lib.ssd_chunk_scan_varlen_workspace_size
+    ws.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    ws.restype = ctypes.c_size_t
+    # 24 requests over 8192 rows, 256 heads, 8 groups: 24 + 64 = 88 slots
+    assert ws(ctypes.byref(dims(ssd, batch=24, seqlen=8192, ngroups=8, nheads=256)), 128) == \
+        8 * 88 * (65536 + 20480 + 8) + 256 * 88 * 512
+    assert ws(ctypes.byref(dims(ssd, batch=3, seqlen=300)), 128) == 2 * 6 * 86024 + 4 * 6 * 512   # 3 + 3 slots
+    assert ws(ctypes.byref(dims(ssd, batch=3, seqlen=300)), 256) == 0
+    assert ws(ctypes.byref(dims(ssd, batch=3, seqlen=0)), 128) == 0
+    assert ws(ctypes.byref(dims(ssd, batch=3, seqlen=300, d_state=64)), 128) == 0
+    assert ws(None, 128) == 0
+
+
 def test_conv_validation(ssd, lib):
     E = {n: i for i, n in enumerate(ssd.STATUS)}
     d = dims(ssd)  # CD = 4*64 + 2*2*128 = 768
