@@ -1463,9 +1463,39 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanArgs a, WsV
     else run_x<1, CONV>(sm, a, cx, lane);
 }
 
+// A single sequence longer than kSegRows tokens is scanned in segments of kSegRows, chained through an fp32
+// state in the workspace: one segment's pre-pass tiles (210 MB at 8 groups, 256 heads) stay in the
+// last-level cache for the scan that reads them, where the whole sequence's would not (measured on the
+// 262144-token layer: 6.6 ms in one pass, 5.9 ms in 32768-token segments, the same y and final state).
+constexpr int64_t kSegRows = 32768;
+// byte offset of the state between segments in the workspace: after one segment's tiles, dt rows and scales
+inline int64_t seg_state_off(int64_t nheads, int64_t ngroups) {
+    return (ws_bytes(ngroups * (kSegRows / Q), nheads * (kSegRows / Q)) + 15) / 16 * 16;
+}
+
 template <typename TY, bool CONV, bool LP>
 static hipError_t launch_t(const ScanArgs& a, void* workspace, const ConvIn& cv, hipStream_t s) {
     if (a.batch * a.nheads == 0) return hipSuccess;
+    if constexpr (!CONV && !LP) {
+        if (a.batch == 1 && !a.seq.cu_seqlens && a.seqlen > kSegRows) {
+            float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                                  seg_state_off(a.nheads, a.ngroups));
+            for (int64_t r0 = 0; r0 < a.seqlen; r0 += kSegRows) {
+                ScanArgs g = a;
+                g.seqlen = a.seqlen - r0 < kSegRows ? a.seqlen - r0 : kSegRows;
+                g.x = static_cast<const bf16*>(a.x) + r0 * a.x_row_stride;
+                g.B = static_cast<const bf16*>(a.B) + r0 * a.bc_row_stride;
+                g.C = static_cast<const bf16*>(a.C) + r0 * a.bc_row_stride;
+                g.dt = static_cast<const bf16*>(a.dt) + r0 * a.nheads;
+                g.y = static_cast<TY*>(a.y) + r0 * a.nheads * static_cast<int64_t>(P);
+                g.init_state = r0 == 0 ? a.init_state : mid;
+                g.final_state = r0 + g.seqlen >= a.seqlen ? a.final_state : mid;
+                const hipError_t e = launch_t<TY, CONV, LP>(g, workspace, cv, s);   // one segment each
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
+    }
     // chunks per (batch entry, group), or packed: chunk slots per group (one workspace layout, [G][slot])
     const bool packed = a.seq.cu_seqlens != nullptr;
     const int64_t nc = packed ? packed_slots(a.batch, a.seqlen) : (a.seqlen + Q - 1) / Q;
@@ -1504,6 +1534,12 @@ size_t f16_scan_varlen_workspace_bytes(int64_t nseq, int64_t rows, int nheads, i
 
 size_t f16_scan_workspace_bytes(int64_t batch, int64_t seqlen, int nheads, int ngroups) {
     const int64_t nc = (seqlen + scan16::Q - 1) / scan16::Q;
+    if (batch == 1 && seqlen > scan16::kSegRows) {   // at least one segment's tiles and the state between segments
+        const int64_t whole = scan16::ws_bytes(ngroups * nc, nheads * nc);
+        const int64_t seg = scan16::seg_state_off(nheads, ngroups) +
+                            static_cast<int64_t>(nheads) * scan16::P * scan16::NS * static_cast<int64_t>(sizeof(float));
+        return static_cast<size_t>(whole > seg ? whole : seg);
+    }
     return static_cast<size_t>(scan16::ws_bytes(batch * ngroups * nc, batch * nheads * nc));
 }
 

@@ -202,6 +202,35 @@ def test_scan_f16_dt_read_as_rows(orc, H, G, L, prologue):
         assert_close(fin, fr, BF16_BAR, f"final state (dt shifted: {shift})")
 
 
+@pytest.mark.parametrize("L", [32768 + 300, 2 * 32768])
+def test_scan_f16_long_sequence_in_segments(orc, L):
+    """A single sequence longer than 32768 tokens is scanned in 32768-token segments chained through an fp32
+    state in the workspace (a ragged last segment; an initial state updated in place): against the oracle on
+    two heads of different groups, and y and the final state equal to the same scan run as two calls."""
+    d = LayerDims(1, L, 8, 64, 2, 128)
+    s = cuda(scan_inputs(d, 70 + L % 7, slow=True))
+    st = s["init_state"].clone()
+    y = ssd.ssd_chunk_scan(s["x"], s["Bm"], s["Cm"], s["dt"], s["A"], s["D"], st, st, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for h in (1, 6):
+        g = h // 4
+        yr, fr = orc.scan(f64(s["x"][:, :, h:h + 1]), f64(s["Bm"][:, :, g:g + 1]), f64(s["Cm"][:, :, g:g + 1]),
+                          f64(s["dt"][:, :, h:h + 1]), f64(s["A"][h:h + 1]), f64(s["D"][h:h + 1]),
+                          f64(s["init_state"][:, h:h + 1]))
+        assert_close(y[:, :, h:h + 1], yr, BF16_BAR, f"y head {h}")
+        assert_close(st[:, h:h + 1], fr, BF16_BAR, f"final state head {h}")
+    # the same in two calls at the segment boundary (each at most one segment): bitwise equal
+    mid = torch.empty_like(st)
+    k = 32768
+    y1 = ssd.ssd_chunk_scan(s["x"][:, :k], s["Bm"][:, :k], s["Cm"][:, :k], s["dt"][:, :k], s["A"], s["D"],
+                            s["init_state"], mid, y_dtype=torch.float32)
+    st2 = torch.empty_like(st)
+    y2 = ssd.ssd_chunk_scan(s["x"][:, k:], s["Bm"][:, k:], s["Cm"][:, k:], s["dt"][:, k:], s["A"], s["D"],
+                            mid, st2, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], 1), y) and torch.equal(st2, st)
+
+
 @pytest.mark.parametrize("ws", [pytest.param(None, id="f16"), pytest.param(False, id="split")])
 def test_scan_bf16_output_is_rounded_fp32_output(ws):
     d = LayerDims(2, 300, 4, 64, 2, 128)
